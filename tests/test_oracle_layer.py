@@ -1,0 +1,162 @@
+"""Pins of the oracle layer and stack with constructed weights.
+
+Zero matrices (Q8_0 blocks with d = 0), identity and selection matrices
+(Q8_0, d = 1, q = 1 on chosen entries) turn the layer into closed forms that
+expose the residual wiring, the GQA head mapping, the inclusion of the new
+token in attention, the f16 rounding of the cache and the SwiGLU order.
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+import synth
+from synth import workloads as wl
+from tests import blocks
+
+ONE = blocks.f16_bits(1.0)
+
+
+def q8_matrix(rows, cols, entries=(), d_bits=ONE):
+    """Q8_0 matrix with q = 1 at the (r, c) entries and 0 elsewhere (d = 0 => zero matrix)."""
+    q = np.zeros((rows, cols), np.int64)
+    for r, c in entries:
+        q[r, c] = 1
+    out = bytearray()
+    for r in range(rows):
+        for b in range(cols // 32):
+            out += blocks.enc_q8_0(d_bits, q[r, 32 * b:32 * b + 32])
+    return np.frombuffer(bytes(out), np.uint8).copy()
+
+
+def make_layer(shape, mats, max_ctx, n_past, wid=wl.W_TEST, layer=0):
+    li = wl.gen_layer(shape, wl.ALL_Q8_0, wid, layer, max_ctx, n_past, weights=False)
+    li.mats = {m: mats[m] for m in wl.MATS}
+    return li
+
+
+SHP = wl.LayerShape(hidden=64, n_head=4, n_kv_head=2, head_dim=16, ffn=64, rope_theta=1e4)
+
+
+def zero_mats(shape):
+    return {m: q8_matrix(*shape.mat_shape(m), d_bits=0) for m in wl.MATS}
+
+
+def test_zero_weights_is_identity_and_appends_zero_kv():
+    li = make_layer(SHP, zero_mats(SHP), 16, 5)
+    x = wl.gen_x(SHP.hidden, wl.W_TEST, 1)
+    out = oracle.layer(li, x, pos=5)
+    assert np.array_equal(out[0], x.astype(np.float64))
+    # zero values (a rotation of +0 may give -0)
+    assert not li.k_cache[:, 5].view(np.float16).any() and not li.v_cache[:, 5].view(np.float16).any()
+
+
+def test_attention_path_gqa_mapping_and_residual():
+    # Wq = Wk = 0 => every score is 0 => o_h = mean of V[g(h)] over 0..pos (new entry included);
+    # Wv passes xn[0:32] into the two kv heads; Wo = I; FFN zero => out = x + o.
+    mats = zero_mats(SHP)
+    mats["wv"] = q8_matrix(32, 64, [(i, i) for i in range(32)])
+    mats["wo"] = q8_matrix(64, 64, [(i, i) for i in range(64)])
+    pos = 6
+    li = make_layer(SHP, mats, 12, pos)
+    x = wl.gen_x(SHP.hidden, wl.W_TEST, 2)
+    vc_before = li.v_cache.copy()
+    out = oracle.layer(li, x, pos=pos)[0]
+    xn = oracle.rmsnorm(x, li.attn_norm, SHP.rms_eps)
+    new_v = xn[:32].astype(np.float16).view(np.uint16).reshape(2, 16)
+    assert np.array_equal(li.v_cache[:, pos], new_v)
+    vf = vc_before.view(np.float16).astype(np.float64)
+    vf[:, pos] = new_v.view(np.float16)
+    o = np.concatenate([vf[h // 2, :pos + 1].mean(axis=0) for h in range(4)])
+    assert np.allclose(out, x.astype(np.float64) + o, rtol=1e-13, atol=1e-13)
+
+
+def test_rope_applied_to_cached_key():
+    mats = zero_mats(SHP)
+    mats["wk"] = q8_matrix(32, 64, [(i, i + 5) for i in range(32)])
+    pos = 9
+    li = make_layer(SHP, mats, 12, pos)
+    x = wl.gen_x(SHP.hidden, wl.W_TEST, 3)
+    oracle.layer(li, x, pos=pos)
+    xn = oracle.rmsnorm(x, li.attn_norm, SHP.rms_eps)
+    k = oracle.rope(xn[5:37], 2, 16, pos, SHP.rope_theta)
+    assert np.array_equal(li.k_cache[:, pos], k.astype(np.float16).view(np.uint16).reshape(2, 16))
+
+
+def test_ffn_path_swiglu_closed_form():
+    mats = zero_mats(SHP)
+    eye = [(i, i) for i in range(64)]
+    mats["wg"] = q8_matrix(64, 64, eye)
+    mats["wu"] = q8_matrix(64, 64, eye)
+    mats["wd"] = q8_matrix(64, 64, eye)
+    li = make_layer(SHP, mats, 8, 3)
+    x = wl.gen_x(SHP.hidden, wl.W_TEST, 4) * 3.0
+    out = oracle.layer(li, x, pos=3)[0]
+    hn = oracle.rmsnorm(x, li.ffn_norm, SHP.rms_eps)
+    assert np.allclose(out, x.astype(np.float64) + hn * expit(hn) * hn, rtol=1e-13)
+
+
+def test_gate_and_up_are_not_swapped():
+    # gate = 2 * xn, up = xn  =>  a = silu(2 xn) * xn  (swapping gives silu(xn) * 2 xn)
+    mats = zero_mats(SHP)
+    mats["wg"] = q8_matrix(64, 64, [(i, i) for i in range(64)], d_bits=blocks.f16_bits(2.0))
+    mats["wu"] = q8_matrix(64, 64, [(i, i) for i in range(64)])
+    mats["wd"] = q8_matrix(64, 64, [(i, i) for i in range(64)])
+    li = make_layer(SHP, mats, 8, 3)
+    x = wl.gen_x(SHP.hidden, wl.W_TEST, 5)
+    out = oracle.layer(li, x, pos=3)[0]
+    hn = oracle.rmsnorm(x, li.ffn_norm, SHP.rms_eps)
+    assert np.allclose(out - x, 2 * hn * expit(2 * hn) * hn, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("fmts", [wl.ALL_Q4_0, wl.Q4_K_M])
+def test_batched_tokens_equal_sequential(fmts):
+    # verify pass over M tokens == M single-token passes at increasing positions
+    shp = wl.TINY
+    M, pos = 3, 7
+    li_a = wl.gen_layer(shp, fmts, wl.W_TEST, 11, 16, pos)
+    li_b = wl.gen_layer(shp, fmts, wl.W_TEST, 11, 16, pos)
+    x = np.stack([wl.gen_x(shp.hidden, wl.W_TEST, 20 + i) for i in range(M)])
+    out_a = oracle.layer(li_a, x, pos=pos, M=M)
+    out_b = np.stack([oracle.layer(li_b, x[i], pos=pos + i)[0] for i in range(M)])
+    assert np.array_equal(out_a, out_b)
+    assert np.array_equal(li_a.k_cache, li_b.k_cache) and np.array_equal(li_a.v_cache, li_b.v_cache)
+
+
+def test_stack_with_zero_layers_follows_lm_head_permutation():
+    shp = SHP
+    vocab = shp.hidden
+    layers = [make_layer(shp, zero_mats(shp), 8, 2, layer=l) for l in range(2)]
+    emb = q8_matrix(vocab, shp.hidden, [(i, i) for i in range(vocab)])
+    perm = np.random.default_rng(9).permutation(vocab)
+    lm = q8_matrix(vocab, shp.hidden, [(int(perm[i]), i) for i in range(vocab)])
+    g = wl.gen_gains(shp, wl.W_TEST, 0, wl.T_OUT_NORM)
+    m = oracle.OracleModel(shp, layers, oracle.Q8_0, emb, oracle.Q8_0, lm, g, vocab)
+    for t in [0, 5, 63]:
+        nxt, margin, _, hidden = m.decode([t], pos=2, want_hidden=True)
+        assert nxt[0] == perm[t]
+        assert margin[0] > 0
+        assert np.array_equal(hidden[0], np.eye(vocab)[t])
+
+
+def test_stack_verify_equals_sequential_decode():
+    shp = wl.TINY
+    vocab = 96
+    M, pos = 4, 5
+
+    def model():
+        layers = [wl.gen_layer(shp, wl.Q4_K_M, wl.W_TEST, 30 + l, 16, pos) for l in range(2)]
+        emb = wl.gen_matrix(oracle.Q6_K, vocab, shp.hidden, wl.W_TEST, 0, wl.T_TOK_EMB)
+        lm = wl.gen_matrix(oracle.Q6_K, vocab, shp.hidden, wl.W_TEST, 0, wl.T_LM_HEAD)
+        g = wl.gen_gains(shp, wl.W_TEST, 0, wl.T_OUT_NORM)
+        return oracle.OracleModel(shp, layers, oracle.Q6_K, emb, oracle.Q6_K, lm, g, vocab)
+
+    toks = wl.gen_tokens(wl.W_TEST, M, vocab)
+    a, _, la, _ = model().decode(toks, pos, want_logits=True)
+    mb = model()
+    for i in range(M):
+        b, _, lb, _ = mb.decode(toks[i:i + 1], pos + i, want_logits=True)
+        assert b[0] == a[i]
+        assert np.array_equal(lb[0], la[i])
