@@ -1,0 +1,194 @@
+/*
+ * nt.h -- C ABI of libnt, a gfx950 (MI355X) library for batch-1 decode of a
+ * Llama decoder whose projections are block-quantized GGUF tensors.
+ *
+ * What the library computes comes from the ntransformer pages:
+ *   p1  = "Ntransformer" (unwiki summary page)
+ *   p2  = "ntransformer - moteur d'inference NVMe-to-GPU ..." (GeekNews FR)
+ * The pages list the weight formats (p1 "About"; p2 "Presentation de
+ * NTransformer"), the Llama pieces RoPE, GQA, SwiGLU, RMSNorm and the KV cache
+ * (p1 feature list; p2 "Fonctionnalites principales"), the per-token kernels
+ * GEMV, RMSNorm, RoPE, SwiGLU and softmax plus a sampler (p2 "Architecture et
+ * structure du code"), the F16 KV cache (p1 roadmap phase 3), self-speculative
+ * decoding (p1 feature list) and the double-buffered layer streaming (p1
+ * "SLEP streaming"; p2 "Streaming direct NVMe").  A public C API is only
+ * planned there (p1 roadmap phase 5); the calls below are this library's.
+ *
+ * Conventions for every call:
+ *  - Ownership: the caller allocates and owns every buffer (device memory for
+ *    weights, activations, caches and workspace; pinned host memory for
+ *    streamed layers).  The library never allocates, frees or synchronizes.
+ *  - Streams: `stream` / `copy_stream` are hipStream_t values passed as void*.
+ *    NULL means the default stream.  Every call only enqueues work.
+ *  - Errors: arguments are validated before anything is enqueued; a negative
+ *    nt_status is returned and nothing runs.  A failed launch returns
+ *    NT_EHIP.  Faults inside kernels surface at the caller's next sync.
+ *  - Alignment: weight matrices, activation vectors and workspaces must be
+ *    16-byte aligned (NT_EALIGN otherwise).
+ *  - Calls are re-entrant; concurrent calls on different streams must not
+ *    share output, cache or workspace buffers.
+ */
+#ifndef NT_H
+#define NT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nt_status {
+  NT_OK = 0,
+  NT_EINVAL = -1,       /* bad argument: unknown format, bad size, NULL pointer */
+  NT_EALIGN = -2,       /* a pointer is not 16-byte aligned                     */
+  NT_EWORKSPACE = -3,   /* workspace smaller than the *_workspace_bytes query   */
+  NT_EHIP = -4,         /* a HIP launch or copy failed                          */
+  NT_EUNSUPPORTED = -5  /* shape outside what the kernels handle (see limits)   */
+} nt_status;
+
+/* GGUF block formats (p1 "About" format list).  Byte layouts:
+ *   NT_Q8_0  34 B / 32 weights : f16 d, int8 q[32];          w = d*q
+ *   NT_Q4_0  18 B / 32 weights : f16 d, u8 qs[16];           w = d*(q-8),
+ *            q of element j<16 = low nibble of qs[j], of j+16 = high nibble.
+ *   NT_Q4_K 144 B / 256 weights: f16 d, f16 dmin, u8 scales[12], u8 qs[128];
+ *            8 sub-blocks of 32 with 6-bit scale sc and min m (GGUF packing),
+ *            w = d*sc*q - dmin*m; chunk c (64 weights) uses qs[32c..32c+31],
+ *            low nibbles first 32 weights, high nibbles next 32.
+ *   NT_Q6_K 210 B / 256 weights: u8 ql[128], u8 qh[64], int8 sc[16], f16 d;
+ *            w_e = d*sc[e/16]*(q_e-32), q_e 6-bit from ql nibble + qh 2 bits
+ *            (GGUF order).
+ * A matrix is `rows` consecutive rows, each cols/QK consecutive blocks. */
+typedef enum nt_fmt { NT_Q8_0 = 0, NT_Q4_0 = 1, NT_Q4_K = 2, NT_Q6_K = 3 } nt_fmt;
+
+/* Weights per block (32 or 256), 0 for an unknown format. */
+int nt_block_elems(int fmt);
+/* Bytes per block (34, 18, 144, 210), 0 for an unknown format. */
+int nt_block_bytes(int fmt);
+/* Bytes of one row of `cols` weights; 0 if fmt is unknown or cols % QK != 0. */
+int64_t nt_row_bytes(int fmt, int64_t cols);
+/* Static text for a status code. */
+const char* nt_status_str(int status);
+/* Largest `cols` a GEMV accepts (the activation vector is staged on chip). */
+int64_t nt_max_cols(void);
+
+/*
+ * y = W x (GEMV on quantized weights; p2 "Architecture et structure du code").
+ *   W: device, fmt blocks, rows x cols, 16-byte aligned.
+ *   x: device fp32 [cols], 16-byte aligned.   y: device fp32 [rows], overwritten.
+ *   cols must be a positive multiple of the format's QK and <= nt_max_cols().
+ *   rows == 0 is a no-op.  Inside the kernel x is held as 16-bit fixed point
+ *   per 32-element block (relative error of y about 1e-5).
+ */
+int nt_gemv_q(int fmt, const void* W, const float* x, float* y, int64_t rows, int64_t cols, void* stream);
+
+/*
+ * Y[m] = W X[m] for M tokens at once (the verify pass of self-speculative
+ * decoding runs M drafted tokens through every projection; p1 feature list).
+ *   X: device fp32 [M][cols]; Y: device fp32 [M][rows]; 1 <= M <= 8.
+ *   Weights are read once for all M tokens.
+ */
+int nt_gemm_q_small(int fmt, const void* W, const float* X, float* Y, int M, int64_t rows, int64_t cols,
+                    void* stream);
+
+/* Shape of one Llama decoder layer. */
+typedef struct nt_layer_cfg {
+  int32_t hidden;     /* model width                                   */
+  int32_t n_head;     /* query heads                                   */
+  int32_t n_kv_head;  /* key/value heads (GQA: n_head % n_kv_head == 0) */
+  int32_t head_dim;   /* even, <= 256                                  */
+  int32_t ffn;        /* SwiGLU inner width                            */
+  int32_t max_ctx;    /* capacity of the KV cache in positions         */
+  float rope_theta;   /* RoPE base                                     */
+  float rms_eps;      /* RMSNorm epsilon                               */
+} nt_layer_cfg;
+
+/* A quantized matrix: format and device pointer to its blocks. */
+typedef struct nt_qmat {
+  int32_t fmt;
+  const void* data;
+} nt_qmat;
+
+/* Device pointers of one layer.  Matrix shapes (rows x cols):
+ *   wq [n_head*head_dim x hidden], wk/wv [n_kv_head*head_dim x hidden],
+ *   wo [hidden x n_head*head_dim], wg/wu [ffn x hidden], wd [hidden x ffn].
+ * k_cache / v_cache: f16 bits [n_kv_head][max_ctx][head_dim]. */
+typedef struct nt_layer {
+  const float* attn_norm; /* RMSNorm gains before attention [hidden] */
+  const float* ffn_norm;  /* RMSNorm gains before the FFN   [hidden] */
+  nt_qmat wq, wk, wv, wo, wg, wu, wd;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+} nt_layer;
+
+/* Workspace bytes nt_decode_layer needs for M tokens (0 on bad cfg). */
+size_t nt_layer_workspace_bytes(const nt_layer_cfg* cfg, int M);
+
+/*
+ * One pre-norm Llama decoder layer for M tokens at positions pos..pos+M-1
+ * (p1 feature list: RoPE, GQA, SwiGLU, RMSNorm, KV cache):
+ *   xn = RMSNorm(x, attn_norm); q,k,v = Wq xn, Wk xn, Wv xn; RoPE(q, k);
+ *   K,V[pos+i] = f16(k_i), f16(v_i); token i attends to 0..pos+i;
+ *   h = x + Wo o;  x <- h + Wd (silu(Wg hn) * Wu hn),  hn = RMSNorm(h, ffn_norm).
+ *   cfg/layer: host structs (copied at the call); layer's pointers are device.
+ *   x: device fp32 [M][hidden], updated in place.
+ *   pos_dev: device int32 holding pos (read by the kernels, so a captured
+ *            graph can be replayed with a new position); if pos < 0 or
+ *            pos + M > max_ctx the kernels skip the cache write and attention.
+ *   ws: device workspace of ws_bytes >= nt_layer_workspace_bytes(cfg, M).
+ * The call does not advance pos.
+ */
+int nt_decode_layer(const nt_layer_cfg* cfg, const nt_layer* layer, float* x, int M, const int32_t* pos_dev,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* A whole decoder stack. */
+typedef struct nt_model {
+  nt_layer_cfg cfg;
+  int32_t n_layer;
+  int32_t vocab;
+  nt_qmat tok_emb;          /* [vocab x hidden] embedding rows             */
+  nt_qmat lm_head;          /* [vocab x hidden]                            */
+  const float* out_norm;    /* final RMSNorm gains [hidden]                */
+  const nt_layer* layers;   /* host array of n_layer layers                */
+  /* Layer streaming (p1 "SLEP streaming"): layers >= first_streamed keep
+   * their seven matrices in pinned host memory and are copied, one layer at
+   * a time, into two device staging buffers on copy_stream while the
+   * previous layer computes.  first_streamed == n_layer disables it. */
+  int32_t first_streamed;
+  const void* const* host_layer; /* [n_layer] pinned blob of layer i's matrices
+                                    (wq,wk,wv,wo,wg,wu,wd back to back, each
+                                    padded to 256 B), used for i >= first_streamed */
+  void* stage[2];                /* device staging buffers                   */
+  size_t stage_bytes;            /* bytes of each staging buffer             */
+  void* copy_stream;             /* hipStream_t for the copies               */
+} nt_model;
+
+/* Workspace bytes nt_decode_step / nt_verify_step need for M tokens. */
+size_t nt_step_workspace_bytes(const nt_model* model, int M);
+
+/* Bytes of a streamed layer blob (the sum of its seven padded matrices). */
+size_t nt_layer_blob_bytes(const nt_layer_cfg* cfg, const nt_layer* fmts_only);
+
+/*
+ * One greedy decode step: embedding row of *token_dev -> n_layer layers at
+ * *pos_dev -> final RMSNorm -> LM head -> argmax (lowest index on ties)
+ * written to *next_token_dev.  logits_dev (fp32 [vocab]) may be NULL.
+ * Token and position live on the device so the step can be captured in a
+ * graph and replayed.
+ */
+int nt_decode_step(const nt_model* model, const int32_t* token_dev, const int32_t* pos_dev,
+                   int32_t* next_token_dev, float* logits_dev, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Verify pass of self-speculative decoding: M (1..8) tokens at positions
+ * pos..pos+M-1 through the whole stack in one pass; argmax_dev[i] is the
+ * greedy token after token i.  logits_dev (fp32 [M][vocab]) may be NULL.
+ */
+int nt_verify_step(const nt_model* model, const int32_t* tokens_dev, int M, const int32_t* pos_dev,
+                   int32_t* argmax_dev, float* logits_dev, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NT_H */

@@ -1,0 +1,134 @@
+"""Python binding of libnt (the gfx950 quantized decode library).
+
+Argument marshalling only: every step runs in the HIP kernels of libnt.so,
+called through its C ABI (include/nt.h).  PyTorch provides device memory and
+streams.  There is no fallback: if libnt.so is missing or cannot be loaded,
+importing the functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libnt.so")
+
+NT_Q8_0, NT_Q4_0, NT_Q4_K, NT_Q6_K = 0, 1, 2, 3
+STATUS = {0: "NT_OK", -1: "NT_EINVAL", -2: "NT_EALIGN", -3: "NT_EWORKSPACE", -4: "NT_EHIP", -5: "NT_EUNSUPPORTED"}
+
+
+class NtError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+        self.status = status
+
+
+class LayerCfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_head", ctypes.c_int32), ("n_kv_head", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+
+
+class QMat(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("data", ctypes.c_void_p)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("attn_norm", ctypes.c_void_p), ("ffn_norm", ctypes.c_void_p),
+                ("wq", QMat), ("wk", QMat), ("wv", QMat), ("wo", QMat), ("wg", QMat), ("wu", QMat), ("wd", QMat),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p)]
+
+
+class Model(ctypes.Structure):
+    _fields_ = [("cfg", LayerCfg), ("n_layer", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("tok_emb", QMat), ("lm_head", QMat), ("out_norm", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(Layer)), ("first_streamed", ctypes.c_int32),
+                ("host_layer", ctypes.POINTER(ctypes.c_void_p)), ("stage", ctypes.c_void_p * 2),
+                ("stage_bytes", ctypes.c_size_t), ("copy_stream", ctypes.c_void_p)]
+
+
+_lib = None
+
+EXPORTS = {
+    # name: (restype, argtypes)
+    "nt_block_elems": (ctypes.c_int, [ctypes.c_int]),
+    "nt_block_bytes": (ctypes.c_int, [ctypes.c_int]),
+    "nt_row_bytes": (ctypes.c_int64, [ctypes.c_int, ctypes.c_int64]),
+    "nt_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "nt_max_cols": (ctypes.c_int64, []),
+    "nt_gemv_q": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
+    "nt_gemm_q_small": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
+    "nt_layer_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(LayerCfg), ctypes.c_int]),
+    "nt_decode_layer": (ctypes.c_int, [ctypes.POINTER(LayerCfg), ctypes.POINTER(Layer), ctypes.c_void_p,
+                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]),
+    "nt_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Model), ctypes.c_int]),
+    "nt_layer_blob_bytes": (ctypes.c_size_t, [ctypes.POINTER(LayerCfg), ctypes.POINTER(Layer)]),
+    "nt_decode_step": (ctypes.c_int, [ctypes.POINTER(Model), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "nt_verify_step": (ctypes.c_int, [ctypes.POINTER(Model), ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p]),
+}
+
+
+def lib():
+    """Load libnt.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run quantized_decode_dequant_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise NtError(fn, rc)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def block_elems(fmt: int) -> int:
+    return lib().nt_block_elems(fmt)
+
+
+def block_bytes(fmt: int) -> int:
+    return lib().nt_block_bytes(fmt)
+
+
+def row_bytes(fmt: int, cols: int) -> int:
+    return lib().nt_row_bytes(fmt, cols)
+
+
+def gemv_q(fmt: int, W, x, y, rows: int, cols: int, stream=None) -> None:
+    """y = W x  (nt_gemv_q)."""
+    _check("nt_gemv_q", lib().nt_gemv_q(fmt, _ptr(W), _ptr(x), _ptr(y), rows, cols, _stream(stream)))
+
+
+def gemm_q_small(fmt: int, W, X, Y, M: int, rows: int, cols: int, stream=None) -> None:
+    """Y[m] = W X[m] for M <= 8 tokens  (nt_gemm_q_small)."""
+    _check("nt_gemm_q_small",
+           lib().nt_gemm_q_small(fmt, _ptr(W), _ptr(X), _ptr(Y), M, rows, cols, _stream(stream)))
