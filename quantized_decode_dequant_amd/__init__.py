@@ -132,3 +132,93 @@ def gemm_q_small(fmt: int, W, X, Y, M: int, rows: int, cols: int, stream=None) -
     """Y[m] = W X[m] for M <= 8 tokens  (nt_gemm_q_small)."""
     _check("nt_gemm_q_small",
            lib().nt_gemm_q_small(fmt, _ptr(W), _ptr(X), _ptr(Y), M, rows, cols, _stream(stream)))
+
+
+def layer_cfg(hidden, n_head, n_kv_head, head_dim, ffn, max_ctx, rope_theta=5e5, rms_eps=1e-5) -> LayerCfg:
+    return LayerCfg(hidden, n_head, n_kv_head, head_dim, ffn, max_ctx, rope_theta, rms_eps)
+
+
+MAT_NAMES = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
+
+
+def make_layer(attn_norm, ffn_norm, mats: dict, fmts: dict, k_cache, v_cache) -> Layer:
+    """nt_layer over device tensors (mats: name -> uint8 tensor, fmts: name -> format id)."""
+    L = Layer()
+    L.attn_norm = _ptr(attn_norm)
+    L.ffn_norm = _ptr(ffn_norm)
+    for n in MAT_NAMES:
+        setattr(L, n, QMat(fmts[n], _ptr(mats[n]) if mats.get(n) is not None else None))
+    L.k_cache = _ptr(k_cache)
+    L.v_cache = _ptr(v_cache)
+    return L
+
+
+def layer_workspace_bytes(cfg: LayerCfg, M: int = 1) -> int:
+    return lib().nt_layer_workspace_bytes(ctypes.byref(cfg), M)
+
+
+def decode_layer(cfg: LayerCfg, layer: Layer, x, M: int, pos_dev, ws, stream=None) -> None:
+    """One decoder layer on x ([M][hidden] fp32, in place)  (nt_decode_layer)."""
+    _check("nt_decode_layer", lib().nt_decode_layer(ctypes.byref(cfg), ctypes.byref(layer), _ptr(x), M,
+                                                    _ptr(pos_dev), _ptr(ws), ws.numel() * ws.element_size(),
+                                                    _stream(stream)))
+
+
+def layer_blob_bytes(cfg: LayerCfg, layer: Layer) -> int:
+    return lib().nt_layer_blob_bytes(ctypes.byref(cfg), ctypes.byref(layer))
+
+
+def blob_offsets(cfg: LayerCfg, fmts: dict, shapes: dict) -> list:
+    """Byte offsets of the seven matrices inside a streamed-layer blob (each padded to 256 B)."""
+    offs, o = [], 0
+    for n in MAT_NAMES:
+        offs.append(o)
+        r, c = shapes[n]
+        o += (r * (c // block_elems(fmts[n])) * block_bytes(fmts[n]) + 255) // 256 * 256
+    offs.append(o)
+    return offs
+
+
+class ModelHandle:
+    """Keeps an nt_model and the ctypes arrays it points to alive."""
+
+    def __init__(self, cfg: LayerCfg, layers: list, vocab: int, tok_emb, tok_emb_fmt: int, lm_head, lm_head_fmt: int,
+                 out_norm, first_streamed: int | None = None, host_layers=None, stage=(None, None),
+                 stage_bytes: int = 0, copy_stream=None):
+        self.layers_arr = (Layer * max(1, len(layers)))(*layers)
+        n = len(layers)
+        self.first_streamed = n if first_streamed is None else first_streamed
+        self.host_arr = (ctypes.c_void_p * max(1, n))()
+        if host_layers is not None:
+            for i, h in enumerate(host_layers):
+                self.host_arr[i] = _ptr(h) if h is not None else None
+        m = Model()
+        m.cfg = cfg
+        m.n_layer = n
+        m.vocab = vocab
+        m.tok_emb = QMat(tok_emb_fmt, _ptr(tok_emb))
+        m.lm_head = QMat(lm_head_fmt, _ptr(lm_head))
+        m.out_norm = _ptr(out_norm)
+        m.layers = ctypes.cast(self.layers_arr, ctypes.POINTER(Layer))
+        m.first_streamed = self.first_streamed
+        m.host_layer = ctypes.cast(self.host_arr, ctypes.POINTER(ctypes.c_void_p))
+        m.stage[0] = _ptr(stage[0])
+        m.stage[1] = _ptr(stage[1])
+        m.stage_bytes = stage_bytes
+        m.copy_stream = _stream(copy_stream) if copy_stream is not None else None
+        self.m = m
+
+    def workspace_bytes(self, M: int = 1) -> int:
+        return lib().nt_step_workspace_bytes(ctypes.byref(self.m), M)
+
+    def decode_step(self, token_dev, pos_dev, next_dev, ws, logits_dev=None, stream=None) -> None:
+        """nt_decode_step."""
+        _check("nt_decode_step", lib().nt_decode_step(ctypes.byref(self.m), _ptr(token_dev), _ptr(pos_dev),
+                                                      _ptr(next_dev), _ptr(logits_dev), _ptr(ws),
+                                                      ws.numel() * ws.element_size(), _stream(stream)))
+
+    def verify_step(self, tokens_dev, M: int, pos_dev, argmax_dev, ws, logits_dev=None, stream=None) -> None:
+        """nt_verify_step."""
+        _check("nt_verify_step", lib().nt_verify_step(ctypes.byref(self.m), _ptr(tokens_dev), M, _ptr(pos_dev),
+                                                      _ptr(argmax_dev), _ptr(logits_dev), _ptr(ws),
+                                                      ws.numel() * ws.element_size(), _stream(stream)))

@@ -2,6 +2,9 @@
 // launch planning and kernel launches.  No allocation, no synchronization.
 #include <stdint.h>
 
+#include <algorithm>
+#include <mutex>
+
 #include "nt_internal.h"
 
 using namespace nt;
@@ -9,6 +12,302 @@ using namespace nt;
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Workspace of one decode layer for M tokens (offsets from the base).
+struct LayerWs {
+  size_t q, part_o, part_ml, o, a, err, total;
+  int chunk, nsplit;
+};
+
+bool cfg_ok(const nt_layer_cfg& c) {
+  if (c.hidden <= 0 || c.n_head <= 0 || c.n_kv_head <= 0 || c.ffn <= 0 || c.max_ctx <= 0) return false;
+  if (c.n_head % c.n_kv_head != 0 || c.n_head / c.n_kv_head > 8) return false;
+  if (c.head_dim != 32 && c.head_dim != 64 && c.head_dim != 128 && c.head_dim != 256) return false;
+  if (c.hidden % 32 || c.ffn % 32 || (c.n_head * c.head_dim) % 32) return false;
+  if (c.hidden > kMaxCols || c.ffn > kMaxCols || c.n_head * c.head_dim > kMaxCols) return false;
+  if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return false;
+  return true;
+}
+
+LayerWs layer_ws(const nt_layer_cfg& c, int M) {
+  LayerWs w{};
+  attn_plan(c.n_kv_head, c.max_ctx, w.chunk, w.nsplit);
+  const size_t nq = (size_t)c.n_head * c.head_dim;
+  size_t off = 0;
+  w.q = off; off += up256((size_t)M * nq * 4);
+  w.part_o = off; off += up256((size_t)M * w.nsplit * nq * 4);
+  w.part_ml = off; off += up256((size_t)M * w.nsplit * c.n_head * 2 * 4);
+  w.o = off; off += up256((size_t)M * nq * 4);
+  w.a = off; off += up256((size_t)c.ffn * 4);
+  w.err = off; off += 256;
+  w.total = off;
+  return w;
+}
+
+// Does a matrix of this format have the expected shape's column count?
+bool fmt_cols_ok(int fmt, int64_t cols) { return block_elems(fmt) != 0 && cols % block_elems(fmt) == 0; }
+
+int check_layer(const nt_layer_cfg& c, const nt_layer& L) {
+  const int64_t nq = (int64_t)c.n_head * c.head_dim;
+  const nt_qmat* mats[7] = {&L.wq, &L.wk, &L.wv, &L.wo, &L.wg, &L.wu, &L.wd};
+  const int64_t cols[7] = {c.hidden, c.hidden, c.hidden, nq, c.hidden, c.hidden, c.ffn};
+  for (int i = 0; i < 7; ++i) {
+    if (!fmt_cols_ok(mats[i]->fmt, cols[i])) return NT_EINVAL;
+    if (!mats[i]->data) return NT_EINVAL;
+    if (!aligned16(mats[i]->data)) return NT_EALIGN;
+  }
+  if (!L.attn_norm || !L.ffn_norm || !L.k_cache || !L.v_cache) return NT_EINVAL;
+  if (!aligned16(L.attn_norm) || !aligned16(L.ffn_norm)) return NT_EALIGN;
+  return NT_OK;
+}
+
+const uint8_t* u8(const void* p) { return static_cast<const uint8_t*>(p); }
+
+// The launches of one layer (arguments already validated).
+int run_layer(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const int32_t* pos, uint8_t* ws,
+              const LayerWs& w, hipStream_t st) {
+  const int nq = c.n_head * c.head_dim, nkv = c.n_kv_head * c.head_dim;
+  float* q = reinterpret_cast<float*>(ws + w.q);
+  float* part_o = reinterpret_cast<float*>(ws + w.part_o);
+  float* part_ml = reinterpret_cast<float*>(ws + w.part_ml);
+  float* o = reinterpret_cast<float*>(ws + w.o);
+  float* a = reinterpret_cast<float*>(ws + w.a);
+  int* err = reinterpret_cast<int*>(ws + w.err);
+  int rc;
+  // 1. RMSNorm -> Q,K,V projections -> RoPE -> q, K/V append
+  {
+    Job job;
+    const uint8_t* W[3] = {u8(L.wq.data), u8(L.wk.data), u8(L.wv.data)};
+    const int fmt[3] = {L.wq.fmt, L.wk.fmt, L.wv.fmt};
+    const int rows[3] = {nq, nkv, nkv};
+    if ((rc = plan_job(job, 3, W, fmt, rows, c.hidden, 0, 1)) != NT_OK) return rc;
+    for (int i = 0; i < M; ++i) {
+      ProArgs pro{x + (int64_t)i * c.hidden, L.attn_norm, c.rms_eps, 0};
+      EpiArgs ea{};
+      ea.q_out = q + (int64_t)i * nq;
+      ea.k_cache = L.k_cache;
+      ea.v_cache = L.v_cache;
+      ea.pos = pos;
+      ea.err = err;
+      ea.head_dim = c.head_dim;
+      ea.max_ctx = c.max_ctx;
+      ea.rope_theta = c.rope_theta;
+      ea.q_rows = nq;
+      ea.kv_rows = nkv;
+      ea.pos_add = i;
+      if ((rc = launch_gemv(job, pro, EPI_QKV, ea, st)) != NT_OK) return rc;
+    }
+  }
+  // 2. attention over the cache (split over positions) and combine
+  if ((rc = launch_attention(q, L.k_cache, L.v_cache, pos, M, c.n_head, c.n_kv_head, c.head_dim, c.max_ctx, w.chunk,
+                             w.nsplit, part_o, part_ml, o, st)) != NT_OK)
+    return rc;
+  Job jo, jf, jd;
+  {
+    const uint8_t* W[1] = {u8(L.wo.data)};
+    const int fmt[1] = {L.wo.fmt};
+    const int rows[1] = {c.hidden};
+    if ((rc = plan_job(jo, 1, W, fmt, rows, nq, 0, 0)) != NT_OK) return rc;
+  }
+  {
+    const uint8_t* W[2] = {u8(L.wg.data), u8(L.wu.data)};
+    const int fmt[2] = {L.wg.fmt, L.wu.fmt};
+    const int rows[2] = {c.ffn, c.ffn};
+    if ((rc = plan_job(jf, 2, W, fmt, rows, c.hidden, 1, 0)) != NT_OK) return rc;
+  }
+  {
+    const uint8_t* W[1] = {u8(L.wd.data)};
+    const int fmt[1] = {L.wd.fmt};
+    const int rows[1] = {c.hidden};
+    if ((rc = plan_job(jd, 1, W, fmt, rows, c.ffn, 0, 0)) != NT_OK) return rc;
+  }
+  for (int i = 0; i < M; ++i) {
+    float* xi = x + (int64_t)i * c.hidden;
+    // 3. h = x + Wo o
+    {
+      ProArgs pro{o + (int64_t)i * nq, nullptr, 0.f, 0};
+      EpiArgs ea{};
+      ea.y = xi;
+      if ((rc = launch_gemv(jo, pro, EPI_RESID, ea, st)) != NT_OK) return rc;
+    }
+    // 4. a = silu(Wg hn) * (Wu hn), hn = RMSNorm(h)
+    {
+      ProArgs pro{xi, L.ffn_norm, c.rms_eps, 0};
+      EpiArgs ea{};
+      ea.y = a;
+      if ((rc = launch_gemv(jf, pro, EPI_SWIGLU, ea, st)) != NT_OK) return rc;
+    }
+    // 5. x = h + Wd a
+    {
+      ProArgs pro{a, nullptr, 0.f, 0};
+      EpiArgs ea{};
+      ea.y = xi;
+      if ((rc = launch_gemv(jd, pro, EPI_RESID, ea, st)) != NT_OK) return rc;
+    }
+  }
+  return NT_OK;
+}
+
+// ---- decode step
+struct StepWs {
+  size_t x, layer, logits, pv, pi, total;
+  LayerWs lw;
+};
+
+int64_t qmat_bytes(int fmt, int64_t rows, int64_t cols) {
+  const int qk = block_elems(fmt);
+  return qk ? rows * (cols / qk) * block_bytes(fmt) : 0;
+}
+
+// Seven matrices of a streamed layer, back to back, each padded to 256 B.
+void blob_offsets(const nt_layer_cfg& c, const nt_layer& L, size_t (&off)[8]) {
+  const int64_t nq = (int64_t)c.n_head * c.head_dim, nkv = (int64_t)c.n_kv_head * c.head_dim;
+  const nt_qmat* m[7] = {&L.wq, &L.wk, &L.wv, &L.wo, &L.wg, &L.wu, &L.wd};
+  const int64_t rows[7] = {nq, nkv, nkv, c.hidden, c.ffn, c.ffn, c.hidden};
+  const int64_t cols[7] = {c.hidden, c.hidden, c.hidden, nq, c.hidden, c.hidden, c.ffn};
+  size_t o = 0;
+  for (int i = 0; i < 7; ++i) {
+    off[i] = o;
+    o += up256((size_t)qmat_bytes(m[i]->fmt, rows[i], cols[i]));
+  }
+  off[7] = o;
+}
+
+StepWs step_ws(const nt_model& m, int M) {
+  StepWs w{};
+  w.lw = layer_ws(m.cfg, M);
+  size_t off = 0;
+  w.x = off; off += up256((size_t)M * m.cfg.hidden * 4);
+  w.layer = off; off += w.lw.total;
+  w.logits = off; off += up256((size_t)M * m.vocab * 4);
+  w.pv = off; off += up256((size_t)M * 256 * 4);
+  w.pi = off; off += up256((size_t)M * 256 * 4);
+  w.total = off;
+  return w;
+}
+
+// Events of the streaming pipeline, one set per device, made on first use.
+struct StreamEvents {
+  hipEvent_t ready[2] = {nullptr, nullptr};
+  hipEvent_t freed[2] = {nullptr, nullptr};
+  bool init = false;
+};
+
+std::mutex g_ev_mu;
+
+StreamEvents* stream_events() {
+  static StreamEvents ev[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(g_ev_mu);
+  StreamEvents& e = ev[dev & 63];
+  if (!e.init) {
+    for (int i = 0; i < 2; ++i) {
+      if (hipEventCreateWithFlags(&e.ready[i], hipEventDisableTiming) != hipSuccess) return nullptr;
+      if (hipEventCreateWithFlags(&e.freed[i], hipEventDisableTiming) != hipSuccess) return nullptr;
+    }
+    e.init = true;
+  }
+  return &e;
+}
+
+int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos, int32_t* out, float* logits_user,
+             void* ws_v, size_t ws_bytes, hipStream_t st) {
+  if (M < 1 || M > 8) return NT_EINVAL;
+  if (!cfg_ok(m.cfg) || m.n_layer < 0 || m.vocab <= 0 || !tokens || !pos || !out || !ws_v) return NT_EINVAL;
+  if (m.n_layer > 0 && !m.layers) return NT_EINVAL;
+  if (!fmt_cols_ok(m.tok_emb.fmt, m.cfg.hidden) || !fmt_cols_ok(m.lm_head.fmt, m.cfg.hidden)) return NT_EINVAL;
+  if (!m.tok_emb.data || !m.lm_head.data || !m.out_norm) return NT_EINVAL;
+  if (!aligned16(m.lm_head.data) || !aligned16(m.out_norm) || !aligned16(ws_v)) return NT_EALIGN;
+  const int fs = m.first_streamed;
+  if (fs < 0 || fs > m.n_layer) return NT_EINVAL;
+  const bool streaming = fs < m.n_layer;
+  const StepWs w = step_ws(m, M);
+  if (ws_bytes < w.total) return NT_EWORKSPACE;
+  size_t boff[8] = {0};
+  for (int l = 0; l < m.n_layer; ++l) {
+    nt_layer L = m.layers[l];
+    if (l >= fs) {
+      // streamed: matrix pointers come from the staging buffers
+      blob_offsets(m.cfg, L, boff);
+      if (!m.host_layer || !m.host_layer[l] || !m.stage[0] || !m.stage[1]) return NT_EINVAL;
+      if (m.stage_bytes < boff[7]) return NT_EINVAL;
+      if (!aligned16(m.stage[0]) || !aligned16(m.stage[1])) return NT_EALIGN;
+      const nt_qmat* mats[7] = {&L.wq, &L.wk, &L.wv, &L.wo, &L.wg, &L.wu, &L.wd};
+      for (int i = 0; i < 7; ++i) const_cast<nt_qmat*>(mats[i])->data = m.stage[0];
+    }
+    const int rc = check_layer(m.cfg, L);
+    if (rc != NT_OK) return rc;
+  }
+  uint8_t* ws = static_cast<uint8_t*>(ws_v);
+  float* x = reinterpret_cast<float*>(ws + w.x);
+  float* logits = logits_user ? logits_user : reinterpret_cast<float*>(ws + w.logits);
+  int rc = launch_embed(m.tok_emb.fmt, m.tok_emb.data, tokens, M, m.vocab, m.cfg.hidden, x, st);
+  if (rc != NT_OK) return rc;
+  StreamEvents* ev = nullptr;
+  hipStream_t cs = static_cast<hipStream_t>(m.copy_stream);
+  auto issue_copy = [&](int j) -> int {
+    // streamed layer j (0-based among streamed) into stage[j % 2]
+    const int l = fs + j, b = j & 1;
+    nt_layer L = m.layers[l];
+    blob_offsets(m.cfg, L, boff);
+    if (j >= 2 && hipStreamWaitEvent(cs, ev->freed[b], 0) != hipSuccess) return NT_EHIP;
+    if (hipMemcpyAsync(m.stage[b], m.host_layer[l], boff[7], hipMemcpyHostToDevice, cs) != hipSuccess) return NT_EHIP;
+    if (hipEventRecord(ev->ready[b], cs) != hipSuccess) return NT_EHIP;
+    return NT_OK;
+  };
+  const int ns = m.n_layer - fs;
+  if (streaming) {
+    if (!(ev = stream_events())) return NT_EHIP;
+    // the copies may only start once everything queued before this step on
+    // the compute stream (e.g. a previous step still reading the staging
+    // buffers) is done
+    if (hipEventRecord(ev->freed[0], st) != hipSuccess || hipStreamWaitEvent(cs, ev->freed[0], 0) != hipSuccess)
+      return NT_EHIP;
+    for (int j = 0; j < std::min(2, ns); ++j)
+      if ((rc = issue_copy(j)) != NT_OK) return rc;
+  }
+  for (int l = 0; l < m.n_layer; ++l) {
+    nt_layer L = m.layers[l];
+    if (l >= fs) {
+      const int j = l - fs, b = j & 1;
+      blob_offsets(m.cfg, L, boff);
+      uint8_t* base = static_cast<uint8_t*>(m.stage[b]);
+      L.wq.data = base + boff[0];
+      L.wk.data = base + boff[1];
+      L.wv.data = base + boff[2];
+      L.wo.data = base + boff[3];
+      L.wg.data = base + boff[4];
+      L.wu.data = base + boff[5];
+      L.wd.data = base + boff[6];
+      if (hipStreamWaitEvent(st, ev->ready[b], 0) != hipSuccess) return NT_EHIP;
+    }
+    if ((rc = run_layer(m.cfg, L, x, M, pos, ws + w.layer, w.lw, st)) != NT_OK) return rc;
+    if (l >= fs) {
+      const int j = l - fs, b = j & 1;
+      if (hipEventRecord(ev->freed[b], st) != hipSuccess) return NT_EHIP;
+      if (j + 2 < ns && (rc = issue_copy(j + 2)) != NT_OK) return rc;
+    }
+  }
+  // final RMSNorm -> LM head -> argmax
+  Job jl;
+  {
+    const uint8_t* W[1] = {u8(m.lm_head.data)};
+    const int fmt[1] = {m.lm_head.fmt};
+    const int rows[1] = {m.vocab};
+    if ((rc = plan_job(jl, 1, W, fmt, rows, m.cfg.hidden, 0, 0)) != NT_OK) return rc;
+  }
+  for (int i = 0; i < M; ++i) {
+    ProArgs pro{x + (int64_t)i * m.cfg.hidden, m.out_norm, m.cfg.rms_eps, 0};
+    EpiArgs ea{};
+    ea.y = logits + (int64_t)i * m.vocab;
+    if ((rc = launch_gemv(jl, pro, EPI_STORE, ea, st)) != NT_OK) return rc;
+  }
+  return launch_argmax(logits, M, m.vocab, reinterpret_cast<float*>(ws + w.pv), reinterpret_cast<int*>(ws + w.pi), out,
+                       st);
+}
 
 }  // namespace
 
@@ -45,7 +344,7 @@ int nt_gemv_q(int fmt, const void* W, const float* x, float* y, int64_t rows, in
   if (rows == 0) return NT_OK;
   if (!W || !x || !y) return NT_EINVAL;
   if (!aligned16(W) || !aligned16(x)) return NT_EALIGN;
-  TileJob job;
+  Job job;
   const uint8_t* Wp = static_cast<const uint8_t*>(W);
   const int r = (int)rows;
   int rc = plan_job(job, 1, &Wp, &fmt, &r, (int)cols, 0, 0);
@@ -56,21 +355,70 @@ int nt_gemv_q(int fmt, const void* W, const float* x, float* y, int64_t rows, in
   return launch_gemv(job, pro, EPI_STORE, ea, static_cast<hipStream_t>(stream));
 }
 
-}  // extern "C"
+int nt_gemm_q_small(int fmt, const void* W, const float* X, float* Y, int M, int64_t rows, int64_t cols,
+                    void* stream) {
+  if (M < 1 || M > 8) return NT_EINVAL;
+  const int qk = block_elems(fmt);
+  if (qk == 0 || rows < 0 || cols <= 0 || cols % qk != 0) return NT_EINVAL;
+  if (rows > INT32_MAX || cols > kMaxCols) return NT_EUNSUPPORTED;
+  if (rows == 0) return NT_OK;
+  if (!W || !X || !Y) return NT_EINVAL;
+  if (!aligned16(W) || !aligned16(X) || (M > 1 && (cols * 4) % 16 != 0)) return NT_EALIGN;
+  Job job;
+  const uint8_t* Wp = static_cast<const uint8_t*>(W);
+  const int r = (int)rows;
+  int rc = plan_job(job, 1, &Wp, &fmt, &r, (int)cols, 0, 0);
+  if (rc != NT_OK) return rc;
+  for (int m = 0; m < M; ++m) {
+    ProArgs pro{X + (int64_t)m * cols, nullptr, 0.f, 0};
+    EpiArgs ea{};
+    ea.y = Y + (int64_t)m * rows;
+    if ((rc = launch_gemv(job, pro, EPI_STORE, ea, static_cast<hipStream_t>(stream))) != NT_OK) return rc;
+  }
+  return NT_OK;
+}
 
-// ---- entry points not yet implemented in this file (filled in below as they land)
-extern "C" {
-int nt_gemm_q_small(int, const void*, const float*, float*, int, int64_t, int64_t, void*) { return NT_EUNSUPPORTED; }
-size_t nt_layer_workspace_bytes(const nt_layer_cfg*, int) { return 0; }
-int nt_decode_layer(const nt_layer_cfg*, const nt_layer*, float*, int, const int32_t*, void*, size_t, void*) {
-  return NT_EUNSUPPORTED;
+size_t nt_layer_workspace_bytes(const nt_layer_cfg* cfg, int M) {
+  if (!cfg || !cfg_ok(*cfg) || M < 1 || M > 8) return 0;
+  return layer_ws(*cfg, M).total;
 }
-size_t nt_step_workspace_bytes(const nt_model*, int) { return 0; }
-size_t nt_layer_blob_bytes(const nt_layer_cfg*, const nt_layer*) { return 0; }
-int nt_decode_step(const nt_model*, const int32_t*, const int32_t*, int32_t*, float*, void*, size_t, void*) {
-  return NT_EUNSUPPORTED;
+
+int nt_decode_layer(const nt_layer_cfg* cfg, const nt_layer* layer, float* x, int M, const int32_t* pos_dev,
+                    void* ws, size_t ws_bytes, void* stream) {
+  if (!cfg || !layer || !x || !pos_dev || !ws) return NT_EINVAL;
+  if (M < 1 || M > 8 || !cfg_ok(*cfg)) return NT_EINVAL;
+  int rc = check_layer(*cfg, *layer);
+  if (rc != NT_OK) return rc;
+  if (!aligned16(x) || !aligned16(ws)) return NT_EALIGN;
+  const LayerWs w = layer_ws(*cfg, M);
+  if (ws_bytes < w.total) return NT_EWORKSPACE;
+  return run_layer(*cfg, *layer, x, M, pos_dev, static_cast<uint8_t*>(ws), w, static_cast<hipStream_t>(stream));
 }
-int nt_verify_step(const nt_model*, const int32_t*, int, const int32_t*, int32_t*, float*, void*, size_t, void*) {
-  return NT_EUNSUPPORTED;
+
+size_t nt_step_workspace_bytes(const nt_model* model, int M) {
+  if (!model || !cfg_ok(model->cfg) || M < 1 || M > 8 || model->vocab <= 0) return 0;
+  return step_ws(*model, M).total;
 }
+
+size_t nt_layer_blob_bytes(const nt_layer_cfg* cfg, const nt_layer* fmts_only) {
+  if (!cfg || !fmts_only || !cfg_ok(*cfg)) return 0;
+  size_t off[8];
+  blob_offsets(*cfg, *fmts_only, off);
+  return off[7];
 }
+
+int nt_decode_step(const nt_model* model, const int32_t* token_dev, const int32_t* pos_dev, int32_t* next_token_dev,
+                   float* logits_dev, void* ws, size_t ws_bytes, void* stream) {
+  if (!model) return NT_EINVAL;
+  return run_step(*model, token_dev, 1, pos_dev, next_token_dev, logits_dev, ws, ws_bytes,
+                  static_cast<hipStream_t>(stream));
+}
+
+int nt_verify_step(const nt_model* model, const int32_t* tokens_dev, int M, const int32_t* pos_dev,
+                   int32_t* argmax_dev, float* logits_dev, void* ws, size_t ws_bytes, void* stream) {
+  if (!model) return NT_EINVAL;
+  return run_step(*model, tokens_dev, M, pos_dev, argmax_dev, logits_dev, ws, ws_bytes,
+                  static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

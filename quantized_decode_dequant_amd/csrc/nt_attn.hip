@@ -1,0 +1,361 @@
+// nt_attn.hip -- grouped-query decode attention over an f16 KV cache, plus
+// the small kernels of a decode step (embedding row, argmax).
+//
+// Attention (p1 feature list: GQA and KV cache; p2 "Architecture et
+// structure du code": softmax kernel): for query head h of kv group
+// g = h / (n_head / n_kv), scores s_t = q_h . K_g[t] / sqrt(head_dim) over
+// t = 0..n_pos-1, p = softmax(s), o_h = sum_t p_t V_g[t].
+//
+// Split over positions: workgroup (g, s) takes positions [s*chunk,
+// (s+1)*chunk) of kv head g for all query heads of the group, so every K/V
+// byte is read once.  It writes an unnormalised partial (running max m,
+// sum l, sum p*v) per head; attn_combine merges the splits.  Inside a
+// workgroup, LP = head_dim/8 lanes share one position (each lane holds 8
+// dims of K or V as one 16-byte load), so a wave covers 64/LP positions per
+// step with coalesced 16-byte loads straight from HBM; the per-position dot
+// products are finished with a butterfly over the LP lanes.
+
+#include <float.h>
+
+#include <algorithm>
+
+#include "nt_internal.h"
+
+namespace nt {
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int kMaxGroup = 8;  // query heads per kv head
+
+__device__ __forceinline__ void h8_to_f(uint4 v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
+    f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+  }
+}
+
+// q: fp32 [n_query][n_head][HD] (query i at position pos+i attends to
+// 0..pos+i).  Partials: part_o [n_query][nsplit][n_head][HD],
+// part_ml [n_query][nsplit][n_head][2].
+template <int HD>
+__global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __restrict__ q, const uint16_t* __restrict__ kc,
+                                                             const uint16_t* __restrict__ vc, const int32_t* pos_ptr,
+                                                             int query, int n_head, int n_kv, int max_ctx, int chunk,
+                                                             int nsplit, float* __restrict__ part_o,
+                                                             float* __restrict__ part_ml) {
+  constexpr int LP = HD / 8;        // lanes per position
+  constexpr int PPW = 64 / LP;      // positions per wave step
+  constexpr int NW = kAttnThreads / 64;
+  __shared__ float s_sc[kMaxGroup][512 + 1];
+  __shared__ float s_red[NW][kMaxGroup][HD];
+  __shared__ float s_m[kMaxGroup], s_l[kMaxGroup];
+
+  const int g = blockIdx.x, split = blockIdx.y;
+  const int G = n_head / n_kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane % LP, slot = lane / LP;  // dims [8*sub, 8*sub+8) of position slot
+  const int pos = *pos_ptr;
+  const int n_pos = pos + query + 1;
+  const bool ok = pos >= 0 && pos + query < max_ctx;
+  const int t0 = split * chunk;
+  const int t1 = ok ? min(t0 + chunk, n_pos) : t0;
+  const int nt = max(0, t1 - t0);
+
+  // query slices held in registers: 8 dims of each head of the group
+  float qr[kMaxGroup][8];
+  const float scale = 1.0f / sqrtf((float)HD);
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      qr[h][j] = h < G ? q[((int64_t)query * n_head + g * G + h) * HD + 8 * sub + j] * scale : 0.f;
+  }
+
+  // scores
+  const uint16_t* kg = kc + (int64_t)g * max_ctx * HD;
+  for (int tb = wave * PPW; tb < nt; tb += NW * PPW) {
+    const int t = tb + slot;
+    float s[kMaxGroup];
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) s[h] = 0.f;
+    if (t < nt) {
+      const uint4 kv = *reinterpret_cast<const uint4*>(kg + (int64_t)(t0 + t) * HD + 8 * sub);
+      float kf[8];
+      h8_to_f(kv, kf);
+#pragma unroll
+      for (int h = 0; h < kMaxGroup; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a += qr[h][j] * kf[j];
+        s[h] = a;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+#pragma unroll
+      for (int o = LP / 2; o > 0; o >>= 1) s[h] += __shfl_xor(s[h], o, 64);
+    }
+    if (sub == 0 && t < nt) {
+#pragma unroll
+      for (int h = 0; h < kMaxGroup; ++h)
+        if (h < G) s_sc[h][t] = s[h];
+    }
+  }
+  __syncthreads();
+
+  // per-head max and sum of exponentials over this split (one wave per head)
+  for (int h = wave; h < G; h += NW) {
+    float m = -FLT_MAX;
+    for (int t = lane; t < nt; t += 64) m = fmaxf(m, s_sc[h][t]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float l = 0.f;
+    for (int t = lane; t < nt; t += 64) {
+      const float p = expf(s_sc[h][t] - m);
+      s_sc[h][t] = p;
+      l += p;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+    if (lane == 0) {
+      s_m[h] = m;
+      s_l[h] = l;
+    }
+  }
+  __syncthreads();
+
+  // p . V
+  float acc[kMaxGroup][8];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
+  const uint16_t* vg = vc + (int64_t)g * max_ctx * HD;
+  for (int tb = wave * PPW; tb < nt; tb += NW * PPW) {
+    const int t = tb + slot;
+    if (t < nt) {
+      const uint4 vv = *reinterpret_cast<const uint4*>(vg + (int64_t)(t0 + t) * HD + 8 * sub);
+      float vf[8];
+      h8_to_f(vv, vf);
+#pragma unroll
+      for (int h = 0; h < kMaxGroup; ++h) {
+        if (h < G) {
+          const float p = s_sc[h][t];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[h][j] += p * vf[j];
+        }
+      }
+    }
+  }
+  // sum over the position slots of the wave (lanes with equal `sub`)
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int o = LP; o < 64; o <<= 1) acc[h][j] += __shfl_xor(acc[h][j], o, 64);
+  if (slot == 0) {
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+      if (h < G)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s_red[wave][h][8 * sub + j] = acc[h][j];
+  }
+  __syncthreads();
+  // sum over waves and write the partial
+  for (int i = tid; i < G * HD; i += kAttnThreads) {
+    const int h = i / HD, d = i % HD;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += s_red[w][h][d];
+    part_o[(((int64_t)query * nsplit + split) * n_head + g * G + h) * HD + d] = v;
+  }
+  if (tid < G) {
+    const int64_t mi = (((int64_t)query * nsplit + split) * n_head + g * G + tid) * 2;
+    part_ml[mi] = nt > 0 ? s_m[tid] : -FLT_MAX;
+    part_ml[mi + 1] = nt > 0 ? s_l[tid] : 0.f;
+  }
+}
+
+// o[query][h][d] = sum_s e^(m_s - M) o_s[d] / sum_s e^(m_s - M) l_s over the
+// splits that hold positions.
+__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                                      const int32_t* pos_ptr, int n_head, int head_dim, int chunk,
+                                                      int nsplit, int max_ctx, float* __restrict__ o) {
+  const int h = blockIdx.x, query = blockIdx.y;
+  const int pos = *pos_ptr;
+  const bool ok = pos >= 0 && pos + query < max_ctx;
+  const int n_pos = pos + query + 1;
+  const int ns = ok ? min(nsplit, (n_pos + chunk - 1) / chunk) : 0;
+  float M = -FLT_MAX;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[(((int64_t)query * nsplit + s) * n_head + h) * 2]);
+  float L = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const int64_t mi = (((int64_t)query * nsplit + s) * n_head + h) * 2;
+    L += expf(part_ml[mi] - M) * part_ml[mi + 1];
+  }
+  for (int d = threadIdx.x; d < head_dim; d += blockDim.x) {
+    float v = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const int64_t mi = (((int64_t)query * nsplit + s) * n_head + h) * 2;
+      v += expf(part_ml[mi] - M) * part_o[(((int64_t)query * nsplit + s) * n_head + h) * head_dim + d];
+    }
+    o[((int64_t)query * n_head + h) * head_dim + d] = ns > 0 ? v / L : 0.f;
+  }
+}
+
+// ------------------------------------------------------------ embedding row
+// x[m][:] = decoded row tokens[m] of an embedding matrix (fp32).  One thread
+// per 32-weight group; the formulas are the block definitions of nt.h.
+__global__ __launch_bounds__(256) void k_embed(int fmt, const uint8_t* __restrict__ E, const int32_t* tokens, int vocab,
+                                               int cols, float* __restrict__ x) {
+  const int m = blockIdx.y;
+  int tok = tokens[m];
+  tok = min(max(tok, 0), vocab - 1);
+  const int grp = blockIdx.x * blockDim.x + threadIdx.x;  // 32-weight group
+  if (grp >= cols / 32) return;
+  const int qk = block_elems(fmt), bb = block_bytes(fmt);
+  const uint8_t* row = E + (int64_t)tok * (cols / qk) * bb;
+  float* out = x + (int64_t)m * cols + 32 * grp;
+  auto h2f = [](const uint8_t* p) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(p[0] | (p[1] << 8))); };
+  if (fmt == NT_Q8_0) {
+    const uint8_t* b = row + (int64_t)grp * 34;
+    const float d = h2f(b);
+    for (int j = 0; j < 32; ++j) out[j] = d * (float)(int8_t)b[2 + j];
+  } else if (fmt == NT_Q4_0) {
+    const uint8_t* b = row + (int64_t)grp * 18;
+    const float d = h2f(b);
+    for (int j = 0; j < 16; ++j) {
+      out[j] = d * (float)((b[2 + j] & 15) - 8);
+      out[j + 16] = d * (float)((b[2 + j] >> 4) - 8);
+    }
+  } else if (fmt == NT_Q4_K) {
+    const uint8_t* b = row + (int64_t)(grp / 8) * 144;
+    const int s = grp % 8;  // sub-block
+    const float d = h2f(b), dmin = h2f(b + 2);
+    const uint8_t* sc = b + 4;
+    int scale, mn;
+    if (s < 4) {
+      scale = sc[s] & 63;
+      mn = sc[s + 4] & 63;
+    } else {
+      scale = (sc[s + 4] & 15) | ((sc[s - 4] >> 6) << 4);
+      mn = (sc[s + 4] >> 4) | ((sc[s] >> 6) << 4);
+    }
+    const uint8_t* qs = b + 16 + 32 * (s / 2);
+    for (int l = 0; l < 32; ++l) {
+      const int q = (s & 1) ? (qs[l] >> 4) : (qs[l] & 15);
+      out[l] = d * (float)scale * (float)q - dmin * (float)mn;
+    }
+  } else {  // Q6_K
+    const uint8_t* b = row + (int64_t)(grp / 8) * 210;
+    const int e0 = 32 * (grp % 8);
+    const float d = h2f(b + 208);
+    for (int l = 0; l < 32; ++l) {
+      const int e = e0 + l;
+      const int n = e / 128, k = (e % 128) / 32, ll = e % 32;
+      const uint8_t lo = b[64 * n + 32 * (k % 2) + ll];
+      const int nib = (k / 2) ? (lo >> 4) : (lo & 15);
+      const int hi = (b[128 + 32 * n + ll] >> (2 * k)) & 3;
+      out[l] = d * (float)(int8_t)b[192 + e / 16] * (float)((nib | (hi << 4)) - 32);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ argmax
+// Greedy sampling (p2 "Architecture et structure du code": sampler): index
+// of the largest logit, lowest index among equal maxima.
+__device__ __forceinline__ void better(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_argmax_part(const float* __restrict__ logits, int n, int per_block,
+                                                     float* __restrict__ pv, int* __restrict__ pi) {
+  const int m = blockIdx.y;
+  const float* lg = logits + (int64_t)m * n;
+  const int b0 = blockIdx.x * per_block, b1 = min(n, b0 + per_block);
+  float v = -INFINITY;
+  int idx = INT32_MAX;
+  for (int i = b0 + threadIdx.x; i < b1; i += blockDim.x) better(v, idx, lg[i], i);
+  for (int o = 32; o > 0; o >>= 1) better(v, idx, __shfl_xor(v, o, 64), __shfl_xor(idx, o, 64));
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  if ((threadIdx.x & 63) == 0) {
+    sv[threadIdx.x >> 6] = v;
+    si[threadIdx.x >> 6] = idx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) better(v, idx, sv[w], si[w]);
+    pv[(int64_t)m * gridDim.x + blockIdx.x] = v;
+    pi[(int64_t)m * gridDim.x + blockIdx.x] = idx;
+  }
+}
+
+__global__ __launch_bounds__(64) void k_argmax_final(const float* __restrict__ pv, const int* __restrict__ pi, int nparts,
+                                                     int32_t* __restrict__ out) {
+  const int m = blockIdx.x;
+  float v = -INFINITY;
+  int idx = INT32_MAX;
+  for (int i = threadIdx.x; i < nparts; i += 64) better(v, idx, pv[(int64_t)m * nparts + i], pi[(int64_t)m * nparts + i]);
+  for (int o = 32; o > 0; o >>= 1) better(v, idx, __shfl_xor(v, o, 64), __shfl_xor(idx, o, 64));
+  if (threadIdx.x == 0) out[m] = idx == INT32_MAX ? 0 : idx;
+}
+
+}  // namespace
+
+// Split geometry: chunks of 64-position multiples so that n_kv * nsplit is
+// about 512 workgroups (two per CU of a 256-CU chip) at full context; at most
+// 512 positions per chunk.  Independent of the device, so workspace sizes are.
+void attn_plan(int n_kv, int max_ctx, int& chunk, int& nsplit) {
+  const int64_t want = 512;
+  int64_t c = ((int64_t)max_ctx * n_kv + want - 1) / want;
+  c = ((c + 63) / 64) * 64;
+  if (c < 64) c = 64;
+  if (c > 512) c = 512;
+  chunk = (int)c;
+  nsplit = (max_ctx + chunk - 1) / chunk;
+}
+
+int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, const int32_t* pos, int n_query,
+                     int n_head, int n_kv, int head_dim, int max_ctx, int chunk, int nsplit, float* part_o,
+                     float* part_ml, float* o, hipStream_t stream) {
+  for (int qi = 0; qi < n_query; ++qi) {
+    const dim3 grid(n_kv, nsplit);
+    switch (head_dim) {
+      case 32: hipLaunchKernelGGL(k_attn_split<32>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, chunk, nsplit, part_o, part_ml); break;
+      case 64: hipLaunchKernelGGL(k_attn_split<64>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, chunk, nsplit, part_o, part_ml); break;
+      case 128: hipLaunchKernelGGL(k_attn_split<128>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, chunk, nsplit, part_o, part_ml); break;
+      case 256: hipLaunchKernelGGL(k_attn_split<256>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, chunk, nsplit, part_o, part_ml); break;
+      default: return NT_EUNSUPPORTED;
+    }
+  }
+  hipLaunchKernelGGL(k_attn_combine, dim3(n_head, n_query), dim3(128), 0, stream, part_o, part_ml, pos, n_head, head_dim,
+                     chunk, nsplit, max_ctx, o);
+  return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
+}
+
+int launch_embed(int fmt, const void* E, const int32_t* tokens, int M, int vocab, int cols, float* x,
+                 hipStream_t stream) {
+  const int groups = cols / 32;
+  hipLaunchKernelGGL(k_embed, dim3((groups + 255) / 256, M), dim3(256), 0, stream, fmt,
+                     static_cast<const uint8_t*>(E), tokens, vocab, cols, x);
+  return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
+}
+
+int argmax_parts(int n) { return std::min(256, (n + 1023) / 1024); }
+
+int launch_argmax(const float* logits, int M, int n, float* pv, int* pi, int32_t* out, hipStream_t stream) {
+  const int parts = argmax_parts(n);
+  const int per = (n + parts - 1) / parts;
+  hipLaunchKernelGGL(k_argmax_part, dim3(parts, M), dim3(256), 0, stream, logits, n, per, pv, pi);
+  hipLaunchKernelGGL(k_argmax_final, dim3(M), dim3(64), 0, stream, pv, pi, parts, out);
+  return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
+}
+
+}  // namespace nt

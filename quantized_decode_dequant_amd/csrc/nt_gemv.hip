@@ -10,16 +10,19 @@
 //             high and a low int8 plane (X = 256*hi + lo) plus per-16 sums of
 //             X.  Weight x activation products then run on v_dot4_i32_i8
 //             with exact integer sums per quantization sub-block.
-//   tiles     A tile is a group of consecutive rows of one matrix -- a
-//             contiguous byte range -- streamed HBM -> registers with 16-byte
-//             coalesced loads (one tile in flight while the previous one is
-//             computed), then written to LDS.  Lanes read their blocks from
-//             LDS at any byte alignment (Q8_0, Q4_0 and Q6_K blocks are only
-//             2-byte aligned), unpack quants in registers and accumulate.
-//   reduce    Lanes of a wave sum with a butterfly; waves sharing a row sum
-//             through LDS.
+//   stream    After the prologue every wave works alone (no more workgroup
+//             barriers).  It owns a contiguous range of work items (rows, or
+//             row pairs) and streams their bytes through a private 8 KB LDS
+//             slab: a segment of a row -- a contiguous byte range -- is
+//             loaded HBM -> registers with 16-byte coalesced loads, written
+//             to the slab, and the next segment's loads are issued before the
+//             current one is computed, so every wave keeps ~8 KB in flight.
+//             Lanes read their blocks from the slab at any byte alignment
+//             (Q8_0, Q4_0 and Q6_K blocks are only 2-byte aligned), unpack
+//             quants in registers and accumulate.
+//   reduce    Lanes of a wave sum with a butterfly per row.
 //   epilogue  Plain store, residual add, SwiGLU (gate and up rows in one
-//             tile) or RoPE + q store + f16 K/V append.
+//             item) or RoPE + q store + f16 K/V append (row pairs).
 //
 // The block layouts are the GGUF ones the pages' format list refers to
 // (p1 "About"); the unpacking below follows them.
@@ -33,7 +36,6 @@ extern __shared__ __attribute__((aligned(16))) uint8_t nt_smem[];
 namespace nt {
 namespace {
 
-constexpr int kMaxYpart = 128;
 constexpr float kXMax = 32639.0f;  // |X| bound; keeps the high plane in [-127, 127]
 
 __device__ __forceinline__ uint32_t ld32(uint32_t off) { return *reinterpret_cast<const uint32_t*>(nt_smem + off); }
@@ -78,12 +80,12 @@ struct XL {
 // or 64 weights (Q6_K).  `row` is the LDS byte offset of the row's first block.
 
 // Q8_0: unit u is block u.  w = d*q.
-__device__ __forceinline__ float unit_q8_0(uint32_t row, int u, const XL& x) {
+__device__ __forceinline__ float unit_q8_0(uint32_t row, int u, uint32_t xe, const XL& x) {
   const uint32_t blk = row + 34u * u;
   const float d = h2f(ld16(blk));
   uint32_t q[8];
   ld_unaligned<8>(blk + 2, q);
-  const uint32_t e0 = 32u * u;
+  const uint32_t e0 = xe + 32u * u;
   const uint4 h0 = ld128(x.hi + e0), h1 = ld128(x.hi + e0 + 16);
   const uint4 l0 = ld128(x.lo + e0), l1 = ld128(x.lo + e0 + 16);
   int H = 0, L = 0;
@@ -96,17 +98,17 @@ __device__ __forceinline__ float unit_q8_0(uint32_t row, int u, const XL& x) {
   H = dot4(q[6], h1.z, H); L = dot4(q[6], l1.z, L);
   H = dot4(q[7], h1.w, H); L = dot4(q[7], l1.w, L);
   const int S = (H << 8) + L;
-  return d * ldf(x.sc + 4u * u) * (float)S;
+  return d * ldf(x.sc + (e0 >> 3)) * (float)S;
 }
 
 // Q4_0: unit u is block u.  Byte j: low nibble -> element j, high -> j+16.
 // w = d*(q-8), so sum w*X = d*(sum q*X - 8*sum X).
-__device__ __forceinline__ float unit_q4_0(uint32_t row, int u, const XL& x) {
+__device__ __forceinline__ float unit_q4_0(uint32_t row, int u, uint32_t xe, const XL& x) {
   const uint32_t blk = row + 18u * u;
   const float d = h2f(ld16(blk));
   uint32_t q[4];
   ld_unaligned<4>(blk + 2, q);
-  const uint32_t e0 = 32u * u;
+  const uint32_t e0 = xe + 32u * u;
   const uint4 h0 = ld128(x.hi + e0), h1 = ld128(x.hi + e0 + 16);
   const uint4 l0 = ld128(x.lo + e0), l1 = ld128(x.lo + e0 + 16);
   int H = 0, L = 0;
@@ -122,9 +124,9 @@ __device__ __forceinline__ float unit_q4_0(uint32_t row, int u, const XL& x) {
   NT_Q40_STEP(q[2], h0.z, l0.z, h1.z, l1.z)
   NT_Q40_STEP(q[3], h0.w, l0.w, h1.w, l1.w)
 #undef NT_Q40_STEP
-  const int xs = ldi32(x.sum + 8u * u) + ldi32(x.sum + 8u * u + 4);
+  const int xs = ldi32(x.sum + (e0 >> 2)) + ldi32(x.sum + (e0 >> 2) + 4);
   const int S = (H << 8) + L - 8 * xs;
-  return d * ldf(x.sc + 4u * u) * (float)S;
+  return d * ldf(x.sc + (e0 >> 3)) * (float)S;
 }
 
 // Q4_K: 6-bit scale and min of sub-block s from the 12 packed bytes
@@ -148,7 +150,7 @@ __device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t
 // weights, bytes 32c..32c+31), half h = u%2.  Low nibbles are elements
 // 64c+16h+i (sub-block 2c), high nibbles 64c+32+16h+i (sub-block 2c+1).
 // w = d*sc*q - dmin*m.
-__device__ __forceinline__ float unit_q4_k(uint32_t row, int u, const XL& x) {
+__device__ __forceinline__ float unit_q4_k(uint32_t row, int u, uint32_t xe, const XL& x) {
   const int sb = u >> 3, part = u & 7, c = part >> 1, h = part & 1;
   const uint32_t blk = row + 144u * sb;
   const uint4 hd = ld128(blk);
@@ -157,7 +159,7 @@ __device__ __forceinline__ float unit_q4_k(uint32_t row, int u, const XL& x) {
   int scA, mA, scB, mB;
   q4k_scale_min(hd.y, hd.z, hd.w, 2 * c, scA, mA);
   q4k_scale_min(hd.y, hd.z, hd.w, 2 * c + 1, scB, mB);
-  const uint32_t eA = 256u * sb + 64 * c + 16 * h, eB = eA + 32;
+  const uint32_t eA = xe + 256u * sb + 64 * c + 16 * h, eB = eA + 32;
   const uint4 ah = ld128(x.hi + eA), al = ld128(x.lo + eA);
   const uint4 bh = ld128(x.hi + eB), bl = ld128(x.lo + eB);
   int AH = 0, AL = 0, BH = 0, BL = 0;
@@ -185,7 +187,7 @@ __device__ __forceinline__ float unit_q4_k(uint32_t row, int u, const XL& x) {
 // low four bits from nibble k/2 of ql[64n + 32(k%2) + l0 + i], high two bits
 // from bits 2k..2k+1 of qh[32n + l0 + i], and scale sc[8n + 2k + l0/16].
 // w = d*sc*(q-32).
-__device__ __forceinline__ float unit_q6_k(uint32_t row, int u, const XL& x) {
+__device__ __forceinline__ float unit_q6_k(uint32_t row, int u, uint32_t xe, const XL& x) {
   const int sb = u >> 2, part = u & 3, n = part >> 1, hl = part & 1;
   const uint32_t blk = row + 210u * sb;
   uint32_t qa[4], qb[4], qh[4], scw[3];
@@ -194,7 +196,7 @@ __device__ __forceinline__ float unit_q6_k(uint32_t row, int u, const XL& x) {
   ld_unaligned<4>(blk + 128 + 32 * n + 16 * hl, qh);
   ld_unaligned<3>(blk + 192 + 8 * n, scw);  // sc[8n .. 8n+7] (+4 spare bytes)
   const float d = h2f(ld16(blk + 208));
-  const uint32_t e0 = 256u * sb + 128 * n + 16 * hl;
+  const uint32_t e0 = xe + 256u * sb + 128 * n + 16 * hl;
   float acc = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -220,80 +222,11 @@ __device__ __forceinline__ float unit_q6_k(uint32_t row, int u, const XL& x) {
   return d * acc;
 }
 
-// ------------------------------------------------------------ tile geometry
-struct Geo {
-  int m, r0, nr;
-  const uint8_t* a0;  // 16-B aligned chunk bases of the tile's byte segments
-  const uint8_t* a1;
-  int n0, n1;           // 16-B chunks per segment
-  uint32_t d0, d1;      // LDS byte offset of each segment's first row
-};
-
-__device__ __forceinline__ Geo tile_geo(const TileJob& job, int tile) {
-  Geo g;
-  int m = 0;
-  while (m + 1 < job.nmat && tile >= job.tile_start[m + 1]) ++m;
-  g.m = m;
-  const int T = job.tile_rows[m];
-  g.r0 = (tile - job.tile_start[m]) * T;
-  g.nr = min(T, job.rows[m] - g.r0);
-  const uint8_t* p0 = job.W[m] + (int64_t)g.r0 * job.rb[m];
-  g.a0 = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(p0) & ~uintptr_t(15));
-  g.d0 = (uint32_t)(p0 - g.a0);
-  g.n0 = (int)((g.d0 + (int64_t)g.nr * job.rb[m] + 15) >> 4);
-  if (job.paired) {
-    const uint8_t* p1 = job.W[1] + (int64_t)g.r0 * job.rb[1];
-    g.a1 = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(p1) & ~uintptr_t(15));
-    g.d1 = 16u * g.n0 + (uint32_t)(p1 - g.a1);
-    g.n1 = (int)(((uint32_t)(p1 - g.a1) + (int64_t)g.nr * job.rb[1] + 15) >> 4);
-  } else {
-    g.a1 = g.a0;
-    g.n1 = 0;
-    g.d1 = 0;
-  }
-  return g;
-}
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef const __attribute__((address_space(1))) u32x4* gptr_u32x4;
-
-// One 16-byte chunk of weights.  Chunks are 16-byte aligned and contain at
-// least one byte of the matrix, so a chunk never crosses a page boundary and
-// is always mapped, even where it runs past the matrix's last byte (those
-// bytes are never used).  Weights are read once: the load is non-temporal.
-__device__ __forceinline__ uint4 load_chunk(const uint8_t* p) {
-  const u32x4 v = __builtin_nontemporal_load((gptr_u32x4)(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ void prefetch(const Geo& g, int lpw, int tid, int NT, uint4 (&pre)[kLpwMax]) {
-#pragma unroll
-  for (int i = 0; i < kLpwMax; ++i) {
-    if (i < lpw) {
-      const int c = tid + i * NT;
-      if (c < g.n0)
-        pre[i] = load_chunk(g.a0 + 16 * (int64_t)c);
-      else if (c < g.n0 + g.n1)
-        pre[i] = load_chunk(g.a1 + 16 * (int64_t)(c - g.n0));
-    }
-  }
-}
-
-__device__ __forceinline__ void store_tile(const Geo& g, int lpw, int tid, int NT, const uint4 (&pre)[kLpwMax]) {
-#pragma unroll
-  for (int i = 0; i < kLpwMax; ++i) {
-    if (i < lpw) {
-      const int c = tid + i * NT;
-      if (c < g.n0 + g.n1) st128(16u * c, pre[i]);  // segment 1 follows segment 0's chunks
-    }
-  }
-}
-
 // ----------------------------------------------------------------- prologue
 // Stage the activation: v = src (or RMSNorm(src) * gain), then per 32-block
 // s = max|v| / 32639, X = rint(v / s), hi = (X + 128) >> 8, lo = X - 256 hi.
-__device__ __forceinline__ void stage_x(const TileJob& job, const ProArgs& pro, int tid) {
-  const int cols = job.cols, NT = job.nthreads;
+__device__ __forceinline__ void stage_x(const Job& job, const ProArgs& pro, int tid) {
+  const int cols = job.cols, NT = job.nwaves * 64;
   const float* src = pro.src;
   float r = 1.0f;
   if (pro.gain) {
@@ -306,7 +239,7 @@ __device__ __forceinline__ void stage_x(const TileJob& job, const ProArgs& pro, 
     if ((tid & 63) == 0) stf(job.red + 4u * (tid >> 6), ss);
     __syncthreads();
     float tot = 0.f;
-    for (int w = 0; w < (NT >> 6); ++w) tot += ldf(job.red + 4u * w);
+    for (int w = 0; w < job.nwaves; ++w) tot += ldf(job.red + 4u * w);
     r = 1.0f / sqrtf(tot / (float)cols + pro.eps);
   }
   const int nb = cols >> 5;
@@ -359,131 +292,198 @@ __device__ __forceinline__ void stage_x(const TileJob& job, const ProArgs& pro, 
   __syncthreads();
 }
 
-// ------------------------------------------------------------------ compute
-__device__ __forceinline__ int units_per_row(int fmt, int cols) { return fmt == NT_Q6_K ? cols >> 6 : cols >> 5; }
 
-__device__ __forceinline__ void tile_dims(const TileJob& job, const Geo& g, int& T, int& nv, int& WPR) {
-  const int NW = job.nthreads >> 6;
-  T = job.tile_rows[g.m] * (job.paired ? 2 : 1);
-  nv = g.nr * (job.paired ? 2 : 1);
-  WPR = T >= NW ? 1 : NW / T;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) u32x4* gptr_u32x4;
+
+// One 16-byte chunk of weights.  Chunks are 16-byte aligned and contain at
+// least one byte of the matrix, so a chunk never crosses a page boundary and
+// is always mapped, even where it runs past the matrix's last byte (those
+// bytes are never used).  Weights are read once: the load is non-temporal.
+__device__ __forceinline__ uint4 load_chunk(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load((gptr_u32x4)(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ void compute_tile(const TileJob& job, const Geo& g, int tid) {
-  const int NW = job.nthreads >> 6, wave = tid >> 6, lane = tid & 63;
-  int T, nv, WPR;
-  tile_dims(job, g, T, nv, WPR);
-  const int vstep = NW / WPR;
-  const int part = wave % WPR;
-  const XL x{job.x_hi, job.x_lo, job.x_sc, job.x_sum};
-  for (int v = wave / WPR; v < nv; v += vstep) {
-    const int seg = (job.paired && v >= g.nr) ? 1 : 0;
-    const int mi = seg ? 1 : g.m;
-    const int fmt = job.fmt[mi];
-    const uint32_t row = (seg ? g.d1 : g.d0) + (uint32_t)((seg ? v - g.nr : v) * job.rb[mi]);
-    const int U = units_per_row(fmt, job.cols);
-    float acc = 0.f;
-    const int u0 = part * 64 + lane, us = 64 * WPR;
-    switch (fmt) {
-      case NT_Q4_K:
-        for (int u = u0; u < U; u += us) acc += unit_q4_k(row, u, x);
-        break;
-      case NT_Q6_K:
-        for (int u = u0; u < U; u += us) acc += unit_q6_k(row, u, x);
-        break;
-      case NT_Q8_0:
-        for (int u = u0; u < U; u += us) acc += unit_q8_0(row, u, x);
-        break;
-      default:
-        for (int u = u0; u < U; u += us) acc += unit_q4_0(row, u, x);
-        break;
-    }
-    acc = wave_sum(acc);
-    if (lane == 0) stf(job.ypart + 4u * (v * WPR + part), acc);
+// ----------------------------------------------------------- segment stream
+// Position in a wave's stream: item `it`, row `g` within the item, segment
+// `s` within the row.
+struct Pos {
+  int it, g, s;
+};
+
+// Byte range of one segment and where its data sits in the slab.
+struct Seg {
+  const uint8_t* a;  // 16-B aligned address of the first chunk
+  int nchunks;
+  uint32_t d;        // byte offset of the segment's first block in the slab
+  int m;             // matrix
+  int row;           // row within the matrix
+  int nblk;          // blocks in the segment
+  uint32_t xe;       // element index (column) of the segment's first weight
+};
+
+__device__ __forceinline__ int item_matrix(const Job& job, int it) {
+  int m = 0;
+  while (m + 1 < job.nmat && it >= job.item_start[m + 1]) ++m;
+  return m;
+}
+
+__device__ __forceinline__ int rows_per_item(const Job& job) { return (job.paired || job.pairs) ? 2 : 1; }
+
+__device__ __forceinline__ Seg seg_of(const Job& job, const Pos& p) {
+  Seg sg;
+  const int mi = item_matrix(job, p.it);
+  const int li = p.it - job.item_start[mi];
+  if (job.paired) {
+    sg.m = p.g;
+    sg.row = li;
+  } else {
+    sg.m = mi;
+    sg.row = job.pairs ? 2 * li + p.g : li;
+  }
+  const int m = sg.m;
+  const int fmt = job.fmt[m];
+  const int bb = block_bytes(fmt);
+  const int nbr = job.cols / block_elems(fmt);
+  const int b0 = p.s * job.seg_blocks[m];
+  sg.nblk = min(job.seg_blocks[m], nbr - b0);
+  sg.xe = (uint32_t)b0 * block_elems(fmt);
+  const uint8_t* start = job.W[m] + (int64_t)sg.row * job.rb[m] + (int64_t)b0 * bb;
+  sg.a = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(start) & ~uintptr_t(15));
+  sg.d = (uint32_t)(start - sg.a);
+  sg.nchunks = (int)((sg.d + (uint32_t)(sg.nblk * bb) + 15) >> 4);
+  return sg;
+}
+
+// Advance to the next segment; returns false past the wave's last item.
+__device__ __forceinline__ bool advance(const Job& job, Pos& p, int it_end) {
+  const int m = job.paired ? p.g : item_matrix(job, p.it);
+  if (++p.s < job.nseg[m]) return true;
+  p.s = 0;
+  if (++p.g < rows_per_item(job)) return true;
+  p.g = 0;
+  return ++p.it < it_end;
+}
+
+__device__ __forceinline__ void seg_load(const Seg& sg, int lane, uint4 (&pre)[kSlabLoads]) {
+#pragma unroll
+  for (int i = 0; i < kSlabLoads; ++i) {
+    const int c = lane + 64 * i;
+    if (c < sg.nchunks) pre[i] = load_chunk(sg.a + 16 * (int64_t)c);
   }
 }
 
-__device__ __forceinline__ float row_sum(const TileJob& job, int v, int WPR) {
-  float s = 0.f;
-  for (int p = 0; p < WPR; ++p) s += ldf(job.ypart + 4u * (v * WPR + p));
-  return s;
+__device__ __forceinline__ void seg_store(const Seg& sg, uint32_t slab, int lane, const uint4 (&pre)[kSlabLoads]) {
+#pragma unroll
+  for (int i = 0; i < kSlabLoads; ++i) {
+    const int c = lane + 64 * i;
+    if (c < sg.nchunks) st128(slab + 16u * c, pre[i]);
+  }
+}
+
+__device__ __forceinline__ float seg_compute(const Job& job, const Seg& sg, uint32_t slab, int lane) {
+  const XL x{job.x_hi, job.x_lo, job.x_sc, job.x_sum};
+  const uint32_t row = slab + sg.d;
+  float acc = 0.f;
+  switch (job.fmt[sg.m]) {
+    case NT_Q4_K:
+      for (int u = lane; u < 8 * sg.nblk; u += 64) acc += unit_q4_k(row, u, sg.xe, x);
+      break;
+    case NT_Q6_K:
+      for (int u = lane; u < 4 * sg.nblk; u += 64) acc += unit_q6_k(row, u, sg.xe, x);
+      break;
+    case NT_Q8_0:
+      for (int u = lane; u < sg.nblk; u += 64) acc += unit_q8_0(row, u, sg.xe, x);
+      break;
+    default:
+      for (int u = lane; u < sg.nblk; u += 64) acc += unit_q4_0(row, u, sg.xe, x);
+      break;
+  }
+  return acc;
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Results of one item (row sums s0 and, for two-row items, s1).
 template <int EPI>
-__device__ __forceinline__ void epilogue(const TileJob& job, const Geo& g, const EpiArgs& ea, int tid) {
-  int T, nv, WPR;
-  tile_dims(job, g, T, nv, WPR);
-  const int NT = job.nthreads;
+__device__ __forceinline__ void item_epilogue(const Job& job, int it, float s0, float s1, const EpiArgs& ea) {
+  const int mi = item_matrix(job, it);
+  const int li = it - job.item_start[mi];
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
-    for (int t = tid; t < g.nr; t += NT) {
-      const int R = job.row_base[g.m] + g.r0 + t;
-      const float s = row_sum(job, t, WPR);
-      if constexpr (EPI == EPI_RESID) ea.y[R] += s;
-      else ea.y[R] = s;
-    }
+    const int R = job.row_base[mi] + li;
+    if constexpr (EPI == EPI_RESID) ea.y[R] += s0;
+    else ea.y[R] = s0;
   } else if constexpr (EPI == EPI_SWIGLU) {
-    for (int t = tid; t < g.nr; t += NT) {
-      const float gate = row_sum(job, t, WPR), up = row_sum(job, g.nr + t, WPR);
-      ea.y[g.r0 + t] = silu(gate) * up;
-    }
+    ea.y[li] = silu(s0) * s1;
   } else if constexpr (EPI == EPI_QKV) {
-    const int pos = *ea.pos;
-    const bool pos_ok = pos >= 0 && pos < ea.max_ctx;
-    if (!pos_ok && tid == 0 && ea.err) *ea.err = 1;
-    for (int t = tid; 2 * t < g.nr; t += NT) {
-      const int R = job.row_base[g.m] + g.r0 + 2 * t;  // even row of an adjacent pair
-      float a = row_sum(job, 2 * t, WPR), b = row_sum(job, 2 * t + 1, WPR);
-      const int dd = R % ea.head_dim;
-      if (R < ea.q_rows + ea.kv_rows) {
-        // RoPE: pair (2i, 2i+1) of a head turns by pos * theta^(-2i/head_dim);
-        // the angle is formed in double so large positions keep fp32 accuracy.
-        const double freq = exp2(-(double)dd / (double)ea.head_dim * log2((double)ea.rope_theta));
-        const double ang = (double)pos * freq;
-        const float c = (float)cos(ang), s = (float)sin(ang);
-        const float a2 = a * c - b * s, b2 = a * s + b * c;
-        a = a2;
-        b = b2;
-      }
-      if (R < ea.q_rows) {
-        ea.q_out[R] = a;
-        ea.q_out[R + 1] = b;
-      } else if (pos_ok) {
-        const bool is_k = R < ea.q_rows + ea.kv_rows;
-        const int rr = R - ea.q_rows - (is_k ? 0 : ea.kv_rows);
-        const int kh = rr / ea.head_dim;
-        uint16_t* cache = is_k ? ea.k_cache : ea.v_cache;
-        const int64_t off = ((int64_t)kh * ea.max_ctx + pos) * ea.head_dim + dd;
-        const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-        cache[off] = __builtin_bit_cast(uint16_t, ha);
-        cache[off + 1] = __builtin_bit_cast(uint16_t, hb);
-      }
+    const int pos = *ea.pos + ea.pos_add;
+    const bool pos_ok = pos >= ea.pos_add && pos < ea.max_ctx;
+    if (!pos_ok && ea.err) *ea.err = 1;
+    const int R = job.row_base[mi] + 2 * li;  // even row of an adjacent pair
+    float a = s0, b = s1;
+    const int dd = R % ea.head_dim;
+    if (R < ea.q_rows + ea.kv_rows) {
+      // RoPE: pair (2i, 2i+1) of a head turns by pos * theta^(-2i/head_dim);
+      // the angle is formed in double so large positions keep fp32 accuracy.
+      const double freq = exp2(-(double)dd / (double)ea.head_dim * log2((double)ea.rope_theta));
+      const double ang = (double)pos * freq;
+      const float c = (float)cos(ang), s = (float)sin(ang);
+      const float a2 = a * c - b * s, b2 = a * s + b * c;
+      a = a2;
+      b = b2;
+    }
+    if (R < ea.q_rows) {
+      ea.q_out[R] = a;
+      ea.q_out[R + 1] = b;
+    } else if (pos_ok) {
+      const bool is_k = R < ea.q_rows + ea.kv_rows;
+      const int rr = R - ea.q_rows - (is_k ? 0 : ea.kv_rows);
+      const int kh = rr / ea.head_dim;
+      uint16_t* cache = is_k ? ea.k_cache : ea.v_cache;
+      const int64_t off = ((int64_t)kh * ea.max_ctx + pos) * ea.head_dim + dd;
+      const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+      cache[off] = __builtin_bit_cast(uint16_t, ha);
+      cache[off + 1] = __builtin_bit_cast(uint16_t, hb);
     }
   }
 }
 
 template <int EPI>
-__global__ __launch_bounds__(kMaxThreads) void k_qgemv(TileJob job, ProArgs pro, EpiArgs ea) {
-  const int tid = threadIdx.x, NT = job.nthreads;
-  const int ntiles = job.tile_start[job.nmat];
-  int tile = blockIdx.x;
-  uint4 pre[kLpwMax];
-  Geo g = tile_geo(job, tile < ntiles ? tile : 0);
-  if (tile < ntiles) prefetch(g, job.lpw, tid, NT, pre);
-  stage_x(job, pro, tid);
-  for (; tile < ntiles; tile += gridDim.x) {
-    store_tile(g, job.lpw, tid, NT, pre);
-    __syncthreads();
-    const Geo cur = g;
-    const int nxt = tile + gridDim.x;
-    if (nxt < ntiles) {
-      g = tile_geo(job, nxt);
-      prefetch(g, job.lpw, tid, NT, pre);
+__global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, EpiArgs ea) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nitems = job.item_start[job.nmat];
+  const int64_t gw = (int64_t)blockIdx.x * job.nwaves + wave;
+  const int64_t GW = (int64_t)gridDim.x * job.nwaves;
+  const int it_begin = (int)(gw * nitems / GW), it_end = (int)((gw + 1) * nitems / GW);
+  const uint32_t slab = job.slab + (uint32_t)wave * kSlab;
+  uint4 pre[kSlabLoads];
+  Pos p{it_begin, 0, 0};
+  bool live = it_begin < it_end;
+  Seg cur = seg_of(job, Pos{live ? it_begin : 0, 0, 0});
+  if (live) seg_load(cur, lane, pre);
+  stage_x(job, pro, tid);  // the only workgroup barrier
+  float acc0 = 0.f, acc1 = 0.f;
+  while (live) {
+    seg_store(cur, slab, lane, pre);
+    const Pos here = p;
+    const Seg seg = cur;
+    live = advance(job, p, it_end);
+    if (live) {
+      cur = seg_of(job, p);
+      seg_load(cur, lane, pre);
     }
-    compute_tile(job, cur, tid);
-    __syncthreads();
-    epilogue<EPI>(job, cur, ea, tid);
+    const float part = seg_compute(job, seg, slab, lane);
+    if (here.g == 0) acc0 += part;
+    else acc1 += part;
+    // last segment of the item: reduce and finish it
+    if (!live || p.it != here.it) {
+      const float s0 = wave_sum(acc0);
+      const float s1 = wave_sum(acc1);
+      if (lane == 0) item_epilogue<EPI>(job, here.it, s0, s1, ea);
+      acc0 = 0.f;
+      acc1 = 0.f;
+    }
   }
 }
 
@@ -505,7 +505,7 @@ DevInfo& dev_info() {
 }
 
 template <int EPI>
-int launch_epi(const TileJob& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t stream) {
+int launch_epi(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute((const void*)k_qgemv<EPI>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
@@ -513,80 +513,67 @@ int launch_epi(const TileJob& job, const ProArgs& pro, const EpiArgs& ea, hipStr
       return NT_EHIP;
     attr_set = true;
   }
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_qgemv<EPI>, job.nthreads, job.lds_bytes) != hipSuccess)
-    return NT_EHIP;
-  if (per_cu < 1) return NT_EUNSUPPORTED;
-  const int ntiles = job.tile_start[job.nmat];
-  const int grid = min(ntiles, per_cu * dev_info().cus);
-  if (grid <= 0) return NT_OK;
-  hipLaunchKernelGGL(k_qgemv<EPI>, dim3(grid), dim3(job.nthreads), job.lds_bytes, stream, job, pro, ea);
+  const int nitems = job.item_start[job.nmat];
+  // one workgroup per CU; fewer when there are not enough items for its waves
+  const int grid = std::max(1, std::min(dev_info().cus, (nitems + job.nwaves - 1) / job.nwaves));
+  if (nitems <= 0) return NT_OK;
+  hipLaunchKernelGGL(k_qgemv<EPI>, dim3(grid), dim3(64 * job.nwaves), job.lds_bytes, stream, job, pro, ea);
   return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
 }
 
 }  // namespace
 
-// Geometry of a launch: workgroup size from the size of the staged
-// activation, rows per tile so a tile carries ~20 KB (256 threads) or ~48 KB
-// (512 threads) of weights, and the LDS layout.
-int plan_job(TileJob& job, int nmat, const uint8_t* const* W, const int* fmt, const int* rows, int cols, int paired,
-             int rope_pairs) {
+// Geometry of a launch: segments of at most kSegMax bytes (whole blocks,
+// rows split evenly), the LDS layout, and as many waves (<= 12) as LDS
+// allows once the staged activation is in.
+int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const int* rows, int cols, int paired,
+             int pairs) {
   if (nmat < 1 || nmat > kMaxMats || (paired && nmat != 2)) return NT_EINVAL;
   if (cols <= 0 || cols > kMaxCols) return NT_EUNSUPPORTED;
-  const int64_t x_bytes = (int64_t)cols * 2 + (cols / 32) * 4 + (cols / 16) * 4;
-  job = TileJob{};
+  job = Job{};
   job.nmat = nmat;
   job.paired = paired;
+  job.pairs = pairs;
   job.cols = cols;
-  job.nthreads = x_bytes <= 24 * 1024 ? 256 : 512;
-  const int NW = job.nthreads / 64;
-  const int64_t target = job.nthreads == 256 ? 20 * 1024 : 48 * 1024;
-  int64_t need = 0;
-  int tiles = 0, rbase = 0;
+  int items = 0, rbase = 0;
   for (int m = 0; m < nmat; ++m) {
     const int qk = block_elems(fmt[m]);
     if (qk == 0 || cols % qk != 0) return NT_EINVAL;
+    if (pairs && (rows[m] & 1)) return NT_EINVAL;
+    if (paired && rows[m] != rows[0]) return NT_EINVAL;
     job.W[m] = W[m];
     job.fmt[m] = fmt[m];
     job.rows[m] = rows[m];
-    job.rb[m] = (int64_t)(cols / qk) * block_bytes(fmt[m]);
-  }
-  for (int m = 0; m < nmat; ++m) {
-    const int64_t rb_eff = paired ? job.rb[0] + job.rb[1] : job.rb[m];
-    int T = 1;
-    while (T < 64 && 2 * T * rb_eff <= target) T *= 2;
-    if (rope_pairs && T < 2) T = 2;
-    job.tile_rows[m] = T;
-    const int nseg = paired ? 2 : 1;
-    need = std::max<int64_t>(need, T * rb_eff + 32 * nseg);
-    (void)NW;
-    job.tile_start[m] = tiles;
+    const int bb = block_bytes(fmt[m]);
+    const int nbr = cols / qk;
+    job.rb[m] = (int64_t)nbr * bb;
+    const int nseg = (int)((job.rb[m] + kSegMax - 1) / kSegMax);
+    job.seg_blocks[m] = (nbr + nseg - 1) / nseg;
+    job.nseg[m] = (nbr + job.seg_blocks[m] - 1) / job.seg_blocks[m];
+    job.item_start[m] = items;
     job.row_base[m] = rbase;
     rbase += rows[m];
-    if (!paired || m == 0) tiles += (rows[m] + T - 1) / T;
+    if (!paired || m == 0) items += pairs ? rows[m] / 2 : rows[m];
   }
-  if (paired) {
-    job.tile_rows[1] = job.tile_rows[0];
-    job.tile_start[1] = tiles;
-  }
-  job.tile_start[nmat] = tiles;
-  const int64_t per_load = (int64_t)job.nthreads * 16;
-  job.lpw = (int)((need + per_load - 1) / per_load);
-  if (job.lpw > kLpwMax) return NT_EUNSUPPORTED;
-  job.tile_cap = (uint32_t)(job.lpw * per_load);
-  uint32_t off = job.tile_cap;
+  if (paired) job.item_start[1] = items;
+  job.item_start[nmat] = items;
+  uint32_t off = 0;
   job.x_hi = off; off += cols;
   job.x_lo = off; off += cols;
   job.x_sc = off; off += (cols / 32) * 4;
   job.x_sum = off; off += (cols / 16) * 4;
-  job.ypart = off; off += kMaxYpart * 4;
   job.red = off; off += 16 * 4;
-  job.lds_bytes = (off + 15) & ~15u;
-  if (job.lds_bytes > 160 * 1024) return NT_EUNSUPPORTED;
+  off = (off + 15) & ~15u;
+  job.slab = off;
+  const int64_t room = 160 * 1024 - (int64_t)off;
+  const int nw = (int)std::min<int64_t>(kMaxWaves, room / kSlab);
+  if (nw < 4) return NT_EUNSUPPORTED;
+  job.nwaves = nw;
+  job.lds_bytes = off + (uint32_t)nw * kSlab;
   return NT_OK;
 }
 
-int launch_gemv(const TileJob& job, const ProArgs& pro, int epi, const EpiArgs& ea, hipStream_t stream) {
+int launch_gemv(const Job& job, const ProArgs& pro, int epi, const EpiArgs& ea, hipStream_t stream) {
   switch (epi) {
     case EPI_STORE: return launch_epi<EPI_STORE>(job, pro, ea, stream);
     case EPI_RESID: return launch_epi<EPI_RESID>(job, pro, ea, stream);

@@ -1,0 +1,113 @@
+"""Parity of nt_decode_layer (HIP) against the fp64 oracle layer.
+
+Bar: ||x_out - x_oracle||_inf / ||x_oracle||_inf <= 5e-3 per token; the
+appended f16 K/V rows agree within 2e-3 of their largest magnitude.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import workloads as wl
+from tests.gpu_util import device, rel_inf, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+LAYER_TOL = 5e-3
+KV_TOL = 2e-3
+
+
+def run_layer(shape, fmts, wid, layer, max_ctx, n_past, M, x=None):
+    import torch
+    import quantized_decode_dequant_amd as nt
+    from quantized_decode_dequant_amd.model import DeviceLayer, cfg_of
+    say(f"layer hidden={shape.hidden} fmts={[synth.FMT_NAMES[fmts[m]] for m in wl.MATS]} pos={n_past} M={M}")
+    li = wl.gen_layer(shape, fmts, wid, layer, max_ctx, n_past)
+    if x is None:
+        x = np.stack([wl.gen_x(shape.hidden, wid, layer, 200 + i) for i in range(M)])
+    dl = DeviceLayer(li, device())
+    cfg = cfg_of(shape, max_ctx)
+    ws = torch.zeros(nt.layer_workspace_bytes(cfg, M), dtype=torch.uint8, device=device())
+    xd = to_dev(x.astype(np.float32).reshape(-1))
+    pos = torch.tensor([n_past], dtype=torch.int32, device=device())
+    nt.decode_layer(cfg, dl.struct, xd, M, pos, ws)
+    torch.cuda.synchronize()
+    got = xd.cpu().numpy().reshape(M, shape.hidden)
+    kc = dl.k_cache.cpu().numpy().view(np.uint16)
+    vc = dl.v_cache.cpu().numpy().view(np.uint16)
+    ref = oracle.layer(li, x, n_past, M)  # updates li's caches in place
+    return got, ref, kc, vc, li
+
+
+def check(got, ref, kc, vc, li, n_past, M):
+    for i in range(M):
+        err = rel_inf(got[i], ref[i])
+        say(f"  token {i}: layer rel err {err:.2e}")
+        assert err <= LAYER_TOL
+    for c_gpu, c_ref in ((kc, li.k_cache), (vc, li.v_cache)):
+        new_g = c_gpu[:, n_past:n_past + M].view(np.float16).astype(np.float64)
+        new_r = c_ref[:, n_past:n_past + M].view(np.float16).astype(np.float64)
+        assert rel_inf(new_g, new_r) <= KV_TOL
+        # everything else in the cache is untouched
+        assert np.array_equal(np.delete(c_gpu, range(n_past, n_past + M), axis=1),
+                              np.delete(c_ref, range(n_past, n_past + M), axis=1))
+
+
+@pytest.mark.parametrize("fmts", [wl.ALL_Q8_0, wl.ALL_Q4_0, wl.Q4_K_M, wl.ALL_Q6_K], ids=["q8_0", "q4_0", "q4_k_m", "q6_k"])
+@pytest.mark.parametrize("n_past,M", [(37, 1), (0, 1), (20, 3), (63, 1)])
+def test_layer_tiny(fmts, n_past, M):
+    got, ref, kc, vc, li = run_layer(wl.TINY, fmts, wl.W_TEST, 3, 64, n_past, M)
+    check(got, ref, kc, vc, li, n_past, M)
+
+
+def test_layer_8b_q4_0_full():
+    # Llama-3-8B-shaped layer, Q4_0, 512 cached positions
+    got, ref, kc, vc, li = run_layer(wl.LLAMA8B, wl.ALL_Q4_0, wl.W_LAYER_8B, 0, 520, 512, 1)
+    check(got, ref, kc, vc, li, 512, 1)
+
+
+def test_layer_70b_q4_k_m_full():
+    # Llama-70B-shaped layer in the Q4_K_M mix, 4096 cached positions
+    got, ref, kc, vc, li = run_layer(wl.LLAMA70B, wl.Q4_K_M, wl.W_GEMV_70B, 0, 4104, 4096, 1)
+    check(got, ref, kc, vc, li, 4096, 1)
+
+
+def test_layer_position_out_of_range_leaves_cache_alone():
+    import torch
+    import quantized_decode_dequant_amd as nt
+    from quantized_decode_dequant_amd.model import DeviceLayer, cfg_of
+    shape, max_ctx = wl.TINY, 16
+    li = wl.gen_layer(shape, wl.ALL_Q4_0, wl.W_TEST, 4, max_ctx, 10)
+    dl = DeviceLayer(li, device())
+    k0 = dl.k_cache.clone()
+    v0 = dl.v_cache.clone()
+    cfg = cfg_of(shape, max_ctx)
+    ws = torch.zeros(nt.layer_workspace_bytes(cfg, 2), dtype=torch.uint8, device=device())
+    xd = to_dev(np.ones(2 * shape.hidden, np.float32))
+    for bad in (max_ctx, max_ctx + 100, -1):
+        pos = torch.tensor([bad], dtype=torch.int32, device=device())
+        nt.decode_layer(cfg, dl.struct, xd, 1, pos, ws)
+    pos = torch.tensor([max_ctx - 1], dtype=torch.int32, device=device())
+    nt.decode_layer(cfg, dl.struct, xd, 2, pos, ws)  # second token would land past the end
+    torch.cuda.synchronize()
+    assert torch.equal(dl.v_cache[:, :max_ctx - 1], v0[:, :max_ctx - 1])
+    assert torch.equal(dl.k_cache[:, :max_ctx - 1], k0[:, :max_ctx - 1])
+
+
+def test_layer_argument_errors():
+    import torch
+    import quantized_decode_dequant_amd as nt
+    from quantized_decode_dequant_amd.model import DeviceLayer, cfg_of
+    li = wl.gen_layer(wl.TINY, wl.ALL_Q4_0, wl.W_TEST, 5, 16, 4)
+    dl = DeviceLayer(li, device())
+    cfg = cfg_of(wl.TINY, 16)
+    need = nt.layer_workspace_bytes(cfg, 1)
+    ws = torch.zeros(need - 256, dtype=torch.uint8, device=device())
+    xd = to_dev(np.ones(wl.TINY.hidden, np.float32))
+    pos = torch.tensor([4], dtype=torch.int32, device=device())
+    with pytest.raises(nt.NtError) as e:
+        nt.decode_layer(cfg, dl.struct, xd, 1, pos, ws)
+    assert e.value.status == -3
+    with pytest.raises(nt.NtError) as e:
+        nt.decode_layer(cfg, dl.struct, xd, 9, pos, torch.zeros(need, dtype=torch.uint8, device=device()))
+    assert e.value.status == -1
