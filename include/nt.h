@@ -187,6 +187,26 @@ int nt_decode_step(const nt_model* model, const int32_t* token_dev, const int32_
 int nt_verify_step(const nt_model* model, const int32_t* tokens_dev, int M, const int32_t* pos_dev,
                    int32_t* argmax_dev, float* logits_dev, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Instrumentation.  nt_trace_begin(kind) makes the library record a HIP event
+ * pair, on the launch stream, around every following launch of one kernel
+ * kind (up to 4096 launches); nt_trace_end waits for those events and returns
+ * the number of launches traced and their summed duration in milliseconds
+ * (*total_ms).  Kinds: 0 plain GEMV, 1 GEMV + residual add (O and down
+ * projections), 2 QKV + RoPE + KV append, 3 gate/up + SwiGLU, 4 attention.
+ * Tracing is per process and not thread safe; it adds two event records per
+ * traced launch.
+ */
+typedef enum nt_trace_kind {
+  NT_TRACE_GEMV = 0,
+  NT_TRACE_GEMV_RESID = 1,
+  NT_TRACE_QKV = 2,
+  NT_TRACE_FFN_UP = 3,
+  NT_TRACE_ATTN = 4
+} nt_trace_kind;
+int nt_trace_begin(int kind);
+int nt_trace_end(int* launches, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

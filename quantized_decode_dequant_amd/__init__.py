@@ -71,7 +71,24 @@ EXPORTS = {
     "nt_verify_step": (ctypes.c_int, [ctypes.POINTER(Model), ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                       ctypes.c_void_p]),
+    "nt_trace_begin": (ctypes.c_int, [ctypes.c_int]),
+    "nt_trace_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]),
 }
+
+TRACE_GEMV, TRACE_GEMV_RESID, TRACE_QKV, TRACE_FFN_UP, TRACE_ATTN = 0, 1, 2, 3, 4
+
+
+def trace_begin(kind: int) -> None:
+    """Time every following launch of one kernel kind with HIP events (nt_trace_begin)."""
+    _check("nt_trace_begin", lib().nt_trace_begin(kind))
+
+
+def trace_end() -> tuple[int, float]:
+    """(launches traced, summed milliseconds) since trace_begin (nt_trace_end)."""
+    n = ctypes.c_int()
+    ms = ctypes.c_double()
+    _check("nt_trace_end", lib().nt_trace_end(ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
 
 
 def lib():

@@ -84,7 +84,7 @@ int run_layer(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const i
     const int rows[3] = {nq, nkv, nkv};
     if ((rc = plan_job(job, 3, W, fmt, rows, c.hidden, 0, 1)) != NT_OK) return rc;
     for (int i = 0; i < M; ++i) {
-      ProArgs pro{x + (int64_t)i * c.hidden, L.attn_norm, c.rms_eps, 0};
+      ProArgs pro{x + (int64_t)i * c.hidden, L.attn_norm, c.rms_eps, 0, c.head_dim, c.rope_theta, pos, i};
       EpiArgs ea{};
       ea.q_out = q + (int64_t)i * nq;
       ea.k_cache = L.k_cache;
@@ -127,21 +127,21 @@ int run_layer(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const i
     float* xi = x + (int64_t)i * c.hidden;
     // 3. h = x + Wo o
     {
-      ProArgs pro{o + (int64_t)i * nq, nullptr, 0.f, 0};
+      ProArgs pro{o + (int64_t)i * nq, nullptr, 0.f, 0, 0, 0.f, nullptr, 0};
       EpiArgs ea{};
       ea.y = xi;
       if ((rc = launch_gemv(jo, pro, EPI_RESID, ea, st)) != NT_OK) return rc;
     }
     // 4. a = silu(Wg hn) * (Wu hn), hn = RMSNorm(h)
     {
-      ProArgs pro{xi, L.ffn_norm, c.rms_eps, 0};
+      ProArgs pro{xi, L.ffn_norm, c.rms_eps, 0, 0, 0.f, nullptr, 0};
       EpiArgs ea{};
       ea.y = a;
       if ((rc = launch_gemv(jf, pro, EPI_SWIGLU, ea, st)) != NT_OK) return rc;
     }
     // 5. x = h + Wd a
     {
-      ProArgs pro{a, nullptr, 0.f, 0};
+      ProArgs pro{a, nullptr, 0.f, 0, 0, 0.f, nullptr, 0};
       EpiArgs ea{};
       ea.y = xi;
       if ((rc = launch_gemv(jd, pro, EPI_RESID, ea, st)) != NT_OK) return rc;
@@ -300,7 +300,7 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
     if ((rc = plan_job(jl, 1, W, fmt, rows, m.cfg.hidden, 0, 0)) != NT_OK) return rc;
   }
   for (int i = 0; i < M; ++i) {
-    ProArgs pro{x + (int64_t)i * m.cfg.hidden, m.out_norm, m.cfg.rms_eps, 0};
+    ProArgs pro{x + (int64_t)i * m.cfg.hidden, m.out_norm, m.cfg.rms_eps, 0, 0, 0.f, nullptr, 0};
     EpiArgs ea{};
     ea.y = logits + (int64_t)i * m.vocab;
     if ((rc = launch_gemv(jl, pro, EPI_STORE, ea, st)) != NT_OK) return rc;
@@ -349,7 +349,7 @@ int nt_gemv_q(int fmt, const void* W, const float* x, float* y, int64_t rows, in
   const int r = (int)rows;
   int rc = plan_job(job, 1, &Wp, &fmt, &r, (int)cols, 0, 0);
   if (rc != NT_OK) return rc;
-  ProArgs pro{x, nullptr, 0.f, 0};
+  ProArgs pro{x, nullptr, 0.f, 0, 0, 0.f, nullptr, 0};
   EpiArgs ea{};
   ea.y = y;
   return launch_gemv(job, pro, EPI_STORE, ea, static_cast<hipStream_t>(stream));
@@ -370,7 +370,7 @@ int nt_gemm_q_small(int fmt, const void* W, const float* X, float* Y, int M, int
   int rc = plan_job(job, 1, &Wp, &fmt, &r, (int)cols, 0, 0);
   if (rc != NT_OK) return rc;
   for (int m = 0; m < M; ++m) {
-    ProArgs pro{X + (int64_t)m * cols, nullptr, 0.f, 0};
+    ProArgs pro{X + (int64_t)m * cols, nullptr, 0.f, 0, 0, 0.f, nullptr, 0};
     EpiArgs ea{};
     ea.y = Y + (int64_t)m * rows;
     if ((rc = launch_gemv(job, pro, EPI_STORE, ea, static_cast<hipStream_t>(stream))) != NT_OK) return rc;

@@ -325,6 +325,7 @@ void attn_plan(int n_kv, int max_ctx, int& chunk, int& nsplit) {
 int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, const int32_t* pos, int n_query,
                      int n_head, int n_kv, int head_dim, int max_ctx, int chunk, int nsplit, float* part_o,
                      float* part_ml, float* o, hipStream_t stream) {
+  trace_before(NT_TRACE_ATTN, stream);
   for (int qi = 0; qi < n_query; ++qi) {
     const dim3 grid(n_kv, nsplit);
     switch (head_dim) {
@@ -337,7 +338,9 @@ int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, con
   }
   hipLaunchKernelGGL(k_attn_combine, dim3(n_head, n_query), dim3(128), 0, stream, part_o, part_ml, pos, n_head, head_dim,
                      chunk, nsplit, max_ctx, o);
-  return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
+  const bool ok = hipGetLastError() == hipSuccess;
+  trace_after(NT_TRACE_ATTN, stream);
+  return ok ? NT_OK : NT_EHIP;
 }
 
 int launch_embed(int fmt, const void* E, const int32_t* tokens, int M, int vocab, int cols, float* x,

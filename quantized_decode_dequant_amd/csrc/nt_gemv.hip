@@ -2,25 +2,30 @@
 //
 // One engine serves every projection of the decode (GEMV is the per-token
 // kernel the ntransformer pages list first; p2 "Architecture et structure du
-// code").  Structure of one workgroup:
+// code").  One workgroup runs per CU.
 //
 //   prologue  The activation vector (optionally RMSNorm'ed with gains) is
 //             staged on chip as 16-bit fixed point per 32-element block: an
 //             fp32 scale s_b and integers X in [-32639, 32639], split into a
 //             high and a low int8 plane (X = 256*hi + lo) plus per-16 sums of
 //             X.  Weight x activation products then run on v_dot4_i32_i8
-//             with exact integer sums per quantization sub-block.
-//   stream    After the prologue every wave works alone (no more workgroup
-//             barriers).  It owns a contiguous range of work items (rows, or
-//             row pairs) and streams their bytes through a private 8 KB LDS
-//             slab: a segment of a row -- a contiguous byte range -- is
-//             loaded HBM -> registers with 16-byte coalesced loads, written
-//             to the slab, and the next segment's loads are issued before the
-//             current one is computed, so every wave keeps ~8 KB in flight.
-//             Lanes read their blocks from the slab at any byte alignment
-//             (Q8_0, Q4_0 and Q6_K blocks are only 2-byte aligned), unpack
-//             quants in registers and accumulate.
-//   reduce    Lanes of a wave sum with a butterfly per row.
+//             with exact integer sums per quantization sub-block.  This is
+//             the only workgroup barrier.
+//   columns   A lane owns one 64-weight column unit of the current column
+//             slice (4096 weights) and keeps its staged activation in
+//             registers; a wave works through a group of rows slice by
+//             slice, so the activation is read from LDS once per slice and
+//             row group, not once per row.
+//   stream    Each wave owns a contiguous range of work items (groups of rows)
+//             and streams their bytes, segment by segment (one row within
+//             one column slice: a contiguous byte range), HBM -> registers
+//             with 16-byte coalesced non-temporal loads.  Two segments are in
+//             flight while the previous one is written to the wave's LDS
+//             slab and computed: lanes read their blocks from the slab at
+//             any byte alignment (Q8_0, Q4_0 and Q6_K blocks are only 2-byte
+//             aligned), unpack quants in registers and accumulate.
+//   reduce    Per segment, a butterfly over the wave's lanes; per row, the
+//             slices add up in the wave's LDS row sums.
 //   epilogue  Plain store, residual add, SwiGLU (gate and up rows in one
 //             item) or RoPE + q store + f16 K/V append (row pairs).
 //
@@ -64,69 +69,105 @@ __device__ __forceinline__ void ld_unaligned(uint32_t off, uint32_t (&out)[N]) {
   for (int i = 0; i < N; ++i) out[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// Sum over the 64 lanes of a wave: an inclusive scan with DPP row shifts and
+// row broadcasts leaves the total in lane 63, which is read into a scalar.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_shift(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, false));
 }
 
-// Offsets of the staged activation in LDS.
-struct XL {
-  uint32_t hi, lo, sc, sum;
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_shift<0x111, 0xf>(v);  // row_shr:1 within rows of 16 lanes
+  v += dpp_shift<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_shift<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_shift<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_shift<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_shift<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+
+// Activation of the lane's two column units in the current slice: int8 high
+// and low planes of 64 elements each, the scale of each 32-block and the sum
+// of X over each 16 elements.
+struct XR {
+  uint32_t hi[kUnitsPerLane][16], lo[kUnitsPerLane][16];
+  float sc[kUnitsPerLane][2];
+  int sm[kUnitsPerLane][4];
 };
 
-// ---------------------------------------------------------------- units
-// A unit is the work of one lane on one row: 32 weights (Q8_0, Q4_0, Q4_K)
-// or 64 weights (Q6_K).  `row` is the LDS byte offset of the row's first block.
-
-// Q8_0: unit u is block u.  w = d*q.
-__device__ __forceinline__ float unit_q8_0(uint32_t row, int u, uint32_t xe, const XL& x) {
-  const uint32_t blk = row + 34u * u;
-  const float d = h2f(ld16(blk));
-  uint32_t q[8];
-  ld_unaligned<8>(blk + 2, q);
-  const uint32_t e0 = xe + 32u * u;
-  const uint4 h0 = ld128(x.hi + e0), h1 = ld128(x.hi + e0 + 16);
-  const uint4 l0 = ld128(x.lo + e0), l1 = ld128(x.lo + e0 + 16);
-  int H = 0, L = 0;
-  H = dot4(q[0], h0.x, H); L = dot4(q[0], l0.x, L);
-  H = dot4(q[1], h0.y, H); L = dot4(q[1], l0.y, L);
-  H = dot4(q[2], h0.z, H); L = dot4(q[2], l0.z, L);
-  H = dot4(q[3], h0.w, H); L = dot4(q[3], l0.w, L);
-  H = dot4(q[4], h1.x, H); L = dot4(q[4], l1.x, L);
-  H = dot4(q[5], h1.y, H); L = dot4(q[5], l1.y, L);
-  H = dot4(q[6], h1.z, H); L = dot4(q[6], l1.z, L);
-  H = dot4(q[7], h1.w, H); L = dot4(q[7], l1.w, L);
-  const int S = (H << 8) + L;
-  return d * ldf(x.sc + (e0 >> 3)) * (float)S;
+__device__ __forceinline__ void load_xr(const Job& job, int slice, int lane, XR& xr) {
+#pragma unroll
+  for (int j = 0; j < kUnitsPerLane; ++j) {
+    const int k = lane + 64 * j;
+    const uint32_t e0 = 64u * (uint32_t)(slice * job.ups + k);
+    if (k < job.ups && e0 < (uint32_t)job.cols) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 h = ld128(job.x_hi + e0 + 16 * i), l = ld128(job.x_lo + e0 + 16 * i);
+        xr.hi[j][4 * i] = h.x; xr.hi[j][4 * i + 1] = h.y; xr.hi[j][4 * i + 2] = h.z; xr.hi[j][4 * i + 3] = h.w;
+        xr.lo[j][4 * i] = l.x; xr.lo[j][4 * i + 1] = l.y; xr.lo[j][4 * i + 2] = l.z; xr.lo[j][4 * i + 3] = l.w;
+      }
+      xr.sc[j][0] = ldf(job.x_sc + (e0 >> 3));
+      xr.sc[j][1] = ldf(job.x_sc + (e0 >> 3) + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr.sm[j][i] = ldi32(job.x_sum + (e0 >> 2) + 4 * i);
+    }
+  }
 }
 
-// Q4_0: unit u is block u.  Byte j: low nibble -> element j, high -> j+16.
-// w = d*(q-8), so sum w*X = d*(sum q*X - 8*sum X).
-__device__ __forceinline__ float unit_q4_0(uint32_t row, int u, uint32_t xe, const XL& x) {
-  const uint32_t blk = row + 18u * u;
-  const float d = h2f(ld16(blk));
-  uint32_t q[4];
-  ld_unaligned<4>(blk + 2, q);
-  const uint32_t e0 = xe + 32u * u;
-  const uint4 h0 = ld128(x.hi + e0), h1 = ld128(x.hi + e0 + 16);
-  const uint4 l0 = ld128(x.lo + e0), l1 = ld128(x.lo + e0 + 16);
-  int H = 0, L = 0;
-#define NT_Q40_STEP(W, HA, LA, HB, LB)                 \
-  {                                                    \
-    const uint32_t lo4 = (W) & 0x0F0F0F0Fu;            \
-    const uint32_t hi4 = ((W) >> 4) & 0x0F0F0F0Fu;    \
-    H = dot4(lo4, HA, H); L = dot4(lo4, LA, L);        \
-    H = dot4(hi4, HB, H); L = dot4(hi4, LB, L);        \
+// ---------------------------------------------------------------- units
+// A unit is 64 consecutive weights of one row: column unit k of the slice.
+// `seg` is the LDS byte offset of the segment's first block; XH/XL/XS/XM the
+// lane's activation registers for the unit.
+
+#define NT_XARGS const uint32_t(&xh)[16], const uint32_t(&xl)[16], const float(&xs)[2], const int(&xm)[4]
+
+// Q8_0: blocks 2k and 2k+1 (the second only if `two`).  w = d*q.
+__device__ __forceinline__ float unit_q8_0(uint32_t seg, int k, bool two, NT_XARGS) {
+  float acc = 0.f;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    if (b == 1 && !two) break;
+    const uint32_t blk = seg + 34u * (2 * k + b);
+    const float d = h2f(ld16(blk));
+    uint32_t q[8];
+    ld_unaligned<8>(blk + 2, q);
+    int H = 0, L = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      H = dot4(q[i], xh[8 * b + i], H);
+      L = dot4(q[i], xl[8 * b + i], L);
+    }
+    acc += d * xs[b] * (float)((H << 8) + L);
   }
-  NT_Q40_STEP(q[0], h0.x, l0.x, h1.x, l1.x)
-  NT_Q40_STEP(q[1], h0.y, l0.y, h1.y, l1.y)
-  NT_Q40_STEP(q[2], h0.z, l0.z, h1.z, l1.z)
-  NT_Q40_STEP(q[3], h0.w, l0.w, h1.w, l1.w)
-#undef NT_Q40_STEP
-  const int xs = ldi32(x.sum + (e0 >> 2)) + ldi32(x.sum + (e0 >> 2) + 4);
-  const int S = (H << 8) + L - 8 * xs;
-  return d * ldf(x.sc + (e0 >> 3)) * (float)S;
+  return acc;
+}
+
+// Q4_0: blocks 2k and 2k+1.  Byte j of a block: low nibble -> element j,
+// high nibble -> element j+16.  w = d*(q-8), so sum w*X = d*(sum q*X - 8 sum X).
+__device__ __forceinline__ float unit_q4_0(uint32_t seg, int k, bool two, NT_XARGS) {
+  float acc = 0.f;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    if (b == 1 && !two) break;
+    const uint32_t blk = seg + 18u * (2 * k + b);
+    const float d = h2f(ld16(blk));
+    uint32_t q[4];
+    ld_unaligned<4>(blk + 2, q);
+    int H = 0, L = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo4 = q[i] & 0x0F0F0F0Fu, hi4 = (q[i] >> 4) & 0x0F0F0F0Fu;
+      H = dot4(lo4, xh[8 * b + i], H);
+      L = dot4(lo4, xl[8 * b + i], L);
+      H = dot4(hi4, xh[8 * b + 4 + i], H);
+      L = dot4(hi4, xl[8 * b + 4 + i], L);
+    }
+    const int S = (H << 8) + L - 8 * (xm[2 * b] + xm[2 * b + 1]);
+    acc += d * xs[b] * (float)S;
+  }
+  return acc;
 }
 
 // Q4_K: 6-bit scale and min of sub-block s from the 12 packed bytes
@@ -146,85 +187,75 @@ __device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t
   }
 }
 
-// Q4_K: unit u = 16 bytes of quants: superblock u/8, chunk c = (u%8)/2 (64
-// weights, bytes 32c..32c+31), half h = u%2.  Low nibbles are elements
-// 64c+16h+i (sub-block 2c), high nibbles 64c+32+16h+i (sub-block 2c+1).
-// w = d*sc*q - dmin*m.
-__device__ __forceinline__ float unit_q4_k(uint32_t row, int u, uint32_t xe, const XL& x) {
-  const int sb = u >> 3, part = u & 7, c = part >> 1, h = part & 1;
-  const uint32_t blk = row + 144u * sb;
+// Q4_K: unit k is chunk c = k%4 (64 weights) of superblock k/4: quant bytes
+// 32c..32c+31, whose low nibbles are the chunk's first 32 weights (sub-block
+// 2c) and high nibbles the next 32 (sub-block 2c+1).  w = d*sc*q - dmin*m.
+__device__ __forceinline__ float unit_q4_k(uint32_t seg, int k, NT_XARGS) {
+  const int sb = k >> 2, c = k & 3;
+  const uint32_t blk = seg + 144u * sb;
   const uint4 hd = ld128(blk);
-  const uint4 qs = ld128(blk + 16 + 32 * c + 16 * h);
+  const uint4 q0 = ld128(blk + 16 + 32 * c), q1 = ld128(blk + 32 + 32 * c);
   const float d = h2f(hd.x & 0xffffu), dmin = h2f(hd.x >> 16);
   int scA, mA, scB, mB;
   q4k_scale_min(hd.y, hd.z, hd.w, 2 * c, scA, mA);
   q4k_scale_min(hd.y, hd.z, hd.w, 2 * c + 1, scB, mB);
-  const uint32_t eA = xe + 256u * sb + 64 * c + 16 * h, eB = eA + 32;
-  const uint4 ah = ld128(x.hi + eA), al = ld128(x.lo + eA);
-  const uint4 bh = ld128(x.hi + eB), bl = ld128(x.lo + eB);
+  const uint32_t qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
   int AH = 0, AL = 0, BH = 0, BL = 0;
-#define NT_Q4K_STEP(W, AHX, ALX, BHX, BLX)             \
-  {                                                    \
-    const uint32_t lo4 = (W) & 0x0F0F0F0Fu;            \
-    const uint32_t hi4 = ((W) >> 4) & 0x0F0F0F0Fu;     \
-    AH = dot4(lo4, AHX, AH); AL = dot4(lo4, ALX, AL);  \
-    BH = dot4(hi4, BHX, BH); BL = dot4(hi4, BLX, BL);  \
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t lo4 = qv[i] & 0x0F0F0F0Fu, hi4 = (qv[i] >> 4) & 0x0F0F0F0Fu;
+    AH = dot4(lo4, xh[i], AH);
+    AL = dot4(lo4, xl[i], AL);
+    BH = dot4(hi4, xh[8 + i], BH);
+    BL = dot4(hi4, xl[8 + i], BL);
   }
-  NT_Q4K_STEP(qs.x, ah.x, al.x, bh.x, bl.x)
-  NT_Q4K_STEP(qs.y, ah.y, al.y, bh.y, bl.y)
-  NT_Q4K_STEP(qs.z, ah.z, al.z, bh.z, bl.z)
-  NT_Q4K_STEP(qs.w, ah.w, al.w, bh.w, bl.w)
-#undef NT_Q4K_STEP
   const int SA = (AH << 8) + AL, SB = (BH << 8) + BL;
-  const int XA = ldi32(x.sum + 4u * (eA >> 4)), XB = ldi32(x.sum + 4u * (eB >> 4));
-  const float sA = ldf(x.sc + 4u * (eA >> 5)), sB = ldf(x.sc + 4u * (eB >> 5));
-  return sA * (d * (float)scA * (float)SA - dmin * (float)mA * (float)XA) +
-         sB * (d * (float)scB * (float)SB - dmin * (float)mB * (float)XB);
+  return xs[0] * (d * (float)scA * (float)SA - dmin * (float)mA * (float)(xm[0] + xm[1])) +
+         xs[1] * (d * (float)scB * (float)SB - dmin * (float)mB * (float)(xm[2] + xm[3]));
 }
 
-// Q6_K: unit u = 64 weights: superblock u/4, half n = (u%4)/2, l0 = 16*(u%2).
-// For quarter k = 0..3 the elements are 128n + 32k + l0 + i (i < 16), with
-// low four bits from nibble k/2 of ql[64n + 32(k%2) + l0 + i], high two bits
-// from bits 2k..2k+1 of qh[32n + l0 + i], and scale sc[8n + 2k + l0/16].
-// w = d*sc*(q-32).
-__device__ __forceinline__ float unit_q6_k(uint32_t row, int u, uint32_t xe, const XL& x) {
-  const int sb = u >> 2, part = u & 3, n = part >> 1, hl = part & 1;
-  const uint32_t blk = row + 210u * sb;
-  uint32_t qa[4], qb[4], qh[4], scw[3];
-  ld_unaligned<4>(blk + 64 * n + 16 * hl, qa);
-  ld_unaligned<4>(blk + 64 * n + 32 + 16 * hl, qb);
-  ld_unaligned<4>(blk + 128 + 32 * n + 16 * hl, qh);
-  ld_unaligned<3>(blk + 192 + 8 * n, scw);  // sc[8n .. 8n+7] (+4 spare bytes)
+// Q6_K: unit k covers elements 64p..64p+63 of superblock k/4, p = k%4, i.e.
+// half n = p/2, quarters q = 2h and 2h+1 (h = p%2).  Element 32q'+l of half n
+// (q' = 0..3, l < 32) takes its low four bits from nibble q'/2 of
+// ql[64n + 32(q'%2) + l], its high two bits from bits 2q'..2q'+1 of
+// qh[32n + l], and scale sc[8n + 2q' + l/16].  w = d*sc*(q-32).
+__device__ __forceinline__ float unit_q6_k(uint32_t seg, int k, NT_XARGS) {
+  const int sb = k >> 2, p = k & 3, n = p >> 1, h = p & 1;
+  const uint32_t blk = seg + 210u * sb;
+  uint32_t qa[8], qb[8], qh[8], scw[1];
+  ld_unaligned<8>(blk + 64 * n, qa);       // ql[64n .. 64n+31]
+  ld_unaligned<8>(blk + 64 * n + 32, qb);  // ql[64n+32 .. 64n+63]
+  ld_unaligned<8>(blk + 128 + 32 * n, qh); // qh[32n .. 32n+31]
+  ld_unaligned<1>(blk + 192 + 8 * n + 4 * h, scw);
   const float d = h2f(ld16(blk + 208));
-  const uint32_t e0 = xe + 256u * sb + 128 * n + 16 * hl;
+  const int sh = 4 * h;
+  int H[4] = {0, 0, 0, 0}, L[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t hb = qh[i] >> sh;
+    const uint32_t a = ((qa[i] >> sh) & 0x0F0F0F0Fu) | ((hb << 4) & 0x30303030u);
+    const uint32_t b = ((qb[i] >> sh) & 0x0F0F0F0Fu) | ((hb << 2) & 0x30303030u);
+    H[i >> 2] = dot4(a, xh[i], H[i >> 2]);
+    L[i >> 2] = dot4(a, xl[i], L[i >> 2]);
+    H[2 + (i >> 2)] = dot4(b, xh[8 + i], H[2 + (i >> 2)]);
+    L[2 + (i >> 2)] = dot4(b, xl[8 + i], L[2 + (i >> 2)]);
+  }
   float acc = 0.f;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t e = e0 + 32 * k;
-    const uint4 xh = ld128(x.hi + e), xl = ld128(x.lo + e);
-    const uint32_t xhv[4] = {xh.x, xh.y, xh.z, xh.w}, xlv[4] = {xl.x, xl.y, xl.z, xl.w};
-    int H = 0, L = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t q;
-      if (k == 0) q = (qa[i] & 0x0F0F0F0Fu) | ((qh[i] << 4) & 0x30303030u);
-      else if (k == 1) q = (qb[i] & 0x0F0F0F0Fu) | ((qh[i] << 2) & 0x30303030u);
-      else if (k == 2) q = ((qa[i] >> 4) & 0x0F0F0F0Fu) | (qh[i] & 0x30303030u);
-      else q = ((qb[i] >> 4) & 0x0F0F0F0Fu) | ((qh[i] >> 2) & 0x30303030u);
-      H = dot4(q, xhv[i], H);
-      L = dot4(q, xlv[i], L);
-    }
-    const int S = (H << 8) + L - 32 * ldi32(x.sum + 4u * (e >> 4));
-    const int sidx = 2 * k + hl;  // scale byte within sc[8n .. 8n+7]
-    const int sc = (int)(int8_t)(scw[sidx >> 2] >> (8 * (sidx & 3)));
-    acc += (float)S * ((float)sc * ldf(x.sc + 4u * (e >> 5)));
+  for (int g = 0; g < 4; ++g) {
+    const int S = (H[g] << 8) + L[g] - 32 * xm[g];
+    const int sc = (int)(int8_t)(scw[0] >> (8 * g));
+    acc += (float)S * ((float)sc * xs[g >> 1]);
   }
   return d * acc;
 }
 
+#undef NT_XARGS
+
 // ----------------------------------------------------------------- prologue
 // Stage the activation: v = src (or RMSNorm(src) * gain), then per 32-block
 // s = max|v| / 32639, X = rint(v / s), hi = (X + 128) >> 8, lo = X - 256 hi.
+// For the QKV launch it also tabulates the RoPE rotation of this position.
 __device__ __forceinline__ void stage_x(const Job& job, const ProArgs& pro, int tid) {
   const int cols = job.cols, NT = job.nwaves * 64;
   const float* src = pro.src;
@@ -255,43 +286,50 @@ __device__ __forceinline__ void stage_x(const Job& job, const ProArgs& pro, int 
       const float4* g4 = reinterpret_cast<const float4*>(pro.gain + 32 * b);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float4 t = g4[j];
-        v[4 * j] = v[4 * j] * r * t.x;
-        v[4 * j + 1] = v[4 * j + 1] * r * t.y;
-        v[4 * j + 2] = v[4 * j + 2] * r * t.z;
-        v[4 * j + 3] = v[4 * j + 3] * r * t.w;
+        const float4 g = g4[j];
+        v[4 * j] = v[4 * j] * r * g.x;
+        v[4 * j + 1] = v[4 * j + 1] * r * g.y;
+        v[4 * j + 2] = v[4 * j + 2] * r * g.z;
+        v[4 * j + 3] = v[4 * j + 3] * r * g.w;
       }
     }
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
     const float inv = amax > 0.f ? kXMax / amax : 0.f;
-    const float scale = amax / kXMax;
-    uint32_t H[8], L[8];
-    int s0 = 0, s1 = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { H[j] = 0; L[j] = 0; }
+    for (int half = 0; half < 2; ++half) {
+      uint32_t H[4] = {0, 0, 0, 0}, L[4] = {0, 0, 0, 0};
+      int sum = 0;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      int X = __float2int_rn(v[j] * inv);
-      X = max(-32639, min(32639, X));
-      const int hi = (X + 128) >> 8;
-      const int lo = X - (hi << 8);
-      H[j >> 2] |= (uint32_t)(hi & 255) << (8 * (j & 3));
-      L[j >> 2] |= (uint32_t)(lo & 255) << (8 * (j & 3));
-      if (j < 16) s0 += X; else s1 += X;
+      for (int k = 0; k < 16; ++k) {
+        int X = __float2int_rn(v[16 * half + k] * inv);
+        X = max(-32639, min(32639, X));
+        const int hi = (X + 128) >> 8;
+        const int lo = X - (hi << 8);
+        H[k >> 2] |= (uint32_t)(hi & 255) << (8 * (k & 3));
+        L[k >> 2] |= (uint32_t)(lo & 255) << (8 * (k & 3));
+        sum += X;
+      }
+      st128(job.x_hi + 32u * b + 16 * half, make_uint4(H[0], H[1], H[2], H[3]));
+      st128(job.x_lo + 32u * b + 16 * half, make_uint4(L[0], L[1], L[2], L[3]));
+      sti32(job.x_sum + 8u * b + 4 * half, sum);
     }
-    st128(job.x_hi + 32u * b, make_uint4(H[0], H[1], H[2], H[3]));
-    st128(job.x_hi + 32u * b + 16, make_uint4(H[4], H[5], H[6], H[7]));
-    st128(job.x_lo + 32u * b, make_uint4(L[0], L[1], L[2], L[3]));
-    st128(job.x_lo + 32u * b + 16, make_uint4(L[4], L[5], L[6], L[7]));
-    stf(job.x_sc + 4u * b, scale);
-    sti32(job.x_sum + 8u * b, s0);
-    sti32(job.x_sum + 8u * b + 4, s1);
+    stf(job.x_sc + 4u * b, amax / kXMax);
+  }
+  if (pro.rope_hd > 0) {
+    // pair i turns by pos * theta^(-2i/head_dim); the angle is formed in
+    // double so large positions keep fp32 accuracy
+    for (int i = tid; i < pro.rope_hd / 2; i += NT) {
+      const int pos = *pro.pos + pro.pos_add;
+      const double freq = exp2(-(double)(2 * i) / (double)pro.rope_hd * log2((double)pro.rope_theta));
+      const double ang = (double)pos * freq;
+      stf(job.rope + 8u * i, (float)cos(ang));
+      stf(job.rope + 8u * i + 4, (float)sin(ang));
+    }
   }
   __syncthreads();
 }
-
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(1))) u32x4* gptr_u32x4;
@@ -306,184 +344,242 @@ __device__ __forceinline__ uint4 load_chunk(const uint8_t* p) {
 }
 
 // ----------------------------------------------------------- segment stream
-// Position in a wave's stream: item `it`, row `g` within the item, segment
-// `s` within the row.
-struct Pos {
-  int it, g, s;
+// A wave's stream walks its items; within an item, column slices outer and
+// row slots inner (so the activation registers change once per slice).  The
+// cursor is wave-uniform and kept in scalar registers; moving to the next
+// segment is a pointer add except at item, slice or (paired) matrix changes.
+struct Cur {
+  int it, s, g;       // item, slice, row slot
+  int m, r0, nr, ns;  // item: matrix, first row, rows (per matrix), slots
+  int mseg;           // matrix of the current segment
+  const uint8_t* ptr; // first byte of the current segment
 };
+
+__device__ __forceinline__ void item_begin(const Job& job, Cur& c) {
+  int m = 0;
+  while (m + 1 < job.nmat && c.it >= job.item_start[m + 1]) ++m;
+  c.m = m;
+  c.r0 = (c.it - job.item_start[m]) * job.R;
+  c.nr = min(job.R, job.rows[m] - c.r0);
+  c.ns = job.paired ? 2 * c.nr : c.nr;
+}
+
+__device__ __forceinline__ void seg_locate(const Job& job, Cur& c) {
+  const bool second = job.paired && c.g >= c.nr;
+  c.mseg = second ? 1 : c.m;
+  const int row = c.r0 + (second ? c.g - c.nr : c.g);
+  c.ptr = job.W[c.mseg] + (int64_t)row * job.rb[c.mseg] + (int64_t)c.s * job.slice_bytes[c.mseg];
+}
+
+__device__ __forceinline__ void cur_begin(const Job& job, Cur& c, int it) {
+  c.it = it;
+  c.s = 0;
+  c.g = 0;
+  item_begin(job, c);
+  seg_locate(job, c);
+}
+
+// Next segment; false past the wave's last item.
+__device__ __forceinline__ bool cur_next(const Job& job, Cur& c, int it_end) {
+  if (++c.g < c.ns) {
+    if (job.paired && c.g == c.nr) seg_locate(job, c);
+    else c.ptr += job.rb[c.mseg];
+    return true;
+  }
+  c.g = 0;
+  if (++c.s < job.nslice) {
+    seg_locate(job, c);
+    return true;
+  }
+  c.s = 0;
+  if (++c.it >= it_end) return false;
+  item_begin(job, c);
+  seg_locate(job, c);
+  return true;
+}
 
 // Byte range of one segment and where its data sits in the slab.
 struct Seg {
   const uint8_t* a;  // 16-B aligned address of the first chunk
   int nchunks;
-  uint32_t d;        // byte offset of the segment's first block in the slab
-  int m;             // matrix
-  int row;           // row within the matrix
-  int nblk;          // blocks in the segment
-  uint32_t xe;       // element index (column) of the segment's first weight
+  uint32_t d;        // offset of the segment's first block from the first chunk
+  int fmt;
+  int nunits;        // column units in the slice
+  int half;          // the last unit holds a single 32-weight block
 };
 
-__device__ __forceinline__ int item_matrix(const Job& job, int it) {
-  int m = 0;
-  while (m + 1 < job.nmat && it >= job.item_start[m + 1]) ++m;
-  return m;
-}
-
-__device__ __forceinline__ int rows_per_item(const Job& job) { return (job.paired || job.pairs) ? 2 : 1; }
-
-__device__ __forceinline__ Seg seg_of(const Job& job, const Pos& p) {
+__device__ __forceinline__ Seg seg_of(const Job& job, const Cur& c) {
   Seg sg;
-  const int mi = item_matrix(job, p.it);
-  const int li = p.it - job.item_start[mi];
-  if (job.paired) {
-    sg.m = p.g;
-    sg.row = li;
-  } else {
-    sg.m = mi;
-    sg.row = job.pairs ? 2 * li + p.g : li;
-  }
-  const int m = sg.m;
-  const int fmt = job.fmt[m];
-  const int bb = block_bytes(fmt);
-  const int nbr = job.cols / block_elems(fmt);
-  const int b0 = p.s * job.seg_blocks[m];
-  sg.nblk = min(job.seg_blocks[m], nbr - b0);
-  sg.xe = (uint32_t)b0 * block_elems(fmt);
-  const uint8_t* start = job.W[m] + (int64_t)sg.row * job.rb[m] + (int64_t)b0 * bb;
-  sg.a = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(start) & ~uintptr_t(15));
-  sg.d = (uint32_t)(start - sg.a);
-  sg.nchunks = (int)((sg.d + (uint32_t)(sg.nblk * bb) + 15) >> 4);
+  sg.fmt = job.fmt[c.mseg];
+  const bool last = c.s == job.nslice - 1;
+  const int ne = last ? job.last_ne : job.ups * 64;
+  sg.nunits = last ? job.last_units : job.ups;
+  sg.half = (ne & 63) != 0;
+  const int64_t bytes = last ? (int64_t)(ne / block_elems(sg.fmt)) * block_bytes(sg.fmt) : job.slice_bytes[c.mseg];
+  sg.a = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(c.ptr) & ~uintptr_t(15));
+  sg.d = (uint32_t)(c.ptr - sg.a);
+  sg.nchunks = (int)((sg.d + bytes + 15) >> 4);
   return sg;
 }
 
-// Advance to the next segment; returns false past the wave's last item.
-__device__ __forceinline__ bool advance(const Job& job, Pos& p, int it_end) {
-  const int m = job.paired ? p.g : item_matrix(job, p.it);
-  if (++p.s < job.nseg[m]) return true;
-  p.s = 0;
-  if (++p.g < rows_per_item(job)) return true;
-  p.g = 0;
-  return ++p.it < it_end;
-}
-
-__device__ __forceinline__ void seg_load(const Seg& sg, int lane, uint4 (&pre)[kSlabLoads]) {
+// Every lane issues exactly LPL loads (lanes past the segment's end re-read
+// its first chunk), so the number of loads in flight is the same on every
+// path and the waits before the slab store count exactly the older segment.
+template <int LPL>
+__device__ __forceinline__ void seg_load(const Seg& sg, int lane, uint4 (&pre)[LPL]) {
 #pragma unroll
-  for (int i = 0; i < kSlabLoads; ++i) {
+  for (int i = 0; i < LPL; ++i) {
     const int c = lane + 64 * i;
-    if (c < sg.nchunks) pre[i] = load_chunk(sg.a + 16 * (int64_t)c);
+    pre[i] = load_chunk(sg.a + 16 * (c < sg.nchunks ? c : 0));
   }
 }
 
-__device__ __forceinline__ void seg_store(const Seg& sg, uint32_t slab, int lane, const uint4 (&pre)[kSlabLoads]) {
+template <int LPL>
+__device__ __forceinline__ void seg_store(const Seg& sg, uint32_t slab, int lane, const uint4 (&pre)[LPL]) {
 #pragma unroll
-  for (int i = 0; i < kSlabLoads; ++i) {
+  for (int i = 0; i < LPL; ++i) {
     const int c = lane + 64 * i;
     if (c < sg.nchunks) st128(slab + 16u * c, pre[i]);
   }
 }
 
-__device__ __forceinline__ float seg_compute(const Job& job, const Seg& sg, uint32_t slab, int lane) {
-  const XL x{job.x_hi, job.x_lo, job.x_sc, job.x_sum};
-  const uint32_t row = slab + sg.d;
+// This lane's part of one segment's dot product.
+__device__ __forceinline__ float seg_compute(const Seg& sg, uint32_t slab, int lane, const XR& xr) {
+  const uint32_t seg = slab + sg.d;
   float acc = 0.f;
-  switch (job.fmt[sg.m]) {
-    case NT_Q4_K:
-      for (int u = lane; u < 8 * sg.nblk; u += 64) acc += unit_q4_k(row, u, sg.xe, x);
-      break;
-    case NT_Q6_K:
-      for (int u = lane; u < 4 * sg.nblk; u += 64) acc += unit_q6_k(row, u, sg.xe, x);
-      break;
-    case NT_Q8_0:
-      for (int u = lane; u < sg.nblk; u += 64) acc += unit_q8_0(row, u, sg.xe, x);
-      break;
-    default:
-      for (int u = lane; u < sg.nblk; u += 64) acc += unit_q4_0(row, u, sg.xe, x);
-      break;
+#pragma unroll
+  for (int j = 0; j < kUnitsPerLane; ++j) {
+    const int k = lane + 64 * j;
+    if (k < sg.nunits) {
+      switch (sg.fmt) {
+        case NT_Q4_K: acc += unit_q4_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j]); break;
+        case NT_Q6_K: acc += unit_q6_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j]); break;
+        case NT_Q8_0:
+          acc += unit_q8_0(seg, k, !(sg.half && k == sg.nunits - 1), xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j]);
+          break;
+        default:
+          acc += unit_q4_0(seg, k, !(sg.half && k == sg.nunits - 1), xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j]);
+          break;
+      }
+    }
   }
   return acc;
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// Results of one item (row sums s0 and, for two-row items, s1).
+// Finish an item: row sums are in the wave's LDS row sums `yp`; lane t
+// handles row (or row pair) t.
 template <int EPI>
-__device__ __forceinline__ void item_epilogue(const Job& job, int it, float s0, float s1, const EpiArgs& ea) {
-  const int mi = item_matrix(job, it);
-  const int li = it - job.item_start[mi];
+__device__ __forceinline__ void item_epilogue(const Job& job, const Cur& ii, uint32_t yp, int lane, const EpiArgs& ea) {
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
-    const int R = job.row_base[mi] + li;
-    if constexpr (EPI == EPI_RESID) ea.y[R] += s0;
-    else ea.y[R] = s0;
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    ea.y[li] = silu(s0) * s1;
-  } else if constexpr (EPI == EPI_QKV) {
-    const int pos = *ea.pos + ea.pos_add;
-    const bool pos_ok = pos >= ea.pos_add && pos < ea.max_ctx;
-    if (!pos_ok && ea.err) *ea.err = 1;
-    const int R = job.row_base[mi] + 2 * li;  // even row of an adjacent pair
-    float a = s0, b = s1;
-    const int dd = R % ea.head_dim;
-    if (R < ea.q_rows + ea.kv_rows) {
-      // RoPE: pair (2i, 2i+1) of a head turns by pos * theta^(-2i/head_dim);
-      // the angle is formed in double so large positions keep fp32 accuracy.
-      const double freq = exp2(-(double)dd / (double)ea.head_dim * log2((double)ea.rope_theta));
-      const double ang = (double)pos * freq;
-      const float c = (float)cos(ang), s = (float)sin(ang);
-      const float a2 = a * c - b * s, b2 = a * s + b * c;
-      a = a2;
-      b = b2;
+    if (lane < ii.nr) {
+      const int R = job.row_base[ii.m] + ii.r0 + lane;
+      const float s = ldf(yp + 4u * lane);
+      if constexpr (EPI == EPI_RESID) ea.y[R] += s;
+      else ea.y[R] = s;
     }
-    if (R < ea.q_rows) {
-      ea.q_out[R] = a;
-      ea.q_out[R + 1] = b;
-    } else if (pos_ok) {
-      const bool is_k = R < ea.q_rows + ea.kv_rows;
-      const int rr = R - ea.q_rows - (is_k ? 0 : ea.kv_rows);
-      const int kh = rr / ea.head_dim;
-      uint16_t* cache = is_k ? ea.k_cache : ea.v_cache;
-      const int64_t off = ((int64_t)kh * ea.max_ctx + pos) * ea.head_dim + dd;
-      const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-      cache[off] = __builtin_bit_cast(uint16_t, ha);
-      cache[off + 1] = __builtin_bit_cast(uint16_t, hb);
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    if (lane < ii.nr) ea.y[ii.r0 + lane] = silu(ldf(yp + 4u * lane)) * ldf(yp + 4u * (ii.nr + lane));
+  } else if constexpr (EPI == EPI_QKV) {
+    if (2 * lane < ii.nr) {
+      const int pos = *ea.pos + ea.pos_add;
+      const bool pos_ok = pos >= ea.pos_add && pos < ea.max_ctx;
+      if (!pos_ok && ea.err) *ea.err = 1;
+      const int R = job.row_base[ii.m] + ii.r0 + 2 * lane;  // even row of an adjacent pair
+      float a = ldf(yp + 8u * lane), b = ldf(yp + 8u * lane + 4);
+      const int dd = R % ea.head_dim;
+      if (R < ea.q_rows + ea.kv_rows) {
+        // RoPE: pair (2i, 2i+1) of a head turns by pos * theta^(-2i/head_dim)
+        // (the prologue tabulated cos and sin)
+        const float c = ldf(job.rope + 4u * dd), s = ldf(job.rope + 4u * dd + 4);
+        const float a2 = a * c - b * s, b2 = a * s + b * c;
+        a = a2;
+        b = b2;
+      }
+      if (R < ea.q_rows) {
+        ea.q_out[R] = a;
+        ea.q_out[R + 1] = b;
+      } else if (pos_ok) {
+        const bool is_k = R < ea.q_rows + ea.kv_rows;
+        const int rr = R - ea.q_rows - (is_k ? 0 : ea.kv_rows);
+        const int kh = rr / ea.head_dim;
+        uint16_t* cache = is_k ? ea.k_cache : ea.v_cache;
+        const int64_t off = ((int64_t)kh * ea.max_ctx + pos) * ea.head_dim + dd;
+        const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+        cache[off] = __builtin_bit_cast(uint16_t, ha);
+        cache[off + 1] = __builtin_bit_cast(uint16_t, hb);
+      }
     }
   }
 }
 
-template <int EPI>
+// One step of the stream: the segment at `c` (its loads are in `pre`, its
+// description in `sg`) is stored to the slab, the loads of the segment two
+// ahead (`ah`) are issued into `pre`, and the stored segment is computed.
+// Returns false after the wave's last segment.
+template <int EPI, int LPL>
+__device__ __forceinline__ bool stream_step(const Job& job, const EpiArgs& ea, int lane, int it_end, uint32_t slab,
+                                            uint32_t yp, Cur& c, Cur& ah, bool& ah_ok, int& xslice, XR& xr,
+                                            uint4 (&pre)[LPL], Seg& sg) {
+  const Seg cur = sg;
+  seg_store(cur, slab, lane, pre);
+  if (ah_ok) {
+    sg = seg_of(job, ah);
+    seg_load(sg, lane, pre);
+    ah_ok = cur_next(job, ah, it_end);
+  }
+  if (c.s != xslice) {
+    load_xr(job, c.s, lane, xr);
+    xslice = c.s;
+  }
+  const float part = wave_sum(seg_compute(cur, slab, lane, xr));
+  if (lane == 0) {
+    const uint32_t a = yp + 4u * c.g;
+    stf(a, c.s == 0 ? part : ldf(a) + part);
+  }
+  const bool item_done = c.s == job.nslice - 1 && c.g == c.ns - 1;
+  if (item_done) item_epilogue<EPI>(job, c, yp, lane, ea);
+  return cur_next(job, c, it_end);
+}
+
+template <int EPI, int LPL>
 __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, EpiArgs ea) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform: keep everything derived from it (item range,
+  // stream position, segment addresses) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nitems = job.item_start[job.nmat];
   const int64_t gw = (int64_t)blockIdx.x * job.nwaves + wave;
   const int64_t GW = (int64_t)gridDim.x * job.nwaves;
   const int it_begin = (int)(gw * nitems / GW), it_end = (int)((gw + 1) * nitems / GW);
-  const uint32_t slab = job.slab + (uint32_t)wave * kSlab;
-  uint4 pre[kSlabLoads];
-  Pos p{it_begin, 0, 0};
-  bool live = it_begin < it_end;
-  Seg cur = seg_of(job, Pos{live ? it_begin : 0, 0, 0});
-  if (live) seg_load(cur, lane, pre);
+  const uint32_t slab = job.slab + (uint32_t)wave * (uint32_t)(LPL * 1024);
+  const uint32_t yp = job.ypart + (uint32_t)wave * (4 * 2 * kMaxRows);
+  uint4 pa[LPL], pb[LPL];
+  Seg sa, sb;
+  const bool live = it_begin < it_end;
+  Cur c, ah;
+  bool ah_ok = live;
+  if (live) {
+    cur_begin(job, c, it_begin);
+    ah = c;
+    // two segments in flight before the prologue
+    sa = seg_of(job, ah);
+    seg_load(sa, lane, pa);
+    ah_ok = cur_next(job, ah, it_end);
+    if (ah_ok) {
+      sb = seg_of(job, ah);
+      seg_load(sb, lane, pb);
+      ah_ok = cur_next(job, ah, it_end);
+    }
+  }
   stage_x(job, pro, tid);  // the only workgroup barrier
-  float acc0 = 0.f, acc1 = 0.f;
-  while (live) {
-    seg_store(cur, slab, lane, pre);
-    const Pos here = p;
-    const Seg seg = cur;
-    live = advance(job, p, it_end);
-    if (live) {
-      cur = seg_of(job, p);
-      seg_load(cur, lane, pre);
-    }
-    const float part = seg_compute(job, seg, slab, lane);
-    if (here.g == 0) acc0 += part;
-    else acc1 += part;
-    // last segment of the item: reduce and finish it
-    if (!live || p.it != here.it) {
-      const float s0 = wave_sum(acc0);
-      const float s1 = wave_sum(acc1);
-      if (lane == 0) item_epilogue<EPI>(job, here.it, s0, s1, ea);
-      acc0 = 0.f;
-      acc1 = 0.f;
-    }
+  if (!live) return;
+  XR xr;
+  int xslice = -1;
+  while (true) {
+    if (!stream_step<EPI, LPL>(job, ea, lane, it_end, slab, yp, c, ah, ah_ok, xslice, xr, pa, sa)) break;
+    if (!stream_step<EPI, LPL>(job, ea, lane, it_end, slab, yp, c, ah, ah_ok, xslice, xr, pb, sb)) break;
   }
 }
 
@@ -504,28 +600,38 @@ DevInfo& dev_info() {
   return d;
 }
 
-template <int EPI>
-int launch_epi(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t stream) {
+template <int EPI, int LPL>
+int launch_lpl(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_qgemv<EPI>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
-        hipSuccess)
+    if (hipFuncSetAttribute((const void*)k_qgemv<EPI, LPL>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024) != hipSuccess)
       return NT_EHIP;
     attr_set = true;
   }
-  const int nitems = job.item_start[job.nmat];
-  // one workgroup per CU; fewer when there are not enough items for its waves
-  const int grid = std::max(1, std::min(dev_info().cus, (nitems + job.nwaves - 1) / job.nwaves));
-  if (nitems <= 0) return NT_OK;
-  hipLaunchKernelGGL(k_qgemv<EPI>, dim3(grid), dim3(64 * job.nwaves), job.lds_bytes, stream, job, pro, ea);
-  return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
+  trace_before(EPI, stream);
+  hipLaunchKernelGGL((k_qgemv<EPI, LPL>), dim3(job.grid), dim3(64 * job.nwaves), job.lds_bytes, stream, job, pro, ea);
+  const bool ok = hipGetLastError() == hipSuccess;
+  trace_after(EPI, stream);
+  return ok ? NT_OK : NT_EHIP;
+}
+
+template <int EPI>
+int launch_epi(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t stream) {
+  if (job.item_start[job.nmat] <= 0) return NT_OK;
+  switch (job.lpl) {
+    case 3: return launch_lpl<EPI, 3>(job, pro, ea, stream);
+    case 4: return launch_lpl<EPI, 4>(job, pro, ea, stream);
+    case 5: return launch_lpl<EPI, 5>(job, pro, ea, stream);
+  }
+  return NT_EUNSUPPORTED;
 }
 
 }  // namespace
 
-// Geometry of a launch: segments of at most kSegMax bytes (whole blocks,
-// rows split evenly), the LDS layout, and as many waves (<= 12) as LDS
-// allows once the staged activation is in.
+// Geometry of a launch: column slices of at most 4096 weights (whole
+// blocks), rows per item, the LDS layout, and the grid (one workgroup per CU,
+// fewer when there are too few items).
 int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const int* rows, int cols, int paired,
              int pairs) {
   if (nmat < 1 || nmat > kMaxMats || (paired && nmat != 2)) return NT_EINVAL;
@@ -535,41 +641,74 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
   job.paired = paired;
   job.pairs = pairs;
   job.cols = cols;
-  int items = 0, rbase = 0;
+  bool kquant = false;
+  int64_t total_rows = 0;
   for (int m = 0; m < nmat; ++m) {
     const int qk = block_elems(fmt[m]);
     if (qk == 0 || cols % qk != 0) return NT_EINVAL;
     if (pairs && (rows[m] & 1)) return NT_EINVAL;
     if (paired && rows[m] != rows[0]) return NT_EINVAL;
+    if (rows[m] < 0) return NT_EINVAL;
+    kquant |= qk == 256;
     job.W[m] = W[m];
     job.fmt[m] = fmt[m];
     job.rows[m] = rows[m];
-    const int bb = block_bytes(fmt[m]);
-    const int nbr = cols / qk;
-    job.rb[m] = (int64_t)nbr * bb;
-    const int nseg = (int)((job.rb[m] + kSegMax - 1) / kSegMax);
-    job.seg_blocks[m] = (nbr + nseg - 1) / nseg;
-    job.nseg[m] = (nbr + job.seg_blocks[m] - 1) / job.seg_blocks[m];
+    job.rb[m] = (int64_t)(cols / qk) * block_bytes(fmt[m]);
+    if (!paired || m == 0) total_rows += rows[m];
+  }
+  const int units = (cols + 63) / 64;
+  job.nslice = (units + kSliceUnits - 1) / kSliceUnits;
+  int ups = (units + job.nslice - 1) / job.nslice;
+  if (kquant) ups = (ups + 3) & ~3;  // slices end on 256-weight superblocks
+  job.ups = ups;
+  job.nslice = (units + ups - 1) / ups;
+  job.last_ne = cols - (job.nslice - 1) * ups * 64;
+  job.last_units = (job.last_ne + 63) / 64;
+  for (int m = 0; m < nmat; ++m) job.slice_bytes[m] = (int64_t)(ups * 64 / block_elems(fmt[m])) * block_bytes(fmt[m]);
+  // loads per lane: the largest segment plus its misalignment, in 1 KB rounds
+  int64_t seg_max = 0;
+  for (int m = 0; m < nmat; ++m)
+    seg_max = std::max<int64_t>(seg_max, (int64_t)std::min(cols, ups * 64) / block_elems(fmt[m]) * block_bytes(fmt[m]));
+  const int need = (int)((seg_max + 15 + 15) / 16 + 63) / 64;
+  job.lpl = need <= 3 ? 3 : need;
+  if (need > kSlabLoads) return NT_EUNSUPPORTED;
+  job.nwaves = kMaxWaves;
+  const int cus = dev_info().cus;
+  const int64_t waves = (int64_t)cus * job.nwaves;
+  // rows per item: RoPE pairs need 2; with one slice rows never share the
+  // activation registers, so 1; with several, enough rows that a wave's
+  // rows fill its share of the matrix (fewer reloads of the activation)
+  int R = 1;
+  if (job.nslice > 1) {
+    const int64_t per_wave = (total_rows + waves - 1) / waves;
+    R = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxRows, per_wave));
+  }
+  if (pairs) R = std::max(2, R & ~1);
+  job.R = R;
+  int items = 0, rbase = 0;
+  for (int m = 0; m < nmat; ++m) {
     job.item_start[m] = items;
     job.row_base[m] = rbase;
     rbase += rows[m];
-    if (!paired || m == 0) items += pairs ? rows[m] / 2 : rows[m];
+    if (!paired || m == 0) items += (rows[m] + R - 1) / R;
   }
   if (paired) job.item_start[1] = items;
   job.item_start[nmat] = items;
   uint32_t off = 0;
-  job.x_hi = off; off += cols;
-  job.x_lo = off; off += cols;
-  job.x_sc = off; off += (cols / 32) * 4;
-  job.x_sum = off; off += (cols / 16) * 4;
+  job.x_hi = off; off += cols + 64;
+  job.x_lo = off; off += cols + 64;
+  off = (off + 15) & ~15u;
+  job.x_sc = off; off += (cols / 32 + 2) * 4;
+  job.x_sum = off; off += (cols / 16 + 4) * 4;
   job.red = off; off += 16 * 4;
+  job.rope = off; off += 128 * 8;  // cos/sin of up to 128 rotation pairs (head_dim <= 256)
+  job.ypart = off; off += job.nwaves * 4 * 2 * kMaxRows;
   off = (off + 15) & ~15u;
   job.slab = off;
-  const int64_t room = 160 * 1024 - (int64_t)off;
-  const int nw = (int)std::min<int64_t>(kMaxWaves, room / kSlab);
-  if (nw < 4) return NT_EUNSUPPORTED;
-  job.nwaves = nw;
-  job.lds_bytes = off + (uint32_t)nw * kSlab;
+  off += (uint32_t)(job.nwaves * job.lpl * 1024);
+  job.lds_bytes = off;
+  if (job.lds_bytes > 160 * 1024) return NT_EUNSUPPORTED;
+  job.grid = (int)std::max<int64_t>(1, std::min<int64_t>(cus, (items + job.nwaves - 1) / job.nwaves));
   return NT_OK;
 }
 

@@ -9,15 +9,19 @@
 
 namespace nt {
 
-constexpr int kMaxWaves = 12;     // waves per workgroup of the GEMV engine
+constexpr int kMaxWaves = 16;     // waves per workgroup of the GEMV engine (one workgroup per CU)
 constexpr int kMaxThreads = 64 * kMaxWaves;
-constexpr int kSlab = 8192;       // bytes of one wave's LDS staging slab
-constexpr int kSlabLoads = kSlab / (64 * 16);  // 16-B loads per lane to fill a slab
-constexpr int kSegMax = kSlab - 32;            // weight bytes of one segment, at most
+constexpr int kUnitsPerLane = 1;  // 64-weight column units a lane owns in one column slice
+constexpr int kSliceUnits = 64 * kUnitsPerLane;  // column units per slice (4096 weights)
+constexpr int kSlabLoads = 5;     // 16-B loads per lane for the largest segment (Q8_0: 4352 B + alignment)
+constexpr int kSlab = kSlabLoads * 64 * 16;  // bytes of one wave's LDS staging slab
+constexpr int kMaxRows = 8;       // rows per work item
 constexpr int kMaxMats = 3;       // matrices one engine launch walks (Q, K, V)
 constexpr int64_t kMaxCols = 49152;
 
-__host__ __device__ inline int block_elems(int fmt) { return fmt == NT_Q4_K || fmt == NT_Q6_K ? 256 : (fmt == NT_Q8_0 || fmt == NT_Q4_0 ? 32 : 0); }
+__host__ __device__ inline int block_elems(int fmt) {
+  return fmt == NT_Q4_K || fmt == NT_Q6_K ? 256 : (fmt == NT_Q8_0 || fmt == NT_Q4_0 ? 32 : 0);
+}
 __host__ __device__ inline int block_bytes(int fmt) {
   switch (fmt) {
     case NT_Q8_0: return 34;
@@ -28,12 +32,16 @@ __host__ __device__ inline int block_bytes(int fmt) {
   return 0;
 }
 
-// How a launch of the GEMV engine walks its matrices.  The work is a list of
-// items; an item is one row, an adjacent row pair of one matrix (`pairs`:
-// RoPE needs both rows), or row r of W[0] and of W[1] (`paired`: SwiGLU
-// needs gate and up).  Each wave takes a contiguous range of items and
-// streams their rows, in segments of at most kSegMax bytes, through its own
-// LDS slab.  All matrices share `cols`.
+// How a launch of the GEMV engine walks its matrices.
+//  - Columns are cut into `nslice` slices of `ups` 64-weight units; a lane
+//    owns units lane and lane+64 of the current slice and keeps their
+//    staged activation in registers.
+//  - The work is a list of items of up to R consecutive rows of one matrix
+//    (`pairs`: R is even, RoPE needs row pairs), or R rows of W[0] together
+//    with the same rows of W[1] (`paired`: SwiGLU needs gate and up).
+//  - A wave owns a contiguous range of items and streams, item by item and
+//    slice by slice, each (row, slice) byte range -- a segment -- through
+//    its LDS slab.  All matrices share `cols`.
 struct Job {
   const uint8_t* W[kMaxMats];
   int64_t rb[kMaxMats];       // bytes per row
@@ -41,15 +49,21 @@ struct Job {
   int rows[kMaxMats];
   int row_base[kMaxMats];     // first output row of each matrix (concatenated outputs)
   int item_start[kMaxMats + 1];
-  int seg_blocks[kMaxMats];   // blocks per segment
-  int nseg[kMaxMats];         // segments per row
+  int64_t slice_bytes[kMaxMats];  // bytes of one full column slice of a row
+  int R;                      // rows per item
+  int ups;                    // units per slice
+  int nslice;
+  int last_units;             // units of the last slice (may be partial)
+  int last_ne;                // weights of the last slice
   int nmat;
   int paired;
   int pairs;
   int cols;
   int nwaves;                 // waves per workgroup
+  int grid;                   // workgroups
+  int lpl;                    // 16-B loads per lane per segment (3, 4 or 5)
   // dynamic LDS layout (byte offsets)
-  uint32_t x_hi, x_lo, x_sc, x_sum, red, slab;
+  uint32_t x_hi, x_lo, x_sc, x_sum, red, slab, ypart, rope;
   uint32_t lds_bytes;
 };
 
@@ -59,6 +73,12 @@ struct ProArgs {
   const float* gain;   // RMSNorm gains or nullptr
   float eps;
   int64_t src_stride;
+  // RoPE table for the QKV epilogue (rope_hd == 0: none): cos/sin of
+  // pos * theta^(-2i/rope_hd), i < rope_hd/2, pos = *pos + pos_add
+  int rope_hd;
+  float rope_theta;
+  const int32_t* pos;
+  int pos_add;
 };
 
 enum Epi : int {
@@ -90,6 +110,11 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
 
 // Launch the engine (prologue: optional RMSNorm; epilogue: epi).
 int launch_gemv(const Job& job, const ProArgs& pro, int epi, const EpiArgs& ea, hipStream_t stream);
+
+// Launch tracing (nt_trace.hip): wraps one launch of `kind` in events when
+// tracing that kind.
+void trace_before(int kind, hipStream_t stream);
+void trace_after(int kind, hipStream_t stream);
 
 // Attention and step kernels (nt_attn.hip).
 void attn_plan(int n_kv, int max_ctx, int& chunk, int& nsplit);
