@@ -124,15 +124,71 @@ def cpu_baseline(sample_layers: int, n_layer_full: int, n_past: int):
                        f"layer time scaled x{n_layer_full / sample_layers:.0f}")
 
 
+def read_ceiling(dev) -> float:
+    """Achievable HBM read bandwidth: nt_read_probe over 8 x 256 MiB buffers
+    in rotation (more than the 256 MB last-level cache)."""
+    import torch
+
+    import quantized_decode_dequant_amd as nt
+    bufs = [torch.empty(256 << 20, dtype=torch.uint8, device=dev) for _ in range(8)]
+    out = torch.zeros(4, dtype=torch.int32, device=dev)
+    for i in range(4):
+        nt.read_probe(bufs[i % 8], out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(32):
+        nt.read_probe(bufs[i % 8], out)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 32 * (256 << 20) / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del bufs
+    torch.cuda.empty_cache()
+    return gbs
+
+
+def summarize_profile(d: str) -> None:
+    """Per-kernel table from rocprofv3 output: kernel durations (rocpd SQLite
+    database of --kernel-trace) and mean counter values per dispatch (csv of --pmc)."""
+    import csv
+    import glob
+    import sqlite3
+    from collections import defaultdict
+
+    def short(n):
+        return n.replace("void ", "").replace("nt::(anonymous namespace)::", "").split("(")[0][:70]
+
+    for db in sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True)):
+        c = sqlite3.connect(db)
+        rows = c.execute("select name, total_calls, total_duration, average, percentage from top_kernels").fetchall()
+        print(f"{'kernel':70s} {'calls':>6s} {'total_us':>11s} {'avg_us':>9s} {'pct':>6s}")
+        for name, calls, tot, avg, pct in rows:
+            print(f"{short(name):70s} {calls:6d} {tot:11.1f} {avg:9.2f} {pct:6.2f}")
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        agg = defaultdict(lambda: defaultdict(list))
+        for r in csv.DictReader(open(f)):
+            agg[short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        for k, cs in agg.items():
+            print(f"{k:70s} " + "  ".join(f"{n}={sum(v) / len(v):.6g} (n={len(v)})" for n, v in sorted(cs.items())))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--layers", type=int, default=80, help="stack depth (80 is the workload)")
-    ap.add_argument("--cpu-sample-layers", type=int, default=2)
+    ap.add_argument("--cpu-sample-layers", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one device copy of 256 MiB (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize", metavar="DIR", help="print per-kernel statistics of a rocprofv3 output "
+                    "directory (kernel trace or counter csv) and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profile(args.summarize)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the decode path is not sharded (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -158,6 +214,15 @@ def main():
             tok.copy_(nxt)
             pos.add_(1)
 
+    if args.copy_probe:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE read 256 MiB each when the counters are exact
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    read_gbs = read_ceiling(dev)
+    log(f"[bench] streaming-read ceiling (nt_read_probe): {read_gbs:.0f} GB/s")
     log(f"[bench] warmup {args.warmup} steps")
     run(args.warmup)
     torch.cuda.synchronize()
@@ -220,6 +285,7 @@ def main():
         },
         "weight_gbs": round(wbytes / (ms_per_step / 1e3) / 1e9, 1),
         "weight_roofline_frac": round(wbytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "read_ceiling_gbs": round(read_gbs, 1),
         "roofline": {
             "kernel": "k_qgemv<EPI_SWIGLU> (gate/up GEMV + SwiGLU, Q4_K 2x28672x8192)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -83,10 +83,11 @@ int64_t nt_max_cols(void);
 int nt_gemv_q(int fmt, const void* W, const float* x, float* y, int64_t rows, int64_t cols, void* stream);
 
 /*
- * Y[m] = W X[m] for M tokens at once (the verify pass of self-speculative
- * decoding runs M drafted tokens through every projection; p1 feature list).
- *   X: device fp32 [M][cols]; Y: device fp32 [M][rows]; 1 <= M <= 8.
- *   Weights are read once for all M tokens.
+ * Y[m] = W X[m] for M tokens (the verify pass of self-speculative decoding
+ * runs M drafted tokens through every projection; p1 feature list).
+ *   X: device fp32 [M][cols], rows 16-byte aligned; Y: device fp32 [M][rows];
+ *   1 <= M <= 8.  Same arithmetic as nt_gemv_q; currently one weight pass per
+ *   token.
  */
 int nt_gemm_q_small(int fmt, const void* W, const float* X, float* Y, int M, int64_t rows, int64_t cols,
                     void* stream);
@@ -190,7 +191,7 @@ int nt_verify_step(const nt_model* model, const int32_t* tokens_dev, int M, cons
 /*
  * Instrumentation.  nt_trace_begin(kind) makes the library record a HIP event
  * pair, on the launch stream, around every following launch of one kernel
- * kind (up to 4096 launches); nt_trace_end waits for those events and returns
+ * kind (up to 16384 launches); nt_trace_end waits for those events and returns
  * the number of launches traced and their summed duration in milliseconds
  * (*total_ms).  Kinds: 0 plain GEMV, 1 GEMV + residual add (O and down
  * projections), 2 QKV + RoPE + KV append, 3 gate/up + SwiGLU, 4 attention.
@@ -206,6 +207,14 @@ typedef enum nt_trace_kind {
 } nt_trace_kind;
 int nt_trace_begin(int kind);
 int nt_trace_end(int* launches, double* total_ms);
+
+/*
+ * Measurement aid: a pure streaming read of `bytes` (a multiple of 16) from
+ * the 16-byte aligned device buffer `buf`, with non-temporal 16-byte loads,
+ * eight in flight per lane and 12 waves per CU; a checksum goes to the device
+ * word *out.  Its time gives the achievable HBM read bandwidth.
+ */
+int nt_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream);
 
 #ifdef __cplusplus
 }

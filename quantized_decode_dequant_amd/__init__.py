@@ -73,9 +73,16 @@ EXPORTS = {
                                       ctypes.c_void_p]),
     "nt_trace_begin": (ctypes.c_int, [ctypes.c_int]),
     "nt_trace_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]),
+    "nt_read_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 TRACE_GEMV, TRACE_GEMV_RESID, TRACE_QKV, TRACE_FFN_UP, TRACE_ATTN = 0, 1, 2, 3, 4
+
+
+def read_probe(buf, out, stream=None) -> None:
+    """Streaming read of a whole uint8 device tensor (nt_read_probe)."""
+    _check("nt_read_probe", lib().nt_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                                                _stream(stream)))
 
 
 def trace_begin(kind: int) -> None:

@@ -28,12 +28,13 @@ bool cfg_ok(const nt_layer_cfg& c) {
   if (c.hidden % 32 || c.ffn % 32 || (c.n_head * c.head_dim) % 32) return false;
   if (c.hidden > kMaxCols || c.ffn > kMaxCols || c.n_head * c.head_dim > kMaxCols) return false;
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return false;
+  if ((int64_t)c.max_ctx > 1024LL * (16384 / c.head_dim)) return false;  // at most 1024 attention splits
   return true;
 }
 
 LayerWs layer_ws(const nt_layer_cfg& c, int M) {
   LayerWs w{};
-  attn_plan(c.n_kv_head, c.max_ctx, w.chunk, w.nsplit);
+  attn_plan(c.head_dim, c.max_ctx, w.chunk, w.nsplit);
   const size_t nq = (size_t)c.n_head * c.head_dim;
   size_t off = 0;
   w.q = off; off += up256((size_t)M * nq * 4);

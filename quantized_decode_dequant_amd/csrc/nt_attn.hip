@@ -26,6 +26,7 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kMaxGroup = 8;  // query heads per kv head
+constexpr int kMaxSplits = 1024;  // position splits of one attention
 
 __device__ __forceinline__ void h8_to_f(uint4 v, float (&f)[8]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -36,86 +37,110 @@ __device__ __forceinline__ void h8_to_f(uint4 v, float (&f)[8]) {
   }
 }
 
+// Sum over the 16 lanes of a DPP row (lanes that share one position):
+// rotations by 8, 4, 2, 1 leave the sum in every lane of the row.
+template <int CTRL>
+__device__ __forceinline__ float row_rot(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+template <int LP>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (LP == 16) {
+    v += row_rot<0x128>(v);  // row_ror:8
+    v += row_rot<0x124>(v);  // row_ror:4
+    v += row_rot<0x122>(v);  // row_ror:2
+    v += row_rot<0x121>(v);  // row_ror:1
+  } else {
+#pragma unroll
+    for (int o = LP / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  }
+  return v;
+}
+
+// Positions per split for a head size: every thread then holds 8 chunks of
+// 16 bytes of K and 8 of V (K and V tiles of 32 KB per workgroup).
+template <int HD>
+constexpr int attn_chunk() { return 16384 / HD; }
+
 // q: fp32 [n_query][n_head][HD] (query i at position pos+i attends to
 // 0..pos+i).  Partials: part_o [n_query][nsplit][n_head][HD],
 // part_ml [n_query][nsplit][n_head][2].
 template <int HD>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __restrict__ q, const uint16_t* __restrict__ kc,
                                                              const uint16_t* __restrict__ vc, const int32_t* pos_ptr,
-                                                             int query, int n_head, int n_kv, int max_ctx, int chunk,
-                                                             int nsplit, float* __restrict__ part_o,
-                                                             float* __restrict__ part_ml) {
-  constexpr int LP = HD / 8;        // lanes per position
-  constexpr int PPW = 64 / LP;      // positions per wave step
-  constexpr int NW = kAttnThreads / 64;
-  __shared__ float s_sc[kMaxGroup][512 + 1];
-  __shared__ float s_red[NW][kMaxGroup][HD];
+                                                             int query, int n_head, int n_kv, int max_ctx, int nsplit,
+                                                             float* __restrict__ part_o, float* __restrict__ part_ml) {
+  constexpr int LP = HD / 8;              // lanes per position (8 dims each)
+  constexpr int PPR = kAttnThreads / LP;  // positions per round
+  constexpr int CHUNK = attn_chunk<HD>();
+  constexpr int ROUNDS = CHUNK / PPR;     // = 8
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[CHUNK * HD];
+  __shared__ float s_p[kMaxGroup][CHUNK];
   __shared__ float s_m[kMaxGroup], s_l[kMaxGroup];
 
   const int g = blockIdx.x, split = blockIdx.y;
   const int G = n_head / n_kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sub = lane % LP, slot = lane / LP;  // dims [8*sub, 8*sub+8) of position slot
+  const int sub = tid % LP, slot = tid / LP;  // dims [8*sub, 8*sub+8) of positions slot + PPR*r
   const int pos = *pos_ptr;
   const int n_pos = pos + query + 1;
   const bool ok = pos >= 0 && pos + query < max_ctx;
-  const int t0 = split * chunk;
-  const int t1 = ok ? min(t0 + chunk, n_pos) : t0;
-  const int nt = max(0, t1 - t0);
+  const int t0 = split * CHUNK;
+  const int nt = ok ? max(0, min(CHUNK, n_pos - t0)) : 0;
 
-  // query slices held in registers: 8 dims of each head of the group
+  // all K and V loads of this tile up front (positions past the end re-read row t0)
+  const uint16_t* kg = kc + ((int64_t)g * max_ctx + t0) * HD + 8 * sub;
+  const uint16_t* vg = vc + ((int64_t)g * max_ctx + t0) * HD + 8 * sub;
+  uint4 kr[ROUNDS], vr[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int t = slot + PPR * r;
+    const int64_t off = (int64_t)(t < nt ? t : 0) * HD;
+    kr[r] = *reinterpret_cast<const uint4*>(kg + off);
+    vr[r] = *reinterpret_cast<const uint4*>(vg + off);
+  }
+  // query slices: 8 dims of each head of the group, scaled by 1/sqrt(HD)
   float qr[kMaxGroup][8];
   const float scale = 1.0f / sqrtf((float)HD);
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
+  for (int h = 0; h < kMaxGroup; ++h)
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       qr[h][j] = h < G ? q[((int64_t)query * n_head + g * G + h) * HD + 8 * sub + j] * scale : 0.f;
-  }
 
   // scores
-  const uint16_t* kg = kc + (int64_t)g * max_ctx * HD;
-  for (int tb = wave * PPW; tb < nt; tb += NW * PPW) {
-    const int t = tb + slot;
-    float s[kMaxGroup];
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) s[h] = 0.f;
-    if (t < nt) {
-      const uint4 kv = *reinterpret_cast<const uint4*>(kg + (int64_t)(t0 + t) * HD + 8 * sub);
-      float kf[8];
-      h8_to_f(kv, kf);
+  for (int r = 0; r < ROUNDS; ++r) {
+    float kf[8];
+    h8_to_f(kr[r], kf);
+    const int t = slot + PPR * r;
 #pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
+    for (int h = 0; h < kMaxGroup; ++h) {
+      if (h < G) {
         float a = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) a += qr[h][j] * kf[j];
-        s[h] = a;
+        a = group_sum<LP>(a);
+        if (sub == 0 && t < nt) s_p[h][t] = a;
       }
     }
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-#pragma unroll
-      for (int o = LP / 2; o > 0; o >>= 1) s[h] += __shfl_xor(s[h], o, 64);
-    }
-    if (sub == 0 && t < nt) {
-#pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h)
-        if (h < G) s_sc[h][t] = s[h];
-    }
+    // V tile to LDS (position-major, as in the cache)
+    *reinterpret_cast<uint4*>(s_v + t * HD + 8 * sub) = vr[r];
   }
   __syncthreads();
 
-  // per-head max and sum of exponentials over this split (one wave per head)
-  for (int h = wave; h < G; h += NW) {
+  // softmax numerators and sums over this split, one wave per head
+  for (int h = wave; h < G; h += kAttnThreads / 64) {
     float m = -FLT_MAX;
-    for (int t = lane; t < nt; t += 64) m = fmaxf(m, s_sc[h][t]);
+    for (int t = lane; t < nt; t += 64) m = fmaxf(m, s_p[h][t]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     float l = 0.f;
     for (int t = lane; t < nt; t += 64) {
-      const float p = expf(s_sc[h][t] - m);
-      s_sc[h][t] = p;
-      l += p;
+      const float e = expf(s_p[h][t] - m);
+      s_p[h][t] = e;
+      l += e;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
@@ -126,51 +151,30 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
   }
   __syncthreads();
 
-  // p . V
-  float acc[kMaxGroup][8];
-#pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
-  const uint16_t* vg = vc + (int64_t)g * max_ctx * HD;
-  for (int tb = wave * PPW; tb < nt; tb += NW * PPW) {
-    const int t = tb + slot;
-    if (t < nt) {
-      const uint4 vv = *reinterpret_cast<const uint4*>(vg + (int64_t)(t0 + t) * HD + 8 * sub);
+  // p . V: thread (head h, dims [8d, 8d+8), half) over half of the positions
+  constexpr int NDG = HD / 8;                           // dim groups
+  constexpr int PER = kAttnThreads / (kMaxGroup * NDG); // threads per (h, dim group): 2 for HD 128
+  const int h = tid / (NDG * PER), dgi = (tid / PER) % NDG, part = tid % PER;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (h < G) {
+    for (int t = part; t < nt; t += PER) {
+      const float p = s_p[h][t];
       float vf[8];
-      h8_to_f(vv, vf);
+      h8_to_f(*reinterpret_cast<const uint4*>(s_v + t * HD + 8 * dgi), vf);
 #pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        if (h < G) {
-          const float p = s_sc[h][t];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[h][j] += p * vf[j];
-        }
-      }
+      for (int j = 0; j < 8; ++j) acc[j] += p * vf[j];
     }
   }
-  // sum over the position slots of the wave (lanes with equal `sub`)
-#pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
+  if constexpr (PER > 1) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int o = LP; o < 64; o <<= 1) acc[h][j] += __shfl_xor(acc[h][j], o, 64);
-  if (slot == 0) {
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h)
-      if (h < G)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) s_red[wave][h][8 * sub + j] = acc[h][j];
+      for (int o = PER / 2; o > 0; o >>= 1) acc[j] += __shfl_xor(acc[j], o, 64);
   }
-  __syncthreads();
-  // sum over waves and write the partial
-  for (int i = tid; i < G * HD; i += kAttnThreads) {
-    const int h = i / HD, d = i % HD;
-    float v = 0.f;
+  if (h < G && part == 0) {
+    float* dst = part_o + (((int64_t)query * nsplit + split) * n_head + g * G + h) * HD + 8 * dgi;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) v += s_red[w][h][d];
-    part_o[(((int64_t)query * nsplit + split) * n_head + g * G + h) * HD + d] = v;
+    for (int j = 0; j < 8; ++j) dst[j] = acc[j];
   }
   if (tid < G) {
     const int64_t mi = (((int64_t)query * nsplit + split) * n_head + g * G + tid) * 2;
@@ -180,29 +184,46 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
 }
 
 // o[query][h][d] = sum_s e^(m_s - M) o_s[d] / sum_s e^(m_s - M) l_s over the
-// splits that hold positions.
+// splits that hold positions.  One workgroup per (head, query); the split
+// weights are formed once in LDS and every thread sums its dimension with
+// all loads in flight.
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                       const int32_t* pos_ptr, int n_head, int head_dim, int chunk,
                                                       int nsplit, int max_ctx, float* __restrict__ o) {
-  const int h = blockIdx.x, query = blockIdx.y;
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[4];
+  const int h = blockIdx.x, query = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pos = *pos_ptr;
   const bool ok = pos >= 0 && pos + query < max_ctx;
   const int n_pos = pos + query + 1;
   const int ns = ok ? min(nsplit, (n_pos + chunk - 1) / chunk) : 0;
-  float M = -FLT_MAX;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[(((int64_t)query * nsplit + s) * n_head + h) * 2]);
-  float L = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const int64_t mi = (((int64_t)query * nsplit + s) * n_head + h) * 2;
-    L += expf(part_ml[mi] - M) * part_ml[mi + 1];
+  const float* ml = part_ml + ((int64_t)query * nsplit * n_head + h) * 2;
+  // M = max over splits
+  float m = -FLT_MAX;
+  for (int s = tid; s < ns; s += blockDim.x) m = fmaxf(m, ml[(int64_t)s * n_head * 2]);
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+  // weights e^(m_s - M) and L = sum of weighted l_s
+  float lsum = 0.f;
+  for (int s = tid; s < ns; s += blockDim.x) {
+    const float w = expf(ml[(int64_t)s * n_head * 2] - m);
+    s_w[s] = w;
+    lsum += w * ml[(int64_t)s * n_head * 2 + 1];
   }
-  for (int d = threadIdx.x; d < head_dim; d += blockDim.x) {
+  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
+  if (lane == 0) s_red[wave] = lsum;
+  __syncthreads();
+  const float L = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  const float inv = ns > 0 ? 1.0f / L : 0.f;
+  const float* po = part_o + ((int64_t)query * nsplit * n_head + h) * head_dim;
+  for (int d = tid; d < head_dim; d += blockDim.x) {
     float v = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const int64_t mi = (((int64_t)query * nsplit + s) * n_head + h) * 2;
-      v += expf(part_ml[mi] - M) * part_o[(((int64_t)query * nsplit + s) * n_head + h) * head_dim + d];
-    }
-    o[((int64_t)query * n_head + h) * head_dim + d] = ns > 0 ? v / L : 0.f;
+#pragma unroll 8
+    for (int s = 0; s < ns; ++s) v += s_w[s] * po[(int64_t)s * n_head * head_dim + d];
+    o[((int64_t)query * n_head + h) * head_dim + d] = v * inv;
   }
 }
 
@@ -309,16 +330,10 @@ __global__ __launch_bounds__(64) void k_argmax_final(const float* __restrict__ p
 
 }  // namespace
 
-// Split geometry: chunks of 64-position multiples so that n_kv * nsplit is
-// about 512 workgroups (two per CU of a 256-CU chip) at full context; at most
-// 512 positions per chunk.  Independent of the device, so workspace sizes are.
-void attn_plan(int n_kv, int max_ctx, int& chunk, int& nsplit) {
-  const int64_t want = 512;
-  int64_t c = ((int64_t)max_ctx * n_kv + want - 1) / want;
-  c = ((c + 63) / 64) * 64;
-  if (c < 64) c = 64;
-  if (c > 512) c = 512;
-  chunk = (int)c;
+// Split geometry: 16384/head_dim positions per split (K and V tiles of
+// 32 KB).  Independent of the device, so workspace sizes are.
+void attn_plan(int head_dim, int max_ctx, int& chunk, int& nsplit) {
+  chunk = 16384 / head_dim;
   nsplit = (max_ctx + chunk - 1) / chunk;
 }
 
@@ -329,14 +344,14 @@ int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, con
   for (int qi = 0; qi < n_query; ++qi) {
     const dim3 grid(n_kv, nsplit);
     switch (head_dim) {
-      case 32: hipLaunchKernelGGL(k_attn_split<32>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, chunk, nsplit, part_o, part_ml); break;
-      case 64: hipLaunchKernelGGL(k_attn_split<64>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, chunk, nsplit, part_o, part_ml); break;
-      case 128: hipLaunchKernelGGL(k_attn_split<128>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, chunk, nsplit, part_o, part_ml); break;
-      case 256: hipLaunchKernelGGL(k_attn_split<256>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, chunk, nsplit, part_o, part_ml); break;
+      case 32: hipLaunchKernelGGL(k_attn_split<32>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, nsplit, part_o, part_ml); break;
+      case 64: hipLaunchKernelGGL(k_attn_split<64>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, nsplit, part_o, part_ml); break;
+      case 128: hipLaunchKernelGGL(k_attn_split<128>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, nsplit, part_o, part_ml); break;
+      case 256: hipLaunchKernelGGL(k_attn_split<256>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, nsplit, part_o, part_ml); break;
       default: return NT_EUNSUPPORTED;
     }
   }
-  hipLaunchKernelGGL(k_attn_combine, dim3(n_head, n_query), dim3(128), 0, stream, part_o, part_ml, pos, n_head, head_dim,
+  hipLaunchKernelGGL(k_attn_combine, dim3(n_head, n_query), dim3(256), 0, stream, part_o, part_ml, pos, n_head, head_dim,
                      chunk, nsplit, max_ctx, o);
   const bool ok = hipGetLastError() == hipSuccess;
   trace_after(NT_TRACE_ATTN, stream);

@@ -190,11 +190,9 @@ __device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t
 // Q4_K: unit k is chunk c = k%4 (64 weights) of superblock k/4: quant bytes
 // 32c..32c+31, whose low nibbles are the chunk's first 32 weights (sub-block
 // 2c) and high nibbles the next 32 (sub-block 2c+1).  w = d*sc*q - dmin*m.
-__device__ __forceinline__ float unit_q4_k(uint32_t seg, int k, NT_XARGS) {
-  const int sb = k >> 2, c = k & 3;
-  const uint32_t blk = seg + 144u * sb;
-  const uint4 hd = ld128(blk);
-  const uint4 q0 = ld128(blk + 16 + 32 * c), q1 = ld128(blk + 32 + 32 * c);
+// hd: the superblock's first 16 bytes (d, dmin, scales); q0, q1: the chunk's
+// 32 quant bytes.
+__device__ __forceinline__ float q4k_dot(const uint4& hd, const uint4& q0, const uint4& q1, int c, NT_XARGS) {
   const float d = h2f(hd.x & 0xffffu), dmin = h2f(hd.x >> 16);
   int scA, mA, scB, mB;
   q4k_scale_min(hd.y, hd.z, hd.w, 2 * c, scA, mA);
@@ -212,6 +210,12 @@ __device__ __forceinline__ float unit_q4_k(uint32_t seg, int k, NT_XARGS) {
   const int SA = (AH << 8) + AL, SB = (BH << 8) + BL;
   return xs[0] * (d * (float)scA * (float)SA - dmin * (float)mA * (float)(xm[0] + xm[1])) +
          xs[1] * (d * (float)scB * (float)SB - dmin * (float)mB * (float)(xm[2] + xm[3]));
+}
+
+__device__ __forceinline__ float unit_q4_k(uint32_t seg, int k, NT_XARGS) {
+  const uint32_t blk = seg + 144u * (k >> 2);
+  const int c = k & 3;
+  return q4k_dot(ld128(blk), ld128(blk + 16 + 32 * c), ld128(blk + 32 + 32 * c), c, xh, xl, xs, xm);
 }
 
 // Q6_K: unit k covers elements 64p..64p+63 of superblock k/4, p = k%4, i.e.
@@ -351,7 +355,10 @@ __device__ __forceinline__ uint4 load_chunk(const uint8_t* p) {
 struct Cur {
   int it, s, g;       // item, slice, row slot
   int m, r0, nr, ns;  // item: matrix, first row, rows (per matrix), slots
-  int mseg;           // matrix of the current segment
+  int mseg;           // matrix of the current segment, and its
+  int fmt;            //   format,
+  int64_t rb;         //   row bytes and
+  int64_t sbytes;     //   bytes of a full column slice
   const uint8_t* ptr; // first byte of the current segment
 };
 
@@ -367,8 +374,11 @@ __device__ __forceinline__ void item_begin(const Job& job, Cur& c) {
 __device__ __forceinline__ void seg_locate(const Job& job, Cur& c) {
   const bool second = job.paired && c.g >= c.nr;
   c.mseg = second ? 1 : c.m;
+  c.fmt = job.fmt[c.mseg];
+  c.rb = job.rb[c.mseg];
+  c.sbytes = job.slice_bytes[c.mseg];
   const int row = c.r0 + (second ? c.g - c.nr : c.g);
-  c.ptr = job.W[c.mseg] + (int64_t)row * job.rb[c.mseg] + (int64_t)c.s * job.slice_bytes[c.mseg];
+  c.ptr = job.W[c.mseg] + (int64_t)row * c.rb + (int64_t)c.s * c.sbytes;
 }
 
 __device__ __forceinline__ void cur_begin(const Job& job, Cur& c, int it) {
@@ -383,7 +393,7 @@ __device__ __forceinline__ void cur_begin(const Job& job, Cur& c, int it) {
 __device__ __forceinline__ bool cur_next(const Job& job, Cur& c, int it_end) {
   if (++c.g < c.ns) {
     if (job.paired && c.g == c.nr) seg_locate(job, c);
-    else c.ptr += job.rb[c.mseg];
+    else c.ptr += c.rb;
     return true;
   }
   c.g = 0;
@@ -410,12 +420,12 @@ struct Seg {
 
 __device__ __forceinline__ Seg seg_of(const Job& job, const Cur& c) {
   Seg sg;
-  sg.fmt = job.fmt[c.mseg];
+  sg.fmt = c.fmt;
   const bool last = c.s == job.nslice - 1;
   const int ne = last ? job.last_ne : job.ups * 64;
   sg.nunits = last ? job.last_units : job.ups;
   sg.half = (ne & 63) != 0;
-  const int64_t bytes = last ? (int64_t)(ne / block_elems(sg.fmt)) * block_bytes(sg.fmt) : job.slice_bytes[c.mseg];
+  const int64_t bytes = last ? (int64_t)(ne / block_elems(sg.fmt)) * block_bytes(sg.fmt) : c.sbytes;
   sg.a = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(c.ptr) & ~uintptr_t(15));
   sg.d = (uint32_t)(c.ptr - sg.a);
   sg.nchunks = (int)((sg.d + bytes + 15) >> 4);
@@ -434,23 +444,24 @@ __device__ __forceinline__ void seg_load(const Seg& sg, int lane, uint4 (&pre)[L
   }
 }
 
+// The slab holds LPL KB, so every chunk slot is written (slots past the
+// segment's end get the re-read first chunk, which nothing reads): no
+// divergent branch.
 template <int LPL>
-__device__ __forceinline__ void seg_store(const Seg& sg, uint32_t slab, int lane, const uint4 (&pre)[LPL]) {
+__device__ __forceinline__ void seg_store(uint32_t slab, int lane, const uint4 (&pre)[LPL]) {
 #pragma unroll
-  for (int i = 0; i < LPL; ++i) {
-    const int c = lane + 64 * i;
-    if (c < sg.nchunks) st128(slab + 16u * c, pre[i]);
-  }
+  for (int i = 0; i < LPL; ++i) st128(slab + 16u * (lane + 64 * i), pre[i]);
 }
 
-// This lane's part of one segment's dot product.
+// This lane's part of one segment's dot product, from the slab.
 __device__ __forceinline__ float seg_compute(const Seg& sg, uint32_t slab, int lane, const XR& xr) {
   const uint32_t seg = slab + sg.d;
   float acc = 0.f;
+  const bool full = sg.nunits >= 64 * kUnitsPerLane && !sg.half;  // uniform
 #pragma unroll
   for (int j = 0; j < kUnitsPerLane; ++j) {
     const int k = lane + 64 * j;
-    if (k < sg.nunits) {
+    if (full || k < sg.nunits) {
       switch (sg.fmt) {
         case NT_Q4_K: acc += unit_q4_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j]); break;
         case NT_Q6_K: acc += unit_q6_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j]); break;
@@ -523,7 +534,7 @@ __device__ __forceinline__ bool stream_step(const Job& job, const EpiArgs& ea, i
                                             uint32_t yp, Cur& c, Cur& ah, bool& ah_ok, int& xslice, XR& xr,
                                             uint4 (&pre)[LPL], Seg& sg) {
   const Seg cur = sg;
-  seg_store(cur, slab, lane, pre);
+  seg_store(slab, lane, pre);
   if (ah_ok) {
     sg = seg_of(job, ah);
     seg_load(sg, lane, pre);
@@ -534,7 +545,8 @@ __device__ __forceinline__ bool stream_step(const Job& job, const EpiArgs& ea, i
     xslice = c.s;
   }
   const float part = wave_sum(seg_compute(cur, slab, lane, xr));
-  if (lane == 0) {
+  {
+    // every lane writes the same uniform value: no divergent branch
     const uint32_t a = yp + 4u * c.g;
     stf(a, c.s == 0 ? part : ldf(a) + part);
   }

@@ -117,7 +117,7 @@ void trace_before(int kind, hipStream_t stream);
 void trace_after(int kind, hipStream_t stream);
 
 // Attention and step kernels (nt_attn.hip).
-void attn_plan(int n_kv, int max_ctx, int& chunk, int& nsplit);
+void attn_plan(int head_dim, int max_ctx, int& chunk, int& nsplit);
 int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, const int32_t* pos, int n_query,
                      int n_head, int n_kv, int head_dim, int max_ctx, int chunk, int nsplit, float* part_o,
                      float* part_ml, float* o, hipStream_t stream);

@@ -8,7 +8,7 @@
 namespace nt {
 namespace {
 
-constexpr int kTraceCap = 4096;
+constexpr int kTraceCap = 16384;
 
 struct Trace {
   int kind = -1;
@@ -68,3 +68,42 @@ int nt_trace_end(int* launches, double* total_ms) {
 }
 
 }  // extern "C"
+
+namespace nt {
+namespace {
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) u32x4_t* gp_u32x4;
+
+// Grid-stride over groups of 8 chunks per lane; all 8 loads issued before use.
+__global__ __launch_bounds__(256) void k_read_probe(const uint8_t* buf, size_t n16, uint32_t* out) {
+  const size_t tid = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  const size_t nthr = (size_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  for (size_t base = tid; base < n16; base += 8 * nthr) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const size_t c = base + i * nthr;
+      v[i] = __builtin_nontemporal_load((gp_u32x4)(buf + 16 * (c < n16 ? c : base)));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  }
+  if (acc == 0x9E3779B9u) *out = acc;  // keeps the loads; practically never taken
+}
+
+}  // namespace
+}  // namespace nt
+
+extern "C" int nt_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+  if (!buf || !out || bytes % 16 != 0) return NT_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(buf) & 15) != 0) return NT_EALIGN;
+  if (bytes == 0) return NT_OK;
+  int dev = 0, cus = 256;
+  (void)hipGetDevice(&dev);
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  hipLaunchKernelGGL(nt::k_read_probe, dim3(cus * 3), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint8_t*>(buf), bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
+}
