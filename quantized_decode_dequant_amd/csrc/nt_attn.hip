@@ -92,22 +92,35 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
   // all K and V loads of this tile up front (positions past the end re-read row t0)
   const uint16_t* kg = kc + ((int64_t)g * max_ctx + t0) * HD + 8 * sub;
   const uint16_t* vg = vc + ((int64_t)g * max_ctx + t0) * HD + 8 * sub;
-  uint4 kr[ROUNDS], vr[ROUNDS];
+  uint4 kr[ROUNDS];
+  {
+    uint4 vr[ROUNDS];
 #pragma unroll
-  for (int r = 0; r < ROUNDS; ++r) {
-    const int t = slot + PPR * r;
-    const int64_t off = (int64_t)(t < nt ? t : 0) * HD;
-    kr[r] = *reinterpret_cast<const uint4*>(kg + off);
-    vr[r] = *reinterpret_cast<const uint4*>(vg + off);
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int t = slot + PPR * r;
+      const int64_t off = (int64_t)(t < nt ? t : 0) * HD;
+      kr[r] = *reinterpret_cast<const uint4*>(kg + off);
+      vr[r] = *reinterpret_cast<const uint4*>(vg + off);
+    }
+    // V tile to LDS (position-major, as in the cache); V's registers end here
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r)
+      *reinterpret_cast<uint4*>(s_v + (slot + PPR * r) * HD + 8 * sub) = vr[r];
   }
-  // query slices: 8 dims of each head of the group, scaled by 1/sqrt(HD)
+  // query slices: 8 dims of each head of the group, scaled by 1/sqrt(HD);
+  // loaded unconditionally as float4 (heads past the group re-read head 0 and
+  // are zeroed) so the loads are one batch, not a chain of waits
   float qr[kMaxGroup][8];
   const float scale = 1.0f / sqrtf((float)HD);
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      qr[h][j] = h < G ? q[((int64_t)query * n_head + g * G + h) * HD + 8 * sub + j] * scale : 0.f;
+  for (int h = 0; h < kMaxGroup; ++h) {
+    const float4* qp = reinterpret_cast<const float4*>(
+        q + ((int64_t)query * n_head + g * G + (h < G ? h : 0)) * HD + 8 * sub);
+    const float4 a = qp[0], b = qp[1];
+    const float f = h < G ? scale : 0.f;
+    qr[h][0] = a.x * f; qr[h][1] = a.y * f; qr[h][2] = a.z * f; qr[h][3] = a.w * f;
+    qr[h][4] = b.x * f; qr[h][5] = b.y * f; qr[h][6] = b.z * f; qr[h][7] = b.w * f;
+  }
 
   // scores
 #pragma unroll
@@ -125,8 +138,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
         if (sub == 0 && t < nt) s_p[h][t] = a;
       }
     }
-    // V tile to LDS (position-major, as in the cache)
-    *reinterpret_cast<uint4*>(s_v + t * HD + 8 * sub) = vr[r];
   }
   __syncthreads();
 
