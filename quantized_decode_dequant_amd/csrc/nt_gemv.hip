@@ -9,25 +9,30 @@
 //             fp32 scale s_b and integers X in [-32639, 32639], split into a
 //             high and a low int8 plane (X = 256*hi + lo) plus per-16 sums of
 //             X.  Weight x activation products then run on v_dot4_i32_i8
-//             with exact integer sums per quantization sub-block.  This is
-//             the only workgroup barrier.
+//             with exact integer sums per quantization sub-block.  Its loads
+//             are issued before the first weight loads, so it does not wait
+//             for them.
 //   columns   A lane owns one 64-weight column unit of the current column
 //             slice (4096 weights) and keeps its staged activation in
-//             registers; a wave works through a group of rows slice by
-//             slice, so the activation is read from LDS once per slice and
-//             row group, not once per row.
-//   stream    Each wave owns a contiguous range of work items (groups of rows)
-//             and streams their bytes, segment by segment (one row within
-//             one column slice: a contiguous byte range), HBM -> registers
-//             with 16-byte coalesced non-temporal loads.  Two segments are in
-//             flight while the previous one is written to the wave's LDS
-//             slab and computed: lanes read their blocks from the slab at
-//             any byte alignment (Q8_0, Q4_0 and Q6_K blocks are only 2-byte
-//             aligned), unpack quants in registers and accumulate.
-//   reduce    Per segment, a butterfly over the wave's lanes; per row, the
-//             slices add up in the wave's LDS row sums.
-//   epilogue  Plain store, residual add, SwiGLU (gate and up rows in one
-//             item) or RoPE + q store + f16 K/V append (row pairs).
+//             registers, reloaded only when the wave moves to another slice.
+//   schedule  Workgroup b owns a contiguous range of output rows; its work
+//             is a list of segments (one row of one matrix within one column
+//             slice: a contiguous byte range), slice-major.  Waves claim
+//             segments one at a time from an LDS counter, so the waves that
+//             the SIMD arbiter favours simply take more of them and all
+//             finish together.
+//   stream    Segments move HBM -> registers with 16-byte coalesced
+//             non-temporal loads, two in flight per wave while the previous
+//             one is written to the wave's LDS slab and computed: lanes read
+//             their blocks from the slab at any byte alignment (Q8_0, Q4_0
+//             and Q6_K blocks are only 2-byte aligned), unpack quants in
+//             registers and accumulate.
+//   reduce    Per segment, a butterfly over the wave's lanes into an LDS
+//             table of (row, slice) partial sums.
+//   epilogue  After a workgroup barrier, each output row adds its slices in
+//             order (deterministic) and is stored: plain, residual add,
+//             SwiGLU (gate and up rows) or RoPE + q store + f16 K/V append
+//             (row pairs).
 //
 // The block layouts are the GGUF ones the pages' format list refers to
 // (p1 "About"); the unpacking below follows them.
@@ -260,71 +265,111 @@ __device__ __forceinline__ float unit_q6_k(uint32_t seg, int k, NT_XARGS) {
 // Stage the activation: v = src (or RMSNorm(src) * gain), then per 32-block
 // s = max|v| / 32639, X = rint(v / s), hi = (X + 128) >> 8, lo = X - 256 hi.
 // For the QKV launch it also tabulates the RoPE rotation of this position.
-__device__ __forceinline__ void stage_x(const Job& job, const ProArgs& pro, int tid) {
-  const int cols = job.cols, NT = job.nwaves * 64;
-  const float* src = pro.src;
+//
+// Thread t owns 32-element block t (and t + NT, ... for very wide inputs).
+// The loads of its first block are issued before the first weight segments
+// (stage_load), so waiting for them does not wait for the weights: memory
+// operations retire in order.
+
+// The thread's first block: src values, times the gains when normalising.
+struct XStage {
+  float v[32];
+  float ss;  // sum of squares of the raw src values (RMSNorm)
+};
+
+// Loads are unconditional (without gains the source is read twice) so the
+// number of loads in flight does not depend on the path.
+__device__ __forceinline__ void load_block(const ProArgs& pro, int b, float (&v)[32], float (&g)[32]) {
+  const float4* s4 = reinterpret_cast<const float4*>(pro.src + 32 * b);
+  const float4* g4 = reinterpret_cast<const float4*>((pro.gain ? pro.gain : pro.src) + 32 * b);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float4 t = s4[j];
+    v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float4 t = g4[j];
+    g[4 * j] = t.x; g[4 * j + 1] = t.y; g[4 * j + 2] = t.z; g[4 * j + 3] = t.w;
+  }
+}
+
+// Sum of squares of v into ss; v becomes v * gain.
+__device__ __forceinline__ void apply_gain(const ProArgs& pro, float (&v)[32], const float (&g)[32], float& ss) {
+#pragma unroll
+  for (int j = 0; j < 32; ++j) ss += v[j] * v[j];
+  if (pro.gain) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] *= g[j];
+  }
+}
+
+__device__ __forceinline__ void stage_load(const Job& job, const ProArgs& pro, int tid, XStage& st, float (&g)[32]) {
+  st.ss = 0.f;
+  load_block(pro, tid < (job.cols >> 5) ? tid : 0, st.v, g);  // threads without a block re-read block 0
+}
+
+// Quantize block b of v * r into the LDS planes.
+__device__ __forceinline__ void quant_block(const Job& job, int b, const float (&v)[32], float r) {
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j] * r));
+  const float inv = amax > 0.f ? kXMax / amax : 0.f;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    uint32_t H[4] = {0, 0, 0, 0}, L[4] = {0, 0, 0, 0};
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      int X = __float2int_rn((v[16 * half + k] * r) * inv);
+      X = max(-32639, min(32639, X));
+      const int hi = (X + 128) >> 8;
+      const int lo = X - (hi << 8);
+      H[k >> 2] |= (uint32_t)(hi & 255) << (8 * (k & 3));
+      L[k >> 2] |= (uint32_t)(lo & 255) << (8 * (k & 3));
+      sum += X;
+    }
+    st128(job.x_hi + 32u * b + 16 * half, make_uint4(H[0], H[1], H[2], H[3]));
+    st128(job.x_lo + 32u * b + 16 * half, make_uint4(L[0], L[1], L[2], L[3]));
+    sti32(job.x_sum + 8u * b + 4 * half, sum);
+  }
+  stf(job.x_sc + 4u * b, amax / kXMax);
+}
+
+__device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro, int tid, XStage& st,
+                                             const float (&g0)[32]) {
+  const int NT = job.nwaves * 64, nb = job.cols >> 5;
+  if (tid < nb) apply_gain(pro, st.v, g0, st.ss);
   float r = 1.0f;
   if (pro.gain) {
-    float ss = 0.f;
-    for (int i = 4 * tid; i < cols; i += 4 * NT) {
-      const float4 v = *reinterpret_cast<const float4*>(src + i);
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    // blocks past the first of each thread (inputs wider than 32 * NT)
+    for (int b = tid + NT; b < nb; b += NT) {
+      float v[32], g[32], ss = 0.f;
+      load_block(pro, b, v, g);
+#pragma unroll
+      for (int j = 0; j < 32; ++j) ss += v[j] * v[j];
+      st.ss += ss;
     }
-    ss = wave_sum(ss);
+    const float ss = wave_sum(st.ss);
     if ((tid & 63) == 0) stf(job.red + 4u * (tid >> 6), ss);
     __syncthreads();
     float tot = 0.f;
     for (int w = 0; w < job.nwaves; ++w) tot += ldf(job.red + 4u * w);
-    r = 1.0f / sqrtf(tot / (float)cols + pro.eps);
+    r = 1.0f / sqrtf(tot / (float)job.cols + pro.eps);
   }
-  const int nb = cols >> 5;
-  for (int b = tid; b < nb; b += NT) {
-    float v[32];
-    const float4* s4 = reinterpret_cast<const float4*>(src + 32 * b);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float4 t = s4[j];
-      v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
-    }
-    if (pro.gain) {
-      const float4* g4 = reinterpret_cast<const float4*>(pro.gain + 32 * b);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float4 g = g4[j];
-        v[4 * j] = v[4 * j] * r * g.x;
-        v[4 * j + 1] = v[4 * j + 1] * r * g.y;
-        v[4 * j + 2] = v[4 * j + 2] * r * g.z;
-        v[4 * j + 3] = v[4 * j + 3] * r * g.w;
-      }
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    const float inv = amax > 0.f ? kXMax / amax : 0.f;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint32_t H[4] = {0, 0, 0, 0}, L[4] = {0, 0, 0, 0};
-      int sum = 0;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        int X = __float2int_rn(v[16 * half + k] * inv);
-        X = max(-32639, min(32639, X));
-        const int hi = (X + 128) >> 8;
-        const int lo = X - (hi << 8);
-        H[k >> 2] |= (uint32_t)(hi & 255) << (8 * (k & 3));
-        L[k >> 2] |= (uint32_t)(lo & 255) << (8 * (k & 3));
-        sum += X;
-      }
-      st128(job.x_hi + 32u * b + 16 * half, make_uint4(H[0], H[1], H[2], H[3]));
-      st128(job.x_lo + 32u * b + 16 * half, make_uint4(L[0], L[1], L[2], L[3]));
-      sti32(job.x_sum + 8u * b + 4 * half, sum);
-    }
-    stf(job.x_sc + 4u * b, amax / kXMax);
+  if (tid < nb) quant_block(job, tid, st.v, r);
+  for (int b = tid + NT; b < nb; b += NT) {
+    float v[32], g[32], ss = 0.f;
+    load_block(pro, b, v, g);
+    apply_gain(pro, v, g, ss);
+    quant_block(job, b, v, r);
   }
   if (pro.rope_hd > 0) {
     // pair i turns by pos * theta^(-2i/head_dim); the angle is formed in
-    // double so large positions keep fp32 accuracy
-    for (int i = tid; i < pro.rope_hd / 2; i += NT) {
+    // double so large positions keep fp32 accuracy.  The last threads take
+    // this (they hold no activation block when the input is narrow).
+    const int npair = pro.rope_hd / 2;
+    for (int i = NT - 1 - tid; i >= 0 && i < npair; i += NT) {
       const int pos = *pro.pos + pro.pos_add;
       const double freq = exp2(-(double)(2 * i) / (double)pro.rope_hd * log2((double)pro.rope_theta));
       const double ang = (double)pos * freq;
@@ -348,64 +393,29 @@ __device__ __forceinline__ uint4 load_chunk(const uint8_t* p) {
 }
 
 // ----------------------------------------------------------- segment stream
-// A wave's stream walks its items; within an item, column slices outer and
-// row slots inner (so the activation registers change once per slice).  The
-// cursor is wave-uniform and kept in scalar registers; moving to the next
-// segment is a pointer add except at item, slice or (paired) matrix changes.
-struct Cur {
-  int it, s, g;       // item, slice, row slot
-  int m, r0, nr, ns;  // item: matrix, first row, rows (per matrix), slots
-  int mseg;           // matrix of the current segment, and its
-  int fmt;            //   format,
-  int64_t rb;         //   row bytes and
-  int64_t sbytes;     //   bytes of a full column slice
-  const uint8_t* ptr; // first byte of the current segment
+// Workgroup b's share: output rows [o0, o0 + no); `nv` segment rows (twice
+// the output rows with paired matrices) times `nslice` slices.  Segment id
+// k = s * nv + v (slice-major), so a wave's successive claims mostly stay in
+// one slice and its activation registers rarely change.  Everything here is
+// wave-uniform and lives in scalar registers.
+struct Share {
+  int o0, no;      // first output row, output rows
+  int nv;          // segment rows
+  int nseg;        // segments
+  uint32_t magic;  // floor((2^32 - 1) / nv): slice of a segment id by a multiply
 };
 
-__device__ __forceinline__ void item_begin(const Job& job, Cur& c) {
-  int m = 0;
-  while (m + 1 < job.nmat && c.it >= job.item_start[m + 1]) ++m;
-  c.m = m;
-  c.r0 = (c.it - job.item_start[m]) * job.R;
-  c.nr = min(job.R, job.rows[m] - c.r0);
-  c.ns = job.paired ? 2 * c.nr : c.nr;
-}
-
-__device__ __forceinline__ void seg_locate(const Job& job, Cur& c) {
-  const bool second = job.paired && c.g >= c.nr;
-  c.mseg = second ? 1 : c.m;
-  c.fmt = job.fmt[c.mseg];
-  c.rb = job.rb[c.mseg];
-  c.sbytes = job.slice_bytes[c.mseg];
-  const int row = c.r0 + (second ? c.g - c.nr : c.g);
-  c.ptr = job.W[c.mseg] + (int64_t)row * c.rb + (int64_t)c.s * c.sbytes;
-}
-
-__device__ __forceinline__ void cur_begin(const Job& job, Cur& c, int it) {
-  c.it = it;
-  c.s = 0;
-  c.g = 0;
-  item_begin(job, c);
-  seg_locate(job, c);
-}
-
-// Next segment; false past the wave's last item.
-__device__ __forceinline__ bool cur_next(const Job& job, Cur& c, int it_end) {
-  if (++c.g < c.ns) {
-    if (job.paired && c.g == c.nr) seg_locate(job, c);
-    else c.ptr += c.rb;
-    return true;
-  }
-  c.g = 0;
-  if (++c.s < job.nslice) {
-    seg_locate(job, c);
-    return true;
-  }
-  c.s = 0;
-  if (++c.it >= it_end) return false;
-  item_begin(job, c);
-  seg_locate(job, c);
-  return true;
+__device__ __forceinline__ Share share_of(const Job& job, int b) {
+  Share sh;
+  const bool big = b < job.wg_rem;
+  const int u0 = b * job.wg_base + (big ? b : job.wg_rem);
+  const int nu = job.wg_base + (big ? 1 : 0);
+  sh.o0 = u0 * job.unit;
+  sh.no = nu * job.unit;
+  sh.nv = job.paired ? 2 * sh.no : sh.no;
+  sh.nseg = sh.nv * job.nslice;
+  sh.magic = job.magic[big ? 1 : 0];
+  return sh;
 }
 
 // Byte range of one segment and where its data sits in the slab.
@@ -416,19 +426,62 @@ struct Seg {
   int fmt;
   int nunits;        // column units in the slice
   int half;          // the last unit holds a single 32-weight block
+  int s, v;          // slice and segment row
 };
 
-__device__ __forceinline__ Seg seg_of(const Job& job, const Cur& c) {
+__device__ __forceinline__ Seg seg_at(const Job& job, const Share& sh, int k) {
   Seg sg;
-  sg.fmt = c.fmt;
-  const bool last = c.s == job.nslice - 1;
+  // s = k / nv: the multiply undershoots by at most one
+  uint32_t q = __umulhi((uint32_t)k, sh.magic);
+  int v = k - (int)q * sh.nv;
+  if (v >= sh.nv) {
+    ++q;
+    v -= sh.nv;
+  }
+  const int s = (int)q;
+  sg.s = s;
+  sg.v = v;
+  int m, row;
+  if (job.paired) {
+    const bool up = v >= sh.no;
+    m = up ? 1 : 0;
+    row = sh.o0 + (up ? v - sh.no : v);
+  } else {
+    row = sh.o0 + v;
+    m = (job.nmat > 2 && row >= job.row_base[2]) ? 2 : ((job.nmat > 1 && row >= job.row_base[1]) ? 1 : 0);
+    row -= m == 2 ? job.row_base[2] : (m == 1 ? job.row_base[1] : 0);
+  }
+  // per-matrix fields by selects (a dynamic index would leave scalar registers)
+  const uint8_t* W = m == 2 ? job.W[2] : (m == 1 ? job.W[1] : job.W[0]);
+  const int64_t rb = m == 2 ? job.rb[2] : (m == 1 ? job.rb[1] : job.rb[0]);
+  const int64_t sbytes = m == 2 ? job.slice_bytes[2] : (m == 1 ? job.slice_bytes[1] : job.slice_bytes[0]);
+  sg.fmt = m == 2 ? job.fmt[2] : (m == 1 ? job.fmt[1] : job.fmt[0]);
+  const uint8_t* ptr = W + (int64_t)row * rb + (int64_t)s * sbytes;
+  const bool last = s == job.nslice - 1;
   const int ne = last ? job.last_ne : job.ups * 64;
   sg.nunits = last ? job.last_units : job.ups;
   sg.half = (ne & 63) != 0;
-  const int64_t bytes = last ? (int64_t)(ne / block_elems(sg.fmt)) * block_bytes(sg.fmt) : c.sbytes;
-  sg.a = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(c.ptr) & ~uintptr_t(15));
-  sg.d = (uint32_t)(c.ptr - sg.a);
+  const int64_t bytes = last ? (int64_t)(ne / block_elems(sg.fmt)) * block_bytes(sg.fmt) : sbytes;
+  sg.a = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(ptr) & ~uintptr_t(15));
+  sg.d = (uint32_t)(ptr - sg.a);
   sg.nchunks = (int)((sg.d + bytes + 15) >> 4);
+  return sg;
+}
+
+// Stand-in when a wave has no segment to load: one chunk at the start of the
+// first matrix.  Loads are still issued for it, so every path through the
+// stream issues the same number of loads and the waits before a slab store
+// count exactly the older segment (waits merge across paths pessimistically).
+__device__ __forceinline__ Seg seg_null(const Job& job) {
+  Seg sg;
+  sg.a = job.W[0];
+  sg.nchunks = 1;
+  sg.d = 0;
+  sg.fmt = job.fmt[0];
+  sg.nunits = 0;
+  sg.half = 0;
+  sg.s = 0;
+  sg.v = 0;
   return sg;
 }
 
@@ -479,26 +532,34 @@ __device__ __forceinline__ float seg_compute(const Seg& sg, uint32_t slab, int l
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// Finish an item: row sums are in the wave's LDS row sums `yp`; lane t
-// handles row (or row pair) t.
+// Sum of segment row v over the slices, in slice order (deterministic).
+__device__ __forceinline__ float row_total(const Job& job, int v) {
+  const uint32_t a = job.acc + 4u * (uint32_t)(v * job.nslice);
+  float t = ldf(a);
+  for (int s = 1; s < job.nslice; ++s) t += ldf(a + 4u * s);
+  return t;
+}
+
+// Finish the workgroup's rows (after the barrier that follows the stream):
+// thread t handles output row (or row pair) t.
 template <int EPI>
-__device__ __forceinline__ void item_epilogue(const Job& job, const Cur& ii, uint32_t yp, int lane, const EpiArgs& ea) {
+__device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, int tid, const EpiArgs& ea) {
+  const int NT = job.nwaves * 64;
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
-    if (lane < ii.nr) {
-      const int R = job.row_base[ii.m] + ii.r0 + lane;
-      const float s = ldf(yp + 4u * lane);
-      if constexpr (EPI == EPI_RESID) ea.y[R] += s;
-      else ea.y[R] = s;
+    for (int t = tid; t < sh.no; t += NT) {
+      const float s = row_total(job, t);
+      if constexpr (EPI == EPI_RESID) ea.y[sh.o0 + t] += s;
+      else ea.y[sh.o0 + t] = s;
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    if (lane < ii.nr) ea.y[ii.r0 + lane] = silu(ldf(yp + 4u * lane)) * ldf(yp + 4u * (ii.nr + lane));
+    for (int t = tid; t < sh.no; t += NT) ea.y[sh.o0 + t] = silu(row_total(job, t)) * row_total(job, sh.no + t);
   } else if constexpr (EPI == EPI_QKV) {
-    if (2 * lane < ii.nr) {
-      const int pos = *ea.pos + ea.pos_add;
-      const bool pos_ok = pos >= ea.pos_add && pos < ea.max_ctx;
-      if (!pos_ok && ea.err) *ea.err = 1;
-      const int R = job.row_base[ii.m] + ii.r0 + 2 * lane;  // even row of an adjacent pair
-      float a = ldf(yp + 8u * lane), b = ldf(yp + 8u * lane + 4);
+    const int pos = *ea.pos + ea.pos_add;
+    const bool pos_ok = pos >= ea.pos_add && pos < ea.max_ctx;
+    if (!pos_ok && ea.err && tid == 0) *ea.err = 1;
+    for (int t = tid; 2 * t < sh.no; t += NT) {
+      const int R = sh.o0 + 2 * t;  // even row of an adjacent pair (concatenated Q, K, V rows)
+      float a = row_total(job, 2 * t), b = row_total(job, 2 * t + 1);
       const int dd = R % ea.head_dim;
       if (R < ea.q_rows + ea.kv_rows) {
         // RoPE: pair (2i, 2i+1) of a head turns by pos * theta^(-2i/head_dim)
@@ -525,74 +586,81 @@ __device__ __forceinline__ void item_epilogue(const Job& job, const Cur& ii, uin
   }
 }
 
-// One step of the stream: the segment at `c` (its loads are in `pre`, its
-// description in `sg`) is stored to the slab, the loads of the segment two
-// ahead (`ah`) are issued into `pre`, and the stored segment is computed.
-// Returns false after the wave's last segment.
-template <int EPI, int LPL>
-__device__ __forceinline__ bool stream_step(const Job& job, const EpiArgs& ea, int lane, int it_end, uint32_t slab,
-                                            uint32_t yp, Cur& c, Cur& ah, bool& ah_ok, int& xslice, XR& xr,
-                                            uint4 (&pre)[LPL], Seg& sg) {
+// Next segment for this wave: a claim on the workgroup's LDS counter.  Ids
+// below 2 * nwaves were handed out statically (wave w: w and w + nwaves).
+__device__ __forceinline__ int claim(const Job& job, int lane) {
+  int old = 0;
+  int* ctr = static_cast<int*>(__builtin_assume_aligned(nt_smem + job.ctl, 16));
+  if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return 2 * job.nwaves + __builtin_amdgcn_readfirstlane(old);
+}
+
+// One step of the stream: the segment in buffer `pre` (described by `sg`,
+// id k_cur) is stored to the slab, a newly claimed segment's loads are
+// issued into `pre`, and the stored segment is computed into its (row,
+// slice) partial sum.  The other buffer holds segment k_nxt (already in
+// flight).  A step past the wave's last segment only issues its stand-in
+// loads: the stream loop then has a single exit, at the bottom, so the wait
+// analysis never sees the buffers' load order swapped.
+template <int LPL>
+__device__ __forceinline__ void stream_step(const Job& job, const Share& sh, int lane, uint32_t slab, int& k_cur,
+                                            int& k_nxt, bool& claiming, int& xslice, XR& xr, uint4 (&pre)[LPL],
+                                            Seg& sg) {
   const Seg cur = sg;
+  const bool valid = k_cur < sh.nseg;
   seg_store(slab, lane, pre);
-  if (ah_ok) {
-    sg = seg_of(job, ah);
-    seg_load(sg, lane, pre);
-    ah_ok = cur_next(job, ah, it_end);
+  int k2 = sh.nseg;
+  if (claiming) {
+    k2 = claim(job, lane);
+    claiming = k2 < sh.nseg;
   }
-  if (c.s != xslice) {
-    load_xr(job, c.s, lane, xr);
-    xslice = c.s;
-  }
-  const float part = wave_sum(seg_compute(cur, slab, lane, xr));
-  {
+  sg = k2 < sh.nseg ? seg_at(job, sh, k2) : seg_null(job);
+  seg_load(sg, lane, pre);
+  if (valid) {
+    if (cur.s != xslice) {
+      load_xr(job, cur.s, lane, xr);
+      xslice = cur.s;
+    }
+    const float part = wave_sum(seg_compute(cur, slab, lane, xr));
     // every lane writes the same uniform value: no divergent branch
-    const uint32_t a = yp + 4u * c.g;
-    stf(a, c.s == 0 ? part : ldf(a) + part);
+    stf(job.acc + 4u * (uint32_t)(cur.v * job.nslice + cur.s), part);
   }
-  const bool item_done = c.s == job.nslice - 1 && c.g == c.ns - 1;
-  if (item_done) item_epilogue<EPI>(job, c, yp, lane, ea);
-  return cur_next(job, c, it_end);
+  k_cur = k_nxt;
+  k_nxt = k2;
 }
 
 template <int EPI, int LPL>
 __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, EpiArgs ea) {
   const int tid = threadIdx.x, lane = tid & 63;
-  // the wave index is uniform: keep everything derived from it (item range,
-  // stream position, segment addresses) in scalar registers
+  // the wave index is uniform: keep everything derived from it (segment ids
+  // and addresses) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nitems = job.item_start[job.nmat];
-  const int64_t gw = (int64_t)blockIdx.x * job.nwaves + wave;
-  const int64_t GW = (int64_t)gridDim.x * job.nwaves;
-  const int it_begin = (int)(gw * nitems / GW), it_end = (int)((gw + 1) * nitems / GW);
+  const Share sh = share_of(job, blockIdx.x);
   const uint32_t slab = job.slab + (uint32_t)wave * (uint32_t)(LPL * 1024);
-  const uint32_t yp = job.ypart + (uint32_t)wave * (4 * 2 * kMaxRows);
+  if (tid == 0) sti32(job.ctl, 0);  // claim counter; the prologue's barrier publishes it
+  XStage xst;
+  float g0[32];
+  stage_load(job, pro, tid, xst, g0);  // activation loads first: they retire first
   uint4 pa[LPL], pb[LPL];
   Seg sa, sb;
-  const bool live = it_begin < it_end;
-  Cur c, ah;
-  bool ah_ok = live;
-  if (live) {
-    cur_begin(job, c, it_begin);
-    ah = c;
-    // two segments in flight before the prologue
-    sa = seg_of(job, ah);
-    seg_load(sa, lane, pa);
-    ah_ok = cur_next(job, ah, it_end);
-    if (ah_ok) {
-      sb = seg_of(job, ah);
-      seg_load(sb, lane, pb);
-      ah_ok = cur_next(job, ah, it_end);
-    }
+  int k_cur = wave, k_nxt = wave + job.nwaves;
+  // two segments in flight before the prologue (unconditional loads: see seg_null)
+  sa = k_cur < sh.nseg ? seg_at(job, sh, k_cur) : seg_null(job);
+  seg_load(sa, lane, pa);
+  sb = k_nxt < sh.nseg ? seg_at(job, sh, k_nxt) : seg_null(job);
+  seg_load(sb, lane, pb);
+  stage_finish(job, pro, tid, xst, g0);  // ends with a workgroup barrier
+  if (k_cur < sh.nseg) {
+    XR xr;
+    int xslice = -1;
+    bool claiming = k_nxt < sh.nseg;
+    do {
+      stream_step<LPL>(job, sh, lane, slab, k_cur, k_nxt, claiming, xslice, xr, pa, sa);
+      stream_step<LPL>(job, sh, lane, slab, k_cur, k_nxt, claiming, xslice, xr, pb, sb);
+    } while (k_cur < sh.nseg);
   }
-  stage_x(job, pro, tid);  // the only workgroup barrier
-  if (!live) return;
-  XR xr;
-  int xslice = -1;
-  while (true) {
-    if (!stream_step<EPI, LPL>(job, ea, lane, it_end, slab, yp, c, ah, ah_ok, xslice, xr, pa, sa)) break;
-    if (!stream_step<EPI, LPL>(job, ea, lane, it_end, slab, yp, c, ah, ah_ok, xslice, xr, pb, sb)) break;
-  }
+  __syncthreads();
+  share_epilogue<EPI>(job, sh, tid, ea);
 }
 
 struct DevInfo {
@@ -630,7 +698,7 @@ int launch_lpl(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_
 
 template <int EPI>
 int launch_epi(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t stream) {
-  if (job.item_start[job.nmat] <= 0) return NT_OK;
+  if (job.orows <= 0) return NT_OK;
   switch (job.lpl) {
     case 3: return launch_lpl<EPI, 3>(job, pro, ea, stream);
     case 4: return launch_lpl<EPI, 4>(job, pro, ea, stream);
@@ -642,8 +710,9 @@ int launch_epi(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_
 }  // namespace
 
 // Geometry of a launch: column slices of at most 4096 weights (whole
-// blocks), rows per item, the LDS layout, and the grid (one workgroup per CU,
-// fewer when there are too few items).
+// blocks), each workgroup's share of output rows, the LDS layout, and the
+// grid (one workgroup per CU, fewer when there is little work, more when a
+// share's partial-sum table would not fit).
 int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const int* rows, int cols, int paired,
              int pairs) {
   if (nmat < 1 || nmat > kMaxMats || (paired && nmat != 2)) return NT_EINVAL;
@@ -654,7 +723,7 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
   job.pairs = pairs;
   job.cols = cols;
   bool kquant = false;
-  int64_t total_rows = 0;
+  int64_t orows = 0;
   for (int m = 0; m < nmat; ++m) {
     const int qk = block_elems(fmt[m]);
     if (qk == 0 || cols % qk != 0) return NT_EINVAL;
@@ -666,8 +735,12 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
     job.fmt[m] = fmt[m];
     job.rows[m] = rows[m];
     job.rb[m] = (int64_t)(cols / qk) * block_bytes(fmt[m]);
-    if (!paired || m == 0) total_rows += rows[m];
+    job.row_base[m] = paired ? 0 : (int)orows;
+    if (!paired || m == 0) orows += rows[m];
   }
+  if (orows > INT32_MAX / 2) return NT_EUNSUPPORTED;
+  job.orows = (int)orows;
+  job.unit = pairs ? 2 : 1;
   const int units = (cols + 63) / 64;
   job.nslice = (units + kSliceUnits - 1) / kSliceUnits;
   int ups = (units + job.nslice - 1) / job.nslice;
@@ -686,26 +759,25 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
   if (need > kSlabLoads) return NT_EUNSUPPORTED;
   job.nwaves = kMaxWaves;
   const int cus = dev_info().cus;
-  const int64_t waves = (int64_t)cus * job.nwaves;
-  // rows per item: RoPE pairs need 2; with one slice rows never share the
-  // activation registers, so 1; with several, enough rows that a wave's
-  // rows fill its share of the matrix (fewer reloads of the activation)
-  int R = 1;
-  if (job.nslice > 1) {
-    const int64_t per_wave = (total_rows + waves - 1) / waves;
-    R = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxRows, per_wave));
+  // workgroups: about one per CU, no more than one per wave's worth of
+  // segments, and enough that a share's (row, slice) table fits kAccFloats
+  const int vper = paired ? 2 : 1;  // segment rows per output row
+  const int64_t nu = orows / job.unit;
+  const int64_t segs = orows * vper * job.nslice;
+  int64_t grid = std::min<int64_t>(cus, (segs + job.nwaves - 1) / job.nwaves);
+  const int64_t units_cap = kAccFloats / ((int64_t)job.nslice * job.unit * vper);
+  if (units_cap < 1) return NT_EUNSUPPORTED;
+  grid = std::max<int64_t>(grid, (nu + units_cap - 1) / units_cap);
+  grid = std::max<int64_t>(1, std::min<int64_t>(grid, std::max<int64_t>(nu, 1)));
+  if (grid > INT32_MAX) return NT_EUNSUPPORTED;
+  job.grid = (int)grid;
+  job.wg_base = (int)(nu / grid);
+  job.wg_rem = (int)(nu % grid);
+  for (int i = 0; i < 2; ++i) {
+    const int64_t nv = (int64_t)(job.wg_base + i) * job.unit * vper;
+    job.magic[i] = nv > 0 ? (uint32_t)(0xffffffffull / (uint64_t)nv) : 0u;
   }
-  if (pairs) R = std::max(2, R & ~1);
-  job.R = R;
-  int items = 0, rbase = 0;
-  for (int m = 0; m < nmat; ++m) {
-    job.item_start[m] = items;
-    job.row_base[m] = rbase;
-    rbase += rows[m];
-    if (!paired || m == 0) items += (rows[m] + R - 1) / R;
-  }
-  if (paired) job.item_start[1] = items;
-  job.item_start[nmat] = items;
+  const int64_t nv_max = (int64_t)(job.wg_base + (job.wg_rem ? 1 : 0)) * job.unit * vper;
   uint32_t off = 0;
   job.x_hi = off; off += cols + 64;
   job.x_lo = off; off += cols + 64;
@@ -713,14 +785,14 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
   job.x_sc = off; off += (cols / 32 + 2) * 4;
   job.x_sum = off; off += (cols / 16 + 4) * 4;
   job.red = off; off += 16 * 4;
+  job.ctl = off; off += 16;
   job.rope = off; off += 128 * 8;  // cos/sin of up to 128 rotation pairs (head_dim <= 256)
-  job.ypart = off; off += job.nwaves * 4 * 2 * kMaxRows;
+  job.acc = off; off += (uint32_t)(nv_max * job.nslice * 4);
   off = (off + 15) & ~15u;
   job.slab = off;
   off += (uint32_t)(job.nwaves * job.lpl * 1024);
   job.lds_bytes = off;
   if (job.lds_bytes > 160 * 1024) return NT_EUNSUPPORTED;
-  job.grid = (int)std::max<int64_t>(1, std::min<int64_t>(cus, (items + job.nwaves - 1) / job.nwaves));
   return NT_OK;
 }
 

@@ -15,7 +15,7 @@ constexpr int kUnitsPerLane = 1;  // 64-weight column units a lane owns in one c
 constexpr int kSliceUnits = 64 * kUnitsPerLane;  // column units per slice (4096 weights)
 constexpr int kSlabLoads = 5;     // 16-B loads per lane for the largest segment (Q8_0: 4352 B + alignment)
 constexpr int kSlab = kSlabLoads * 64 * 16;  // bytes of one wave's LDS staging slab
-constexpr int kMaxRows = 8;       // rows per work item
+constexpr int kAccFloats = 4096;  // per-workgroup table of (row, slice) partial sums, in floats
 constexpr int kMaxMats = 3;       // matrices one engine launch walks (Q, K, V)
 constexpr int64_t kMaxCols = 49152;
 
@@ -34,23 +34,28 @@ __host__ __device__ inline int block_bytes(int fmt) {
 
 // How a launch of the GEMV engine walks its matrices.
 //  - Columns are cut into `nslice` slices of `ups` 64-weight units; a lane
-//    owns units lane and lane+64 of the current slice and keeps their
-//    staged activation in registers.
-//  - The work is a list of items of up to R consecutive rows of one matrix
-//    (`pairs`: R is even, RoPE needs row pairs), or R rows of W[0] together
-//    with the same rows of W[1] (`paired`: SwiGLU needs gate and up).
-//  - A wave owns a contiguous range of items and streams, item by item and
-//    slice by slice, each (row, slice) byte range -- a segment -- through
-//    its LDS slab.  All matrices share `cols`.
+//    owns unit `lane` of the current slice and keeps its staged activation
+//    in registers.
+//  - Output rows are the matrices' rows one after the other (`nmat` <= 3,
+//    e.g. Q, K, V), or, with `paired`, the rows of W[0] each together with
+//    the same row of W[1] (SwiGLU needs gate and up).  With `pairs`, rows
+//    are handed out in even-aligned pairs (RoPE rotates adjacent rows).
+//  - Workgroup b owns a contiguous range of output rows.  Its work is the
+//    list of segments (one row of one matrix within one column slice: a
+//    contiguous byte range), slice-major; its waves claim segments one at a
+//    time from a counter in LDS, so waves that the SIMD arbiter favours take
+//    more and all finish together.  Each segment's dot product lands in an
+//    LDS table of (row, slice) partial sums; after a workgroup barrier the
+//    epilogue adds the slices in order (deterministic) and writes the rows.
 struct Job {
   const uint8_t* W[kMaxMats];
   int64_t rb[kMaxMats];       // bytes per row
   int fmt[kMaxMats];
   int rows[kMaxMats];
   int row_base[kMaxMats];     // first output row of each matrix (concatenated outputs)
-  int item_start[kMaxMats + 1];
   int64_t slice_bytes[kMaxMats];  // bytes of one full column slice of a row
-  int R;                      // rows per item
+  int orows;                  // output rows
+  int unit;                   // rows are handed to workgroups in multiples of this (2 with pairs)
   int ups;                    // units per slice
   int nslice;
   int last_units;             // units of the last slice (may be partial)
@@ -61,9 +66,11 @@ struct Job {
   int cols;
   int nwaves;                 // waves per workgroup
   int grid;                   // workgroups
+  int wg_base, wg_rem;        // workgroup b owns wg_base (+1 if b < wg_rem) units of `unit` output rows
+  uint32_t magic[2];          // floor((2^32-1)/nv) for the two segment-row counts nv of a workgroup
   int lpl;                    // 16-B loads per lane per segment (3, 4 or 5)
   // dynamic LDS layout (byte offsets)
-  uint32_t x_hi, x_lo, x_sc, x_sum, red, slab, ypart, rope;
+  uint32_t x_hi, x_lo, x_sc, x_sum, red, slab, acc, ctl, rope;
   uint32_t lds_bytes;
 };
 
