@@ -266,110 +266,141 @@ __device__ __forceinline__ float unit_q6_k(uint32_t seg, int k, NT_XARGS) {
 // s = max|v| / 32639, X = rint(v / s), hi = (X + 128) >> 8, lo = X - 256 hi.
 // For the QKV launch it also tabulates the RoPE rotation of this position.
 //
-// Thread t owns 32-element block t (and t + NT, ... for very wide inputs).
-// The loads of its first block are issued before the first weight segments
-// (stage_load), so waiting for them does not wait for the weights: memory
-// operations retire in order.
+// Loads are coalesced: in round r thread t holds elements 4(NT r + t) ..
+// +3, so the 8 lanes of an aligned lane group hold one 32-block and a
+// wave's load covers 1 KB of consecutive bytes.  A wave's activation must
+// have arrived (stage_load, stage_norm) before it issues its first weight
+// loads: behind the launch's burst of weight requests an activation miss
+// would wait several microseconds in the memory queues, and the quantization
+// then overlaps the weights' latency instead.
 
-// The thread's first block: src values, times the gains when normalising.
+constexpr int kXRounds = 8;  // rounds held in registers: inputs up to 4 * 1024 * 8 = 32768 wide
+
 struct XStage {
-  float v[32];
-  float ss;  // sum of squares of the raw src values (RMSNorm)
+  float4 v[kXRounds];  // src, times the gains when normalising
+  float4 g[kXRounds];
 };
 
-// Loads are unconditional (without gains the source is read twice) so the
-// number of loads in flight does not depend on the path.
-__device__ __forceinline__ void load_block(const ProArgs& pro, int b, float (&v)[32], float (&g)[32]) {
-  const float4* s4 = reinterpret_cast<const float4*>(pro.src + 32 * b);
-  const float4* g4 = reinterpret_cast<const float4*>((pro.gain ? pro.gain : pro.src) + 32 * b);
+__device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 mul4(float4 a, float4 b) { return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w); }
+__device__ __forceinline__ float4 scale4(float4 a, float r) { return make_float4(a.x * r, a.y * r, a.z * r, a.w * r); }
+__device__ __forceinline__ float sq4(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
+
+__device__ __forceinline__ void stage_load(const Job& job, const ProArgs& pro, int tid, XStage& st) {
+  const int NT = job.nwaves * 64;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float4 t = s4[j];
-    v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float4 t = g4[j];
-    g[4 * j] = t.x; g[4 * j + 1] = t.y; g[4 * j + 2] = t.z; g[4 * j + 3] = t.w;
+  for (int r = 0; r < kXRounds; ++r) {
+    const int e = 4 * (NT * r + tid);
+    if (e < job.cols) {
+      st.v[r] = ld_f4(pro.src + e);
+      if (pro.gain) st.g[r] = ld_f4(pro.gain + e);
+    }
   }
 }
 
-// Sum of squares of v into ss; v becomes v * gain.
-__device__ __forceinline__ void apply_gain(const ProArgs& pro, float (&v)[32], const float (&g)[32], float& ss) {
-#pragma unroll
-  for (int j = 0; j < 32; ++j) ss += v[j] * v[j];
+// Uses the loaded activation (so its loads are waited for here): the sum of
+// squares of the source and the gain product.
+__device__ __forceinline__ float stage_norm(const Job& job, const ProArgs& pro, int tid, XStage& st) {
+  const int NT = job.nwaves * 64;
+  float ss = 0.f;
   if (pro.gain) {
 #pragma unroll
-    for (int j = 0; j < 32; ++j) v[j] *= g[j];
-  }
-}
-
-__device__ __forceinline__ void stage_load(const Job& job, const ProArgs& pro, int tid, XStage& st, float (&g)[32]) {
-  st.ss = 0.f;
-  load_block(pro, tid < (job.cols >> 5) ? tid : 0, st.v, g);  // threads without a block re-read block 0
-}
-
-// Quantize block b of v * r into the LDS planes.
-__device__ __forceinline__ void quant_block(const Job& job, int b, const float (&v)[32], float r) {
-  float amax = 0.f;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j] * r));
-  const float inv = amax > 0.f ? kXMax / amax : 0.f;
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    uint32_t H[4] = {0, 0, 0, 0}, L[4] = {0, 0, 0, 0};
-    int sum = 0;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      int X = __float2int_rn((v[16 * half + k] * r) * inv);
-      X = max(-32639, min(32639, X));
-      const int hi = (X + 128) >> 8;
-      const int lo = X - (hi << 8);
-      H[k >> 2] |= (uint32_t)(hi & 255) << (8 * (k & 3));
-      L[k >> 2] |= (uint32_t)(lo & 255) << (8 * (k & 3));
-      sum += X;
+    for (int k = 0; k < kXRounds; ++k) {
+      const int e = 4 * (NT * k + tid);
+      if (e < job.cols) {
+        ss += sq4(st.v[k]);
+        st.v[k] = mul4(st.v[k], st.g[k]);
+      }
     }
-    st128(job.x_hi + 32u * b + 16 * half, make_uint4(H[0], H[1], H[2], H[3]));
-    st128(job.x_lo + 32u * b + 16 * half, make_uint4(L[0], L[1], L[2], L[3]));
-    sti32(job.x_sum + 8u * b + 4 * half, sum);
+  } else {
+    // a use of every loaded value, so the waits happen here
+#pragma unroll
+    for (int k = 0; k < kXRounds; ++k) {
+      const int e = 4 * (NT * k + tid);
+      if (e < job.cols) ss += st.v[k].x;
+    }
   }
-  stf(job.x_sc + 4u * b, amax / kXMax);
+  return ss;
 }
 
-__device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro, int tid, XStage& st,
-                                             const float (&g0)[32]) {
-  const int NT = job.nwaves * 64, nb = job.cols >> 5;
-  if (tid < nb) apply_gain(pro, st.v, g0, st.ss);
+// Reductions over the lane groups that hold one 32-block (8 lanes) and one
+// 16-sum (4 lanes): DPP quad permutations and the half-row mirror.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float max8(float x) {
+  x = fmaxf(x, __builtin_bit_cast(float, dpp_i<0xB1>(__builtin_bit_cast(int, x))));  // quad_perm 1,0,3,2
+  x = fmaxf(x, __builtin_bit_cast(float, dpp_i<0x4E>(__builtin_bit_cast(int, x))));  // quad_perm 2,3,0,1
+  return fmaxf(x, __builtin_bit_cast(float, dpp_i<0x141>(__builtin_bit_cast(int, x))));  // row_half_mirror
+}
+__device__ __forceinline__ int sum4(int x) {
+  x += dpp_i<0xB1>(x);
+  return x + dpp_i<0x4E>(x);
+}
+
+// Quantize elements e..e+3 (held by this lane, already scaled) into the LDS
+// planes; the group's first lanes write the block scale and the 16-sums.
+__device__ __forceinline__ void quant4(const Job& job, int lane, int e, float4 w) {
+  float amax = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
+  amax = max8(amax);
+  const float inv = amax > 0.f ? kXMax / amax : 0.f;
+  const float f[4] = {w.x, w.y, w.z, w.w};
+  uint32_t H = 0, L = 0;
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int X = __float2int_rn(f[k] * inv);
+    X = max(-32639, min(32639, X));
+    const int hi = (X + 128) >> 8;
+    const int lo = X - (hi << 8);
+    H |= (uint32_t)(hi & 255) << (8 * k);
+    L |= (uint32_t)(lo & 255) << (8 * k);
+    sum += X;
+  }
+  *reinterpret_cast<uint32_t*>(nt_smem + job.x_hi + e) = H;
+  *reinterpret_cast<uint32_t*>(nt_smem + job.x_lo + e) = L;
+  sum = sum4(sum);
+  if ((lane & 3) == 0) sti32(job.x_sum + 4u * (uint32_t)(e >> 4), sum);
+  if ((lane & 7) == 0) stf(job.x_sc + 4u * (uint32_t)(e >> 5), amax / kXMax);
+}
+
+
+// ss: this thread's sum of squares from stage_norm.
+__device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro, int tid, XStage& st, float ss) {
+  const int NT = job.nwaves * 64, lane = tid & 63;
+  const int nround = (job.cols + 4 * NT - 1) / (4 * NT);
   float r = 1.0f;
   if (pro.gain) {
-    // blocks past the first of each thread (inputs wider than 32 * NT)
-    for (int b = tid + NT; b < nb; b += NT) {
-      float v[32], g[32], ss = 0.f;
-      load_block(pro, b, v, g);
-#pragma unroll
-      for (int j = 0; j < 32; ++j) ss += v[j] * v[j];
-      st.ss += ss;
+    // rounds past the registers (inputs wider than 32768)
+    for (int k = kXRounds; k < nround; ++k) {
+      const int e = 4 * (NT * k + tid);
+      if (e < job.cols) ss += sq4(ld_f4(pro.src + e));
     }
-    const float ss = wave_sum(st.ss);
-    if ((tid & 63) == 0) stf(job.red + 4u * (tid >> 6), ss);
+    ss = wave_sum(ss);
+    if (lane == 0) stf(job.red + 4u * (tid >> 6), ss);
     __syncthreads();
     float tot = 0.f;
     for (int w = 0; w < job.nwaves; ++w) tot += ldf(job.red + 4u * w);
     r = 1.0f / sqrtf(tot / (float)job.cols + pro.eps);
   }
-  if (tid < nb) quant_block(job, tid, st.v, r);
-  for (int b = tid + NT; b < nb; b += NT) {
-    float v[32], g[32], ss = 0.f;
-    load_block(pro, b, v, g);
-    apply_gain(pro, v, g, ss);
-    quant_block(job, b, v, r);
+#pragma unroll
+  for (int k = 0; k < kXRounds; ++k) {
+    const int e = 4 * (NT * k + tid);
+    if (e < job.cols) quant4(job, lane, e, scale4(st.v[k], r));
+  }
+  for (int k = kXRounds; k < nround; ++k) {
+    const int e = 4 * (NT * k + tid);
+    if (e < job.cols) {
+      float4 v = ld_f4(pro.src + e);
+      if (pro.gain) v = mul4(v, ld_f4(pro.gain + e));
+      quant4(job, lane, e, scale4(v, r));
+    }
   }
   if (pro.rope_hd > 0) {
     // pair i turns by pos * theta^(-2i/head_dim); the angle is formed in
-    // double so large positions keep fp32 accuracy.  The last threads take
-    // this (they hold no activation block when the input is narrow).
-    const int npair = pro.rope_hd / 2;
-    for (int i = NT - 1 - tid; i >= 0 && i < npair; i += NT) {
+    // double so large positions keep fp32 accuracy
+    for (int i = tid; i < pro.rope_hd / 2; i += NT) {
       const int pos = *pro.pos + pro.pos_add;
       const double freq = exp2(-(double)(2 * i) / (double)pro.rope_hd * log2((double)pro.rope_theta));
       const double ang = (double)pos * freq;
@@ -639,8 +670,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, Epi
   const uint32_t slab = job.slab + (uint32_t)wave * (uint32_t)(LPL * 1024);
   if (tid == 0) sti32(job.ctl, 0);  // claim counter; the prologue's barrier publishes it
   XStage xst;
-  float g0[32];
-  stage_load(job, pro, tid, xst, g0);  // activation loads first: they retire first
+  stage_load(job, pro, tid, xst);
+  const float ss = stage_norm(job, pro, tid, xst);  // the activation has arrived
   uint4 pa[LPL], pb[LPL];
   Seg sa, sb;
   int k_cur = wave, k_nxt = wave + job.nwaves;
@@ -649,7 +680,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, Epi
   seg_load(sa, lane, pa);
   sb = k_nxt < sh.nseg ? seg_at(job, sh, k_nxt) : seg_null(job);
   seg_load(sb, lane, pb);
-  stage_finish(job, pro, tid, xst, g0);  // ends with a workgroup barrier
+  stage_finish(job, pro, tid, xst, ss);  // ends with a workgroup barrier
   if (k_cur < sh.nseg) {
     XR xr;
     int xslice = -1;
