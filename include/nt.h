@@ -83,14 +83,24 @@ int64_t nt_max_cols(void);
 int nt_gemv_q(int fmt, const void* W, const float* x, float* y, int64_t rows, int64_t cols, void* stream);
 
 /*
- * Y[m] = W X[m] for M tokens (the verify pass of self-speculative decoding
- * runs M drafted tokens through every projection; p1 feature list).
- *   X: device fp32 [M][cols], rows 16-byte aligned; Y: device fp32 [M][rows];
- *   1 <= M <= 8.  Same arithmetic as nt_gemv_q; currently one weight pass per
- *   token.
+ * Workspace bytes nt_gemm_q_small needs for 2 <= M <= 8 tokens (0 for other
+ * M or an unsupported shape; M == 1 needs none).
  */
-int nt_gemm_q_small(int fmt, const void* W, const float* X, float* Y, int M, int64_t rows, int64_t cols,
-                    void* stream);
+size_t nt_gemm_q_small_workspace_bytes(int M, int64_t rows, int64_t cols);
+
+/*
+ * Y[m] = W X[m] for M tokens (the verify pass of self-speculative decoding
+ * runs M drafted tokens through every projection in one pass; p1 "Features").
+ *   X: device fp32 [M][cols], rows 16-byte aligned; Y: device fp32 [M][rows],
+ *   overwritten; 1 <= M <= 8.  The weights are read once for all M tokens:
+ *   int8 MFMA tiles over the same 16-bit fixed-point activation as nt_gemv_q
+ *   (M == 1 is nt_gemv_q).
+ *   ws: device workspace of ws_bytes >= nt_gemm_q_small_workspace_bytes(M,
+ *   rows, cols), 16-byte aligned (may be NULL when M == 1); its contents need
+ *   no initialisation.  Calls that share a workspace must not overlap.
+ */
+int nt_gemm_q_small(int fmt, const void* W, const float* X, float* Y, int M, int64_t rows, int64_t cols, void* ws,
+                    size_t ws_bytes, void* stream);
 
 /* Shape of one Llama decoder layer. */
 typedef struct nt_layer_cfg {

@@ -58,8 +58,10 @@ EXPORTS = {
     "nt_max_cols": (ctypes.c_int64, []),
     "nt_gemv_q": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
+    "nt_gemm_q_small_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]),
     "nt_gemm_q_small": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                       ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
+                                       ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.c_void_p]),
     "nt_layer_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(LayerCfg), ctypes.c_int]),
     "nt_decode_layer": (ctypes.c_int, [ctypes.POINTER(LayerCfg), ctypes.POINTER(Layer), ctypes.c_void_p,
                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
@@ -152,10 +154,17 @@ def gemv_q(fmt: int, W, x, y, rows: int, cols: int, stream=None) -> None:
     _check("nt_gemv_q", lib().nt_gemv_q(fmt, _ptr(W), _ptr(x), _ptr(y), rows, cols, _stream(stream)))
 
 
-def gemm_q_small(fmt: int, W, X, Y, M: int, rows: int, cols: int, stream=None) -> None:
-    """Y[m] = W X[m] for M <= 8 tokens  (nt_gemm_q_small)."""
+def gemm_q_small_workspace_bytes(M: int, rows: int, cols: int) -> int:
+    """Workspace bytes of nt_gemm_q_small (0 when M == 1 or the shape is unsupported)."""
+    return lib().nt_gemm_q_small_workspace_bytes(M, rows, cols)
+
+
+def gemm_q_small(fmt: int, W, X, Y, M: int, rows: int, cols: int, ws=None, stream=None) -> None:
+    """Y[m] = W X[m] for M <= 8 tokens, weights read once  (nt_gemm_q_small)."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("nt_gemm_q_small",
-           lib().nt_gemm_q_small(fmt, _ptr(W), _ptr(X), _ptr(Y), M, rows, cols, _stream(stream)))
+           lib().nt_gemm_q_small(fmt, _ptr(W), _ptr(X), _ptr(Y), M, rows, cols,
+                                 None if ws is None else _ptr(ws), nbytes, _stream(stream)))
 
 
 def layer_cfg(hidden, n_head, n_kv_head, head_dim, ffn, max_ctx, rope_theta=5e5, rms_eps=1e-5) -> LayerCfg:

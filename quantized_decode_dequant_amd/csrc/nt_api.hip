@@ -15,9 +15,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Workspace of one decode layer for M tokens (offsets from the base).
+// Workspace of one decode layer for M tokens (offsets from the base).  With
+// M >= 2 it also holds the small-M GEMM's staged activation and partial sums.
 struct LayerWs {
-  size_t q, part_o, part_ml, o, a, err, total;
+  size_t q, part_o, part_ml, o, a, err, stage, part, total;
   int chunk, nsplit;
 };
 
@@ -41,8 +42,17 @@ LayerWs layer_ws(const nt_layer_cfg& c, int M) {
   w.part_o = off; off += up256((size_t)M * w.nsplit * nq * 4);
   w.part_ml = off; off += up256((size_t)M * w.nsplit * c.n_head * 2 * 4);
   w.o = off; off += up256((size_t)M * nq * 4);
-  w.a = off; off += up256((size_t)c.ffn * 4);
+  w.a = off; off += up256((size_t)M * c.ffn * 4);
   w.err = off; off += 256;
+  if (M >= 2) {
+    const int64_t nkv = (int64_t)c.n_kv_head * c.head_dim;
+    w.stage = off; off += up256(stage_m_bytes(std::max<int>(std::max<int>(c.hidden, (int)nq), c.ffn)));
+    size_t pb = part_m_bytes((int64_t)nq + 2 * nkv, 0, c.hidden, M);
+    pb = std::max(pb, part_m_bytes(c.hidden, 0, (int)nq, M));
+    pb = std::max(pb, part_m_bytes(c.ffn, 1, c.hidden, M));
+    pb = std::max(pb, part_m_bytes(c.hidden, 0, c.ffn, M));
+    w.part = off; off += up256(pb);
+  }
   w.total = off;
   return w;
 }
@@ -66,9 +76,97 @@ int check_layer(const nt_layer_cfg& c, const nt_layer& L) {
 
 const uint8_t* u8(const void* p) { return static_cast<const uint8_t*>(p); }
 
+// The launches of one layer for 2 <= M <= 8 tokens: each projection stages
+// its M activation rows once and reads the weights once (int8 MFMA).
+int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const int32_t* pos, uint8_t* ws,
+                const LayerWs& w, hipStream_t st) {
+  const int nq = c.n_head * c.head_dim, nkv = c.n_kv_head * c.head_dim;
+  float* q = reinterpret_cast<float*>(ws + w.q);
+  float* part_o = reinterpret_cast<float*>(ws + w.part_o);
+  float* part_ml = reinterpret_cast<float*>(ws + w.part_ml);
+  float* o = reinterpret_cast<float*>(ws + w.o);
+  float* a = reinterpret_cast<float*>(ws + w.a);
+  int* err = reinterpret_cast<int*>(ws + w.err);
+  void* stage = ws + w.stage;
+  void* part = ws + w.part;
+  const ProArgs none{nullptr, nullptr, 0.f, 0, 0, 0.f, nullptr, 0};
+  int rc;
+  // 1. RMSNorm -> Q,K,V projections -> RoPE -> q, K/V append (token t at pos + t)
+  {
+    JobM job;
+    const uint8_t* W[3] = {u8(L.wq.data), u8(L.wk.data), u8(L.wv.data)};
+    const int fmt[3] = {L.wq.fmt, L.wk.fmt, L.wv.fmt};
+    const int rows[3] = {nq, nkv, nkv};
+    if ((rc = plan_job_m(job, 3, W, fmt, rows, c.hidden, 0, 1, M)) != NT_OK) return rc;
+    if ((rc = launch_stage_m(x, c.hidden, L.attn_norm, c.rms_eps, M, c.hidden, stage, st)) != NT_OK) return rc;
+    ProArgs pro = none;
+    pro.rope_hd = c.head_dim;
+    pro.rope_theta = c.rope_theta;
+    pro.pos = pos;
+    EpiArgs ea{};
+    ea.q_out = q;
+    ea.ld = nq;
+    ea.k_cache = L.k_cache;
+    ea.v_cache = L.v_cache;
+    ea.pos = pos;
+    ea.err = err;
+    ea.head_dim = c.head_dim;
+    ea.max_ctx = c.max_ctx;
+    ea.rope_theta = c.rope_theta;
+    ea.q_rows = nq;
+    ea.kv_rows = nkv;
+    if ((rc = launch_gemm_m(job, stage, part, pro, EPI_QKV, ea, st)) != NT_OK) return rc;
+  }
+  // 2. attention over the cache (token t sees positions 0..pos+t)
+  if ((rc = launch_attention(q, L.k_cache, L.v_cache, pos, M, c.n_head, c.n_kv_head, c.head_dim, c.max_ctx, w.chunk,
+                             w.nsplit, part_o, part_ml, o, st)) != NT_OK)
+    return rc;
+  // 3. h = x + Wo o
+  {
+    JobM job;
+    const uint8_t* W[1] = {u8(L.wo.data)};
+    const int fmt[1] = {L.wo.fmt};
+    const int rows[1] = {c.hidden};
+    if ((rc = plan_job_m(job, 1, W, fmt, rows, nq, 0, 0, M)) != NT_OK) return rc;
+    if ((rc = launch_stage_m(o, nq, nullptr, 0.f, M, nq, stage, st)) != NT_OK) return rc;
+    EpiArgs ea{};
+    ea.y = x;
+    ea.ld = c.hidden;
+    if ((rc = launch_gemm_m(job, stage, part, none, EPI_RESID, ea, st)) != NT_OK) return rc;
+  }
+  // 4. a = silu(Wg hn) * (Wu hn), hn = RMSNorm(h)
+  {
+    JobM job;
+    const uint8_t* W[2] = {u8(L.wg.data), u8(L.wu.data)};
+    const int fmt[2] = {L.wg.fmt, L.wu.fmt};
+    const int rows[2] = {c.ffn, c.ffn};
+    if ((rc = plan_job_m(job, 2, W, fmt, rows, c.hidden, 1, 0, M)) != NT_OK) return rc;
+    if ((rc = launch_stage_m(x, c.hidden, L.ffn_norm, c.rms_eps, M, c.hidden, stage, st)) != NT_OK) return rc;
+    EpiArgs ea{};
+    ea.y = a;
+    ea.ld = c.ffn;
+    if ((rc = launch_gemm_m(job, stage, part, none, EPI_SWIGLU, ea, st)) != NT_OK) return rc;
+  }
+  // 5. x = h + Wd a
+  {
+    JobM job;
+    const uint8_t* W[1] = {u8(L.wd.data)};
+    const int fmt[1] = {L.wd.fmt};
+    const int rows[1] = {c.hidden};
+    if ((rc = plan_job_m(job, 1, W, fmt, rows, c.ffn, 0, 0, M)) != NT_OK) return rc;
+    if ((rc = launch_stage_m(a, c.ffn, nullptr, 0.f, M, c.ffn, stage, st)) != NT_OK) return rc;
+    EpiArgs ea{};
+    ea.y = x;
+    ea.ld = c.hidden;
+    if ((rc = launch_gemm_m(job, stage, part, none, EPI_RESID, ea, st)) != NT_OK) return rc;
+  }
+  return NT_OK;
+}
+
 // The launches of one layer (arguments already validated).
 int run_layer(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const int32_t* pos, uint8_t* ws,
               const LayerWs& w, hipStream_t st) {
+  if (M >= 2) return run_layer_m(c, L, x, M, pos, ws, w, st);
   const int nq = c.n_head * c.head_dim, nkv = c.n_kv_head * c.head_dim;
   float* q = reinterpret_cast<float*>(ws + w.q);
   float* part_o = reinterpret_cast<float*>(ws + w.part_o);
@@ -153,7 +251,7 @@ int run_layer(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const i
 
 // ---- decode step
 struct StepWs {
-  size_t x, layer, logits, pv, pi, total;
+  size_t x, layer, logits, pv, pi, part_lm, total;
   LayerWs lw;
 };
 
@@ -185,6 +283,10 @@ StepWs step_ws(const nt_model& m, int M) {
   w.logits = off; off += up256((size_t)M * m.vocab * 4);
   w.pv = off; off += up256((size_t)M * 256 * 4);
   w.pi = off; off += up256((size_t)M * 256 * 4);
+  if (M >= 2) {
+    w.part_lm = off;
+    off += up256(part_m_bytes(m.vocab, 0, m.cfg.hidden, M));
+  }
   w.total = off;
   return w;
 }
@@ -293,17 +395,26 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
     }
   }
   // final RMSNorm -> LM head -> argmax
-  Job jl;
-  {
-    const uint8_t* W[1] = {u8(m.lm_head.data)};
-    const int fmt[1] = {m.lm_head.fmt};
-    const int rows[1] = {m.vocab};
-    if ((rc = plan_job(jl, 1, W, fmt, rows, m.cfg.hidden, 0, 0)) != NT_OK) return rc;
-  }
-  for (int i = 0; i < M; ++i) {
-    ProArgs pro{x + (int64_t)i * m.cfg.hidden, m.out_norm, m.cfg.rms_eps, 0, 0, 0.f, nullptr, 0};
+  const uint8_t* Wl[1] = {u8(m.lm_head.data)};
+  const int fmtl[1] = {m.lm_head.fmt};
+  const int rowsl[1] = {m.vocab};
+  if (M >= 2) {
+    JobM jm;
+    if ((rc = plan_job_m(jm, 1, Wl, fmtl, rowsl, m.cfg.hidden, 0, 0, M)) != NT_OK) return rc;
+    void* stage = ws + w.layer + w.lw.stage;
+    if ((rc = launch_stage_m(x, m.cfg.hidden, m.out_norm, m.cfg.rms_eps, M, m.cfg.hidden, stage, st)) != NT_OK)
+      return rc;
+    const ProArgs none{nullptr, nullptr, 0.f, 0, 0, 0.f, nullptr, 0};
     EpiArgs ea{};
-    ea.y = logits + (int64_t)i * m.vocab;
+    ea.y = logits;
+    ea.ld = m.vocab;
+    if ((rc = launch_gemm_m(jm, stage, ws + w.part_lm, none, EPI_STORE, ea, st)) != NT_OK) return rc;
+  } else {
+    Job jl;
+    if ((rc = plan_job(jl, 1, Wl, fmtl, rowsl, m.cfg.hidden, 0, 0)) != NT_OK) return rc;
+    ProArgs pro{x, m.out_norm, m.cfg.rms_eps, 0, 0, 0.f, nullptr, 0};
+    EpiArgs ea{};
+    ea.y = logits;
     if ((rc = launch_gemv(jl, pro, EPI_STORE, ea, st)) != NT_OK) return rc;
   }
   return launch_argmax(logits, M, m.vocab, reinterpret_cast<float*>(ws + w.pv), reinterpret_cast<int*>(ws + w.pi), out,
@@ -356,27 +467,46 @@ int nt_gemv_q(int fmt, const void* W, const float* x, float* y, int64_t rows, in
   return launch_gemv(job, pro, EPI_STORE, ea, static_cast<hipStream_t>(stream));
 }
 
-int nt_gemm_q_small(int fmt, const void* W, const float* X, float* Y, int M, int64_t rows, int64_t cols,
-                    void* stream) {
+size_t nt_gemm_q_small_workspace_bytes(int M, int64_t rows, int64_t cols) {
+  if (M < 2 || M > 8 || rows <= 0 || cols <= 0 || cols > kMaxCols || rows > INT32_MAX / 16) return 0;
+  return up256(stage_m_bytes((int)cols)) + up256(part_m_bytes(rows, 0, (int)cols, M));
+}
+
+int nt_gemm_q_small(int fmt, const void* W, const float* X, float* Y, int M, int64_t rows, int64_t cols, void* ws,
+                    size_t ws_bytes, void* stream) {
   if (M < 1 || M > 8) return NT_EINVAL;
   const int qk = block_elems(fmt);
   if (qk == 0 || rows < 0 || cols <= 0 || cols % qk != 0) return NT_EINVAL;
-  if (rows > INT32_MAX || cols > kMaxCols) return NT_EUNSUPPORTED;
+  if (rows > INT32_MAX / 16 || cols > kMaxCols) return NT_EUNSUPPORTED;
   if (rows == 0) return NT_OK;
   if (!W || !X || !Y) return NT_EINVAL;
   if (!aligned16(W) || !aligned16(X) || (M > 1 && (cols * 4) % 16 != 0)) return NT_EALIGN;
-  Job job;
+  hipStream_t st = static_cast<hipStream_t>(stream);
   const uint8_t* Wp = static_cast<const uint8_t*>(W);
   const int r = (int)rows;
-  int rc = plan_job(job, 1, &Wp, &fmt, &r, (int)cols, 0, 0);
-  if (rc != NT_OK) return rc;
-  for (int m = 0; m < M; ++m) {
-    ProArgs pro{X + (int64_t)m * cols, nullptr, 0.f, 0, 0, 0.f, nullptr, 0};
+  int rc;
+  if (M == 1) {
+    Job job;
+    if ((rc = plan_job(job, 1, &Wp, &fmt, &r, (int)cols, 0, 0)) != NT_OK) return rc;
+    ProArgs pro{X, nullptr, 0.f, 0, 0, 0.f, nullptr, 0};
     EpiArgs ea{};
-    ea.y = Y + (int64_t)m * rows;
-    if ((rc = launch_gemv(job, pro, EPI_STORE, ea, static_cast<hipStream_t>(stream))) != NT_OK) return rc;
+    ea.y = Y;
+    return launch_gemv(job, pro, EPI_STORE, ea, st);
   }
-  return NT_OK;
+  if (!ws) return NT_EINVAL;
+  if (!aligned16(ws)) return NT_EALIGN;
+  if (ws_bytes < nt_gemm_q_small_workspace_bytes(M, rows, cols)) return NT_EWORKSPACE;
+  JobM job;
+  if ((rc = plan_job_m(job, 1, &Wp, &fmt, &r, (int)cols, 0, 0, M)) != NT_OK) return rc;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  void* stage = wsb;
+  void* part = wsb + up256(stage_m_bytes((int)cols));
+  if ((rc = launch_stage_m(X, cols, nullptr, 0.f, M, (int)cols, stage, st)) != NT_OK) return rc;
+  const ProArgs none{nullptr, nullptr, 0.f, 0, 0, 0.f, nullptr, 0};
+  EpiArgs ea{};
+  ea.y = Y;
+  ea.ld = rows;
+  return launch_gemm_m(job, stage, part, none, EPI_STORE, ea, st);
 }
 
 size_t nt_layer_workspace_bytes(const nt_layer_cfg* cfg, int M) {

@@ -1,0 +1,106 @@
+// Device helpers shared by the GEMV engine and the small-M GEMM: LDS
+// accessors on the dynamic LDS block, DPP reductions, non-temporal weight
+// loads and the GGUF Q4_K scale unpacking.
+#pragma once
+
+#include "nt_internal.h"
+
+extern __shared__ __attribute__((aligned(16))) uint8_t nt_smem[];
+
+namespace nt {
+namespace {
+
+constexpr float kXMax = 32639.0f;  // |X| bound of the 16-bit activation; keeps the high plane in [-127, 127]
+
+__device__ __forceinline__ uint32_t ld32(uint32_t off) { return *reinterpret_cast<const uint32_t*>(nt_smem + off); }
+__device__ __forceinline__ int ldi32(uint32_t off) { return *reinterpret_cast<const int*>(nt_smem + off); }
+__device__ __forceinline__ float ldf(uint32_t off) { return *reinterpret_cast<const float*>(nt_smem + off); }
+__device__ __forceinline__ uint32_t ld16(uint32_t off) { return *reinterpret_cast<const uint16_t*>(nt_smem + off); }
+__device__ __forceinline__ uint4 ld128(uint32_t off) { return *reinterpret_cast<const uint4*>(nt_smem + off); }
+__device__ __forceinline__ void st128(uint32_t off, uint4 v) { *reinterpret_cast<uint4*>(nt_smem + off) = v; }
+__device__ __forceinline__ void stf(uint32_t off, float v) { *reinterpret_cast<float*>(nt_smem + off) = v; }
+__device__ __forceinline__ void sti32(uint32_t off, int v) { *reinterpret_cast<int*>(nt_smem + off) = v; }
+
+__device__ __forceinline__ float h2f(uint32_t bits) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits); }
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// N dwords starting at an LDS byte offset that is only 2-byte aligned:
+// read N+1 aligned dwords and funnel-shift them.
+template <int N>
+__device__ __forceinline__ void ld_unaligned(uint32_t off, uint32_t (&out)[N]) {
+  const uint32_t base = off & ~3u, sh = off & 3u;
+  uint32_t w[N + 1];
+#pragma unroll
+  for (int i = 0; i <= N; ++i) w[i] = ld32(base + 4 * i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) out[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
+}
+
+// Sum over the 64 lanes of a wave: an inclusive scan with DPP row shifts and
+// row broadcasts leaves the total in lane 63, which is read into a scalar.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_shift(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_shift<0x111, 0xf>(v);  // row_shr:1 within rows of 16 lanes
+  v += dpp_shift<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_shift<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_shift<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_shift<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_shift<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Reductions over the lane groups that hold one 32-block (8 lanes) and one
+// 16-sum (4 lanes): DPP quad permutations and the half-row mirror.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float max8(float x) {
+  x = fmaxf(x, __builtin_bit_cast(float, dpp_i<0xB1>(__builtin_bit_cast(int, x))));  // quad_perm 1,0,3,2
+  x = fmaxf(x, __builtin_bit_cast(float, dpp_i<0x4E>(__builtin_bit_cast(int, x))));  // quad_perm 2,3,0,1
+  return fmaxf(x, __builtin_bit_cast(float, dpp_i<0x141>(__builtin_bit_cast(int, x))));  // row_half_mirror
+}
+__device__ __forceinline__ int sum4(int x) {
+  x += dpp_i<0xB1>(x);
+  return x + dpp_i<0x4E>(x);
+}
+
+// Q4_K: 6-bit scale and min of sub-block s from the 12 packed bytes
+// (bytes 0-3 in s0, 4-7 in s1, 8-11 in s2).  GGUF packing: for s < 4 the low
+// six bits of bytes s (scale) and s+4 (min); for s >= 4 the nibbles of byte
+// s+4 give the low four bits and the top two bits of bytes s-4 (scale) and
+// s (min) give the high two.
+__device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int s, int& sc, int& m) {
+  if (s < 4) {
+    sc = (s0 >> (8 * s)) & 63;
+    m = (s1 >> (8 * s)) & 63;
+  } else {
+    const int t = 8 * (s - 4);
+    const uint32_t b = s2 >> t;
+    sc = (b & 15) | (((s0 >> t) >> 6 & 3) << 4);
+    m = ((b >> 4) & 15) | (((s1 >> t) >> 6 & 3) << 4);
+  }
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) u32x4* gptr_u32x4;
+
+// One 16-byte chunk of weights.  Chunks are 16-byte aligned and contain at
+// least one byte of the matrix, so a chunk never crosses a page boundary and
+// is always mapped, even where it runs past the matrix's last byte (those
+// bytes are never used).  Weights are read once: the load is non-temporal.
+__device__ __forceinline__ uint4 load_chunk(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load((gptr_u32x4)(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+}  // namespace
+}  // namespace nt

@@ -1,0 +1,762 @@
+// nt_gemm.hip -- quantized small-M GEMM on int8 MFMA: Y[t][r] = sum_k W[r][k]
+// X[t][k] for t < M <= 8 tokens, the verify pass of self-speculative decoding
+// (p1 "Features": self-speculative decoding; p2 "Architecture et structure du
+// code": several draft tokens checked in one pass).  Weights are read once
+// for all M tokens.
+//
+//   staging   k_stage_m puts the M activation rows (optionally RMSNorm'ed)
+//             into the GEMV engine's 16-bit fixed point: per token and
+//             32-block a scale s and integers X = 256 hi + lo.  The int8
+//             planes are laid out as the B operand of v_mfma_i32_16x16x32_i8
+//             (column n = 2t + plane: hi, lo), 512 contiguous bytes per
+//             32-block, plus a record (s, s*sum X, s*sum X over each half) per
+//             block and token.
+//   product   One MFMA multiplies a 16-row x 32-weight tile of raw quants by
+//             every token and plane with exact int32 sums.  Adjacent columns
+//             are combined, S = 256 C_hi + C_lo (exact), and scaled:
+//             y += alpha_r * (s S) - beta_r * (s sum X), where alpha and beta
+//             are the row's scale and offset for that block in its format
+//             (Q6_K: per 16-weight half, two MFMAs with the other half zeroed).
+//   stream    A wave streams tile-slices (16 rows x 256 columns: 16 row
+//             pieces) HBM -> registers -> its LDS slab with non-temporal
+//             16-byte loads, two in flight, as the GEMV engine streams
+//             segments.  A unit (one tile over one column range) accumulates
+//             in registers; units are claimed from an LDS counter inside the
+//             workgroup's share of tiles and land in a (row, column range,
+//             token) table that the epilogue adds in order (deterministic).
+//   epilogue  Store, residual add, SwiGLU or RoPE + q store + f16 K/V append,
+//             per token (token t sits at position pos + t).
+//
+// MFMA operand layout (measured on gfx950): A[i][k] in lane i + 16*(k/8),
+// byte k%8; B[k][n] in lane n + 16*(k/8), byte k%8; C[i][n] in lane
+// n + 16*(i/4), element i%4.
+
+#include <algorithm>
+
+#include "nt_dev.h"
+
+namespace nt {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kStageThreads = 1024;
+
+// ------------------------------------------------------------------ staging
+// Token t = blockIdx.x.  Thread groups of 8 lanes hold one 32-block (4
+// elements each, coalesced as in the GEMV prologue).
+__global__ __launch_bounds__(kStageThreads) void k_stage_m(const float* __restrict__ src, int64_t stride,
+                                                           const float* __restrict__ gain, float eps, int cols,
+                                                           uint8_t* __restrict__ xb, float4* __restrict__ xs) {
+  __shared__ float red[kStageThreads / 64];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const float* x = src + (int64_t)t * stride;
+  float r = 1.0f;
+  if (gain) {
+    float ss = 0.f;
+    for (int e = 4 * tid; e < cols; e += 4 * kStageThreads) {
+      const float4 v = *reinterpret_cast<const float4*>(x + e);
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int w = 0; w < kStageThreads / 64; ++w) tot += red[w];
+    r = 1.0f / sqrtf(tot / (float)cols + eps);
+  }
+  for (int e = 4 * tid; e < cols; e += 4 * kStageThreads) {
+    float4 v = *reinterpret_cast<const float4*>(x + e);
+    if (gain) {
+      const float4 g = *reinterpret_cast<const float4*>(gain + e);
+      v = make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w);
+    }
+    v = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    amax = max8(amax);
+    const float inv = amax > 0.f ? kXMax / amax : 0.f;
+    const float f[4] = {v.x, v.y, v.z, v.w};
+    uint32_t H = 0, L = 0;
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      int X = __float2int_rn(f[k] * inv);
+      X = max(-32639, min(32639, X));
+      const int hi = (X + 128) >> 8;
+      const int lo = X - (hi << 8);
+      H |= (uint32_t)(hi & 255) << (8 * k);
+      L |= (uint32_t)(lo & 255) << (8 * k);
+      sum += X;
+    }
+    // elements k = 4g..4g+3 of block b (g = lane's place in its group):
+    // B-layout lane n + 16*(k/8), byte k%8, for n = 2t (hi) and 2t + 1 (lo)
+    const int b = e >> 5, g = (e >> 2) & 7;
+    uint8_t* blk = xb + 512 * (int64_t)b + 128 * (g >> 1) + 4 * (g & 1);
+    *reinterpret_cast<uint32_t*>(blk + 8 * (2 * t)) = H;
+    *reinterpret_cast<uint32_t*>(blk + 8 * (2 * t + 1)) = L;
+    const int s16 = sum4(sum);                            // lanes g<4: first half, g>=4: second half
+    const int other = dpp_i<0x141>(s16);                  // row_half_mirror: the other half's sum
+    if (g == 0) {
+      const float s = amax / kXMax;
+      xs[(int64_t)b * kMaxTokens + t] = make_float4(s, s * (float)(s16 + other), s * (float)s16, s * (float)other);
+    }
+  }
+}
+
+// --------------------------------------------------------------------- GEMM
+// Workgroup b's share: column range su = b / gps (tile-slices ts0 ..
+// ts0 + nts_r - 1, 32-blocks from gb0) and output tiles [t0, t0 + nt) of it;
+// nvt tiles to stream (2 nt with paired matrices); units u = sub * nvt + vt.
+struct ShareM {
+  int su, ts0, nts_r, gb0, nb;  // range, its tile-slices, first block and blocks
+  int t0, nt, nvt, nsub, nunits;
+  uint32_t magic;               // floor((2^32-1)/nvt)
+};
+
+__device__ __forceinline__ ShareM share_m(const JobM& job, int b) {
+  ShareM sh;
+  sh.su = b / job.gps;
+  const int g = b - sh.su * job.gps;
+  sh.ts0 = sh.su * job.tsper;
+  sh.nts_r = min(job.tsper, job.nts - sh.ts0);
+  sh.gb0 = 8 * sh.ts0;
+  sh.nb = min(8 * (sh.ts0 + sh.nts_r), job.cols / 32) - sh.gb0;
+  const bool big = g < job.wg_rem;
+  sh.t0 = g * job.wg_base + (big ? g : job.wg_rem);
+  sh.nt = job.wg_base + (big ? 1 : 0);
+  sh.nvt = job.paired ? 2 * sh.nt : sh.nt;
+  sh.nsub = (sh.nts_r + job.tsu - 1) / job.tsu;
+  sh.nunits = sh.nvt * sh.nsub;
+  sh.magic = job.magicV[big ? 1 : 0];
+  return sh;
+}
+
+// One tile-slice: 16 row pieces of one matrix, the unit it belongs to and
+// where it sits in that unit.  Wave-uniform (scalar registers).
+struct TSeg {
+  const uint8_t* base;  // first byte of row 0's piece
+  int64_t rb;
+  int fmt, P, piece;    // chunks per piece (worst alignment), bytes per piece
+  uint32_t magicP;
+  int nrow;             // rows of the tile inside the matrix (<= 16)
+  int nblk;             // 32-weight blocks in the tile-slice (<= 8)
+  int lb0;              // first 32-block of the tile-slice, counted from the range's first
+  int vt, sub;          // unit
+  int first, last;      // first / last tile-slice of its unit
+};
+
+__device__ __forceinline__ int unit_len(const JobM& job, const ShareM& sh, int sub) {
+  return min(job.tsu, sh.nts_r - sub * job.tsu);
+}
+
+__device__ __forceinline__ void unit_of(const ShareM& sh, int u, int& sub, int& vt) {
+  uint32_t q = __umulhi((uint32_t)u, sh.magic);
+  vt = u - (int)q * sh.nvt;
+  if (vt >= sh.nvt) {
+    ++q;
+    vt -= sh.nvt;
+  }
+  sub = (int)q;
+}
+
+__device__ __forceinline__ int matrix_of_tile(const JobM& job, int tile) {
+  if (job.paired) return 0;
+  return (job.nmat > 2 && tile >= job.tile_base[2]) ? 2 : ((job.nmat > 1 && tile >= job.tile_base[1]) ? 1 : 0);
+}
+
+__device__ __forceinline__ TSeg tseg_at(const JobM& job, const ShareM& sh, int u, int j) {
+  TSeg sg;
+  int sub, vt;
+  unit_of(sh, u, sub, vt);
+  sg.vt = vt;
+  sg.sub = sub;
+  sg.first = j == 0;
+  sg.last = j == unit_len(job, sh, sub) - 1;
+  const int lts = sub * job.tsu + j;  // tile-slice within the range
+  const int ts = sh.ts0 + lts;
+  int m, tile;
+  if (job.paired) {
+    const bool up = vt >= sh.nt;
+    m = up ? 1 : 0;
+    tile = sh.t0 + (up ? vt - sh.nt : vt);
+  } else {
+    tile = sh.t0 + vt;
+    m = matrix_of_tile(job, tile);
+  }
+  const int lt = tile - (job.paired ? 0 : (m == 2 ? job.tile_base[2] : (m == 1 ? job.tile_base[1] : 0)));
+  const uint8_t* W = m == 2 ? job.W[2] : (m == 1 ? job.W[1] : job.W[0]);
+  sg.rb = m == 2 ? job.rb[2] : (m == 1 ? job.rb[1] : job.rb[0]);
+  sg.fmt = m == 2 ? job.fmt[2] : (m == 1 ? job.fmt[1] : job.fmt[0]);
+  sg.P = m == 2 ? job.P[2] : (m == 1 ? job.P[1] : job.P[0]);
+  sg.magicP = m == 2 ? job.magicP[2] : (m == 1 ? job.magicP[1] : job.magicP[0]);
+  const int tsb = m == 2 ? job.tsb[2] : (m == 1 ? job.tsb[1] : job.tsb[0]);
+  const int rows = m == 2 ? job.rows[2] : (m == 1 ? job.rows[1] : job.rows[0]);
+  sg.nrow = min(kTileRows, rows - kTileRows * lt);
+  const bool kq = block_elems(sg.fmt) == 256;
+  sg.nblk = kq ? 8 : min(8, (job.cols - kTS * ts) >> 5);
+  sg.piece = kq ? tsb : sg.nblk * block_bytes(sg.fmt);
+  sg.lb0 = 8 * lts;
+  sg.base = W + (int64_t)(kTileRows * lt) * sg.rb + (int64_t)ts * tsb;
+  return sg;
+}
+
+// Stand-in when a wave has nothing left: one chunk at the start of W[0]
+// (loads are still issued, so every path issues the same number).
+__device__ __forceinline__ TSeg tseg_null(const JobM& job) {
+  TSeg sg{};
+  sg.base = job.W[0];
+  sg.rb = 0;
+  sg.fmt = job.fmt[0];
+  sg.P = 1;
+  sg.piece = 1;
+  sg.magicP = 65536;
+  sg.nrow = 1;
+  return sg;
+}
+
+// Chunk c of the tile-slice: row c / P, chunk c % P of that row's aligned
+// range.  Chunks a row's piece does not reach (its alignment is better than
+// the worst case) and chunks past 16 P re-read the row's or row 0's first
+// chunk, so every chunk read holds a byte of the matrix.
+template <int LPL>
+__device__ __forceinline__ void tseg_load(const TSeg& sg, int lane, uint4 (&pre)[LPL]) {
+#pragma unroll
+  for (int i = 0; i < LPL; ++i) {
+    const int c = lane + 64 * i;
+    int r = (int)(((uint32_t)c * sg.magicP) >> 16);
+    int k = c - r * sg.P;
+    if (r >= kTileRows) {
+      r = 0;
+      k = 0;
+    }
+    const uint8_t* p = sg.base + (int64_t)min(r, sg.nrow - 1) * sg.rb;
+    const uint32_t d = (uint32_t)(reinterpret_cast<uintptr_t>(p) & 15);
+    if (16 * k >= (int)d + sg.piece) k = 0;
+    pre[i] = load_chunk(reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(p) & ~uintptr_t(15)) + 16 * k);
+  }
+}
+
+template <int LPL>
+__device__ __forceinline__ void tseg_store(uint32_t slab, int lane, const uint4 (&pre)[LPL]) {
+#pragma unroll
+  for (int i = 0; i < LPL; ++i) st128(slab + 16u * (lane + 64 * i), pre[i]);
+}
+
+// LDS offset of row r's piece data in the slab (rows past the tile re-read
+// the last row: their results are never stored).
+__device__ __forceinline__ uint32_t piece_off(const TSeg& sg, uint32_t slab, int r) {
+  const int rr = min(r, sg.nrow - 1);
+  const uint32_t d = (uint32_t)(reinterpret_cast<uintptr_t>(sg.base + (int64_t)rr * sg.rb) & 15);
+  return slab + 16u * (uint32_t)(sg.P * r) + d;
+}
+
+__device__ __forceinline__ long pack2(uint32_t lo, uint32_t hi) { return (long)(((uint64_t)hi << 32) | lo); }
+
+// Scale table of the tile-slice, per (entry, row): entry = 32-block (Q6_K:
+// 16-weight group).  A block's contribution is alpha (s S) - beta (s sum X)
+// with beta = 0 (Q8_0), 8 alpha (Q4_0), 32 alpha (Q6_K); Q4_K keeps
+// (alpha, beta) pairs.  Layout: scl + 4 * (16 entry + row), pairs 8 * (...).
+__device__ __forceinline__ void scale_table(const TSeg& sg, uint32_t po, uint32_t scl, int lane) {
+  const int row = lane & 15, kq = lane >> 4;
+  switch (sg.fmt) {
+    case NT_Q8_0:
+    case NT_Q4_0: {
+      const uint32_t bb = sg.fmt == NT_Q8_0 ? 34u : 18u;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int e = kq + 4 * q;
+        const float a = e < sg.nblk ? h2f(ld16(po + bb * e)) : 0.f;
+        stf(scl + 4u * (uint32_t)(16 * e + row), a);
+      }
+      break;
+    }
+    case NT_Q4_K: {
+      uint32_t h[3];
+      ld_unaligned<3>(po + 4, h);
+      const float d = h2f(ld16(po)), dmin = h2f(ld16(po + 2));
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int e = kq + 4 * q;
+        int sc, m;
+        q4k_scale_min(h[0], h[1], h[2], e, sc, m);
+        *reinterpret_cast<float2*>(nt_smem + scl + 8u * (uint32_t)(16 * e + row)) =
+            make_float2(d * (float)sc, dmin * (float)m);
+      }
+      break;
+    }
+    default: {  // Q6_K: 16 scales of 16 weights
+      const float d = h2f(ld16(po + 208));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = kq + 4 * q;
+        const int sc = (int)(int8_t)nt_smem[po + 192 + e];
+        stf(scl + 4u * (uint32_t)(16 * e + row), d * (float)sc);
+      }
+      break;
+    }
+  }
+}
+
+// A operand: 8 quants (one byte each) of row lane%16, weights 8*(lane/16)..+7
+// of block kb of the tile-slice.
+__device__ __forceinline__ long a_operand(const TSeg& sg, uint32_t po, int kb, int kq) {
+  uint32_t v[2];
+  switch (sg.fmt) {
+    case NT_Q8_0:
+      ld_unaligned<2>(po + 34u * kb + 2 + 8 * kq, v);
+      return pack2(v[0], v[1]);
+    case NT_Q4_0: {
+      ld_unaligned<2>(po + 18u * kb + 2 + 8 * (kq & 1), v);
+      const int sh = 4 * (kq >> 1);
+      return pack2((v[0] >> sh) & 0x0F0F0F0Fu, (v[1] >> sh) & 0x0F0F0F0Fu);
+    }
+    case NT_Q4_K: {
+      ld_unaligned<2>(po + 16 + 32 * (kb >> 1) + 8 * kq, v);
+      const int sh = 4 * (kb & 1);
+      return pack2((v[0] >> sh) & 0x0F0F0F0Fu, (v[1] >> sh) & 0x0F0F0F0Fu);
+    }
+    default: {  // Q6_K: elements 32 kb + 8 kq .. +7: half n, quarter q'
+      const int n = kb >> 2, qq = kb & 3;
+      uint32_t h[2];
+      ld_unaligned<2>(po + 64 * n + 32 * (qq & 1) + 8 * kq, v);
+      ld_unaligned<2>(po + 128 + 32 * n + 8 * kq, h);
+      const int sl = 4 * (qq >> 1), shh = 2 * qq;
+      const uint32_t a0 = ((v[0] >> sl) & 0x0F0F0F0Fu) | (((h[0] >> shh) & 0x03030303u) << 4);
+      const uint32_t a1 = ((v[1] >> sl) & 0x0F0F0F0Fu) | (((h[1] >> shh) & 0x03030303u) << 4);
+      return pack2(a0, a1);
+    }
+  }
+}
+
+// Combine the hi (even column) and lo (odd column) sums of each token and add
+// alpha_j (s S) - beta_j sx for C rows j = 0..3.
+__device__ __forceinline__ void accumulate(v4i c, const float (&al)[4], const float (&be)[4], float s, float sx,
+                                           float (&acc)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int lo = dpp_i<0xB1>(c[j]);  // quad_perm 1,0,3,2: the odd neighbour's (lo plane) sum
+    const float S = (float)((c[j] << 8) + lo);
+    acc[j] += al[j] * (s * S) - be[j] * sx;
+  }
+}
+
+__device__ __forceinline__ void alphas(uint32_t scl, int e, int kq, float (&al)[4]) {
+  const float4 a = *reinterpret_cast<const float4*>(nt_smem + scl + 4u * (uint32_t)(16 * e + 4 * kq));
+  al[0] = a.x; al[1] = a.y; al[2] = a.z; al[3] = a.w;
+}
+
+__device__ __forceinline__ void tseg_compute(const JobM& job, const TSeg& sg, uint32_t slab, uint32_t scl, int lane,
+                                             float (&acc)[4]) {
+  const int kq = lane >> 4, t = (lane & 15) >> 1;
+  const uint32_t po = piece_off(sg, slab, lane & 15);
+  scale_table(sg, po, scl, lane);
+  if (sg.first) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = 0.f;
+  }
+  const v4i zero = {0, 0, 0, 0};
+  for (int kb = 0; kb < sg.nblk; ++kb) {
+    const int lb = sg.lb0 + kb;
+    const long a = a_operand(sg, po, kb, kq);
+    const long bo = *reinterpret_cast<const long*>(nt_smem + job.xbl + 512u * (uint32_t)lb + 8u * lane);
+    const uint32_t rec = job.xsl + 16u * (uint32_t)(lb * kMaxTokens + t);
+    float al[4], be[4];
+    if (sg.fmt == NT_Q6_K) {
+      const float4 r = *reinterpret_cast<const float4*>(nt_smem + rec);
+      const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? a : 0l, bo, zero, 0, 0, 0);
+      const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? 0l : a, bo, zero, 0, 0, 0);
+      alphas(scl, 2 * kb, kq, al);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) be[j] = 32.f * al[j];
+      accumulate(c0, al, be, r.x, r.z, acc);
+      alphas(scl, 2 * kb + 1, kq, al);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) be[j] = 32.f * al[j];
+      accumulate(c1, al, be, r.x, r.w, acc);
+    } else {
+      const float2 r = *reinterpret_cast<const float2*>(nt_smem + rec);
+      const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bo, zero, 0, 0, 0);
+      if (sg.fmt == NT_Q4_K) {
+        const uint32_t e = scl + 8u * (uint32_t)(16 * kb + 4 * kq);
+        const float4 p0 = *reinterpret_cast<const float4*>(nt_smem + e);
+        const float4 p1 = *reinterpret_cast<const float4*>(nt_smem + e + 16);
+        al[0] = p0.x; be[0] = p0.y; al[1] = p0.z; be[1] = p0.w;
+        al[2] = p1.x; be[2] = p1.y; al[3] = p1.z; be[3] = p1.w;
+      } else {
+        alphas(scl, kb, kq, al);
+        const float f = sg.fmt == NT_Q4_0 ? 8.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) be[j] = f * al[j];
+      }
+      accumulate(c, al, be, r.x, r.y, acc);
+    }
+  }
+  if (sg.last && (lane & 1) == 0 && t < job.M) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = kTileRows * sg.vt + 4 * kq + j;
+      stf(job.acc + 4u * (uint32_t)((v * job.nsub + sg.sub) * job.M + t), acc[j]);
+    }
+  }
+}
+
+// Cursor over a wave's units: the first two are static (wave w: units w and
+// w + nwaves), later ones are claimed from the LDS counter.
+struct UCur {
+  int u, j, len;
+  bool second_used, done;
+};
+
+__device__ __forceinline__ int claim_m(const JobM& job, int lane) {
+  int old = 0;
+  int* ctr = static_cast<int*>(__builtin_assume_aligned(nt_smem + job.ctl, 16));
+  if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return 2 * job.nwaves + __builtin_amdgcn_readfirstlane(old);
+}
+
+__device__ __forceinline__ void ucur_set(const JobM& job, const ShareM& sh, UCur& c, int u) {
+  c.u = u;
+  c.j = 0;
+  c.done = u >= sh.nunits;
+  if (!c.done) {
+    int sub, vt;
+    unit_of(sh, u, sub, vt);
+    c.len = unit_len(job, sh, sub);
+  }
+}
+
+// Advance to the next tile-slice; before the LDS counter is initialised
+// (may_claim false) only the static second unit can be taken, and a claim
+// is left pending (u = -1).
+__device__ __forceinline__ void ucur_next(const JobM& job, const ShareM& sh, UCur& c, int wave, int lane,
+                                          bool may_claim) {
+  if (c.done) return;
+  if (++c.j < c.len) return;
+  if (!c.second_used) {
+    c.second_used = true;
+    ucur_set(job, sh, c, wave + job.nwaves);
+    return;  // when that unit does not exist, no later unit does
+  }
+  if (!may_claim) {
+    c.u = -1;
+    return;
+  }
+  ucur_set(job, sh, c, claim_m(job, lane));
+}
+
+// One step: store the tile-slice in `pre`, issue the next one's loads into
+// `pre`, compute the stored one.  A step with nothing to compute only issues
+// stand-in loads: the loop has a single exit (see the GEMV engine).
+template <int LPL>
+__device__ __forceinline__ void stream_m(const JobM& job, const ShareM& sh, int wave, int lane, uint32_t slab,
+                                         uint32_t scl, UCur& ah, float (&acc)[4], uint4 (&pre)[LPL], TSeg& sg,
+                                         bool& cur_valid, bool& nxt_valid) {
+  const TSeg cur = sg;
+  const bool valid = cur_valid;
+  tseg_store(slab, lane, pre);
+  if (!ah.done && ah.u < 0) ucur_set(job, sh, ah, claim_m(job, lane));  // claim left pending before the barrier
+  const bool issue = !ah.done;
+  sg = issue ? tseg_at(job, sh, ah.u, ah.j) : tseg_null(job);
+  tseg_load(sg, lane, pre);
+  if (issue) ucur_next(job, sh, ah, wave, lane, true);
+  if (valid) tseg_compute(job, cur, slab, scl, lane, acc);
+  cur_valid = nxt_valid;
+  nxt_valid = issue;
+}
+
+// Output row of share row v (tile v/16 of the share, row v%16; up rows of a
+// paired launch are offset by orows), or -1 past the matrix.
+__device__ __forceinline__ int64_t part_row(const JobM& job, const ShareM& sh, int v) {
+  int vt = v / kTileRows, up = 0;
+  if (job.paired && vt >= sh.nt) {
+    vt -= sh.nt;
+    up = 1;
+  }
+  const int tile = sh.t0 + vt;
+  const int m = matrix_of_tile(job, tile);
+  const int lr = kTileRows * (tile - (job.paired ? 0 : job.tile_base[m])) + v % kTileRows;
+  if (lr >= job.rows[m]) return -1;
+  return (int64_t)up * job.orows + job.row_base[m] + lr;
+}
+
+template <int LPL>
+__global__ __launch_bounds__(kMaxThreads) void k_qgemm_m(JobM job) {
+  const int tid = threadIdx.x, lane = tid & 63, NT = job.nwaves * 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const ShareM sh = share_m(job, blockIdx.x);
+  const uint32_t slab = job.slab + (uint32_t)wave * (uint32_t)(LPL * 1024);
+  const uint32_t scl = job.scl + (uint32_t)wave * 1024u;
+  if (tid == 0) sti32(job.ctl, 0);
+  // the range's staged activation (B operands, then records), loaded before
+  // any weight so waiting for it does not wait for the weights
+  const int cb = 32 * sh.nb, cr = 8 * sh.nb;  // 16-byte chunks
+  uint4 xa[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int c = tid + NT * i;
+    if (c < cb) xa[i] = *reinterpret_cast<const uint4*>(job.xb + 512 * (int64_t)sh.gb0 + 16 * c);
+    else if (c < cb + cr)
+      xa[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(job.xs) + 128 * (int64_t)sh.gb0 +
+                                              16 * (c - cb));
+  }
+  // two tile-slices in flight before the barrier (static units only)
+  UCur ah{};
+  ah.second_used = false;
+  ucur_set(job, sh, ah, wave);
+  uint4 pa[LPL], pb[LPL];
+  TSeg sa, sb;
+  const bool va = !ah.done;
+  sa = va ? tseg_at(job, sh, ah.u, ah.j) : tseg_null(job);
+  tseg_load(sa, lane, pa);
+  if (va) ucur_next(job, sh, ah, wave, lane, false);
+  const bool vb = !ah.done && ah.u >= 0;
+  sb = vb ? tseg_at(job, sh, ah.u, ah.j) : tseg_null(job);
+  tseg_load(sb, lane, pb);
+  if (vb) ucur_next(job, sh, ah, wave, lane, false);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int c = tid + NT * i;
+    if (c < cb) st128(job.xbl + 16u * c, xa[i]);
+    else if (c < cb + cr) st128(job.xsl + 16u * (c - cb), xa[i]);
+  }
+  __syncthreads();
+  if (va) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    bool cur_valid = va, nxt_valid = vb;
+    do {
+      stream_m<LPL>(job, sh, wave, lane, slab, scl, ah, acc, pa, sa, cur_valid, nxt_valid);
+      stream_m<LPL>(job, sh, wave, lane, slab, scl, ah, acc, pb, sb, cur_valid, nxt_valid);
+    } while (cur_valid);
+  }
+  __syncthreads();
+  // this range's partial sums of the share's rows: part[su][t][row], rows
+  // fastest (coalesced), sub-ranges added in order
+  const int nv = sh.nvt * kTileRows, M = job.M;
+  for (int i = tid; i < nv * M; i += NT) {
+    const int t = i / nv, v = i - t * nv;
+    const int64_t R = part_row(job, sh, v);
+    if (R < 0) continue;
+    float s = 0.f;
+    for (int sub = 0; sub < sh.nsub; ++sub) s += ldf(job.acc + 4u * (uint32_t)((v * job.nsub + sub) * M + t));
+    job.part[((int64_t)sh.su * M + t) * job.ldp + R] = s;
+  }
+}
+
+// ------------------------------------------------------------ reduce + epilogue
+// Adds the column ranges' partial sums in order and applies the epilogue for
+// (token, row) = thread (row pairs for EPI_QKV).
+template <int EPI>
+__global__ __launch_bounds__(256) void k_reduce_m(const float* __restrict__ part, int nsup, int M, int64_t ldp,
+                                                  int orows, ProArgs pro, EpiArgs ea) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  auto total = [&](int t, int64_t R) {
+    float s = 0.f;
+    for (int su = 0; su < nsup; ++su) s += part[((int64_t)su * M + t) * ldp + R];
+    return s;
+  };
+  if constexpr (EPI == EPI_QKV) {
+    const int npr = orows / 2;
+    if (i >= (int64_t)npr * M) return;
+    const int t = (int)(i / npr), R = 2 * (int)(i - (int64_t)t * npr);
+    const int pos = *ea.pos + t;
+    const bool pos_ok = *ea.pos >= 0 && pos < ea.max_ctx;
+    if (!pos_ok && ea.err) *ea.err = 1;
+    float a = total(t, R), b = total(t, R + 1);
+    const int dd = R % ea.head_dim;
+    if (R < ea.q_rows + ea.kv_rows) {
+      // RoPE: the pair turns by pos * theta^(-dd/head_dim), the angle in double
+      const double freq = exp2(-(double)dd / (double)pro.rope_hd * log2((double)pro.rope_theta));
+      const double ang = (double)pos * freq;
+      const float c = (float)cos(ang), s = (float)sin(ang);
+      const float a2 = a * c - b * s, b2 = a * s + b * c;
+      a = a2;
+      b = b2;
+    }
+    if (R < ea.q_rows) {
+      ea.q_out[t * ea.ld + R] = a;
+      ea.q_out[t * ea.ld + R + 1] = b;
+    } else if (pos_ok) {
+      const bool is_k = R < ea.q_rows + ea.kv_rows;
+      const int rr = R - ea.q_rows - (is_k ? 0 : ea.kv_rows);
+      const int kh = rr / ea.head_dim;
+      uint16_t* cache = is_k ? ea.k_cache : ea.v_cache;
+      const int64_t off = ((int64_t)kh * ea.max_ctx + pos) * ea.head_dim + dd;
+      const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+      cache[off] = __builtin_bit_cast(uint16_t, ha);
+      cache[off + 1] = __builtin_bit_cast(uint16_t, hb);
+    }
+  } else {
+    if (i >= (int64_t)orows * M) return;
+    const int t = (int)(i / orows), R = (int)(i - (int64_t)t * orows);
+    if constexpr (EPI == EPI_SWIGLU) {
+      ea.y[t * ea.ld + R] = silu(total(t, R)) * total(t, (int64_t)orows + R);
+    } else if constexpr (EPI == EPI_RESID) {
+      ea.y[t * ea.ld + R] += total(t, R);
+    } else {
+      ea.y[t * ea.ld + R] = total(t, R);
+    }
+  }
+}
+
+int gemm_cus() {
+  int dev = 0, v = 0;
+  (void)hipGetDevice(&dev);
+  (void)hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+  return v > 0 ? v : 256;
+}
+
+template <int LPL>
+int launch_m_lpl(const JobM& job, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)k_qgemm_m<LPL>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
+        hipSuccess)
+      return NT_EHIP;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((k_qgemm_m<LPL>), dim3(job.grid), dim3(64 * job.nwaves), job.lds_bytes, stream, job);
+  return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
+}
+
+template <int EPI>
+int launch_reduce(const JobM& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t stream) {
+  const int64_t n = (int64_t)(EPI == EPI_QKV ? job.orows / 2 : job.orows) * job.M;
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks <= 0) return NT_OK;
+  hipLaunchKernelGGL(k_reduce_m<EPI>, dim3((unsigned)blocks), dim3(256), 0, stream, job.part, job.nsup, job.M, job.ldp,
+                     job.orows, pro, ea);
+  return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
+}
+
+}  // namespace
+
+size_t stage_m_bytes(int cols) {
+  const size_t nb = (size_t)(cols + 31) / 32;
+  return nb * 512 + nb * kMaxTokens * 16;
+}
+
+// Column ranges of a launch: as few as the per-workgroup LDS allows.
+static void ranges_m(int cols, int& nts, int& tsper, int& nsup) {
+  nts = (cols + kTS - 1) / kTS;
+  nsup = (nts + kMaxTsPer - 1) / kMaxTsPer;
+  tsper = (nts + nsup - 1) / nsup;
+  nsup = (nts + tsper - 1) / tsper;
+}
+
+size_t part_m_bytes(int64_t orows, int paired, int cols, int M) {
+  int nts, tsper, nsup;
+  ranges_m(cols, nts, tsper, nsup);
+  return (size_t)nsup * (size_t)M * (size_t)(paired ? 2 : 1) * (size_t)orows * 4;
+}
+
+int launch_stage_m(const float* src, int64_t stride, const float* gain, float eps, int M, int cols, void* stage,
+                   hipStream_t stream) {
+  if (M < 1 || M > kMaxTokens || cols <= 0 || cols % 32) return NT_EINVAL;
+  uint8_t* xb = static_cast<uint8_t*>(stage);
+  float4* xs = reinterpret_cast<float4*>(xb + (size_t)(cols / 32) * 512);
+  hipLaunchKernelGGL(k_stage_m, dim3(M), dim3(kStageThreads), 0, stream, src, stride, gain, eps, cols, xb, xs);
+  return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
+}
+
+// Geometry: tiles per matrix, column ranges, workgroups per range (about
+// one workgroup per CU overall, enough that a share's table fits kAccM),
+// units of about four per wave, chunks per row piece, the LDS layout.
+int plan_job_m(JobM& job, int nmat, const uint8_t* const* W, const int* fmt, const int* rows, int cols, int paired,
+               int pairs, int M) {
+  if (nmat < 1 || nmat > kMaxMats || (paired && nmat != 2)) return NT_EINVAL;
+  if (M < 1 || M > kMaxTokens) return NT_EINVAL;
+  if (cols <= 0 || cols > kMaxCols) return NT_EUNSUPPORTED;
+  job = JobM{};
+  job.nmat = nmat;
+  job.paired = paired;
+  job.pairs = pairs;
+  job.cols = cols;
+  job.M = M;
+  int64_t otiles = 0, orows = 0;
+  int lpl = 3;
+  for (int m = 0; m < nmat; ++m) {
+    const int qk = block_elems(fmt[m]);
+    if (qk == 0 || cols % qk != 0 || rows[m] < 0) return NT_EINVAL;
+    if (pairs && (rows[m] & 1)) return NT_EINVAL;
+    if (paired && rows[m] != rows[0]) return NT_EINVAL;
+    job.W[m] = W[m];
+    job.fmt[m] = fmt[m];
+    job.rows[m] = rows[m];
+    job.rb[m] = (int64_t)(cols / qk) * block_bytes(fmt[m]);
+    job.row_base[m] = paired ? 0 : (int)orows;
+    job.tile_base[m] = paired ? 0 : (int)otiles;
+    job.tsb[m] = (kTS / qk) * block_bytes(fmt[m]);
+    job.P[m] = (job.tsb[m] + 15 + 15) / 16;
+    job.magicP[m] = (65536u + (uint32_t)job.P[m] - 1) / (uint32_t)job.P[m];
+    lpl = std::max(lpl, (kTileRows * job.P[m] + 63) / 64);
+    if (!paired || m == 0) {
+      orows += rows[m];
+      otiles += (rows[m] + kTileRows - 1) / kTileRows;
+    }
+  }
+  job.tile_base[nmat] = (int)otiles;
+  if (lpl > kSlabLoads) return NT_EUNSUPPORTED;
+  if (orows > INT32_MAX / 16) return NT_EUNSUPPORTED;
+  job.lpl = lpl;
+  job.orows = (int)orows;
+  job.otiles = (int)otiles;
+  const int vper = paired ? 2 : 1;
+  job.ldp = (int64_t)vper * orows;
+  ranges_m(cols, job.nts, job.tsper, job.nsup);
+  job.nwaves = kMaxWaves;
+  const int cus = gemm_cus();
+  // workgroups per range, then units per tile so a workgroup has ~4 per wave
+  int64_t gps = std::max<int64_t>(1, std::min<int64_t>(otiles, cus / job.nsup));
+  const int64_t tiles_cap = kAccM / ((int64_t)kTileRows * vper * M);  // tiles a share's table holds with nsub = 1
+  if (tiles_cap < 1) return NT_EUNSUPPORTED;
+  gps = std::max<int64_t>(gps, (otiles + tiles_cap - 1) / tiles_cap);
+  const int64_t nt_max = (otiles + gps - 1) / gps;
+  const int64_t nvt = nt_max * vper;
+  int64_t nsub = std::max<int64_t>(1, std::min<int64_t>(job.tsper, (4 * job.nwaves + nvt - 1) / nvt));
+  while (nsub > 1 && nvt * kTileRows * nsub * M > kAccM) --nsub;
+  job.tsu = (int)((job.tsper + nsub - 1) / nsub);
+  job.nsub = (job.tsper + job.tsu - 1) / job.tsu;
+  job.gps = (int)gps;
+  job.grid = (int)(gps * job.nsup);
+  job.wg_base = (int)(otiles / gps);
+  job.wg_rem = (int)(otiles % gps);
+  for (int i = 0; i < 2; ++i) {
+    const int64_t n = (int64_t)(job.wg_base + i) * vper;
+    job.magicV[i] = n > 0 ? (uint32_t)(0xffffffffull / (uint64_t)n) : 0u;
+  }
+  uint32_t off = 0;
+  job.ctl = off; off += 16;
+  job.xbl = off; off += (uint32_t)(8 * job.tsper * 512);
+  job.xsl = off; off += (uint32_t)(8 * job.tsper * kMaxTokens * 16);
+  job.acc = off; off += (uint32_t)(nvt * kTileRows * job.nsub * M * 4);
+  off = (off + 15) & ~15u;
+  job.scl = off; off += (uint32_t)job.nwaves * 1024u;  // per wave: 16 entries x 16 rows x alpha (Q4_K: 8 x 16 x pairs)
+  job.slab = off; off += (uint32_t)(job.nwaves * job.lpl * 1024);
+  job.lds_bytes = off;
+  if (job.lds_bytes > 160 * 1024) return NT_EUNSUPPORTED;
+  return NT_OK;
+}
+
+int launch_gemm_m(JobM& job, const void* stage, void* part, const ProArgs& pro, int epi, const EpiArgs& ea,
+                  hipStream_t stream) {
+  if (job.otiles <= 0) return NT_OK;
+  job.xb = static_cast<const uint8_t*>(stage);
+  job.xs = reinterpret_cast<const float4*>(job.xb + (size_t)(job.cols / 32) * 512);
+  job.part = static_cast<float*>(part);
+  int rc = NT_EUNSUPPORTED;
+  switch (job.lpl) {
+    case 3: rc = launch_m_lpl<3>(job, stream); break;
+    case 4: rc = launch_m_lpl<4>(job, stream); break;
+    case 5: rc = launch_m_lpl<5>(job, stream); break;
+  }
+  if (rc != NT_OK) return rc;
+  switch (epi) {
+    case EPI_STORE: return launch_reduce<EPI_STORE>(job, pro, ea, stream);
+    case EPI_RESID: return launch_reduce<EPI_RESID>(job, pro, ea, stream);
+    case EPI_QKV: return launch_reduce<EPI_QKV>(job, pro, ea, stream);
+    case EPI_SWIGLU: return launch_reduce<EPI_SWIGLU>(job, pro, ea, stream);
+  }
+  return NT_EINVAL;
+}
+
+}  // namespace nt

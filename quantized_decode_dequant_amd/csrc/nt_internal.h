@@ -97,6 +97,7 @@ enum Epi : int {
 
 struct EpiArgs {
   float* y;            // EPI_STORE / EPI_RESID / EPI_SWIGLU output
+  int64_t ld;          // small-M GEMM: distance between the tokens' rows of y (or q_out)
   // EPI_QKV
   float* q_out;        // fp32 [n_head*head_dim]
   uint16_t* k_cache;
@@ -117,6 +118,63 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
 
 // Launch the engine (prologue: optional RMSNorm; epilogue: epi).
 int launch_gemv(const Job& job, const ProArgs& pro, int epi, const EpiArgs& ea, hipStream_t stream);
+
+// ---- small-M GEMM on int8 MFMA (nt_gemm.hip)
+constexpr int kMaxTokens = 8;     // tokens of one small-M pass
+constexpr int kTS = 256;          // columns per tile-slice (one K-quant superblock)
+constexpr int kTileRows = 16;     // weight rows per MFMA tile
+constexpr int kMaxTsPer = 8;      // tile-slices per column range (its staged activation is 40 KB of LDS)
+constexpr int kAccM = 8192;       // per-workgroup (row, sub-range, token) table, in floats
+
+// How one small-M launch walks its matrices.  Rows are cut into 16-row tiles
+// (tiles of W[0], W[1], W[2] one after the other; with `paired`, W[0]'s tiles
+// each with the same tile of W[1]) and columns into `nsup` ranges of `tsper`
+// tile-slices.  Workgroup b works on range b / gps and a share of the tiles;
+// it stages that range's activation in LDS and its waves claim units (one
+// tile over `tsu` tile-slices) from an LDS counter.  Each workgroup writes
+// per-range partial sums; a reduce launch adds the ranges and applies the
+// epilogue.
+struct JobM {
+  const uint8_t* W[kMaxMats];
+  int64_t rb[kMaxMats];       // bytes per row
+  int fmt[kMaxMats];
+  int rows[kMaxMats];
+  int row_base[kMaxMats];     // first output row of each matrix (concatenated outputs)
+  int tile_base[kMaxMats + 1];  // first tile of each matrix (paired: W[0] only)
+  int tsb[kMaxMats];          // bytes of a full tile-slice row piece
+  int P[kMaxMats];            // 16-B chunks per row piece (worst alignment)
+  uint32_t magicP[kMaxMats];  // ceil(65536 / P): chunk -> row by a multiply
+  int nmat, paired, pairs, cols, M;
+  int orows;                  // output rows (paired: of each matrix)
+  int nts;                    // tile-slices per row
+  int tsper, nsup;            // tile-slices per column range, column ranges
+  int tsu, nsub;              // tile-slices per unit, units per tile in a range
+  int otiles;                 // output tiles
+  int gps;                    // workgroups per column range
+  int wg_base, wg_rem;        // tiles per workgroup of a range: wg_base (+1 if g < wg_rem)
+  uint32_t magicV[2];         // floor((2^32-1)/nvt) for the two tile counts of a workgroup
+  int nwaves, grid, lpl;
+  const uint8_t* xb;          // staged activation in MFMA B layout [cols/32][64 lanes][8 B]
+  const float4* xs;           // [cols/32][8 tokens]: s, s*sum(X), s*sum(X first 16), s*sum(X last 16)
+  float* part;                // partial sums [nsup][M][ldp]
+  int64_t ldp;                // (paired ? 2 : 1) * orows
+  uint32_t xbl, xsl, slab, scl, acc, ctl, lds_bytes;
+};
+
+int plan_job_m(JobM& job, int nmat, const uint8_t* const* W, const int* fmt, const int* rows, int cols, int paired,
+               int pairs, int M);
+size_t stage_m_bytes(int cols);          // bytes of the staged activation (B layout + records)
+// Bytes of the partial sums of a launch over `orows` output rows (paired: of
+// each matrix) and `cols` columns; independent of the device.
+size_t part_m_bytes(int64_t orows, int paired, int cols, int M);
+// Stage M activation rows (optionally RMSNorm'ed) into `stage` (stage_m_bytes(cols) bytes).
+int launch_stage_m(const float* src, int64_t stride, const float* gain, float eps, int M, int cols, void* stage,
+                   hipStream_t stream);
+// The GEMM over a staged activation into `part` (part_m_bytes), then the
+// reduce and epilogue; `pro` supplies only the RoPE fields (rope_hd,
+// rope_theta, pos) for EPI_QKV.
+int launch_gemm_m(JobM& job, const void* stage, void* part, const ProArgs& pro, int epi, const EpiArgs& ea,
+                  hipStream_t stream);
 
 // Launch tracing (nt_trace.hip): wraps one launch of `kind` in events when
 // tracing that kind.
