@@ -12,6 +12,18 @@ Prints one JSON line.  `value` is decode tokens/s with every input resident
 in HBM; `roofline` is the dominant kernel (the fused gate/up + SwiGLU GEMV)
 timed with HIP events on its launch stream inside the timed region;
 `cpu_baseline` is the fp64 oracle timed on this host on a bounded sample.
+
+Secondary workloads (`--workload`, one JSON line each; not the headline):
+  gemv     the single Q8_0 4096x4096 GEMV and the seven 70B-shaped Q4_K_M
+           projections, each rotated over distinct weight copies (more than
+           the 256 MB last-level cache): effective GB/s per GEMV.
+  layer8b  one 8B-shaped Q4_0 decoder layer at position 512, over 32 distinct
+           layers: GB/s per layer.
+  verify   80 Q6_K 70B-shaped layers, 36 resident and 44 streamed from
+           pinned host memory through two HBM staging buffers, verify passes
+           of M = 1, 2, 4, 8 tokens from context 4096: verified positions/s,
+           host-to-device GB/s against a copy-only run, and the overlap of
+           copies with compute against an all-resident run.
 """
 from __future__ import annotations
 
@@ -173,6 +185,168 @@ def summarize_profile(d: str) -> None:
             print(f"{k:70s} " + "  ".join(f"{n}={sum(v) / len(v):.6g} (n={len(v)})" for n, v in sorted(cs.items())))
 
 
+def timed(fn, n: int) -> float:
+    """Mean milliseconds of fn() over n calls on the current stream (after one warm call)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def workload_gemv(dev) -> dict:
+    """Configs 1 and 3: effective GB/s of each GEMV, weights rotated over
+    distinct copies so no launch finds them in the last-level cache."""
+    import torch
+
+    import quantized_decode_dequant_amd as nt
+    import synth
+    from synth import workloads as wl
+
+    read_gbs = read_ceiling(dev)
+    res = {}
+    cases = [("q8_0_4096x4096", wl.Q8_0, 4096, 4096, wl.W_GEMV_Q8, 0)]
+    for n in ["wq", "wk", "wv", "wo", "wg", "wu", "wd"]:
+        r, c = wl.LLAMA70B.mat_shape(n)
+        cases.append((f"70b_{n}_{synth.FMT_NAMES[wl.Q4_K_M[n]]}_{r}x{c}", wl.Q4_K_M[n], r, c, wl.W_GEMV_70B,
+                      wl.MAT_TAG[n]))
+    layer_bytes, layer_ms = 0, 0.0
+    for name, fmt, rows, cols, wid, tag in cases:
+        wbytes = rows * nt.row_bytes(fmt, cols)
+        ncopy = 32 if name.startswith("q8_0") else max(2, -(-512_000_000 // wbytes))
+        base = torch.from_numpy(wl.gen_matrix(fmt, rows, cols, wid, 0, tag)).to(dev)
+        Ws = [base.clone() for _ in range(ncopy)]
+        x = torch.from_numpy(wl.gen_x(cols, wid)).to(dev)
+        y = torch.empty(rows, dtype=torch.float32, device=dev)
+        it = [0]
+
+        def one():
+            nt.gemv_q(fmt, Ws[it[0] % ncopy], x, y, rows, cols)
+            it[0] += 1
+
+        ms = timed(one, max(100, 2 * ncopy))
+        alg = wbytes + 4 * cols + 4 * rows
+        res[name] = dict(us=round(ms * 1e3, 2), gbs=round(alg / ms / 1e6, 1),
+                         frac_peak=round(alg / ms / 1e6 / HBM_PEAK_GBS, 4), copies=ncopy, alg_bytes=alg)
+        if name.startswith("70b"):
+            layer_bytes += alg
+            layer_ms += ms
+        log(f"[bench] {name}: {ms * 1e3:.1f} us, {alg / ms / 1e6:.0f} GB/s")
+        del Ws, base
+    return {"metric": "quant GEMV effective GB/s (% HBM peak)", "unit": "GB/s", "n_gpus": 1,
+            "value": res["q8_0_4096x4096"]["gbs"], "higher_is_better": True, "data": "synthetic",
+            "config": {"workload": "single GEMVs: Q8_0 4096x4096 and the 70B-shaped Q4_K_M projections, "
+                                   "weights rotated over distinct copies"},
+            "read_ceiling_gbs": round(read_gbs, 1), "gemv": res,
+            "seven_gemv_layer_gbs": round(layer_bytes / layer_ms / 1e6, 1)}
+
+
+def workload_layer8b(dev) -> dict:
+    """Config 2: one 8B-shaped Q4_0 layer at position 512, timed over 32
+    distinct layers (3.9 GB of weights, more than the last-level cache)."""
+    import torch
+
+    import quantized_decode_dequant_amd as nt
+    from quantized_decode_dequant_amd.model import DeviceLayer, cfg_of
+    from synth import workloads as wl
+
+    shape, n_past, nl = wl.LLAMA8B, 512, 32
+    cfg = cfg_of(shape, n_past + 1)
+    li = wl.gen_layer(shape, wl.ALL_Q4_0, wl.W_LAYER_8B, 0, n_past + 1, n_past)
+    dls = [DeviceLayer(li, dev) for _ in range(nl)]
+    ws = torch.zeros(nt.layer_workspace_bytes(cfg, 1), dtype=torch.uint8, device=dev)
+    x = torch.from_numpy(wl.gen_x(shape.hidden, wl.W_LAYER_8B)).to(dev)
+    pos = torch.tensor([n_past], dtype=torch.int32, device=dev)
+    it = [0]
+
+    def one():
+        nt.decode_layer(cfg, dls[it[0] % nl].struct, x, 1, pos, ws)
+        it[0] += 1
+
+    ms = timed(one, 4 * nl)
+    wbytes = dls[0].weight_bytes()
+    kv = 2 * shape.n_kv_head * (n_past + 1) * shape.head_dim * 2
+    alg = wbytes + kv + 2 * shape.n_kv_head * shape.head_dim * 2 + 4 * (3 * shape.hidden + shape.ffn)
+    return {"metric": "8B-shaped Q4_0 decoder layer effective GB/s", "unit": "GB/s", "n_gpus": 1,
+            "value": round(alg / ms / 1e6, 1), "higher_is_better": True, "data": "synthetic",
+            "config": {"workload": "llama8b-shaped Q4_0 layer, position 512, 32 distinct layers"},
+            "us_per_layer": round(ms * 1e3, 2), "alg_bytes": alg, "frac_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
+def workload_verify(dev, passes: int) -> dict:
+    """Config 5: streamed verify passes; every layer is a copy of one seeded
+    Q6_K layer (the timing does not depend on the weight values)."""
+    import numpy as np
+    import torch
+
+    import quantized_decode_dequant_amd as nt
+    from quantized_decode_dequant_amd.model import DeviceLayer, cfg_of, pack_blob
+    from synth import workloads as wl
+
+    shape, n_layer, fs, n_past, vocab = wl.LLAMA70B, 80, 36, 4096, 128256
+    max_ctx = n_past + 8
+    cfg = cfg_of(shape, max_ctx)
+    t0 = time.time()
+    li = wl.gen_layer(shape, wl.ALL_Q6_K, wl.W_VERIFY_70B, 0, max_ctx, n_past)
+    blob = pack_blob(cfg, li)
+    sb = blob.size
+    host = [None] * n_layer
+    for l in range(fs, n_layer):
+        host[l] = torch.empty(sb, dtype=torch.uint8, pin_memory=True)
+        host[l].numpy()[:] = blob
+    stage = (torch.empty(sb, dtype=torch.uint8, device=dev), torch.empty(sb, dtype=torch.uint8, device=dev))
+    streamed = [DeviceLayer(li, dev, weights_on_device=(l < fs)) for l in range(n_layer)]
+    log(f"[bench] verify stack ready: {fs} resident + {n_layer - fs} streamed layers of {sb / 1e6:.1f} MB "
+        f"({time.time() - t0:.0f} s)")
+    emb = torch.from_numpy(wl.gen_matrix(wl.Q6_K, vocab, shape.hidden, wl.W_VERIFY_70B, 0, wl.T_TOK_EMB)).to(dev)
+    head = torch.from_numpy(wl.gen_matrix(wl.Q6_K, vocab, shape.hidden, wl.W_VERIFY_70B, 0, wl.T_LM_HEAD)).to(dev)
+    norm = torch.from_numpy(wl.gen_gains(shape, wl.W_VERIFY_70B, 0, wl.T_OUT_NORM)).to(dev)
+    copy_stream = torch.cuda.Stream()
+    hs = nt.ModelHandle(cfg, [d.struct for d in streamed], vocab, emb, wl.Q6_K, head, wl.Q6_K, norm,
+                        first_streamed=fs, host_layers=host, stage=stage, stage_bytes=sb, copy_stream=copy_stream)
+    stream = torch.cuda.current_stream()
+    toks = torch.from_numpy(wl.gen_tokens(wl.W_VERIFY_70B, 8, vocab)).to(dev)
+    pos = torch.tensor([n_past], dtype=torch.int32, device=dev)
+    out = torch.zeros(8, dtype=torch.int32, device=dev)
+    stream_bytes = sb * (n_layer - fs)
+    # copy-only: the 44 layer copies alone
+    def copies():
+        for l in range(fs, n_layer):
+            stage[l & 1].copy_(host[l], non_blocking=True)
+    copy_ms = timed(copies, 2)
+    res = {"h2d_probe_gbs": round(stream_bytes / copy_ms / 1e6, 1), "copy_only_ms": round(copy_ms, 1)}
+    for M in [1, 2, 4, 8]:
+        ws = torch.zeros(hs.workspace_bytes(M), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: hs.verify_step(toks, M, pos, out, ws, None, stream), passes)
+        res[f"M{M}"] = {"pass_ms": round(ms, 1), "verified_pos_per_s": round(M / (ms / 1e3), 2),
+                        "h2d_gbs": round(stream_bytes / ms / 1e6, 1)}
+        log(f"[bench] verify M={M}: {ms:.1f} ms per pass")
+        del ws
+    # compute-only: the same 80 layers all resident
+    del hs
+    resident = [DeviceLayer(li, dev) for _ in range(n_layer)]
+    hr = nt.ModelHandle(cfg, [d.struct for d in resident], vocab, emb, wl.Q6_K, head, wl.Q6_K, norm)
+    for M in [1, 2, 4, 8]:
+        ws = torch.zeros(hr.workspace_bytes(M), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: hr.verify_step(toks, M, pos, out, ws, None, stream), max(3, passes))
+        t_pipe = res[f"M{M}"]["pass_ms"]
+        res[f"M{M}"]["compute_only_ms"] = round(ms, 2)
+        res[f"M{M}"]["overlap_efficiency"] = round((copy_ms + ms - t_pipe) / min(copy_ms, ms), 3)
+        del ws
+    del resident, hr
+    best = max(res[f"M{M}"]["verified_pos_per_s"] for M in [1, 2, 4, 8])
+    return {"metric": "streamed verify: verified positions/s", "unit": "positions/s", "n_gpus": 1,
+            "value": best, "higher_is_better": True, "data": "synthetic",
+            "config": {"workload": "80 Q6_K 70B-shaped layers, 36 resident + 44 streamed from pinned host memory, "
+                                   "verify passes from context 4096", "stream_bytes_per_pass": stream_bytes},
+            "verify": res}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +359,9 @@ def main():
                     help="also run one device copy of 256 MiB (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize", metavar="DIR", help="print per-kernel statistics of a rocprofv3 output "
                     "directory (kernel trace or counter csv) and exit")
+    ap.add_argument("--workload", choices=["decode", "gemv", "layer8b", "verify"], default="decode",
+                    help="decode (the headline, default) or one of the secondary workloads")
+    ap.add_argument("--passes", type=int, default=5, help="verify workload: timed passes per M")
     args = ap.parse_args()
     if args.summarize:
         summarize_profile(args.summarize)
@@ -199,6 +376,11 @@ def main():
     import quantized_decode_dequant_amd as nt
 
     dev = torch.device("cuda:0")
+    if args.workload != "decode":
+        fn = {"gemv": lambda: workload_gemv(dev), "layer8b": lambda: workload_layer8b(dev),
+              "verify": lambda: workload_verify(dev, args.passes)}[args.workload]
+        print(json.dumps(fn()), flush=True)
+        return
     n_past = 4096
     max_ctx = n_past + max(args.steps, args.warmup)
     h, first, vocab, wbytes, shape, fmts = build_stack(args.layers, max_ctx, n_past, dev)
@@ -252,10 +434,13 @@ def main():
     toks = [int(t.item()) for t in tokens]
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/token, {tok_s:.2f} tok/s (wall {wall:.2f} s)")
 
-    # dominant kernel: gate/up + SwiGLU, 2 x ffn x hidden Q4_K weights per launch
-    q4k_row = nt.row_bytes(fmts["wg"], shape.hidden)
-    ffn_bytes = 2 * shape.ffn * q4k_row + shape.hidden * 4 * 2 + shape.ffn * 4
-    ffn_avg_s = ffn_ms / 1e3 / max(1, n_ffn)
+    # dominant kernel: gate/up + SwiGLU, once per layer.  Algorithmic bytes
+    # per launch: the two ffn x hidden weight matrices, x and the norm gains
+    # read, the SwiGLU output written.
+    ffn_bytes = 2 * shape.ffn * nt.row_bytes(fmts["wg"], shape.hidden) + shape.hidden * 4 * 2 + shape.ffn * 4
+    if n_ffn == 0:
+        raise RuntimeError("no gate/up launch was traced")
+    ffn_avg_s = ffn_ms / 1e3 / n_ffn
     achieved = ffn_bytes / ffn_avg_s / 1e9
     traffic = counter_traffic("ffn_gate_up", ffn_bytes)
 
@@ -287,7 +472,7 @@ def main():
         "weight_roofline_frac": round(wbytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "read_ceiling_gbs": round(read_gbs, 1),
         "roofline": {
-            "kernel": "k_qgemv<EPI_SWIGLU> (gate/up GEMV + SwiGLU, Q4_K 2x28672x8192)",
+            "kernel": "k_qgemv<EPI_SWIGLU> (RMSNorm + gate/up GEMV + SwiGLU, Q4_K 2x28672x8192)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,

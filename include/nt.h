@@ -146,7 +146,9 @@ size_t nt_layer_workspace_bytes(const nt_layer_cfg* cfg, int M);
  *   pos_dev: device int32 holding pos (read by the kernels, so a captured
  *            graph can be replayed with a new position); if pos < 0 or
  *            pos + M > max_ctx the kernels skip the cache write and attention.
- *   ws: device workspace of ws_bytes >= nt_layer_workspace_bytes(cfg, M).
+ *   ws: device workspace of ws_bytes >= nt_layer_workspace_bytes(cfg, M);
+ *       its contents need no initialisation.  Calls that share a workspace
+ *       must not overlap.
  * The call does not advance pos.
  */
 int nt_decode_layer(const nt_layer_cfg* cfg, const nt_layer* layer, float* x, int M, const int32_t* pos_dev,

@@ -127,7 +127,7 @@ __device__ __forceinline__ ShareM share_m(const JobM& job, int b) {
   sh.nvt = job.paired ? 2 * sh.nt : sh.nt;
   sh.nsub = (sh.nts_r + job.tsu - 1) / job.tsu;
   sh.nunits = sh.nvt * sh.nsub;
-  sh.magic = job.magicV[big ? 1 : 0];
+  sh.magic = big ? job.magicV[1] : job.magicV[0];
   return sh;
 }
 

@@ -39,532 +39,11 @@
 
 #include <algorithm>
 
-#include "nt_dev.h"
+#include "nt_engine.h"
 
 namespace nt {
 namespace {
 
-
-// Activation of the lane's two column units in the current slice: int8 high
-// and low planes of 64 elements each, the scale of each 32-block and the sum
-// of X over each 16 elements.
-struct XR {
-  uint32_t hi[kUnitsPerLane][16], lo[kUnitsPerLane][16];
-  float sc[kUnitsPerLane][2];
-  int sm[kUnitsPerLane][4];
-};
-
-__device__ __forceinline__ void load_xr(const Job& job, int slice, int lane, XR& xr) {
-#pragma unroll
-  for (int j = 0; j < kUnitsPerLane; ++j) {
-    const int k = lane + 64 * j;
-    const uint32_t e0 = 64u * (uint32_t)(slice * job.ups + k);
-    if (k < job.ups && e0 < (uint32_t)job.cols) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 h = ld128(job.x_hi + e0 + 16 * i), l = ld128(job.x_lo + e0 + 16 * i);
-        xr.hi[j][4 * i] = h.x; xr.hi[j][4 * i + 1] = h.y; xr.hi[j][4 * i + 2] = h.z; xr.hi[j][4 * i + 3] = h.w;
-        xr.lo[j][4 * i] = l.x; xr.lo[j][4 * i + 1] = l.y; xr.lo[j][4 * i + 2] = l.z; xr.lo[j][4 * i + 3] = l.w;
-      }
-      xr.sc[j][0] = ldf(job.x_sc + (e0 >> 3));
-      xr.sc[j][1] = ldf(job.x_sc + (e0 >> 3) + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xr.sm[j][i] = ldi32(job.x_sum + (e0 >> 2) + 4 * i);
-    }
-  }
-}
-
-// ---------------------------------------------------------------- units
-// A unit is 64 consecutive weights of one row: column unit k of the slice.
-// `seg` is the LDS byte offset of the segment's first block; XH/XL/XS/XM the
-// lane's activation registers for the unit.
-
-#define NT_XARGS const uint32_t(&xh)[16], const uint32_t(&xl)[16], const float(&xs)[2], const int(&xm)[4]
-
-// Q8_0: blocks 2k and 2k+1 (the second only if `two`).  w = d*q.
-__device__ __forceinline__ float unit_q8_0(uint32_t seg, int k, bool two, NT_XARGS) {
-  float acc = 0.f;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    if (b == 1 && !two) break;
-    const uint32_t blk = seg + 34u * (2 * k + b);
-    const float d = h2f(ld16(blk));
-    uint32_t q[8];
-    ld_unaligned<8>(blk + 2, q);
-    int H = 0, L = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      H = dot4(q[i], xh[8 * b + i], H);
-      L = dot4(q[i], xl[8 * b + i], L);
-    }
-    acc += d * xs[b] * (float)((H << 8) + L);
-  }
-  return acc;
-}
-
-// Q4_0: blocks 2k and 2k+1.  Byte j of a block: low nibble -> element j,
-// high nibble -> element j+16.  w = d*(q-8), so sum w*X = d*(sum q*X - 8 sum X).
-__device__ __forceinline__ float unit_q4_0(uint32_t seg, int k, bool two, NT_XARGS) {
-  float acc = 0.f;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    if (b == 1 && !two) break;
-    const uint32_t blk = seg + 18u * (2 * k + b);
-    const float d = h2f(ld16(blk));
-    uint32_t q[4];
-    ld_unaligned<4>(blk + 2, q);
-    int H = 0, L = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo4 = q[i] & 0x0F0F0F0Fu, hi4 = (q[i] >> 4) & 0x0F0F0F0Fu;
-      H = dot4(lo4, xh[8 * b + i], H);
-      L = dot4(lo4, xl[8 * b + i], L);
-      H = dot4(hi4, xh[8 * b + 4 + i], H);
-      L = dot4(hi4, xl[8 * b + 4 + i], L);
-    }
-    const int S = (H << 8) + L - 8 * (xm[2 * b] + xm[2 * b + 1]);
-    acc += d * xs[b] * (float)S;
-  }
-  return acc;
-}
-
-// Q4_K: unit k is chunk c = k%4 (64 weights) of superblock k/4: quant bytes
-// 32c..32c+31, whose low nibbles are the chunk's first 32 weights (sub-block
-// 2c) and high nibbles the next 32 (sub-block 2c+1).  w = d*sc*q - dmin*m.
-// hd: the superblock's first 16 bytes (d, dmin, scales); q0, q1: the chunk's
-// 32 quant bytes.
-__device__ __forceinline__ float q4k_dot(const uint4& hd, const uint4& q0, const uint4& q1, int c, NT_XARGS) {
-  const float d = h2f(hd.x & 0xffffu), dmin = h2f(hd.x >> 16);
-  int scA, mA, scB, mB;
-  q4k_scale_min(hd.y, hd.z, hd.w, 2 * c, scA, mA);
-  q4k_scale_min(hd.y, hd.z, hd.w, 2 * c + 1, scB, mB);
-  const uint32_t qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-  int AH = 0, AL = 0, BH = 0, BL = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t lo4 = qv[i] & 0x0F0F0F0Fu, hi4 = (qv[i] >> 4) & 0x0F0F0F0Fu;
-    AH = dot4(lo4, xh[i], AH);
-    AL = dot4(lo4, xl[i], AL);
-    BH = dot4(hi4, xh[8 + i], BH);
-    BL = dot4(hi4, xl[8 + i], BL);
-  }
-  const int SA = (AH << 8) + AL, SB = (BH << 8) + BL;
-  return xs[0] * (d * (float)scA * (float)SA - dmin * (float)mA * (float)(xm[0] + xm[1])) +
-         xs[1] * (d * (float)scB * (float)SB - dmin * (float)mB * (float)(xm[2] + xm[3]));
-}
-
-__device__ __forceinline__ float unit_q4_k(uint32_t seg, int k, NT_XARGS) {
-  const uint32_t blk = seg + 144u * (k >> 2);
-  const int c = k & 3;
-  return q4k_dot(ld128(blk), ld128(blk + 16 + 32 * c), ld128(blk + 32 + 32 * c), c, xh, xl, xs, xm);
-}
-
-// Q6_K: unit k covers elements 64p..64p+63 of superblock k/4, p = k%4, i.e.
-// half n = p/2, quarters q = 2h and 2h+1 (h = p%2).  Element 32q'+l of half n
-// (q' = 0..3, l < 32) takes its low four bits from nibble q'/2 of
-// ql[64n + 32(q'%2) + l], its high two bits from bits 2q'..2q'+1 of
-// qh[32n + l], and scale sc[8n + 2q' + l/16].  w = d*sc*(q-32).
-__device__ __forceinline__ float unit_q6_k(uint32_t seg, int k, NT_XARGS) {
-  const int sb = k >> 2, p = k & 3, n = p >> 1, h = p & 1;
-  const uint32_t blk = seg + 210u * sb;
-  uint32_t qa[8], qb[8], qh[8], scw[1];
-  ld_unaligned<8>(blk + 64 * n, qa);       // ql[64n .. 64n+31]
-  ld_unaligned<8>(blk + 64 * n + 32, qb);  // ql[64n+32 .. 64n+63]
-  ld_unaligned<8>(blk + 128 + 32 * n, qh); // qh[32n .. 32n+31]
-  ld_unaligned<1>(blk + 192 + 8 * n + 4 * h, scw);
-  const float d = h2f(ld16(blk + 208));
-  const int sh = 4 * h;
-  int H[4] = {0, 0, 0, 0}, L[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t hb = qh[i] >> sh;
-    const uint32_t a = ((qa[i] >> sh) & 0x0F0F0F0Fu) | ((hb << 4) & 0x30303030u);
-    const uint32_t b = ((qb[i] >> sh) & 0x0F0F0F0Fu) | ((hb << 2) & 0x30303030u);
-    H[i >> 2] = dot4(a, xh[i], H[i >> 2]);
-    L[i >> 2] = dot4(a, xl[i], L[i >> 2]);
-    H[2 + (i >> 2)] = dot4(b, xh[8 + i], H[2 + (i >> 2)]);
-    L[2 + (i >> 2)] = dot4(b, xl[8 + i], L[2 + (i >> 2)]);
-  }
-  float acc = 0.f;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int S = (H[g] << 8) + L[g] - 32 * xm[g];
-    const int sc = (int)(int8_t)(scw[0] >> (8 * g));
-    acc += (float)S * ((float)sc * xs[g >> 1]);
-  }
-  return d * acc;
-}
-
-#undef NT_XARGS
-
-// ----------------------------------------------------------------- prologue
-// Stage the activation: v = src (or RMSNorm(src) * gain), then per 32-block
-// s = max|v| / 32639, X = rint(v / s), hi = (X + 128) >> 8, lo = X - 256 hi.
-// For the QKV launch it also tabulates the RoPE rotation of this position.
-//
-// Loads are coalesced: in round r thread t holds elements 4(NT r + t) ..
-// +3, so the 8 lanes of an aligned lane group hold one 32-block and a
-// wave's load covers 1 KB of consecutive bytes.  A wave's activation must
-// have arrived (stage_load, stage_norm) before it issues its first weight
-// loads: behind the launch's burst of weight requests an activation miss
-// would wait several microseconds in the memory queues, and the quantization
-// then overlaps the weights' latency instead.
-
-constexpr int kXRounds = 8;  // rounds held in registers: inputs up to 4 * 1024 * 8 = 32768 wide
-
-struct XStage {
-  float4 v[kXRounds];  // src, times the gains when normalising
-  float4 g[kXRounds];
-};
-
-__device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ __forceinline__ float4 mul4(float4 a, float4 b) { return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w); }
-__device__ __forceinline__ float4 scale4(float4 a, float r) { return make_float4(a.x * r, a.y * r, a.z * r, a.w * r); }
-__device__ __forceinline__ float sq4(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
-
-__device__ __forceinline__ void stage_load(const Job& job, const ProArgs& pro, int tid, XStage& st) {
-  const int NT = job.nwaves * 64;
-#pragma unroll
-  for (int r = 0; r < kXRounds; ++r) {
-    const int e = 4 * (NT * r + tid);
-    if (e < job.cols) {
-      st.v[r] = ld_f4(pro.src + e);
-      if (pro.gain) st.g[r] = ld_f4(pro.gain + e);
-    }
-  }
-}
-
-// Uses the loaded activation (so its loads are waited for here): the sum of
-// squares of the source and the gain product.
-__device__ __forceinline__ float stage_norm(const Job& job, const ProArgs& pro, int tid, XStage& st) {
-  const int NT = job.nwaves * 64;
-  float ss = 0.f;
-  if (pro.gain) {
-#pragma unroll
-    for (int k = 0; k < kXRounds; ++k) {
-      const int e = 4 * (NT * k + tid);
-      if (e < job.cols) {
-        ss += sq4(st.v[k]);
-        st.v[k] = mul4(st.v[k], st.g[k]);
-      }
-    }
-  } else {
-    // a use of every loaded value, so the waits happen here
-#pragma unroll
-    for (int k = 0; k < kXRounds; ++k) {
-      const int e = 4 * (NT * k + tid);
-      if (e < job.cols) ss += st.v[k].x;
-    }
-  }
-  return ss;
-}
-
-// Quantize elements e..e+3 (held by this lane, already scaled) into the LDS
-// planes; the group's first lanes write the block scale and the 16-sums.
-__device__ __forceinline__ void quant4(const Job& job, int lane, int e, float4 w) {
-  float amax = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
-  amax = max8(amax);
-  const float inv = amax > 0.f ? kXMax / amax : 0.f;
-  const float f[4] = {w.x, w.y, w.z, w.w};
-  uint32_t H = 0, L = 0;
-  int sum = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    int X = __float2int_rn(f[k] * inv);
-    X = max(-32639, min(32639, X));
-    const int hi = (X + 128) >> 8;
-    const int lo = X - (hi << 8);
-    H |= (uint32_t)(hi & 255) << (8 * k);
-    L |= (uint32_t)(lo & 255) << (8 * k);
-    sum += X;
-  }
-  *reinterpret_cast<uint32_t*>(nt_smem + job.x_hi + e) = H;
-  *reinterpret_cast<uint32_t*>(nt_smem + job.x_lo + e) = L;
-  sum = sum4(sum);
-  if ((lane & 3) == 0) sti32(job.x_sum + 4u * (uint32_t)(e >> 4), sum);
-  if ((lane & 7) == 0) stf(job.x_sc + 4u * (uint32_t)(e >> 5), amax / kXMax);
-}
-
-
-// ss: this thread's sum of squares from stage_norm.
-__device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro, int tid, XStage& st, float ss) {
-  const int NT = job.nwaves * 64, lane = tid & 63;
-  const int nround = (job.cols + 4 * NT - 1) / (4 * NT);
-  float r = 1.0f;
-  if (pro.gain) {
-    // rounds past the registers (inputs wider than 32768)
-    for (int k = kXRounds; k < nround; ++k) {
-      const int e = 4 * (NT * k + tid);
-      if (e < job.cols) ss += sq4(ld_f4(pro.src + e));
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) stf(job.red + 4u * (tid >> 6), ss);
-    __syncthreads();
-    float tot = 0.f;
-    for (int w = 0; w < job.nwaves; ++w) tot += ldf(job.red + 4u * w);
-    r = 1.0f / sqrtf(tot / (float)job.cols + pro.eps);
-  }
-#pragma unroll
-  for (int k = 0; k < kXRounds; ++k) {
-    const int e = 4 * (NT * k + tid);
-    if (e < job.cols) quant4(job, lane, e, scale4(st.v[k], r));
-  }
-  for (int k = kXRounds; k < nround; ++k) {
-    const int e = 4 * (NT * k + tid);
-    if (e < job.cols) {
-      float4 v = ld_f4(pro.src + e);
-      if (pro.gain) v = mul4(v, ld_f4(pro.gain + e));
-      quant4(job, lane, e, scale4(v, r));
-    }
-  }
-  if (pro.rope_hd > 0) {
-    // pair i turns by pos * theta^(-2i/head_dim); the angle is formed in
-    // double so large positions keep fp32 accuracy
-    for (int i = tid; i < pro.rope_hd / 2; i += NT) {
-      const int pos = *pro.pos + pro.pos_add;
-      const double freq = exp2(-(double)(2 * i) / (double)pro.rope_hd * log2((double)pro.rope_theta));
-      const double ang = (double)pos * freq;
-      stf(job.rope + 8u * i, (float)cos(ang));
-      stf(job.rope + 8u * i + 4, (float)sin(ang));
-    }
-  }
-  __syncthreads();
-}
-
-// ----------------------------------------------------------- segment stream
-// Workgroup b's share: output rows [o0, o0 + no); `nv` segment rows (twice
-// the output rows with paired matrices) times `nslice` slices.  Segment id
-// k = s * nv + v (slice-major), so a wave's successive claims mostly stay in
-// one slice and its activation registers rarely change.  Everything here is
-// wave-uniform and lives in scalar registers.
-struct Share {
-  int o0, no;      // first output row, output rows
-  int nv;          // segment rows
-  int nseg;        // segments
-  uint32_t magic;  // floor((2^32 - 1) / nv): slice of a segment id by a multiply
-};
-
-__device__ __forceinline__ Share share_of(const Job& job, int b) {
-  Share sh;
-  const bool big = b < job.wg_rem;
-  const int u0 = b * job.wg_base + (big ? b : job.wg_rem);
-  const int nu = job.wg_base + (big ? 1 : 0);
-  sh.o0 = u0 * job.unit;
-  sh.no = nu * job.unit;
-  sh.nv = job.paired ? 2 * sh.no : sh.no;
-  sh.nseg = sh.nv * job.nslice;
-  sh.magic = job.magic[big ? 1 : 0];
-  return sh;
-}
-
-// Byte range of one segment and where its data sits in the slab.
-struct Seg {
-  const uint8_t* a;  // 16-B aligned address of the first chunk
-  int nchunks;
-  uint32_t d;        // offset of the segment's first block from the first chunk
-  int fmt;
-  int nunits;        // column units in the slice
-  int half;          // the last unit holds a single 32-weight block
-  int s, v;          // slice and segment row
-};
-
-__device__ __forceinline__ Seg seg_at(const Job& job, const Share& sh, int k) {
-  Seg sg;
-  // s = k / nv: the multiply undershoots by at most one
-  uint32_t q = __umulhi((uint32_t)k, sh.magic);
-  int v = k - (int)q * sh.nv;
-  if (v >= sh.nv) {
-    ++q;
-    v -= sh.nv;
-  }
-  const int s = (int)q;
-  sg.s = s;
-  sg.v = v;
-  int m, row;
-  if (job.paired) {
-    const bool up = v >= sh.no;
-    m = up ? 1 : 0;
-    row = sh.o0 + (up ? v - sh.no : v);
-  } else {
-    row = sh.o0 + v;
-    m = (job.nmat > 2 && row >= job.row_base[2]) ? 2 : ((job.nmat > 1 && row >= job.row_base[1]) ? 1 : 0);
-    row -= m == 2 ? job.row_base[2] : (m == 1 ? job.row_base[1] : 0);
-  }
-  // per-matrix fields by selects (a dynamic index would leave scalar registers)
-  const uint8_t* W = m == 2 ? job.W[2] : (m == 1 ? job.W[1] : job.W[0]);
-  const int64_t rb = m == 2 ? job.rb[2] : (m == 1 ? job.rb[1] : job.rb[0]);
-  const int64_t sbytes = m == 2 ? job.slice_bytes[2] : (m == 1 ? job.slice_bytes[1] : job.slice_bytes[0]);
-  sg.fmt = m == 2 ? job.fmt[2] : (m == 1 ? job.fmt[1] : job.fmt[0]);
-  const uint8_t* ptr = W + (int64_t)row * rb + (int64_t)s * sbytes;
-  const bool last = s == job.nslice - 1;
-  const int ne = last ? job.last_ne : job.ups * 64;
-  sg.nunits = last ? job.last_units : job.ups;
-  sg.half = (ne & 63) != 0;
-  const int64_t bytes = last ? (int64_t)(ne / block_elems(sg.fmt)) * block_bytes(sg.fmt) : sbytes;
-  sg.a = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(ptr) & ~uintptr_t(15));
-  sg.d = (uint32_t)(ptr - sg.a);
-  sg.nchunks = (int)((sg.d + bytes + 15) >> 4);
-  return sg;
-}
-
-// Stand-in when a wave has no segment to load: one chunk at the start of the
-// first matrix.  Loads are still issued for it, so every path through the
-// stream issues the same number of loads and the waits before a slab store
-// count exactly the older segment (waits merge across paths pessimistically).
-__device__ __forceinline__ Seg seg_null(const Job& job) {
-  Seg sg;
-  sg.a = job.W[0];
-  sg.nchunks = 1;
-  sg.d = 0;
-  sg.fmt = job.fmt[0];
-  sg.nunits = 0;
-  sg.half = 0;
-  sg.s = 0;
-  sg.v = 0;
-  return sg;
-}
-
-// Every lane issues exactly LPL loads (lanes past the segment's end re-read
-// its first chunk), so the number of loads in flight is the same on every
-// path and the waits before the slab store count exactly the older segment.
-template <int LPL>
-__device__ __forceinline__ void seg_load(const Seg& sg, int lane, uint4 (&pre)[LPL]) {
-#pragma unroll
-  for (int i = 0; i < LPL; ++i) {
-    const int c = lane + 64 * i;
-    pre[i] = load_chunk(sg.a + 16 * (c < sg.nchunks ? c : 0));
-  }
-}
-
-// The slab holds LPL KB, so every chunk slot is written (slots past the
-// segment's end get the re-read first chunk, which nothing reads): no
-// divergent branch.
-template <int LPL>
-__device__ __forceinline__ void seg_store(uint32_t slab, int lane, const uint4 (&pre)[LPL]) {
-#pragma unroll
-  for (int i = 0; i < LPL; ++i) st128(slab + 16u * (lane + 64 * i), pre[i]);
-}
-
-// This lane's part of one segment's dot product, from the slab.
-__device__ __forceinline__ float seg_compute(const Seg& sg, uint32_t slab, int lane, const XR& xr) {
-  const uint32_t seg = slab + sg.d;
-  float acc = 0.f;
-  const bool full = sg.nunits >= 64 * kUnitsPerLane && !sg.half;  // uniform
-#pragma unroll
-  for (int j = 0; j < kUnitsPerLane; ++j) {
-    const int k = lane + 64 * j;
-    if (full || k < sg.nunits) {
-      switch (sg.fmt) {
-        case NT_Q4_K: acc += unit_q4_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j]); break;
-        case NT_Q6_K: acc += unit_q6_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j]); break;
-        case NT_Q8_0:
-          acc += unit_q8_0(seg, k, !(sg.half && k == sg.nunits - 1), xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j]);
-          break;
-        default:
-          acc += unit_q4_0(seg, k, !(sg.half && k == sg.nunits - 1), xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j]);
-          break;
-      }
-    }
-  }
-  return acc;
-}
-
-// Sum of segment row v over the slices, in slice order (deterministic).
-__device__ __forceinline__ float row_total(const Job& job, int v) {
-  const uint32_t a = job.acc + 4u * (uint32_t)(v * job.nslice);
-  float t = ldf(a);
-  for (int s = 1; s < job.nslice; ++s) t += ldf(a + 4u * s);
-  return t;
-}
-
-// Finish the workgroup's rows (after the barrier that follows the stream):
-// thread t handles output row (or row pair) t.
-template <int EPI>
-__device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, int tid, const EpiArgs& ea) {
-  const int NT = job.nwaves * 64;
-  if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
-    for (int t = tid; t < sh.no; t += NT) {
-      const float s = row_total(job, t);
-      if constexpr (EPI == EPI_RESID) ea.y[sh.o0 + t] += s;
-      else ea.y[sh.o0 + t] = s;
-    }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    for (int t = tid; t < sh.no; t += NT) ea.y[sh.o0 + t] = silu(row_total(job, t)) * row_total(job, sh.no + t);
-  } else if constexpr (EPI == EPI_QKV) {
-    const int pos = *ea.pos + ea.pos_add;
-    const bool pos_ok = pos >= ea.pos_add && pos < ea.max_ctx;
-    if (!pos_ok && ea.err && tid == 0) *ea.err = 1;
-    for (int t = tid; 2 * t < sh.no; t += NT) {
-      const int R = sh.o0 + 2 * t;  // even row of an adjacent pair (concatenated Q, K, V rows)
-      float a = row_total(job, 2 * t), b = row_total(job, 2 * t + 1);
-      const int dd = R % ea.head_dim;
-      if (R < ea.q_rows + ea.kv_rows) {
-        // RoPE: pair (2i, 2i+1) of a head turns by pos * theta^(-2i/head_dim)
-        // (the prologue tabulated cos and sin)
-        const float c = ldf(job.rope + 4u * dd), s = ldf(job.rope + 4u * dd + 4);
-        const float a2 = a * c - b * s, b2 = a * s + b * c;
-        a = a2;
-        b = b2;
-      }
-      if (R < ea.q_rows) {
-        ea.q_out[R] = a;
-        ea.q_out[R + 1] = b;
-      } else if (pos_ok) {
-        const bool is_k = R < ea.q_rows + ea.kv_rows;
-        const int rr = R - ea.q_rows - (is_k ? 0 : ea.kv_rows);
-        const int kh = rr / ea.head_dim;
-        uint16_t* cache = is_k ? ea.k_cache : ea.v_cache;
-        const int64_t off = ((int64_t)kh * ea.max_ctx + pos) * ea.head_dim + dd;
-        const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-        cache[off] = __builtin_bit_cast(uint16_t, ha);
-        cache[off + 1] = __builtin_bit_cast(uint16_t, hb);
-      }
-    }
-  }
-}
-
-// Next segment for this wave: a claim on the workgroup's LDS counter.  Ids
-// below 2 * nwaves were handed out statically (wave w: w and w + nwaves).
-__device__ __forceinline__ int claim(const Job& job, int lane) {
-  int old = 0;
-  int* ctr = static_cast<int*>(__builtin_assume_aligned(nt_smem + job.ctl, 16));
-  if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  return 2 * job.nwaves + __builtin_amdgcn_readfirstlane(old);
-}
-
-// One step of the stream: the segment in buffer `pre` (described by `sg`,
-// id k_cur) is stored to the slab, a newly claimed segment's loads are
-// issued into `pre`, and the stored segment is computed into its (row,
-// slice) partial sum.  The other buffer holds segment k_nxt (already in
-// flight).  A step past the wave's last segment only issues its stand-in
-// loads: the stream loop then has a single exit, at the bottom, so the wait
-// analysis never sees the buffers' load order swapped.
-template <int LPL>
-__device__ __forceinline__ void stream_step(const Job& job, const Share& sh, int lane, uint32_t slab, int& k_cur,
-                                            int& k_nxt, bool& claiming, int& xslice, XR& xr, uint4 (&pre)[LPL],
-                                            Seg& sg) {
-  const Seg cur = sg;
-  const bool valid = k_cur < sh.nseg;
-  seg_store(slab, lane, pre);
-  int k2 = sh.nseg;
-  if (claiming) {
-    k2 = claim(job, lane);
-    claiming = k2 < sh.nseg;
-  }
-  sg = k2 < sh.nseg ? seg_at(job, sh, k2) : seg_null(job);
-  seg_load(sg, lane, pre);
-  if (valid) {
-    if (cur.s != xslice) {
-      load_xr(job, cur.s, lane, xr);
-      xslice = cur.s;
-    }
-    const float part = wave_sum(seg_compute(cur, slab, lane, xr));
-    // every lane writes the same uniform value: no divergent branch
-    stf(job.acc + 4u * (uint32_t)(cur.v * job.nslice + cur.s), part);
-  }
-  k_cur = k_nxt;
-  k_nxt = k2;
-}
 
 template <int EPI, int LPL>
 __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, EpiArgs ea) {
@@ -576,7 +55,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, Epi
   const uint32_t slab = job.slab + (uint32_t)wave * (uint32_t)(LPL * 1024);
   if (tid == 0) sti32(job.ctl, 0);  // claim counter; the prologue's barrier publishes it
   XStage xst;
-  stage_load(job, pro, tid, xst);
+  stage_load<false>(job, pro, tid, xst);
   const float ss = stage_norm(job, pro, tid, xst);  // the activation has arrived
   uint4 pa[LPL], pb[LPL];
   Seg sa, sb;
@@ -586,7 +65,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, Epi
   seg_load(sa, lane, pa);
   sb = k_nxt < sh.nseg ? seg_at(job, sh, k_nxt) : seg_null(job);
   seg_load(sb, lane, pb);
-  stage_finish(job, pro, tid, xst, ss);  // ends with a workgroup barrier
+  stage_finish<false>(job, pro, tid, xst, ss);  // ends with a workgroup barrier
   if (k_cur < sh.nseg) {
     XR xr;
     int xslice = -1;
@@ -597,7 +76,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, Epi
     } while (k_cur < sh.nseg);
   }
   __syncthreads();
-  share_epilogue<EPI>(job, sh, tid, ea);
+  share_epilogue<EPI, false>(job, sh, tid, job.nwaves * 64, ea);
 }
 
 struct DevInfo {

@@ -60,6 +60,43 @@ def test_layer_tiny(fmts, n_past, M):
     check(got, ref, kc, vc, li, n_past, M)
 
 
+# 8 query heads per kv head, head_dim 128: the batch-1 layer runs attention,
+# O, gate/up and down as one persistent launch (grid barriers between them)
+GROUP8 = wl.LayerShape(hidden=2048, n_head=16, n_kv_head=2, head_dim=128, ffn=4096)
+
+
+@pytest.mark.parametrize("fmts", [wl.ALL_Q8_0, wl.ALL_Q4_0, wl.Q4_K_M, wl.ALL_Q6_K], ids=["q8_0", "q4_0", "q4_k_m", "q6_k"])
+@pytest.mark.parametrize("n_past", [0, 63, 64, 200, 1000])
+def test_layer_group8_batch1(fmts, n_past):
+    # 1..1001 positions: one split of one round up to many splits, ragged last round
+    got, ref, kc, vc, li = run_layer(GROUP8, fmts, wl.W_TEST, 7, 1024, n_past, 1)
+    check(got, ref, kc, vc, li, n_past, 1)
+
+
+def test_layer_group8_repeat_calls_share_workspace():
+    # the launch leaves its barrier counters at zero: consecutive calls on one
+    # workspace give identical results, and a new workspace gives the same
+    import torch
+    import quantized_decode_dequant_amd as nt
+    from quantized_decode_dequant_amd.model import DeviceLayer, cfg_of
+    shape, max_ctx, n_past = GROUP8, 512, 300
+    li = wl.gen_layer(shape, wl.Q4_K_M, wl.W_TEST, 8, max_ctx, n_past)
+    dl = DeviceLayer(li, device())
+    cfg = cfg_of(shape, max_ctx)
+    x0 = to_dev(wl.gen_x(shape.hidden, wl.W_TEST, 8, 201).astype(np.float32))
+    pos = torch.tensor([n_past], dtype=torch.int32, device=device())
+    ws = torch.zeros(nt.layer_workspace_bytes(cfg, 1), dtype=torch.uint8, device=device())
+    outs = []
+    for i in range(4):
+        xd = x0.clone()
+        w = ws if i < 3 else torch.full_like(ws, 0x5A)  # contents need no initialisation
+        nt.decode_layer(cfg, dl.struct, xd, 1, pos, w)
+        torch.cuda.synchronize()
+        outs.append(xd.cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
 def test_layer_8b_q4_0_full():
     # Llama-3-8B-shaped layer, Q4_0, 512 cached positions
     got, ref, kc, vc, li = run_layer(wl.LLAMA8B, wl.ALL_Q4_0, wl.W_LAYER_8B, 0, 520, 512, 1)
