@@ -9,11 +9,8 @@
 // Split over positions: workgroup (g, s) takes positions [s*chunk,
 // (s+1)*chunk) of kv head g for all query heads of the group, so every K/V
 // byte is read once.  It writes an unnormalised partial (running max m,
-// sum l, sum p*v) per head; attn_combine merges the splits.  Inside a
-// workgroup, LP = head_dim/8 lanes share one position (each lane holds 8
-// dims of K or V as one 16-byte load), so a wave covers 64/LP positions per
-// step with coalesced 16-byte loads straight from HBM; the per-position dot
-// products are finished with a butterfly over the LP lanes.
+// sum l, sum p*v) per head; attn_combine merges the splits.  The two
+// products of a split run on f16 matrix cores (k_attn_split below).
 
 #include <float.h>
 
@@ -28,129 +25,142 @@ constexpr int kAttnThreads = 256;
 constexpr int kMaxGroup = 8;  // query heads per kv head
 constexpr int kMaxSplits = 1024;  // position splits of one attention
 
-__device__ __forceinline__ void h8_to_f(uint4 v, float (&f)[8]) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
-    f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
-  }
-}
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Sum over the 16 lanes of a DPP row (lanes that share one position):
-// rotations by 8, 4, 2, 1 leave the sum in every lane of the row.
-template <int CTRL>
-__device__ __forceinline__ float row_rot(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
-}
-
-template <int LP>
-__device__ __forceinline__ float group_sum(float v) {
-  if constexpr (LP == 16) {
-    v += row_rot<0x128>(v);  // row_ror:8
-    v += row_rot<0x124>(v);  // row_ror:4
-    v += row_rot<0x122>(v);  // row_ror:2
-    v += row_rot<0x121>(v);  // row_ror:1
-  } else {
-#pragma unroll
-    for (int o = LP / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  }
-  return v;
-}
-
-// Positions per split for a head size: every thread then holds 8 chunks of
-// 16 bytes of K and 8 of V (K and V tiles of 32 KB per workgroup).
+// Positions per split for a head size: K and V tiles of at most 32 KB each.
 template <int HD>
-constexpr int attn_chunk() { return 16384 / HD; }
+constexpr int attn_chunk() { return 16384 / HD < 256 ? 16384 / HD : 256; }
 
 // q: fp32 [n_query][n_head][HD] (query i at position pos+i attends to
 // 0..pos+i).  Partials: part_o [n_query][nsplit][n_head][HD],
 // part_ml [n_query][nsplit][n_head][2].
+//
+// Both products run on v_mfma_f32_16x16x32_f16 with the group's query heads
+// as the 16 rows (rows past the group are zero).  K and V are f16 in the
+// cache, so they enter exactly; q and the softmax numerators p are split as
+// x = hi + lo (hi = f16(x), lo = f16(x - hi), about 22 significant bits) and
+// each product is two MFMAs accumulating in fp32.
+//   scores  S = Q K^T: wave w takes positions [w C/4, (w+1) C/4) in 16-column
+//           tiles, K loaded straight from HBM in the B-operand layout;
+//   P V     the V tile is staged position-major in LDS; wave w takes output
+//           columns (16 dims per tile) over all positions (head_dim 32: two
+//           waves per tile, one per half of the positions, summed in LDS).
+// Operand layout (16x16x32): A[i][k] in lane i + 16 (k / 8), element k % 8;
+// B[k][n] in lane n + 16 (k / 8), element k % 8; C[i][n] in lane
+// n + 16 (i / 4), element i % 4.
 template <int HD>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __restrict__ q, const uint16_t* __restrict__ kc,
                                                              const uint16_t* __restrict__ vc, const int32_t* pos_ptr,
                                                              int query, int n_head, int n_kv, int max_ctx, int nsplit,
                                                              float* __restrict__ part_o, float* __restrict__ part_ml) {
-  constexpr int LP = HD / 8;              // lanes per position (8 dims each)
-  constexpr int PPR = kAttnThreads / LP;  // positions per round
-  constexpr int CHUNK = attn_chunk<HD>();
-  constexpr int ROUNDS = CHUNK / PPR;     // = 8
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[CHUNK * HD];
-  __shared__ float s_p[kMaxGroup][CHUNK];
+  constexpr int C = attn_chunk<HD>();
+  constexpr int KS = HD / 32;                    // k-steps of a score tile
+  constexpr int PW = C / 4;                      // positions per wave (scores)
+  constexpr int TW = PW / 16;                    // score tiles per wave
+  constexpr int NTT = HD / 16;                   // output tiles
+  constexpr int TPW = NTT >= 4 ? NTT / 4 : 1;    // output tiles per wave
+  constexpr int KSPLIT = 4 * TPW / NTT;          // waves per output tile (over position parts)
+  constexpr int PKS = C / 32 / KSPLIT;           // P.V k-steps per wave
+  constexpr int VST = HD + 8;                    // V row stride in LDS (f16), rows 16-byte aligned
+  constexpr int NV = C * HD / 8 / kAttnThreads;  // 16-byte V chunks per thread
+  constexpr int CPR = HD / 8;                    // 16-byte chunks per row
+  static_assert(TW >= 1 && NV >= 1 && PKS >= 1 && KSPLIT <= 2, "attention tile shape");
+  __shared__ __attribute__((aligned(16))) _Float16 s_v[C * VST];
+  __shared__ __attribute__((aligned(16))) _Float16 s_ph[kMaxGroup][C];
+  __shared__ __attribute__((aligned(16))) _Float16 s_pl[kMaxGroup][C];
+  __shared__ float s_s[kMaxGroup][C];
   __shared__ float s_m[kMaxGroup], s_l[kMaxGroup];
+  __shared__ v4f s_red[KSPLIT > 1 ? NTT * 64 : 1];
 
   const int g = blockIdx.x, split = blockIdx.y;
   const int G = n_head / n_kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sub = tid % LP, slot = tid / LP;  // dims [8*sub, 8*sub+8) of positions slot + PPR*r
+  const int r16 = lane & 15, q4 = lane >> 4;
   const int pos = *pos_ptr;
   const int n_pos = pos + query + 1;
   const bool ok = pos >= 0 && pos + query < max_ctx;
-  const int t0 = split * CHUNK;
-  const int nt = ok ? max(0, min(CHUNK, n_pos - t0)) : 0;
+  const int t0 = split * C;
+  const int nt = ok ? max(0, min(C, n_pos - t0)) : 0;
+  const uint16_t* kg = kc + ((int64_t)g * max_ctx + t0) * HD;
+  const uint16_t* vg = vc + ((int64_t)g * max_ctx + t0) * HD;
 
-  // all K and V loads of this tile up front (positions past the end re-read row t0)
-  const uint16_t* kg = kc + ((int64_t)g * max_ctx + t0) * HD + 8 * sub;
-  const uint16_t* vg = vc + ((int64_t)g * max_ctx + t0) * HD + 8 * sub;
-  uint4 kr[ROUNDS];
+  // all K and V loads of the tile up front (positions past the end re-read
+  // row t0 and are masked).  K: lane (r16, q4) of wave w, tile j, step ks
+  // holds dims 32 ks + 8 q4 .. +7 of position w PW + 16 j + r16.
+  uint4 kb[TW][KS];
+#pragma unroll
+  for (int j = 0; j < TW; ++j) {
+    const int t = wave * PW + 16 * j + r16;
+    const int64_t row = (int64_t)(t < nt ? t : 0) * HD;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kb[j][ks] = *reinterpret_cast<const uint4*>(kg + row + 32 * ks + 8 * q4);
+  }
   {
-    uint4 vr[ROUNDS];
+    uint4 vr[NV];
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
-      const int t = slot + PPR * r;
-      const int64_t off = (int64_t)(t < nt ? t : 0) * HD;
-      kr[r] = *reinterpret_cast<const uint4*>(kg + off);
-      vr[r] = *reinterpret_cast<const uint4*>(vg + off);
+    for (int r = 0; r < NV; ++r) {
+      const int c = tid + kAttnThreads * r, t = c / CPR, d8 = c % CPR;
+      vr[r] = *reinterpret_cast<const uint4*>(vg + (int64_t)(t < nt ? t : 0) * HD + 8 * d8);
     }
-    // V tile to LDS (position-major, as in the cache); V's registers end here
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r)
-      *reinterpret_cast<uint4*>(s_v + (slot + PPR * r) * HD + 8 * sub) = vr[r];
+    for (int r = 0; r < NV; ++r) {
+      const int c = tid + kAttnThreads * r, t = c / CPR, d8 = c % CPR;
+      *reinterpret_cast<uint4*>(s_v + t * VST + 8 * d8) = vr[r];
+    }
   }
-  // query slices: 8 dims of each head of the group, scaled by 1/sqrt(HD);
-  // loaded unconditionally as float4 (heads past the group re-read head 0 and
-  // are zeroed) so the loads are one batch, not a chain of waits
-  float qr[kMaxGroup][8];
-  const float scale = 1.0f / sqrtf((float)HD);
+  // query rows (heads of the group), scaled by 1/sqrt(HD), as hi + lo
+  v8h qh[KS], ql[KS];
+  {
+    const float scale = 1.0f / sqrtf((float)HD);
+    const bool hv = r16 < G;
+    const float* qp = q + ((int64_t)query * n_head + g * G + (hv ? r16 : 0)) * HD + 8 * q4;
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    const float4* qp = reinterpret_cast<const float4*>(
-        q + ((int64_t)query * n_head + g * G + (h < G ? h : 0)) * HD + 8 * sub);
-    const float4 a = qp[0], b = qp[1];
-    const float f = h < G ? scale : 0.f;
-    qr[h][0] = a.x * f; qr[h][1] = a.y * f; qr[h][2] = a.z * f; qr[h][3] = a.w * f;
-    qr[h][4] = b.x * f; qr[h][5] = b.y * f; qr[h][6] = b.z * f; qr[h][7] = b.w * f;
+    for (int ks = 0; ks < KS; ++ks) {
+      const float4 a = *reinterpret_cast<const float4*>(qp + 32 * ks);
+      const float4 b = *reinterpret_cast<const float4*>(qp + 32 * ks + 4);
+      const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = hv ? f[i] * scale : 0.f;
+        const _Float16 hi = (_Float16)x;
+        qh[ks][i] = hi;
+        ql[ks][i] = (_Float16)(x - (float)hi);
+      }
+    }
   }
 
-  // scores
+  // scores -> LDS s_s[h][t] (masked positions -inf)
 #pragma unroll
-  for (int r = 0; r < ROUNDS; ++r) {
-    float kf[8];
-    h8_to_f(kr[r], kf);
-    const int t = slot + PPR * r;
+  for (int j = 0; j < TW; ++j) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      if (h < G) {
-        float a = 0.f;
+    for (int ks = 0; ks < KS; ++ks) {
+      const v8h b = __builtin_bit_cast(v8h, kb[j][ks]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[ks], b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[ks], b, acc, 0, 0, 0);
+    }
+    const int t = wave * PW + 16 * j + r16;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) a += qr[h][j] * kf[j];
-        a = group_sum<LP>(a);
-        if (sub == 0 && t < nt) s_p[h][t] = a;
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int h = 4 * q4 + e;
+      if (h < G) s_s[h][t] = t < nt ? acc[e] : -INFINITY;
     }
   }
   __syncthreads();
 
-  // softmax numerators and sums over this split, one wave per head
+  // softmax numerators (as hi + lo f16) and sums over this split, one wave per head
   for (int h = wave; h < G; h += kAttnThreads / 64) {
     float m = -FLT_MAX;
-    for (int t = lane; t < nt; t += 64) m = fmaxf(m, s_p[h][t]);
+    for (int t = lane; t < nt; t += 64) m = fmaxf(m, s_s[h][t]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     float l = 0.f;
-    for (int t = lane; t < nt; t += 64) {
-      const float e = expf(s_p[h][t] - m);
-      s_p[h][t] = e;
+    for (int t = lane; t < C; t += 64) {
+      const float e = t < nt ? expf(s_s[h][t] - m) : 0.f;
+      const _Float16 hi = (_Float16)e;
+      s_ph[h][t] = hi;
+      s_pl[h][t] = (_Float16)(e - (float)hi);
       l += e;
     }
 #pragma unroll
@@ -162,30 +172,52 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
   }
   __syncthreads();
 
-  // p . V: thread (head h, dims [8d, 8d+8), half) over half of the positions
-  constexpr int NDG = HD / 8;                           // dim groups
-  constexpr int PER = kAttnThreads / (kMaxGroup * NDG); // threads per (h, dim group): 2 for HD 128
-  const int h = tid / (NDG * PER), dgi = (tid / PER) % NDG, part = tid % PER;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (h < G) {
-    for (int t = part; t < nt; t += PER) {
-      const float p = s_p[h][t];
-      float vf[8];
-      h8_to_f(*reinterpret_cast<const uint4*>(s_v + t * HD + 8 * dgi), vf);
+  // o = P V over this split
+  const int tg = wave % (4 / KSPLIT), kp = wave / (4 / KSPLIT);
+  const bool hv = r16 < G;
+  const int hr = hv ? r16 : 0;
+  v4f oacc[TPW];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += p * vf[j];
+  for (int i = 0; i < TPW; ++i) oacc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < PKS; ++s) {
+    const int tb = (kp * PKS + s) * 32 + 8 * q4;  // this lane's 8 positions
+    const v8h zero = {};
+    const v8h ah = hv ? *reinterpret_cast<const v8h*>(&s_ph[hr][tb]) : zero;
+    const v8h al = hv ? *reinterpret_cast<const v8h*>(&s_pl[hr][tb]) : zero;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int d = 16 * (tg * TPW + i) + r16;
+      v8h b;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = s_v[(tb + e) * VST + d];
+      oacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, b, oacc[i], 0, 0, 0);
+      oacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, b, oacc[i], 0, 0, 0);
     }
   }
-  if constexpr (PER > 1) {
+  if constexpr (KSPLIT > 1) {
+    // the second position part hands its sums to the first
+    if (kp == 1) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+      for (int i = 0; i < TPW; ++i) s_red[(tg * TPW + i) * 64 + lane] = oacc[i];
+    }
+    __syncthreads();
+    if (kp == 0) {
 #pragma unroll
-      for (int o = PER / 2; o > 0; o >>= 1) acc[j] += __shfl_xor(acc[j], o, 64);
+      for (int i = 0; i < TPW; ++i) oacc[i] += s_red[(tg * TPW + i) * 64 + lane];
+    }
   }
-  if (h < G && part == 0) {
-    float* dst = part_o + (((int64_t)query * nsplit + split) * n_head + g * G + h) * HD + 8 * dgi;
+  if (kp == 0) {
+    float* dst = part_o + (((int64_t)query * nsplit + split) * n_head + g * G) * HD;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dst[j] = acc[j];
+    for (int i = 0; i < TPW; ++i) {
+      const int d = 16 * (tg * TPW + i) + r16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int h = 4 * q4 + e;
+        if (h < G) dst[(int64_t)h * HD + d] = oacc[i][e];
+      }
+    }
   }
   if (tid < G) {
     const int64_t mi = (((int64_t)query * nsplit + split) * n_head + g * G + tid) * 2;
@@ -344,7 +376,7 @@ __global__ __launch_bounds__(64) void k_argmax_final(const float* __restrict__ p
 // Split geometry: 16384/head_dim positions per split (K and V tiles of
 // 32 KB).  Independent of the device, so workspace sizes are.
 void attn_plan(int head_dim, int max_ctx, int& chunk, int& nsplit) {
-  chunk = 16384 / head_dim;
+  chunk = std::min(256, 16384 / head_dim);
   nsplit = (max_ctx + chunk - 1) / chunk;
 }
 

@@ -180,56 +180,36 @@ __device__ __forceinline__ float unit_q6_k(uint32_t seg, int k, NT_XARGS) {
 constexpr int kXRounds = 8;  // rounds held in registers: inputs up to 4 * 1024 * 8 = 32768 wide
 
 struct XStage {
-  float4 v[kXRounds];  // src
+  float4 v[kXRounds];  // src (times the gains once stage_norm has run)
+  float4 g[kXRounds];  // RMSNorm gains
+  int pos;             // RoPE position
 };
 
 __device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-// Activation accesses.  COH: the vector is written by other workgroups of the
-// same launch, so it is read and written at device scope (relaxed atomics:
-// loads and stores that bypass the non-coherent caches) instead of plainly.
-template <bool COH>
-__device__ __forceinline__ float4 ld_act(const float* p) {
-  if constexpr (COH) {
-    const uint64_t a = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t b = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p) + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_float4(__builtin_bit_cast(float, (uint32_t)a), __builtin_bit_cast(float, (uint32_t)(a >> 32)),
-                       __builtin_bit_cast(float, (uint32_t)b), __builtin_bit_cast(float, (uint32_t)(b >> 32)));
-  } else {
-    return ld_f4(p);
-  }
-}
-template <bool COH>
-__device__ __forceinline__ float ld_act1(const float* p) {
-  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else return *p;
-}
-template <bool COH>
-__device__ __forceinline__ void st_act(float* p, float v) {
-  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else *p = v;
-}
-template <bool COH>
-__device__ __forceinline__ void st_act32(uint32_t* p, uint32_t v) {
-  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else *p = v;
-}
 __device__ __forceinline__ float4 mul4(float4 a, float4 b) { return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w); }
 __device__ __forceinline__ float4 scale4(float4 a, float r) { return make_float4(a.x * r, a.y * r, a.z * r, a.w * r); }
 __device__ __forceinline__ float sq4(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
 
-template <bool COH>
+// Issues the loads of the source (and of the gains, with RMSNorm): thread t
+// holds elements 4 (NT r + t) .. +3 of round r.
 __device__ __forceinline__ void stage_load(const Job& job, const ProArgs& pro, int tid, XStage& st) {
   const int NT = job.nwaves * 64;
 #pragma unroll
   for (int r = 0; r < kXRounds; ++r) {
     const int e = 4 * (NT * r + tid);
-    if (e < job.cols) st.v[r] = ld_act<COH>(pro.src + e);
+    if (e < job.cols) {
+      st.v[r] = ld_f4(pro.src + e);
+      if (pro.gain) st.g[r] = ld_f4(pro.gain + e);
+    }
   }
+  // after the activation's loads, so their latencies overlap
+  st.pos = pro.rope_hd > 0 ? __builtin_nontemporal_load(pro.pos) + pro.pos_add : 0;
 }
 
-// Uses the loaded activation (so its loads are waited for here): the sum of
-// squares of the source.  The gains are applied in stage_finish.
+// Uses the loaded values (so their loads are waited for here, before any
+// weight load is issued): the sum of squares of the source, then the gains
+// applied in place.
 __device__ __forceinline__ float stage_norm(const Job& job, const ProArgs& pro, int tid, XStage& st) {
   const int NT = job.nwaves * 64;
   float ss = 0.f;
@@ -237,7 +217,10 @@ __device__ __forceinline__ float stage_norm(const Job& job, const ProArgs& pro, 
 #pragma unroll
     for (int k = 0; k < kXRounds; ++k) {
       const int e = 4 * (NT * k + tid);
-      if (e < job.cols) ss += sq4(st.v[k]);
+      if (e < job.cols) {
+        ss += sq4(st.v[k]);
+        st.v[k] = mul4(st.v[k], st.g[k]);
+      }
     }
   } else {
     // a use of every loaded value, so the waits happen here
@@ -247,6 +230,7 @@ __device__ __forceinline__ float stage_norm(const Job& job, const ProArgs& pro, 
       if (e < job.cols) ss += st.v[k].x;
     }
   }
+  if (pro.rope_hd > 0) ss += (float)(st.pos & 1) * 0.f;  // the position has arrived too
   return ss;
 }
 
@@ -278,7 +262,6 @@ __device__ __forceinline__ void quant4(const Job& job, int lane, int e, float4 w
 
 
 // ss: this thread's sum of squares from stage_norm.
-template <bool COH>
 __device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro, int tid, XStage& st, float ss) {
   const int NT = job.nwaves * 64, lane = tid & 63;
   const int nround = (job.cols + 4 * NT - 1) / (4 * NT);
@@ -287,7 +270,7 @@ __device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro,
     // rounds past the registers (inputs wider than 32768)
     for (int k = kXRounds; k < nround; ++k) {
       const int e = 4 * (NT * k + tid);
-      if (e < job.cols) ss += sq4(ld_act<COH>(pro.src + e));
+      if (e < job.cols) ss += sq4(ld_f4(pro.src + e));
     }
     ss = wave_sum(ss);
     if (lane == 0) stf(job.red + 4u * (tid >> 6), ss);
@@ -299,15 +282,12 @@ __device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro,
 #pragma unroll
   for (int k = 0; k < kXRounds; ++k) {
     const int e = 4 * (NT * k + tid);
-    if (e < job.cols) {
-      const float4 v = pro.gain ? mul4(st.v[k], ld_f4(pro.gain + e)) : st.v[k];
-      quant4(job, lane, e, scale4(v, r));
-    }
+    if (e < job.cols) quant4(job, lane, e, scale4(st.v[k], r));
   }
   for (int k = kXRounds; k < nround; ++k) {
     const int e = 4 * (NT * k + tid);
     if (e < job.cols) {
-      float4 v = ld_act<COH>(pro.src + e);
+      float4 v = ld_f4(pro.src + e);
       if (pro.gain) v = mul4(v, ld_f4(pro.gain + e));
       quant4(job, lane, e, scale4(v, r));
     }
@@ -316,7 +296,7 @@ __device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro,
     // pair i turns by pos * theta^(-2i/head_dim); the angle is formed in
     // double so large positions keep fp32 accuracy
     for (int i = tid; i < pro.rope_hd / 2; i += NT) {
-      const int pos = *pro.pos + pro.pos_add;
+      const int pos = st.pos;
       const double freq = exp2(-(double)(2 * i) / (double)pro.rope_hd * log2((double)pro.rope_theta));
       const double ang = (double)pos * freq;
       stf(job.rope + 8u * i, (float)cos(ang));
@@ -474,19 +454,19 @@ __device__ __forceinline__ float row_total(const Job& job, int v) {
 
 // Finish the workgroup's rows (after the barrier that follows the stream):
 // thread t of `nthreads` handles output rows (or row pairs) t, t + nthreads, ...
-template <int EPI, bool COH>
+template <int EPI>
 __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, int tid, int nthreads,
                                                const EpiArgs& ea) {
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
     for (int t = tid; t < sh.no; t += nthreads) {
       const float s = row_total(job, t);
       float* y = ea.y + sh.o0 + t;
-      if constexpr (EPI == EPI_RESID) st_act<COH>(y, ld_act1<COH>(y) + s);
-      else st_act<COH>(y, s);
+      if constexpr (EPI == EPI_RESID) *y += s;
+      else *y = s;
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     for (int t = tid; t < sh.no; t += nthreads)
-      st_act<COH>(ea.y + sh.o0 + t, silu(row_total(job, t)) * row_total(job, sh.no + t));
+      ea.y[sh.o0 + t] = silu(row_total(job, t)) * row_total(job, sh.no + t);
   } else if constexpr (EPI == EPI_QKV) {
     const int pos = *ea.pos + ea.pos_add;
     const bool pos_ok = pos >= ea.pos_add && pos < ea.max_ctx;
@@ -504,8 +484,8 @@ __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, 
         b = b2;
       }
       if (R < ea.q_rows) {
-        st_act<COH>(ea.q_out + R, a);
-        st_act<COH>(ea.q_out + R + 1, b);
+        ea.q_out[R] = a;
+        ea.q_out[R + 1] = b;
       } else if (pos_ok) {
         const bool is_k = R < ea.q_rows + ea.kv_rows;
         const int rr = R - ea.q_rows - (is_k ? 0 : ea.kv_rows);
@@ -513,8 +493,8 @@ __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, 
         uint16_t* cache = is_k ? ea.k_cache : ea.v_cache;
         const int64_t off = ((int64_t)kh * ea.max_ctx + pos) * ea.head_dim + dd;  // even: one aligned 32-bit word
         const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-        st_act32<COH>(reinterpret_cast<uint32_t*>(cache + off),
-                      (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16));
+        *reinterpret_cast<uint32_t*>(cache + off) =
+            (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
       }
     }
   }

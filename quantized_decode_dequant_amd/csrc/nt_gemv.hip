@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, Epi
   const uint32_t slab = job.slab + (uint32_t)wave * (uint32_t)(LPL * 1024);
   if (tid == 0) sti32(job.ctl, 0);  // claim counter; the prologue's barrier publishes it
   XStage xst;
-  stage_load<false>(job, pro, tid, xst);
+  stage_load(job, pro, tid, xst);
   const float ss = stage_norm(job, pro, tid, xst);  // the activation has arrived
   uint4 pa[LPL], pb[LPL];
   Seg sa, sb;
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, Epi
   seg_load(sa, lane, pa);
   sb = k_nxt < sh.nseg ? seg_at(job, sh, k_nxt) : seg_null(job);
   seg_load(sb, lane, pb);
-  stage_finish<false>(job, pro, tid, xst, ss);  // ends with a workgroup barrier
+  stage_finish(job, pro, tid, xst, ss);  // ends with a workgroup barrier
   if (k_cur < sh.nseg) {
     XR xr;
     int xslice = -1;
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, Epi
     } while (k_cur < sh.nseg);
   }
   __syncthreads();
-  share_epilogue<EPI, false>(job, sh, tid, job.nwaves * 64, ea);
+  share_epilogue<EPI>(job, sh, tid, job.nwaves * 64, ea);
 }
 
 struct DevInfo {
