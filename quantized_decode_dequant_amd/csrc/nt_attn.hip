@@ -227,15 +227,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
 }
 
 // o[query][h][d] = sum_s e^(m_s - M) o_s[d] / sum_s e^(m_s - M) l_s over the
-// splits that hold positions.  One workgroup per (head, query); the split
-// weights are formed once in LDS and every thread sums its dimension with
-// all loads in flight.
+// splits that hold positions.  One workgroup per (head, 32 dims, query):
+// the split weights are formed in LDS, then thread (d, j) sums splits
+// j, j + 8, ... of dimension d (independent loads, few per thread) and the
+// eight partial sums are added in order.
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                       const int32_t* pos_ptr, int n_head, int head_dim, int chunk,
                                                       int nsplit, int max_ctx, float* __restrict__ o) {
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[4];
-  const int h = blockIdx.x, query = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float s_acc[8][32];
+  const int nch = head_dim / 32;
+  const int h = blockIdx.x / nch, d0 = 32 * (blockIdx.x % nch), query = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pos = *pos_ptr;
   const bool ok = pos >= 0 && pos + query < max_ctx;
   const int n_pos = pos + query + 1;
@@ -261,12 +265,19 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   __syncthreads();
   const float L = s_red[0] + s_red[1] + s_red[2] + s_red[3];
   const float inv = ns > 0 ? 1.0f / L : 0.f;
-  const float* po = part_o + ((int64_t)query * nsplit * n_head + h) * head_dim;
-  for (int d = tid; d < head_dim; d += blockDim.x) {
-    float v = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < ns; ++s) v += s_w[s] * po[(int64_t)s * n_head * head_dim + d];
-    o[((int64_t)query * n_head + h) * head_dim + d] = v * inv;
+  const int dl = tid & 31, j = tid >> 5;
+  const float* po = part_o + ((int64_t)query * nsplit * n_head + h) * head_dim + d0 + dl;
+  const int64_t sst = (int64_t)n_head * head_dim;
+  float v = 0.f;
+#pragma unroll 4
+  for (int s = j; s < ns; s += 8) v += s_w[s] * po[s * sst];
+  s_acc[j][dl] = v;
+  __syncthreads();
+  if (tid < 32) {
+    float t = s_acc[0][tid];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) t += s_acc[k][tid];
+    o[((int64_t)query * n_head + h) * head_dim + d0 + tid] = t * inv;
   }
 }
 
@@ -394,8 +405,8 @@ int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, con
       default: return NT_EUNSUPPORTED;
     }
   }
-  hipLaunchKernelGGL(k_attn_combine, dim3(n_head, n_query), dim3(256), 0, stream, part_o, part_ml, pos, n_head, head_dim,
-                     chunk, nsplit, max_ctx, o);
+  hipLaunchKernelGGL(k_attn_combine, dim3(n_head * (head_dim / 32), n_query), dim3(256), 0, stream, part_o, part_ml,
+                     pos, n_head, head_dim, chunk, nsplit, max_ctx, o);
   const bool ok = hipGetLastError() == hipSuccess;
   trace_after(NT_TRACE_ATTN, stream);
   return ok ? NT_OK : NT_EHIP;

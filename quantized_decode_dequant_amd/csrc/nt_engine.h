@@ -19,6 +19,7 @@ struct XR {
   uint32_t hi[kUnitsPerLane][16], lo[kUnitsPerLane][16];
   float sc[kUnitsPerLane][2];
   int sm[kUnitsPerLane][4];
+  float sf[kUnitsPerLane][2];  // s * (sum of X) over each 32-block (formats with a per-block offset)
 };
 
 __device__ __forceinline__ void load_xr(const Job& job, int slice, int lane, XR& xr) {
@@ -37,6 +38,8 @@ __device__ __forceinline__ void load_xr(const Job& job, int slice, int lane, XR&
       xr.sc[j][1] = ldf(job.x_sc + (e0 >> 3) + 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) xr.sm[j][i] = ldi32(job.x_sum + (e0 >> 2) + 4 * i);
+      xr.sf[j][0] = xr.sc[j][0] * (float)(xr.sm[j][0] + xr.sm[j][1]);
+      xr.sf[j][1] = xr.sc[j][1] * (float)(xr.sm[j][2] + xr.sm[j][3]);
     }
   }
 }
@@ -46,7 +49,8 @@ __device__ __forceinline__ void load_xr(const Job& job, int slice, int lane, XR&
 // `seg` is the LDS byte offset of the segment's first block; XH/XL/XS/XM the
 // lane's activation registers for the unit.
 
-#define NT_XARGS const uint32_t(&xh)[16], const uint32_t(&xl)[16], const float(&xs)[2], const int(&xm)[4]
+#define NT_XARGS \
+  const uint32_t(&xh)[16], const uint32_t(&xl)[16], const float(&xs)[2], const int(&xm)[4], const float(&xf)[2]
 
 // Q8_0: blocks 2k and 2k+1 (the second only if `two`).  w = d*q.
 __device__ __forceinline__ float unit_q8_0(uint32_t seg, int k, bool two, NT_XARGS) {
@@ -102,9 +106,15 @@ __device__ __forceinline__ float unit_q4_0(uint32_t seg, int k, bool two, NT_XAR
 // 32 quant bytes.
 __device__ __forceinline__ float q4k_dot(const uint4& hd, const uint4& q0, const uint4& q1, int c, NT_XARGS) {
   const float d = h2f(hd.x & 0xffffu), dmin = h2f(hd.x >> 16);
-  int scA, mA, scB, mB;
-  q4k_scale_min(hd.y, hd.z, hd.w, 2 * c, scA, mA);
-  q4k_scale_min(hd.y, hd.z, hd.w, 2 * c + 1, scB, mB);
+  // 6-bit scales and mins of sub-blocks 2c and 2c+1, byte-parallel: bytes
+  // 0 and 1 of SC and MN (sub-blocks 0..3 sit in the low six bits of scale
+  // bytes 0..7; 4..7 take four bits from bytes 8..11 and two from the top of
+  // bytes 0..7)
+  const int h = 16 * (c & 1);
+  const uint32_t a0 = hd.y >> h, a1 = hd.z >> h, a2 = hd.w >> h;
+  const bool lowsb = c < 2;
+  const uint32_t SC = lowsb ? (a0 & 0x3F3Fu) : ((a2 & 0x0F0Fu) | ((a0 >> 2) & 0x3030u));
+  const uint32_t MN = lowsb ? (a1 & 0x3F3Fu) : (((a2 >> 4) & 0x0F0Fu) | ((a1 >> 2) & 0x3030u));
   const uint32_t qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
   int AH = 0, AL = 0, BH = 0, BL = 0;
 #pragma unroll
@@ -116,14 +126,15 @@ __device__ __forceinline__ float q4k_dot(const uint4& hd, const uint4& q0, const
     BL = dot4(hi4, xl[8 + i], BL);
   }
   const int SA = (AH << 8) + AL, SB = (BH << 8) + BL;
-  return xs[0] * (d * (float)scA * (float)SA - dmin * (float)mA * (float)(xm[0] + xm[1])) +
-         xs[1] * (d * (float)scB * (float)SB - dmin * (float)mB * (float)(xm[2] + xm[3]));
+  const float t = xs[0] * (float)(SC & 0xffu) * (float)SA + xs[1] * (float)(SC >> 8) * (float)SB;
+  const float u = (float)(MN & 0xffu) * xf[0] + (float)(MN >> 8) * xf[1];
+  return d * t - dmin * u;
 }
 
 __device__ __forceinline__ float unit_q4_k(uint32_t seg, int k, NT_XARGS) {
   const uint32_t blk = seg + 144u * (k >> 2);
   const int c = k & 3;
-  return q4k_dot(ld128(blk), ld128(blk + 16 + 32 * c), ld128(blk + 32 + 32 * c), c, xh, xl, xs, xm);
+  return q4k_dot(ld128(blk), ld128(blk + 16 + 32 * c), ld128(blk + 32 + 32 * c), c, xh, xl, xs, xm, xf);
 }
 
 // Q6_K: unit k covers elements 64p..64p+63 of superblock k/4, p = k%4, i.e.
@@ -375,7 +386,8 @@ __device__ __forceinline__ Seg seg_at(const Job& job, const Share& sh, int k) {
   const int ne = last ? job.last_ne : job.ups * 64;
   sg.nunits = last ? job.last_units : job.ups;
   sg.half = (ne & 63) != 0;
-  const int64_t bytes = last ? (int64_t)(ne / block_elems(sg.fmt)) * block_bytes(sg.fmt) : sbytes;
+  const int64_t lbytes = m == 2 ? job.last_bytes[2] : (m == 1 ? job.last_bytes[1] : job.last_bytes[0]);
+  const int64_t bytes = last ? lbytes : sbytes;
   sg.a = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(ptr) & ~uintptr_t(15));
   sg.d = (uint32_t)(ptr - sg.a);
   sg.nchunks = (int)((sg.d + bytes + 15) >> 4);
@@ -421,6 +433,9 @@ __device__ __forceinline__ void seg_store(uint32_t slab, int lane, const uint4 (
 }
 
 // This lane's part of one segment's dot product, from the slab.
+// FMT >= 0: every segment of the launch has that format (the other paths
+// are compiled out); FMT < 0: the format is read per segment.
+template <int FMT>
 __device__ __forceinline__ float seg_compute(const Seg& sg, uint32_t slab, int lane, const XR& xr) {
   const uint32_t seg = slab + sg.d;
   float acc = 0.f;
@@ -429,14 +444,14 @@ __device__ __forceinline__ float seg_compute(const Seg& sg, uint32_t slab, int l
   for (int j = 0; j < kUnitsPerLane; ++j) {
     const int k = lane + 64 * j;
     if (full || k < sg.nunits) {
-      switch (sg.fmt) {
-        case NT_Q4_K: acc += unit_q4_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j]); break;
-        case NT_Q6_K: acc += unit_q6_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j]); break;
+      switch (FMT >= 0 ? FMT : sg.fmt) {
+        case NT_Q4_K: acc += unit_q4_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j], xr.sf[j]); break;
+        case NT_Q6_K: acc += unit_q6_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j], xr.sf[j]); break;
         case NT_Q8_0:
-          acc += unit_q8_0(seg, k, !(sg.half && k == sg.nunits - 1), xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j]);
+          acc += unit_q8_0(seg, k, !(sg.half && k == sg.nunits - 1), xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j], xr.sf[j]);
           break;
         default:
-          acc += unit_q4_0(seg, k, !(sg.half && k == sg.nunits - 1), xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j]);
+          acc += unit_q4_0(seg, k, !(sg.half && k == sg.nunits - 1), xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j], xr.sf[j]);
           break;
       }
     }
@@ -516,7 +531,7 @@ __device__ __forceinline__ int claim(const Job& job, int lane) {
 // flight).  A step past the wave's last segment only issues its stand-in
 // loads: the stream loop then has a single exit, at the bottom, so the wait
 // analysis never sees the buffers' load order swapped.
-template <int LPL>
+template <int LPL, int FMT>
 __device__ __forceinline__ void stream_step(const Job& job, const Share& sh, int lane, uint32_t slab, int& k_cur,
                                             int& k_nxt, bool& claiming, int& xslice, XR& xr, uint4 (&pre)[LPL],
                                             Seg& sg) {
@@ -535,7 +550,7 @@ __device__ __forceinline__ void stream_step(const Job& job, const Share& sh, int
       load_xr(job, cur.s, lane, xr);
       xslice = cur.s;
     }
-    const float part = wave_sum(seg_compute(cur, slab, lane, xr));
+    const float part = wave_sum(seg_compute<FMT>(cur, slab, lane, xr));
     // every lane writes the same uniform value: no divergent branch
     stf(job.acc + 4u * (uint32_t)(cur.v * job.nslice + cur.s), part);
   }

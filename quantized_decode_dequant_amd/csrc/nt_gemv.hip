@@ -45,7 +45,7 @@ namespace nt {
 namespace {
 
 
-template <int EPI, int LPL>
+template <int EPI, int LPL, int FMT>
 __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, EpiArgs ea) {
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform: keep everything derived from it (segment ids
@@ -71,8 +71,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, Epi
     int xslice = -1;
     bool claiming = k_nxt < sh.nseg;
     do {
-      stream_step<LPL>(job, sh, lane, slab, k_cur, k_nxt, claiming, xslice, xr, pa, sa);
-      stream_step<LPL>(job, sh, lane, slab, k_cur, k_nxt, claiming, xslice, xr, pb, sb);
+      stream_step<LPL, FMT>(job, sh, lane, slab, k_cur, k_nxt, claiming, xslice, xr, pa, sa);
+      stream_step<LPL, FMT>(job, sh, lane, slab, k_cur, k_nxt, claiming, xslice, xr, pb, sb);
     } while (k_cur < sh.nseg);
   }
   __syncthreads();
@@ -96,20 +96,40 @@ DevInfo& dev_info() {
   return d;
 }
 
-template <int EPI, int LPL>
-int launch_lpl(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t stream) {
+template <int EPI, int LPL, int FMT>
+int launch_k(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_qgemv<EPI, LPL>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    if (hipFuncSetAttribute((const void*)k_qgemv<EPI, LPL, FMT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             160 * 1024) != hipSuccess)
       return NT_EHIP;
     attr_set = true;
   }
   trace_before(EPI, stream);
-  hipLaunchKernelGGL((k_qgemv<EPI, LPL>), dim3(job.grid), dim3(64 * job.nwaves), job.lds_bytes, stream, job, pro, ea);
+  hipLaunchKernelGGL((k_qgemv<EPI, LPL, FMT>), dim3(job.grid), dim3(64 * job.nwaves), job.lds_bytes, stream, job, pro,
+                     ea);
   const bool ok = hipGetLastError() == hipSuccess;
   trace_after(EPI, stream);
   return ok ? NT_OK : NT_EHIP;
+}
+
+// A launch whose matrices share one format runs a kernel compiled for that
+// format where one exists for its loads per lane (the segment size a format
+// reaches sets them); otherwise the kernel that reads the format per segment.
+template <int EPI, int LPL>
+int launch_lpl(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t stream) {
+  int f = job.fmt[0];
+  for (int m = 1; m < job.nmat; ++m)
+    if (job.fmt[m] != f) f = -1;
+  if constexpr (LPL == 3) {
+    if (f == NT_Q4_K) return launch_k<EPI, LPL, NT_Q4_K>(job, pro, ea, stream);
+    if (f == NT_Q4_0) return launch_k<EPI, LPL, NT_Q4_0>(job, pro, ea, stream);
+  }
+  if constexpr (LPL <= 4) {
+    if (f == NT_Q6_K) return launch_k<EPI, LPL, NT_Q6_K>(job, pro, ea, stream);
+  }
+  if (f == NT_Q8_0) return launch_k<EPI, LPL, NT_Q8_0>(job, pro, ea, stream);
+  return launch_k<EPI, LPL, -1>(job, pro, ea, stream);
 }
 
 template <int EPI>
@@ -166,6 +186,7 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
   job.last_ne = cols - (job.nslice - 1) * ups * 64;
   job.last_units = (job.last_ne + 63) / 64;
   for (int m = 0; m < nmat; ++m) job.slice_bytes[m] = (int64_t)(ups * 64 / block_elems(fmt[m])) * block_bytes(fmt[m]);
+  for (int m = 0; m < nmat; ++m) job.last_bytes[m] = (int64_t)(job.last_ne / block_elems(fmt[m])) * block_bytes(fmt[m]);
   // loads per lane: the largest segment plus its misalignment, in 1 KB rounds
   int64_t seg_max = 0;
   for (int m = 0; m < nmat; ++m)

@@ -54,6 +54,7 @@ struct Job {
   int rows[kMaxMats];
   int row_base[kMaxMats];     // first output row of each matrix (concatenated outputs)
   int64_t slice_bytes[kMaxMats];  // bytes of one full column slice of a row
+  int64_t last_bytes[kMaxMats];   // bytes of the last column slice of a row
   int orows;                  // output rows
   int unit;                   // rows are handed to workgroups in multiples of this (2 with pairs)
   int ups;                    // units per slice
