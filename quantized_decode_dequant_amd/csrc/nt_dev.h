@@ -25,6 +25,14 @@ __device__ __forceinline__ float h2f(uint32_t bits) { return (float)__builtin_bi
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
+// The first product of a chain: the three-operand form with a zero
+// accumulator (the builtin with c = 0 becomes a register clear plus the
+// two-operand form).
+__device__ __forceinline__ int dot4z(uint32_t a, uint32_t b) {
+  int r;
+  asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 
 // N dwords starting at an LDS byte offset that is only 2-byte aligned:
 // read N+1 aligned dwords and funnel-shift them.

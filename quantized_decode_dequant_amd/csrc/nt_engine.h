@@ -62,9 +62,9 @@ __device__ __forceinline__ float unit_q8_0(uint32_t seg, int k, bool two, NT_XAR
     const float d = h2f(ld16(blk));
     uint32_t q[8];
     ld_unaligned<8>(blk + 2, q);
-    int H = 0, L = 0;
+    int H = dot4z(q[0], xh[8 * b]), L = dot4z(q[0], xl[8 * b]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 1; i < 8; ++i) {
       H = dot4(q[i], xh[8 * b + i], H);
       L = dot4(q[i], xl[8 * b + i], L);
     }
@@ -88,8 +88,8 @@ __device__ __forceinline__ float unit_q4_0(uint32_t seg, int k, bool two, NT_XAR
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t lo4 = q[i] & 0x0F0F0F0Fu, hi4 = (q[i] >> 4) & 0x0F0F0F0Fu;
-      H = dot4(lo4, xh[8 * b + i], H);
-      L = dot4(lo4, xl[8 * b + i], L);
+      H = i == 0 ? dot4z(lo4, xh[8 * b]) : dot4(lo4, xh[8 * b + i], H);
+      L = i == 0 ? dot4z(lo4, xl[8 * b]) : dot4(lo4, xl[8 * b + i], L);
       H = dot4(hi4, xh[8 * b + 4 + i], H);
       L = dot4(hi4, xl[8 * b + 4 + i], L);
     }
@@ -120,10 +120,10 @@ __device__ __forceinline__ float q4k_dot(const uint4& hd, const uint4& q0, const
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t lo4 = qv[i] & 0x0F0F0F0Fu, hi4 = (qv[i] >> 4) & 0x0F0F0F0Fu;
-    AH = dot4(lo4, xh[i], AH);
-    AL = dot4(lo4, xl[i], AL);
-    BH = dot4(hi4, xh[8 + i], BH);
-    BL = dot4(hi4, xl[8 + i], BL);
+    AH = i == 0 ? dot4z(lo4, xh[0]) : dot4(lo4, xh[i], AH);
+    AL = i == 0 ? dot4z(lo4, xl[0]) : dot4(lo4, xl[i], AL);
+    BH = i == 0 ? dot4z(hi4, xh[8]) : dot4(hi4, xh[8 + i], BH);
+    BL = i == 0 ? dot4z(hi4, xl[8]) : dot4(hi4, xl[8 + i], BL);
   }
   const int SA = (AH << 8) + AL, SB = (BH << 8) + BL;
   const float t = xs[0] * (float)(SC & 0xffu) * (float)SA + xs[1] * (float)(SC >> 8) * (float)SB;
@@ -158,10 +158,11 @@ __device__ __forceinline__ float unit_q6_k(uint32_t seg, int k, NT_XARGS) {
     const uint32_t hb = qh[i] >> sh;
     const uint32_t a = ((qa[i] >> sh) & 0x0F0F0F0Fu) | ((hb << 4) & 0x30303030u);
     const uint32_t b = ((qb[i] >> sh) & 0x0F0F0F0Fu) | ((hb << 2) & 0x30303030u);
-    H[i >> 2] = dot4(a, xh[i], H[i >> 2]);
-    L[i >> 2] = dot4(a, xl[i], L[i >> 2]);
-    H[2 + (i >> 2)] = dot4(b, xh[8 + i], H[2 + (i >> 2)]);
-    L[2 + (i >> 2)] = dot4(b, xl[8 + i], L[2 + (i >> 2)]);
+    const bool first = (i & 3) == 0;
+    H[i >> 2] = first ? dot4z(a, xh[i]) : dot4(a, xh[i], H[i >> 2]);
+    L[i >> 2] = first ? dot4z(a, xl[i]) : dot4(a, xl[i], L[i >> 2]);
+    H[2 + (i >> 2)] = first ? dot4z(b, xh[8 + i]) : dot4(b, xh[8 + i], H[2 + (i >> 2)]);
+    L[2 + (i >> 2)] = first ? dot4z(b, xl[8 + i]) : dot4(b, xl[8 + i], L[2 + (i >> 2)]);
   }
   float acc = 0.f;
 #pragma unroll
@@ -434,7 +435,8 @@ __device__ __forceinline__ void seg_store(uint32_t slab, int lane, const uint4 (
 
 // This lane's part of one segment's dot product, from the slab.
 // FMT >= 0: every segment of the launch has that format (the other paths
-// are compiled out); FMT < 0: the format is read per segment.
+// are compiled out); kFmtK46: Q4_K and Q6_K segments only (the K-quant mix
+// of a Q/K/V launch); other FMT < 0: any format, read per segment.
 template <int FMT>
 __device__ __forceinline__ float seg_compute(const Seg& sg, uint32_t slab, int lane, const XR& xr) {
   const uint32_t seg = slab + sg.d;
@@ -444,7 +446,7 @@ __device__ __forceinline__ float seg_compute(const Seg& sg, uint32_t slab, int l
   for (int j = 0; j < kUnitsPerLane; ++j) {
     const int k = lane + 64 * j;
     if (full || k < sg.nunits) {
-      switch (FMT >= 0 ? FMT : sg.fmt) {
+      switch (FMT >= 0 ? FMT : (FMT == kFmtK46 ? (sg.fmt == NT_Q6_K ? NT_Q6_K : NT_Q4_K) : sg.fmt)) {
         case NT_Q4_K: acc += unit_q4_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j], xr.sf[j]); break;
         case NT_Q6_K: acc += unit_q6_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j], xr.sf[j]); break;
         case NT_Q8_0:

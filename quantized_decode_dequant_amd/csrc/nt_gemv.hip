@@ -119,8 +119,11 @@ int launch_k(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t 
 template <int EPI, int LPL>
 int launch_lpl(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t stream) {
   int f = job.fmt[0];
-  for (int m = 1; m < job.nmat; ++m)
+  bool k46 = true;
+  for (int m = 0; m < job.nmat; ++m) {
     if (job.fmt[m] != f) f = -1;
+    k46 = k46 && (job.fmt[m] == NT_Q4_K || job.fmt[m] == NT_Q6_K);
+  }
   if constexpr (LPL == 3) {
     if (f == NT_Q4_K) return launch_k<EPI, LPL, NT_Q4_K>(job, pro, ea, stream);
     if (f == NT_Q4_0) return launch_k<EPI, LPL, NT_Q4_0>(job, pro, ea, stream);
@@ -129,6 +132,9 @@ int launch_lpl(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_
     if (f == NT_Q6_K) return launch_k<EPI, LPL, NT_Q6_K>(job, pro, ea, stream);
   }
   if (f == NT_Q8_0) return launch_k<EPI, LPL, NT_Q8_0>(job, pro, ea, stream);
+  if constexpr (LPL <= 4) {
+    if (k46) return launch_k<EPI, LPL, kFmtK46>(job, pro, ea, stream);
+  }
   return launch_k<EPI, LPL, -1>(job, pro, ea, stream);
 }
 

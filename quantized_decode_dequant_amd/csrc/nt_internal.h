@@ -11,6 +11,7 @@ namespace nt {
 
 constexpr int kMaxWaves = 16;     // waves per workgroup of the GEMV engine (one workgroup per CU)
 constexpr int kMaxThreads = 64 * kMaxWaves;
+constexpr int kFmtK46 = -2;  // kernel variant for launches that mix only Q4_K and Q6_K matrices
 constexpr int kUnitsPerLane = 1;  // 64-weight column units a lane owns in one column slice
 constexpr int kSliceUnits = 64 * kUnitsPerLane;  // column units per slice (4096 weights)
 constexpr int kSlabLoads = 5;     // 16-B loads per lane for the largest segment (Q8_0: 4352 B + alignment)
