@@ -413,19 +413,17 @@ __device__ __forceinline__ Seg seg_null(const Job& job) {
 }
 
 // Every lane issues exactly LPL loads (lanes past the segment's end re-read
-// its first chunk), so the number of loads in flight is the same on every
+// its last chunk), so the number of loads in flight is the same on every
 // path and the waits before the slab store count exactly the older segment.
 template <int LPL>
 __device__ __forceinline__ void seg_load(const Seg& sg, int lane, uint4 (&pre)[LPL]) {
+  const uint32_t last = 16u * (uint32_t)(sg.nchunks - 1);
 #pragma unroll
-  for (int i = 0; i < LPL; ++i) {
-    const int c = lane + 64 * i;
-    pre[i] = load_chunk(sg.a + 16 * (c < sg.nchunks ? c : 0));
-  }
+  for (int i = 0; i < LPL; ++i) pre[i] = load_chunk(sg.a + min(16u * (uint32_t)(lane + 64 * i), last));
 }
 
 // The slab holds LPL KB, so every chunk slot is written (slots past the
-// segment's end get the re-read first chunk, which nothing reads): no
+// segment's end get the re-read last chunk, which nothing reads): no
 // divergent branch.
 template <int LPL>
 __device__ __forceinline__ void seg_store(uint32_t slab, int lane, const uint4 (&pre)[LPL]) {
@@ -517,32 +515,39 @@ __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, 
   }
 }
 
-// Next segment for this wave: a claim on the workgroup's LDS counter.  Ids
-// below 2 * nwaves were handed out statically (wave w: w and w + nwaves).
-__device__ __forceinline__ int claim(const Job& job, int lane) {
+// Next two segments for this wave: one claim of two consecutive ids on the
+// workgroup's LDS counter.  Ids below 2 * nwaves were handed out statically
+// (wave w: w and w + nwaves).
+__device__ __forceinline__ int claim2(const Job& job, int lane) {
   int old = 0;
   int* ctr = static_cast<int*>(__builtin_assume_aligned(nt_smem + job.ctl, 16));
-  if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (lane == 0) old = __hip_atomic_fetch_add(ctr, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   return 2 * job.nwaves + __builtin_amdgcn_readfirstlane(old);
 }
 
 // One step of the stream: the segment in buffer `pre` (described by `sg`,
-// id k_cur) is stored to the slab, a newly claimed segment's loads are
-// issued into `pre`, and the stored segment is computed into its (row,
-// slice) partial sum.  The other buffer holds segment k_nxt (already in
-// flight).  A step past the wave's last segment only issues its stand-in
+// id k_cur) is stored to the slab, the next segment's loads are issued into
+// `pre`, and the stored segment is computed into its (row, slice) partial
+// sum.  The other buffer holds segment k_nxt (already in flight).  Ids are
+// claimed two at a time: the first step of a pair claims, the second takes
+// the spare.  A step past the wave's last segment only issues its stand-in
 // loads: the stream loop then has a single exit, at the bottom, so the wait
 // analysis never sees the buffers' load order swapped.
-template <int LPL, int FMT>
+template <int LPL, int FMT, bool FIRST>
 __device__ __forceinline__ void stream_step(const Job& job, const Share& sh, int lane, uint32_t slab, int& k_cur,
-                                            int& k_nxt, bool& claiming, int& xslice, XR& xr, uint4 (&pre)[LPL],
-                                            Seg& sg) {
+                                            int& k_nxt, int& k_spare, bool& claiming, int& xslice, XR& xr,
+                                            uint4 (&pre)[LPL], Seg& sg) {
   const Seg cur = sg;
   const bool valid = k_cur < sh.nseg;
   seg_store(slab, lane, pre);
   int k2 = sh.nseg;
   if (claiming) {
-    k2 = claim(job, lane);
+    if constexpr (FIRST) {
+      k2 = claim2(job, lane);
+      k_spare = k2 + 1;
+    } else {
+      k2 = k_spare;
+    }
     claiming = k2 < sh.nseg;
   }
   sg = k2 < sh.nseg ? seg_at(job, sh, k2) : seg_null(job);

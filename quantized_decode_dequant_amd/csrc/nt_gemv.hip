@@ -70,9 +70,10 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, Epi
     XR xr;
     int xslice = -1;
     bool claiming = k_nxt < sh.nseg;
+    int k_spare = sh.nseg;
     do {
-      stream_step<LPL, FMT>(job, sh, lane, slab, k_cur, k_nxt, claiming, xslice, xr, pa, sa);
-      stream_step<LPL, FMT>(job, sh, lane, slab, k_cur, k_nxt, claiming, xslice, xr, pb, sb);
+      stream_step<LPL, FMT, true>(job, sh, lane, slab, k_cur, k_nxt, k_spare, claiming, xslice, xr, pa, sa);
+      stream_step<LPL, FMT, false>(job, sh, lane, slab, k_cur, k_nxt, k_spare, claiming, xslice, xr, pb, sb);
     } while (k_cur < sh.nseg);
   }
   __syncthreads();
