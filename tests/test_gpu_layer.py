@@ -73,6 +73,35 @@ def test_layer_group8_batch1(fmts, n_past):
     check(got, ref, kc, vc, li, n_past, 1)
 
 
+# head sizes and group sizes of the attention tile shapes (head_dim 32: two
+# waves per output tile; 64: one; 128: two tiles per wave; 256: four), with
+# 1, 2, 4 and 8 query heads per kv head
+ATTN_SHAPES = {
+    "hd64_g1": wl.LayerShape(hidden=512, n_head=8, n_kv_head=8, head_dim=64, ffn=1024),
+    "hd64_g2": wl.LayerShape(hidden=512, n_head=8, n_kv_head=4, head_dim=64, ffn=1024),
+    "hd256_g4": wl.LayerShape(hidden=1024, n_head=4, n_kv_head=1, head_dim=256, ffn=1024),
+    "hd256_g8": wl.LayerShape(hidden=2048, n_head=8, n_kv_head=1, head_dim=256, ffn=1024),
+    "hd32_g8": wl.LayerShape(hidden=512, n_head=16, n_kv_head=2, head_dim=32, ffn=1024),
+    "hd128_g1": wl.LayerShape(hidden=512, n_head=4, n_kv_head=4, head_dim=128, ffn=1024),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ATTN_SHAPES))
+@pytest.mark.parametrize("n_past", [0, 70, 300])
+def test_layer_attention_shapes(name, n_past):
+    # every split holds at most 256 positions: 300 cached positions span two
+    # or more splits at every head size, 70 a single ragged one
+    got, ref, kc, vc, li = run_layer(ATTN_SHAPES[name], wl.ALL_Q8_0, wl.W_TEST, 11, 320, n_past, 1)
+    check(got, ref, kc, vc, li, n_past, 1)
+
+
+@pytest.mark.parametrize("name", ["hd64_g2", "hd256_g8"])
+def test_layer_attention_shapes_verify_tokens(name):
+    # three tokens in one pass: token i attends to positions 0..pos+i
+    got, ref, kc, vc, li = run_layer(ATTN_SHAPES[name], wl.ALL_Q4_0, wl.W_TEST, 12, 320, 130, 3)
+    check(got, ref, kc, vc, li, 130, 3)
+
+
 def test_layer_group8_repeat_calls_share_workspace():
     # the launch leaves its barrier counters at zero: consecutive calls on one
     # workspace give identical results, and a new workspace gives the same
