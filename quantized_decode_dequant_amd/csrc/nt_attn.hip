@@ -16,7 +16,7 @@
 
 #include <algorithm>
 
-#include "nt_internal.h"
+#include "nt_dev.h"
 
 namespace nt {
 namespace {
@@ -153,8 +153,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
   for (int h = wave; h < G; h += kAttnThreads / 64) {
     float m = -FLT_MAX;
     for (int t = lane; t < nt; t += 64) m = fmaxf(m, s_s[h][t]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    m = fmaxf(wave_max(m), -FLT_MAX);
     float l = 0.f;
     for (int t = lane; t < C; t += 64) {
       const float e = t < nt ? expf(s_s[h][t] - m) : 0.f;
@@ -163,8 +162,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
       s_pl[h][t] = (_Float16)(e - (float)hi);
       l += e;
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+    l = wave_sum(l);
     if (lane == 0) {
       s_m[h] = m;
       s_l[h] = l;
@@ -228,14 +226,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
 
 // o[query][h][d] = sum_s e^(m_s - M) o_s[d] / sum_s e^(m_s - M) l_s over the
 // splits that hold positions.  One workgroup per (head, 32 dims, query):
-// the split weights are formed in LDS, then thread (d, j) sums splits
-// j, j + 8, ... of dimension d (independent loads, few per thread) and the
-// eight partial sums are added in order.
+// thread (d, j) sums splits j, j + 8, ... of dimension d and the eight
+// partial sums are added in order.  Once the position is known every load
+// is issued at once (each thread's first eight splits of o with the (m, l)
+// pairs), so the kernel waits on memory twice.
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                       const int32_t* pos_ptr, int n_head, int head_dim, int chunk,
                                                       int nsplit, int max_ctx, float* __restrict__ o) {
+  constexpr int kPre = 8;  // splits per thread held in registers
   __shared__ float s_w[kMaxSplits];
-  __shared__ float s_red[4];
+  __shared__ float s_red[8];
   __shared__ float s_acc[8][32];
   const int nch = head_dim / 32;
   const int h = blockIdx.x / nch, d0 = 32 * (blockIdx.x % nch), query = blockIdx.y;
@@ -245,32 +245,51 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   const int n_pos = pos + query + 1;
   const int ns = ok ? min(nsplit, (n_pos + chunk - 1) / chunk) : 0;
   const float* ml = part_ml + ((int64_t)query * nsplit * n_head + h) * 2;
+  const int dl = tid & 31, j = tid >> 5;
+  const float* po = part_o + ((int64_t)query * nsplit * n_head + h) * head_dim + d0 + dl;
+  const int64_t sst = (int64_t)n_head * head_dim;
+  float ov[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int s = j + 8 * k;
+    ov[k] = s < ns ? po[s * sst] : 0.f;
+  }
+  float m0 = -FLT_MAX, l0 = 0.f;
+  if (tid < ns) {
+    m0 = ml[(int64_t)tid * n_head * 2];
+    l0 = ml[(int64_t)tid * n_head * 2 + 1];
+  }
   // M = max over splits
-  float m = -FLT_MAX;
-  for (int s = tid; s < ns; s += blockDim.x) m = fmaxf(m, ml[(int64_t)s * n_head * 2]);
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  float m = m0;
+  for (int s = tid + blockDim.x; s < ns; s += blockDim.x) m = fmaxf(m, ml[(int64_t)s * n_head * 2]);
+  m = wave_max(m);
   if (lane == 0) s_red[wave] = m;
   __syncthreads();
   m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  __syncthreads();
   // weights e^(m_s - M) and L = sum of weighted l_s
   float lsum = 0.f;
-  for (int s = tid; s < ns; s += blockDim.x) {
+  if (tid < ns) {
+    const float w = expf(m0 - m);
+    s_w[tid] = w;
+    lsum = w * l0;
+  }
+  for (int s = tid + blockDim.x; s < ns; s += blockDim.x) {
     const float w = expf(ml[(int64_t)s * n_head * 2] - m);
     s_w[s] = w;
     lsum += w * ml[(int64_t)s * n_head * 2 + 1];
   }
-  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
-  if (lane == 0) s_red[wave] = lsum;
+  lsum = wave_sum(lsum);
+  if (lane == 0) s_red[4 + wave] = lsum;
   __syncthreads();
-  const float L = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  const float L = s_red[4] + s_red[5] + s_red[6] + s_red[7];
   const float inv = ns > 0 ? 1.0f / L : 0.f;
-  const int dl = tid & 31, j = tid >> 5;
-  const float* po = part_o + ((int64_t)query * nsplit * n_head + h) * head_dim + d0 + dl;
-  const int64_t sst = (int64_t)n_head * head_dim;
   float v = 0.f;
-#pragma unroll 4
-  for (int s = j; s < ns; s += 8) v += s_w[s] * po[s * sst];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int s = j + 8 * k;
+    if (s < ns) v += s_w[s] * ov[k];
+  }
+  for (int s = j + 8 * kPre; s < ns; s += 8) v += s_w[s] * po[s * sst];
   s_acc[j][dl] = v;
   __syncthreads();
   if (tid < 32) {

@@ -1,4 +1,4 @@
-// Device helpers shared by the GEMV engine and the small-M GEMM: LDS
+// Device helpers shared by the GEMV engine, the small-M GEMM and attention: LDS
 // accessors on the dynamic LDS block, DPP reductions, non-temporal weight
 // loads and the GGUF Q4_K scale unpacking.
 #pragma once
@@ -60,6 +60,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_shift<0x118, 0xf>(v);  // row_shr:8
   v += dpp_shift<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
   v += dpp_shift<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Maximum over the 64 lanes of a wave, the same scan with -inf for lanes
+// that receive nothing.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_shift_max(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, -__builtin_huge_valf()),
+                                                                __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_shift_max<0x111, 0xf>(v));
+  v = fmaxf(v, dpp_shift_max<0x112, 0xf>(v));
+  v = fmaxf(v, dpp_shift_max<0x114, 0xf>(v));
+  v = fmaxf(v, dpp_shift_max<0x118, 0xf>(v));
+  v = fmaxf(v, dpp_shift_max<0x142, 0xa>(v));
+  v = fmaxf(v, dpp_shift_max<0x143, 0xc>(v));
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
