@@ -274,23 +274,32 @@ __device__ __forceinline__ void quant4(const Job& job, int lane, int e, float4 w
 
 
 // ss: this thread's sum of squares from stage_norm.
-__device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro, int tid, XStage& st, float ss) {
+// The RMSNorm factor r = 1/sqrt(mean(src^2) + eps), or 1 without norm.  It
+// runs before the wave issues any weight load: the workgroup barrier of the
+// reduction then waits for no wave that is stalled issuing its weight
+// requests behind the launch's burst (measured ~2 us per launch when it ran
+// after the prefetch).
+__device__ __forceinline__ float stage_scale(const Job& job, const ProArgs& pro, int tid, float ss) {
+  if (!pro.gain) return 1.0f;
   const int NT = job.nwaves * 64, lane = tid & 63;
   const int nround = (job.cols + 4 * NT - 1) / (4 * NT);
-  float r = 1.0f;
-  if (pro.gain) {
-    // rounds past the registers (inputs wider than 32768)
-    for (int k = kXRounds; k < nround; ++k) {
-      const int e = 4 * (NT * k + tid);
-      if (e < job.cols) ss += sq4(ld_f4(pro.src + e));
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) stf(job.red + 4u * (tid >> 6), ss);
-    __syncthreads();
-    float tot = 0.f;
-    for (int w = 0; w < job.nwaves; ++w) tot += ldf(job.red + 4u * w);
-    r = 1.0f / sqrtf(tot / (float)job.cols + pro.eps);
+  // rounds past the registers (inputs wider than 4 * 64 * nwaves * kXRounds)
+  for (int k = kXRounds; k < nround; ++k) {
+    const int e = 4 * (NT * k + tid);
+    if (e < job.cols) ss += sq4(ld_f4(pro.src + e));
   }
+  ss = wave_sum(ss);
+  if (lane == 0) stf(job.red + 4u * (tid >> 6), ss);
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < job.nwaves; ++w) tot += ldf(job.red + 4u * w);
+  return 1.0f / sqrtf(tot / (float)job.cols + pro.eps);
+}
+
+// r: the factor from stage_scale.
+__device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro, int tid, XStage& st, float r) {
+  const int NT = job.nwaves * 64, lane = tid & 63;
+  const int nround = (job.cols + 4 * NT - 1) / (4 * NT);
 #pragma unroll
   for (int k = 0; k < kXRounds; ++k) {
     const int e = 4 * (NT * k + tid);

@@ -57,6 +57,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, Epi
   XStage xst;
   stage_load(job, pro, tid, xst);
   const float ss = stage_norm(job, pro, tid, xst);  // the activation has arrived
+  const float r = stage_scale(job, pro, tid, ss);
   uint4 pa[LPL], pb[LPL];
   Seg sa, sb;
   int k_cur = wave, k_nxt = wave + job.nwaves;
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, Epi
   seg_load(sa, lane, pa);
   sb = k_nxt < sh.nseg ? seg_at(job, sh, k_nxt) : seg_null(job);
   seg_load(sb, lane, pb);
-  stage_finish(job, pro, tid, xst, ss);  // ends with a workgroup barrier
+  stage_finish(job, pro, tid, xst, r);  // ends with a workgroup barrier
   if (k_cur < sh.nseg) {
     XR xr;
     int xslice = -1;
