@@ -328,13 +328,18 @@ __device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro,
 }
 
 // ----------------------------------------------------------- segment stream
-// Workgroup b's share: output rows [o0, o0 + no); `nv` segment rows (twice
-// the output rows with paired matrices) times `nslice` slices.  Segment id
-// k = s * nv + v (slice-major), so a wave's successive claims mostly stay in
-// one slice and its activation registers rarely change.  Everything here is
-// wave-uniform and lives in scalar registers.
+// Workgroup b's share: units (rows, or row pairs for RoPE) b, b + G, b + 2G,
+// ... of the G workgroups, interleaved so that every share takes the same
+// mix of the launch's matrices (Q/K/V rows differ in format and size) and
+// the same spread over the weight bytes.  Local row t of the share is global
+// row srow(t); `nv` segment rows (twice the output rows with paired
+// matrices) times `nslice` slices.  Segment id k = s * nv + v (slice-major),
+// so a wave's successive claims mostly stay in one slice and its activation
+// registers rarely change.  Everything here is wave-uniform and lives in
+// scalar registers.
 struct Share {
-  int o0, no;      // first output row, output rows
+  int o0, no;      // global row of local row 0, output rows
+  int ostep;       // global rows between consecutive units of the share
   int nv;          // segment rows
   int nseg;        // segments
   uint32_t magic;  // floor((2^32 - 1) / nv): slice of a segment id by a multiply
@@ -343,14 +348,19 @@ struct Share {
 __device__ __forceinline__ Share share_of(const Job& job, int b) {
   Share sh;
   const bool big = b < job.wg_rem;
-  const int u0 = b * job.wg_base + (big ? b : job.wg_rem);
   const int nu = job.wg_base + (big ? 1 : 0);
-  sh.o0 = u0 * job.unit;
+  sh.o0 = b * job.unit;
+  sh.ostep = job.grid * job.unit;
   sh.no = nu * job.unit;
   sh.nv = job.paired ? 2 * sh.no : sh.no;
   sh.nseg = sh.nv * job.nslice;
   sh.magic = big ? job.magic[1] : job.magic[0];
   return sh;
+}
+
+// Global row of local row t of a share.
+__device__ __forceinline__ int srow(const Job& job, const Share& sh, int t) {
+  return job.unit == 2 ? sh.o0 + (t >> 1) * sh.ostep + (t & 1) : sh.o0 + t * sh.ostep;
 }
 
 // Byte range of one segment and where its data sits in the slab.
@@ -380,9 +390,9 @@ __device__ __forceinline__ Seg seg_at(const Job& job, const Share& sh, int k) {
   if (job.paired) {
     const bool up = v >= sh.no;
     m = up ? 1 : 0;
-    row = sh.o0 + (up ? v - sh.no : v);
+    row = srow(job, sh, up ? v - sh.no : v);
   } else {
-    row = sh.o0 + v;
+    row = srow(job, sh, v);
     m = (job.nmat > 2 && row >= job.row_base[2]) ? 2 : ((job.nmat > 1 && row >= job.row_base[1]) ? 1 : 0);
     row -= m == 2 ? job.row_base[2] : (m == 1 ? job.row_base[1] : 0);
   }
@@ -484,19 +494,19 @@ __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, 
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
     for (int t = tid; t < sh.no; t += nthreads) {
       const float s = row_total(job, t);
-      float* y = ea.y + sh.o0 + t;
+      float* y = ea.y + srow(job, sh, t);
       if constexpr (EPI == EPI_RESID) *y += s;
       else *y = s;
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     for (int t = tid; t < sh.no; t += nthreads)
-      ea.y[sh.o0 + t] = silu(row_total(job, t)) * row_total(job, sh.no + t);
+      ea.y[srow(job, sh, t)] = silu(row_total(job, t)) * row_total(job, sh.no + t);
   } else if constexpr (EPI == EPI_QKV) {
     const int pos = *ea.pos + ea.pos_add;
     const bool pos_ok = pos >= ea.pos_add && pos < ea.max_ctx;
     if (!pos_ok && ea.err && tid == 0) *ea.err = 1;
     for (int t = tid; 2 * t < sh.no; t += nthreads) {
-      const int R = sh.o0 + 2 * t;  // even row of an adjacent pair (concatenated Q, K, V rows)
+      const int R = srow(job, sh, 2 * t);  // even row of an adjacent pair (concatenated Q, K, V rows)
       float a = row_total(job, 2 * t), b = row_total(job, 2 * t + 1);
       const int dd = R % ea.head_dim;
       if (R < ea.q_rows + ea.kv_rows) {

@@ -15,12 +15,13 @@
 //   columns   A lane owns one 64-weight column unit of the current column
 //             slice (4096 weights) and keeps its staged activation in
 //             registers, reloaded only when the wave moves to another slice.
-//   schedule  Workgroup b owns a contiguous range of output rows; its work
-//             is a list of segments (one row of one matrix within one column
-//             slice: a contiguous byte range), slice-major.  Waves claim
-//             segments one at a time from an LDS counter, so the waves that
-//             the SIMD arbiter favours simply take more of them and all
-//             finish together.
+//   schedule  Workgroup b owns output rows (or RoPE row pairs) b, b + G,
+//             b + 2G, ... of the G workgroups, so every share holds the same
+//             mix of matrices; its work is a list of segments (one row of
+//             one matrix within one column slice: a contiguous byte range),
+//             slice-major.  Waves claim segments two at a time from an LDS
+//             counter, so the waves that the SIMD arbiter favours simply take
+//             more of them and all finish together.
 //   stream    Segments move HBM -> registers with 16-byte coalesced
 //             non-temporal loads, two in flight per wave while the previous
 //             one is written to the wave's LDS slab and computed: lanes read

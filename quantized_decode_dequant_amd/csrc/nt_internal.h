@@ -41,11 +41,11 @@ __host__ __device__ inline int block_bytes(int fmt) {
 //    e.g. Q, K, V), or, with `paired`, the rows of W[0] each together with
 //    the same row of W[1] (SwiGLU needs gate and up).  With `pairs`, rows
 //    are handed out in even-aligned pairs (RoPE rotates adjacent rows).
-//  - Workgroup b owns a contiguous range of output rows.  Its work is the
-//    list of segments (one row of one matrix within one column slice: a
-//    contiguous byte range), slice-major; its waves claim segments one at a
-//    time from a counter in LDS, so waves that the SIMD arbiter favours take
-//    more and all finish together.  Each segment's dot product lands in an
+//  - Workgroup b owns output rows (or row pairs) b, b + G, b + 2G, ... of
+//    the G workgroups.  Its work is the list of segments (one row of one
+//    matrix within one column slice: a contiguous byte range), slice-major;
+//    its waves claim segments two at a time from a counter in LDS, so waves
+//    that the SIMD arbiter favours take more and all finish together.  Each segment's dot product lands in an
 //    LDS table of (row, slice) partial sums; after a workgroup barrier the
 //    epilogue adds the slices in order (deterministic) and writes the rows.
 struct Job {
