@@ -413,7 +413,11 @@ def main():
     tok.fill_(first)
     pos.fill_(n_past)
     torch.cuda.synchronize()
-    nt.trace_begin(nt.TRACE_FFN_UP)
+    # the roofline kernel's launches are timed with HIP events inside the timed
+    # region; one launch in ten, since each event record costs the stream a
+    # few microseconds (all of them would add ~4% to the step time)
+    trace_every = 10
+    nt.trace_begin(nt.TRACE_FFN_UP, trace_every)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -476,7 +480,8 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "launches": n_ffn, "avg_launch_us": round(ffn_avg_s * 1e6, 2), "bytes_per_launch": ffn_bytes,
+            "launches": n_ffn, "launches_sampled_every": trace_every, "avg_launch_us": round(ffn_avg_s * 1e6, 2),
+            "bytes_per_launch": ffn_bytes,
         },
         "cpu_baseline": cpu,
         "tokens_head": toks[:8],

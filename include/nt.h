@@ -207,6 +207,9 @@ int nt_verify_step(const nt_model* model, const int32_t* tokens_dev, int M, cons
  * the number of launches traced and their summed duration in milliseconds
  * (*total_ms).  Kinds: 0 plain GEMV, 1 GEMV + residual add (O and down
  * projections), 2 QKV + RoPE + KV append, 3 gate/up + SwiGLU, 4 attention.
+ * nt_trace_begin_every(kind, k) records only launches 0, k, 2k, ... of the
+ * kind (k >= 1), so that a long run can be sampled at a fraction of the
+ * event cost (each record costs the stream a few microseconds).
  * Tracing is per process and not thread safe; it adds two event records per
  * traced launch.
  */
@@ -218,6 +221,7 @@ typedef enum nt_trace_kind {
   NT_TRACE_ATTN = 4
 } nt_trace_kind;
 int nt_trace_begin(int kind);
+int nt_trace_begin_every(int kind, int every);
 int nt_trace_end(int* launches, double* total_ms);
 
 /*

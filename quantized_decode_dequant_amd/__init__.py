@@ -74,6 +74,7 @@ EXPORTS = {
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                       ctypes.c_void_p]),
     "nt_trace_begin": (ctypes.c_int, [ctypes.c_int]),
+    "nt_trace_begin_every": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "nt_trace_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]),
     "nt_read_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
 }
@@ -87,9 +88,10 @@ def read_probe(buf, out, stream=None) -> None:
                                                 _stream(stream)))
 
 
-def trace_begin(kind: int) -> None:
-    """Time every following launch of one kernel kind with HIP events (nt_trace_begin)."""
-    _check("nt_trace_begin", lib().nt_trace_begin(kind))
+def trace_begin(kind: int, every: int = 1) -> None:
+    """Time launches 0, every, 2*every, ... of one kernel kind from now on with
+    HIP events (nt_trace_begin_every)."""
+    _check("nt_trace_begin_every", lib().nt_trace_begin_every(kind, every))
 
 
 def trace_end() -> tuple[int, float]:

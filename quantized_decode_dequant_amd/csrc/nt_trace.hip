@@ -12,7 +12,10 @@ constexpr int kTraceCap = 16384;
 
 struct Trace {
   int kind = -1;
-  int n = 0;
+  int n = 0;            // launches recorded
+  int every = 1;        // record one launch in `every`
+  int seen = 0;         // launches of the kind since trace_begin
+  bool open = false;    // the current launch is being recorded
   std::vector<hipEvent_t> start, stop;
 };
 
@@ -21,12 +24,16 @@ Trace g_trace;
 }  // namespace
 
 void trace_before(int kind, hipStream_t stream) {
+  g_trace.open = false;
   if (kind != g_trace.kind || g_trace.n >= kTraceCap) return;
+  if (g_trace.seen++ % g_trace.every != 0) return;
+  g_trace.open = true;
   (void)hipEventRecord(g_trace.start[g_trace.n], stream);
 }
 
 void trace_after(int kind, hipStream_t stream) {
-  if (kind != g_trace.kind || g_trace.n >= kTraceCap) return;
+  if (kind != g_trace.kind || !g_trace.open) return;
+  g_trace.open = false;
   (void)hipEventRecord(g_trace.stop[g_trace.n], stream);
   ++g_trace.n;
 }
@@ -35,9 +42,11 @@ void trace_after(int kind, hipStream_t stream) {
 
 extern "C" {
 
-int nt_trace_begin(int kind) {
+int nt_trace_begin(int kind) { return nt_trace_begin_every(kind, 1); }
+
+int nt_trace_begin_every(int kind, int every) {
   using nt::g_trace;
-  if (kind < 0 || kind > NT_TRACE_ATTN) return NT_EINVAL;
+  if (kind < 0 || kind > NT_TRACE_ATTN || every < 1) return NT_EINVAL;
   if (g_trace.start.empty()) {
     g_trace.start.resize(nt::kTraceCap);
     g_trace.stop.resize(nt::kTraceCap);
@@ -48,6 +57,9 @@ int nt_trace_begin(int kind) {
   }
   g_trace.kind = kind;
   g_trace.n = 0;
+  g_trace.every = every;
+  g_trace.seen = 0;
+  g_trace.open = false;
   return NT_OK;
 }
 
