@@ -99,6 +99,10 @@ def lib():
         L.or_argmax.argtypes = [vp, i64, vp]
         L.or_decode.restype = None
         L.or_decode.argtypes = [ctypes.POINTER(Model), vp, i32, i64, vp, vp, vp, vp]
+        L.or_decode_ex.restype = None
+        L.or_decode_ex.argtypes = [ctypes.POINTER(Model), vp, i32, i64, vp, vp, vp, vp, vp, vp]
+        L.or_select_skip.restype = i32
+        L.or_select_skip.argtypes = [vp, i32, i32, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -246,3 +250,29 @@ class OracleModel:
                         _p(logits) if logits is not None else None, _p(margin),
                         _p(hidden) if hidden is not None else None)
         return nxt, margin, logits, hidden
+
+    def decode_skip(self, tokens, pos: int, skip=None, want_logits: bool = False, want_cosine: bool = False):
+        """Pass with layer skip: skip is None or [n_layer] flags.  Returns (next [M], margins [M],
+        logits [M][vocab] or None, cosine [M][n_layer] or None; NaN where a layer was skipped)."""
+        tokens = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+        M, n = tokens.size, self.m.n_layer
+        sk = None if skip is None else np.ascontiguousarray(np.asarray(skip, dtype=np.uint8).reshape(n))
+        nxt = np.empty(M, dtype=np.int32)
+        margin = np.empty(M, dtype=np.float64)
+        logits = np.empty((M, self.vocab), dtype=np.float64) if want_logits else None
+        cos = np.full((M, n), np.nan, dtype=np.float64) if want_cosine else None
+        lib().or_decode_ex(ctypes.byref(self.m), _p(tokens), M, pos, _p(sk) if sk is not None else None, _p(nxt),
+                           _p(logits) if logits is not None else None, _p(margin), None,
+                           _p(cos) if cos is not None else None)
+        return nxt, margin, logits, cos
+
+
+def select_skip(score, n_skip: int, first: int = 0, last: int | None = None) -> np.ndarray:
+    """or_select_skip: flags of the n_skip layers in [first, last) with the largest scores."""
+    sc = np.ascontiguousarray(np.asarray(score, dtype=np.float64).reshape(-1))
+    n = sc.size
+    last = n if last is None else last
+    mask = np.zeros(n, dtype=np.uint8)
+    if lib().or_select_skip(_p(sc), n, n_skip, first, last, _p(mask)) != 0:
+        raise ValueError("or_select_skip: bad arguments")
+    return mask

@@ -18,7 +18,11 @@
  *   - GEMV, RMSNorm, RoPE, SwiGLU and softmax as the per-token kernels, and a
  *     sampler (p2 "Architecture et structure du code");
  *   - self-speculative decoding, whose verify pass runs M drafted tokens
- *     through the stack (p1 feature list; p2 "Fonctionnalités principales").
+ *     through the stack (p1 feature list; p2 "Fonctionnalités principales");
+ *     greedy speculative decoding emits exactly the plain greedy tokens, so
+ *     the plain greedy stack is its oracle;
+ *   - layer skip, the layers chosen by the cosine similarity of their input
+ *     and output (p1 feature list and roadmap phase 3).
  * The pages stop at list level.  Where they are silent the oracle takes one
  * plain reading, marked READING below; the byte layouts of the K-quant
  * superblocks are the GGUF ones (READING: no format file is at hand, so the
@@ -365,21 +369,49 @@ int64_t or_argmax(const double* v, int64_t n, double* margin) {
 }
 
 /* One decode (M = 1) or verify (M > 1) pass: embedding rows of tokens[0..M)
- * -> n_layer layers at positions pos..pos+M-1 -> final RMSNorm -> LM head ->
+ * -> the layers at positions pos..pos+M-1 -> final RMSNorm -> LM head ->
  * greedy argmax per token (p2 "Architecture et structure du code": sampler).
  * READING: the embedding row is the decoded row `token` of tok_emb.
  * logits ([M][vocab]), margin ([M]) and hidden ([M][hidden], the final
- * residual stream before the output norm) may be NULL. */
-void or_decode(const or_model* m, const int32_t* tokens, int M, int64_t pos, int32_t* next,
-               double* logits, double* margin, double* hidden) {
+ * residual stream before the output norm) may be NULL.
+ *
+ * Layer skip (p1 feature list and roadmap phase 3: layers picked by cosine
+ * similarity are left out of the pass):
+ *  - skip (NULL or [n_layer]): a layer with skip[l] != 0 is not run; the
+ *    residual stream goes on to the next layer unchanged.
+ *  - cosine (NULL or [M][n_layer]): cosine[i][l] receives the cosine
+ *    similarity of token i's residual stream entering layer l and leaving
+ *    it, x_in . x_out / (|x_in| |x_out|), for every layer that runs; entries
+ *    of skipped layers are not written.
+ * READING: the similarity is taken on the residual stream itself (no norm
+ * applied), per token. */
+void or_decode_ex(const or_model* m, const int32_t* tokens, int M, int64_t pos, const uint8_t* skip,
+                  int32_t* next, double* logits, double* margin, double* hidden, double* cosine) {
   const int H = m->cfg.hidden;
   int qk = or_block_elems(m->tok_emb.fmt), bb = or_block_bytes(m->tok_emb.fmt);
   int64_t rb = (int64_t)H / qk * bb;
   double* x = (double*)malloc(sizeof(double) * (size_t)M * H);
+  double* x_in = (double*)malloc(sizeof(double) * (size_t)M * H);
   double* xn = (double*)malloc(sizeof(double) * H);
   double* lg = (double*)malloc(sizeof(double) * (size_t)m->vocab);
   for (int i = 0; i < M; ++i) or_dequant_row(m->tok_emb.fmt, m->tok_emb.data + (int64_t)tokens[i] * rb, H, x + (int64_t)i * H);
-  for (int l = 0; l < m->n_layer; ++l) or_layer(&m->cfg, &m->layers[l], x, M, pos);
+  for (int l = 0; l < m->n_layer; ++l) {
+    if (skip && skip[l]) continue;
+    memcpy(x_in, x, sizeof(double) * (size_t)M * H);
+    or_layer(&m->cfg, &m->layers[l], x, M, pos);
+    if (!cosine) continue;
+    for (int i = 0; i < M; ++i) {
+      const double* a = x_in + (int64_t)i * H;
+      const double* b = x + (int64_t)i * H;
+      double ab = 0.0, aa = 0.0, bb2 = 0.0;
+      for (int r = 0; r < H; ++r) {
+        ab += a[r] * b[r];
+        aa += a[r] * a[r];
+        bb2 += b[r] * b[r];
+      }
+      cosine[(int64_t)i * m->n_layer + l] = ab / (sqrt(aa) * sqrt(bb2));
+    }
+  }
   if (hidden) memcpy(hidden, x, sizeof(double) * (size_t)M * H);
   for (int i = 0; i < M; ++i) {
     or_rmsnorm(x + (int64_t)i * H, m->out_norm, H, m->cfg.rms_eps, xn);
@@ -389,5 +421,35 @@ void or_decode(const or_model* m, const int32_t* tokens, int M, int64_t pos, int
     if (margin) margin[i] = mg;
     if (logits) memcpy(logits + (int64_t)i * m->vocab, lg, sizeof(double) * (size_t)m->vocab);
   }
-  free(x); free(xn); free(lg);
+  free(x); free(x_in); free(xn); free(lg);
+}
+
+/* or_decode_ex with every layer run and no similarities. */
+void or_decode(const or_model* m, const int32_t* tokens, int M, int64_t pos, int32_t* next,
+               double* logits, double* margin, double* hidden) {
+  or_decode_ex(m, tokens, M, pos, NULL, next, logits, margin, hidden, NULL);
+}
+
+/* Which layers to skip: the n_skip layers l in [first, last) whose score[l]
+ * (a layer's mean input/output cosine similarity over calibration tokens) is
+ * largest, since those change the residual stream least (p1 feature list:
+ * 20 of 80 layers skipped by cosine similarity).  Picked one at a time, each
+ * the largest remaining score, the lower index among equal scores.  mask[l]
+ * is 1 for a picked layer and 0 for every other.  Returns 0, or -1 when the
+ * range or count is impossible or an eligible score is NaN.
+ * READING: the pages give the criterion and the count only; the eligible
+ * range (so that e.g. the first and last layers can be kept) and the tie
+ * rule are this oracle's. */
+int or_select_skip(const double* score, int n_layer, int n_skip, int first, int last, uint8_t* mask) {
+  if (n_layer < 0 || first < 0 || first > last || last > n_layer || n_skip < 0 || n_skip > last - first) return -1;
+  for (int l = first; l < last; ++l)
+    if (isnan(score[l])) return -1;
+  for (int l = 0; l < n_layer; ++l) mask[l] = 0;
+  for (int k = 0; k < n_skip; ++k) {
+    int best = -1;
+    for (int l = first; l < last; ++l)
+      if (!mask[l] && (best < 0 || score[l] > score[best])) best = l;
+    mask[best] = 1;
+  }
+  return 0;
 }
