@@ -174,6 +174,11 @@ typedef struct nt_model {
   void* stage[2];                /* device staging buffers                   */
   size_t stage_bytes;            /* bytes of each staging buffer             */
   void* copy_stream;             /* hipStream_t for the copies               */
+  /* Layer skip (p1 feature list; p1 roadmap phase 3): NULL, or a host array
+   * of n_layer flags.  A layer with skip[i] != 0 is not run (and, when
+   * streamed, not copied): the residual stream passes it unchanged.
+   * nt_calibrate_step and nt_select_skip choose the layers. */
+  const uint8_t* skip;
 } nt_model;
 
 /* Workspace bytes nt_decode_step / nt_verify_step need for M tokens. */
@@ -199,6 +204,58 @@ int nt_decode_step(const nt_model* model, const int32_t* token_dev, const int32_
  */
 int nt_verify_step(const nt_model* model, const int32_t* tokens_dev, int M, const int32_t* pos_dev,
                    int32_t* argmax_dev, float* logits_dev, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Calibration of layer skip (p1 feature list: the skipped layers are chosen by
+ * cosine similarity): one nt_decode_step that also adds, for every layer l
+ * that runs, the cosine similarity of the residual stream entering layer l
+ * and leaving it, x_in . x_out / (|x_in| |x_out|) (fp64 sums, added as fp32),
+ * to cos_dev[l].  cos_dev: device fp32 [n_layer]; the caller zeroes it before
+ * the first calibration token, so that after T tokens cos_dev[l] / T is the
+ * layer's mean similarity.  Entries of skipped layers are not touched.  Other
+ * arguments as nt_decode_step (same workspace size).
+ */
+int nt_calibrate_step(const nt_model* model, const int32_t* token_dev, const int32_t* pos_dev,
+                      int32_t* next_token_dev, float* cos_dev, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Host helper choosing the layers to skip: mask[l] = 1 for the n_skip layers
+ * l in [first, last) with the largest score[l] (a layer whose output is most
+ * like its input changes the stream least), picked one at a time with the
+ * lower index first among equal scores; mask[l] = 0 elsewhere.  score and
+ * mask are host arrays of n_layer entries.  NT_EINVAL unless
+ * 0 <= first <= last <= n_layer and 0 <= n_skip <= last - first, or if a score
+ * in [first, last) is NaN.  No GPU work.
+ */
+int nt_select_skip(const float* score, int n_layer, int n_skip, int first, int last, uint8_t* mask);
+
+/* Workspace bytes nt_spec_step needs for K draft tokens (0 if K is outside 1..7). */
+size_t nt_spec_workspace_bytes(const nt_model* model, int K);
+
+/*
+ * One round of self-speculative greedy decoding (p1 feature list: the layers
+ * resident in GPU memory serve as the draft model, with no second model):
+ *   1. draft: K (1..7) greedy decode steps of the stack without the layers
+ *      flagged in draft_skip (host [n_layer] flags, typically the streamed
+ *      layers; NULL drafts with the whole stack): d_0 = *cur_dev and d_{j+1}
+ *      is the draft's greedy token after d_j at position *pos_dev + j;
+ *   2. verify: the whole stack (model->skip still applies) on d_0..d_K at
+ *      positions pos..pos+K in one pass (nt_verify_step, M = K + 1), giving
+ *      the greedy tokens a_0..a_K;
+ *   3. accept: n is the number of leading j < K with d_{j+1} == a_j; the
+ *      round emits a_0..a_n: out_dev[0..n] (out_dev[n+1..K] = -1),
+ *      *n_out_dev = n + 1, *pos_dev += n + 1, *cur_dev = a_n.
+ * The emitted tokens are the ones plain greedy decoding of the stack gives
+ * (the draft only sets how many come per round).  Cache entries past the new
+ * position are stale and get overwritten before anything reads them.
+ * cur_dev, pos_dev, out_dev ([K + 1]) and n_out_dev are device int32; the
+ * state stays on the device, so rounds can be queued back to back.
+ * ws: nt_spec_workspace_bytes(model, K).  The draft steps and the verify pass
+ * must fit the cache: pos + K + 1 <= max_ctx (else, as for nt_decode_layer,
+ * the kernels skip the cache write and attention).
+ */
+int nt_spec_step(const nt_model* model, const uint8_t* draft_skip, int K, int32_t* cur_dev, int32_t* pos_dev,
+                 int32_t* out_dev, int32_t* n_out_dev, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Instrumentation.  nt_trace_begin(kind) makes the library record a HIP event

@@ -44,7 +44,7 @@ class Model(ctypes.Structure):
                 ("tok_emb", QMat), ("lm_head", QMat), ("out_norm", ctypes.c_void_p),
                 ("layers", ctypes.POINTER(Layer)), ("first_streamed", ctypes.c_int32),
                 ("host_layer", ctypes.POINTER(ctypes.c_void_p)), ("stage", ctypes.c_void_p * 2),
-                ("stage_bytes", ctypes.c_size_t), ("copy_stream", ctypes.c_void_p)]
+                ("stage_bytes", ctypes.c_size_t), ("copy_stream", ctypes.c_void_p), ("skip", ctypes.c_void_p)]
 
 
 _lib = None
@@ -73,6 +73,14 @@ EXPORTS = {
     "nt_verify_step": (ctypes.c_int, [ctypes.POINTER(Model), ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                       ctypes.c_void_p]),
+    "nt_calibrate_step": (ctypes.c_int, [ctypes.POINTER(Model), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "nt_select_skip": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p]),
+    "nt_spec_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Model), ctypes.c_int]),
+    "nt_spec_step": (ctypes.c_int, [ctypes.POINTER(Model), ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_size_t, ctypes.c_void_p]),
     "nt_trace_begin": (ctypes.c_int, [ctypes.c_int]),
     "nt_trace_begin_every": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "nt_trace_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]),
@@ -169,6 +177,18 @@ def gemm_q_small(fmt: int, W, X, Y, M: int, rows: int, cols: int, ws=None, strea
                                  None if ws is None else _ptr(ws), nbytes, _stream(stream)))
 
 
+def select_skip(score, n_skip: int, first: int = 0, last: int | None = None):
+    """Flags (numpy uint8 [n_layer]) of the n_skip layers in [first, last) with the largest
+    scores, lower index first among equal scores  (nt_select_skip; host only)."""
+    import numpy as np
+    sc = np.ascontiguousarray(np.asarray(score, dtype=np.float32).reshape(-1))
+    n = sc.size
+    mask = np.zeros(n, dtype=np.uint8)
+    _check("nt_select_skip", lib().nt_select_skip(sc.ctypes.data, n, n_skip, first, n if last is None else last,
+                                                  mask.ctypes.data))
+    return mask
+
+
 def layer_cfg(hidden, n_head, n_kv_head, head_dim, ffn, max_ctx, rope_theta=5e5, rms_eps=1e-5) -> LayerCfg:
     return LayerCfg(hidden, n_head, n_kv_head, head_dim, ffn, max_ctx, rope_theta, rms_eps)
 
@@ -219,9 +239,10 @@ class ModelHandle:
 
     def __init__(self, cfg: LayerCfg, layers: list, vocab: int, tok_emb, tok_emb_fmt: int, lm_head, lm_head_fmt: int,
                  out_norm, first_streamed: int | None = None, host_layers=None, stage=(None, None),
-                 stage_bytes: int = 0, copy_stream=None):
+                 stage_bytes: int = 0, copy_stream=None, skip=None):
         self.layers_arr = (Layer * max(1, len(layers)))(*layers)
         n = len(layers)
+        self.skip_arr = None
         self.first_streamed = n if first_streamed is None else first_streamed
         self.host_arr = (ctypes.c_void_p * max(1, n))()
         if host_layers is not None:
@@ -242,6 +263,23 @@ class ModelHandle:
         m.stage_bytes = stage_bytes
         m.copy_stream = _stream(copy_stream) if copy_stream is not None else None
         self.m = m
+        self.set_skip(skip)
+
+    def _flags(self, flags):
+        if flags is None:
+            return None
+        arr = (ctypes.c_uint8 * max(1, self.m.n_layer))()
+        vals = list(flags)
+        if len(vals) != self.m.n_layer:
+            raise ValueError("skip flags need one entry per layer")
+        for i, v in enumerate(vals):
+            arr[i] = 1 if v else 0
+        return arr
+
+    def set_skip(self, flags) -> None:
+        """Layers with a true flag are not run (nt_model.skip); None runs every layer."""
+        self.skip_arr = self._flags(flags)
+        self.m.skip = ctypes.cast(self.skip_arr, ctypes.c_void_p).value if self.skip_arr is not None else None
 
     def workspace_bytes(self, M: int = 1) -> int:
         return lib().nt_step_workspace_bytes(ctypes.byref(self.m), M)
@@ -257,3 +295,22 @@ class ModelHandle:
         _check("nt_verify_step", lib().nt_verify_step(ctypes.byref(self.m), _ptr(tokens_dev), M, _ptr(pos_dev),
                                                       _ptr(argmax_dev), _ptr(logits_dev), _ptr(ws),
                                                       ws.numel() * ws.element_size(), _stream(stream)))
+
+    def calibrate_step(self, token_dev, pos_dev, next_dev, cos_dev, ws, stream=None) -> None:
+        """nt_calibrate_step: a decode step that adds each layer's input/output cosine
+        similarity to cos_dev (fp32 [n_layer])."""
+        _check("nt_calibrate_step", lib().nt_calibrate_step(ctypes.byref(self.m), _ptr(token_dev), _ptr(pos_dev),
+                                                            _ptr(next_dev), _ptr(cos_dev), _ptr(ws),
+                                                            ws.numel() * ws.element_size(), _stream(stream)))
+
+    def spec_workspace_bytes(self, K: int) -> int:
+        return lib().nt_spec_workspace_bytes(ctypes.byref(self.m), K)
+
+    def spec_step(self, draft_skip, K: int, cur_dev, pos_dev, out_dev, n_out_dev, ws, stream=None) -> None:
+        """nt_spec_step: one self-speculative round (K drafted tokens, one verify pass)."""
+        flags = self._flags(draft_skip)
+        _check("nt_spec_step", lib().nt_spec_step(ctypes.byref(self.m),
+                                                  ctypes.cast(flags, ctypes.c_void_p).value if flags is not None
+                                                  else None, K, _ptr(cur_dev), _ptr(pos_dev), _ptr(out_dev),
+                                                  _ptr(n_out_dev), _ptr(ws), ws.numel() * ws.element_size(),
+                                                  _stream(stream)))

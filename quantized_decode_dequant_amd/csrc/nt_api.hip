@@ -251,7 +251,7 @@ int run_layer(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const i
 
 // ---- decode step
 struct StepWs {
-  size_t x, layer, logits, pv, pi, part_lm, total;
+  size_t x, x_in, layer, logits, pv, pi, part_lm, total;
   LayerWs lw;
 };
 
@@ -279,6 +279,7 @@ StepWs step_ws(const nt_model& m, int M) {
   w.lw = layer_ws(m.cfg, M);
   size_t off = 0;
   w.x = off; off += up256((size_t)M * m.cfg.hidden * 4);
+  w.x_in = off; off += up256((size_t)m.cfg.hidden * 4);  // a layer's input, for the similarity of calibration
   w.layer = off; off += w.lw.total;
   w.logits = off; off += up256((size_t)M * m.vocab * 4);
   w.pv = off; off += up256((size_t)M * 256 * 4);
@@ -316,21 +317,40 @@ StreamEvents* stream_events() {
   return &e;
 }
 
+// Arguments of one pass through the stack beyond the model itself.
+struct StepArgs {
+  const uint8_t* skip2 = nullptr;  // extra skip flags [n_layer] (the draft of a speculative round) or null
+  float* cos_acc = nullptr;        // per-layer similarity sums [n_layer] (M == 1) or null
+};
+
+// One pass (decode for M == 1, verify for M > 1).  With check_only, the
+// arguments are validated and nothing is enqueued.
 int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos, int32_t* out, float* logits_user,
-             void* ws_v, size_t ws_bytes, hipStream_t st) {
+             void* ws_v, size_t ws_bytes, hipStream_t st, const StepArgs& sa = StepArgs(), bool check_only = false) {
   if (M < 1 || M > 8) return NT_EINVAL;
   if (!cfg_ok(m.cfg) || m.n_layer < 0 || m.vocab <= 0 || !tokens || !pos || !out || !ws_v) return NT_EINVAL;
   if (m.n_layer > 0 && !m.layers) return NT_EINVAL;
+  if (sa.cos_acc && M != 1) return NT_EINVAL;
   if (!fmt_cols_ok(m.tok_emb.fmt, m.cfg.hidden) || !fmt_cols_ok(m.lm_head.fmt, m.cfg.hidden)) return NT_EINVAL;
   if (!m.tok_emb.data || !m.lm_head.data || !m.out_norm) return NT_EINVAL;
   if (!aligned16(m.lm_head.data) || !aligned16(m.out_norm) || !aligned16(ws_v)) return NT_EALIGN;
   const int fs = m.first_streamed;
   if (fs < 0 || fs > m.n_layer) return NT_EINVAL;
-  const bool streaming = fs < m.n_layer;
+  auto skipped = [&](int l) { return (m.skip && m.skip[l]) || (sa.skip2 && sa.skip2[l]); };
+  // streamed layers that run, in order: the copy pipeline walks only these
+  int ns = 0;
+  for (int l = fs; l < m.n_layer; ++l) ns += !skipped(l);
+  auto streamed_layer = [&](int j) {
+    for (int l = fs; l < m.n_layer; ++l)
+      if (!skipped(l) && j-- == 0) return l;
+    return -1;
+  };
+  const bool streaming = ns > 0;
   const StepWs w = step_ws(m, M);
   if (ws_bytes < w.total) return NT_EWORKSPACE;
   size_t boff[8] = {0};
   for (int l = 0; l < m.n_layer; ++l) {
+    if (skipped(l)) continue;
     nt_layer L = m.layers[l];
     if (l >= fs) {
       // streamed: matrix pointers come from the staging buffers
@@ -344,16 +364,18 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
     const int rc = check_layer(m.cfg, L);
     if (rc != NT_OK) return rc;
   }
+  if (check_only) return NT_OK;
   uint8_t* ws = static_cast<uint8_t*>(ws_v);
   float* x = reinterpret_cast<float*>(ws + w.x);
+  float* x_in = reinterpret_cast<float*>(ws + w.x_in);
   float* logits = logits_user ? logits_user : reinterpret_cast<float*>(ws + w.logits);
   int rc = launch_embed(m.tok_emb.fmt, m.tok_emb.data, tokens, M, m.vocab, m.cfg.hidden, x, st);
   if (rc != NT_OK) return rc;
   StreamEvents* ev = nullptr;
   hipStream_t cs = static_cast<hipStream_t>(m.copy_stream);
   auto issue_copy = [&](int j) -> int {
-    // streamed layer j (0-based among streamed) into stage[j % 2]
-    const int l = fs + j, b = j & 1;
+    // streamed layer j (0-based among the streamed layers that run) into stage[j % 2]
+    const int l = streamed_layer(j), b = j & 1;
     nt_layer L = m.layers[l];
     blob_offsets(m.cfg, L, boff);
     if (j >= 2 && hipStreamWaitEvent(cs, ev->freed[b], 0) != hipSuccess) return NT_EHIP;
@@ -361,7 +383,6 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
     if (hipEventRecord(ev->ready[b], cs) != hipSuccess) return NT_EHIP;
     return NT_OK;
   };
-  const int ns = m.n_layer - fs;
   if (streaming) {
     if (!(ev = stream_events())) return NT_EHIP;
     // the copies may only start once everything queued before this step on
@@ -372,10 +393,12 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
     for (int j = 0; j < std::min(2, ns); ++j)
       if ((rc = issue_copy(j)) != NT_OK) return rc;
   }
+  int j = 0;  // streamed layers run so far
   for (int l = 0; l < m.n_layer; ++l) {
+    if (skipped(l)) continue;
     nt_layer L = m.layers[l];
+    const int b = j & 1;
     if (l >= fs) {
-      const int j = l - fs, b = j & 1;
       blob_offsets(m.cfg, L, boff);
       uint8_t* base = static_cast<uint8_t*>(m.stage[b]);
       L.wq.data = base + boff[0];
@@ -387,11 +410,15 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
       L.wd.data = base + boff[6];
       if (hipStreamWaitEvent(st, ev->ready[b], 0) != hipSuccess) return NT_EHIP;
     }
+    if (sa.cos_acc &&
+        hipMemcpyAsync(x_in, x, (size_t)m.cfg.hidden * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return NT_EHIP;
     if ((rc = run_layer(m.cfg, L, x, M, pos, ws + w.layer, w.lw, st)) != NT_OK) return rc;
+    if (sa.cos_acc && (rc = launch_cos_acc(x_in, x, m.cfg.hidden, sa.cos_acc + l, st)) != NT_OK) return rc;
     if (l >= fs) {
-      const int j = l - fs, b = j & 1;
       if (hipEventRecord(ev->freed[b], st) != hipSuccess) return NT_EHIP;
       if (j + 2 < ns && (rc = issue_copy(j + 2)) != NT_OK) return rc;
+      ++j;
     }
   }
   // final RMSNorm -> LM head -> argmax
@@ -419,6 +446,23 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
   }
   return launch_argmax(logits, M, m.vocab, reinterpret_cast<float*>(ws + w.pv), reinterpret_cast<int*>(ws + w.pi), out,
                        st);
+}
+
+// Workspace of a speculative round: one pass's workspace (the draft steps
+// and the verify pass run one after the other in it), then the drafted
+// tokens, the verified tokens and the draft positions.
+struct SpecWs {
+  size_t d, a, posj, total;
+};
+
+SpecWs spec_ws(const nt_model& m, int K) {
+  SpecWs s{};
+  size_t off = std::max(step_ws(m, 1).total, step_ws(m, K + 1).total);
+  s.d = off; off += 256;
+  s.a = off; off += 256;
+  s.posj = off; off += 256;
+  s.total = off;
+  return s;
 }
 
 }  // namespace
@@ -550,6 +594,60 @@ int nt_verify_step(const nt_model* model, const int32_t* tokens_dev, int M, cons
   if (!model) return NT_EINVAL;
   return run_step(*model, tokens_dev, M, pos_dev, argmax_dev, logits_dev, ws, ws_bytes,
                   static_cast<hipStream_t>(stream));
+}
+
+int nt_calibrate_step(const nt_model* model, const int32_t* token_dev, const int32_t* pos_dev,
+                      int32_t* next_token_dev, float* cos_dev, void* ws, size_t ws_bytes, void* stream) {
+  if (!model || !cos_dev) return NT_EINVAL;
+  StepArgs sa;
+  sa.cos_acc = cos_dev;
+  return run_step(*model, token_dev, 1, pos_dev, next_token_dev, nullptr, ws, ws_bytes,
+                  static_cast<hipStream_t>(stream), sa);
+}
+
+int nt_select_skip(const float* score, int n_layer, int n_skip, int first, int last, uint8_t* mask) {
+  if (!score || !mask || n_layer < 0 || first < 0 || first > last || last > n_layer || n_skip < 0 ||
+      n_skip > last - first)
+    return NT_EINVAL;
+  for (int l = first; l < last; ++l)
+    if (score[l] != score[l]) return NT_EINVAL;  // NaN
+  for (int l = 0; l < n_layer; ++l) mask[l] = 0;
+  for (int k = 0; k < n_skip; ++k) {
+    int best = -1;
+    for (int l = first; l < last; ++l)
+      if (!mask[l] && (best < 0 || score[l] > score[best])) best = l;
+    mask[best] = 1;
+  }
+  return NT_OK;
+}
+
+size_t nt_spec_workspace_bytes(const nt_model* model, int K) {
+  if (!model || K < 1 || K > 7 || !cfg_ok(model->cfg)) return 0;
+  return spec_ws(*model, K).total;
+}
+
+int nt_spec_step(const nt_model* model, const uint8_t* draft_skip, int K, int32_t* cur_dev, int32_t* pos_dev,
+                 int32_t* out_dev, int32_t* n_out_dev, void* ws_v, size_t ws_bytes, void* stream) {
+  if (!model || K < 1 || K > 7 || !cur_dev || !pos_dev || !out_dev || !n_out_dev || !ws_v) return NT_EINVAL;
+  if (!cfg_ok(model->cfg)) return NT_EINVAL;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const SpecWs s = spec_ws(*model, K);
+  if (ws_bytes < s.total) return NT_EWORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(ws_v);
+  int32_t* d = reinterpret_cast<int32_t*>(ws + s.d);
+  int32_t* a = reinterpret_cast<int32_t*>(ws + s.a);
+  int32_t* posj = reinterpret_cast<int32_t*>(ws + s.posj);
+  StepArgs draft;
+  draft.skip2 = draft_skip;
+  // validate both kinds of pass before anything is enqueued
+  int rc = run_step(*model, d, 1, posj, d + 1, nullptr, ws, ws_bytes, st, draft, true);
+  if (rc != NT_OK) return rc;
+  if ((rc = run_step(*model, d, K + 1, pos_dev, a, nullptr, ws, ws_bytes, st, StepArgs(), true)) != NT_OK) return rc;
+  if ((rc = launch_spec_init(cur_dev, pos_dev, K, d, posj, st)) != NT_OK) return rc;
+  for (int j = 0; j < K; ++j)
+    if ((rc = run_step(*model, d + j, 1, posj + j, d + j + 1, nullptr, ws, ws_bytes, st, draft)) != NT_OK) return rc;
+  if ((rc = run_step(*model, d, K + 1, pos_dev, a, nullptr, ws, ws_bytes, st)) != NT_OK) return rc;
+  return launch_spec_accept(d, a, K, cur_dev, pos_dev, out_dev, n_out_dev, st);
 }
 
 }  // extern "C"

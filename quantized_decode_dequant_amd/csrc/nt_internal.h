@@ -193,4 +193,13 @@ int launch_embed(int fmt, const void* E, const int32_t* tokens, int M, int vocab
 int argmax_parts(int n);
 int launch_argmax(const float* logits, int M, int n, float* pv, int* pi, int32_t* out, hipStream_t stream);
 
+// Layer-skip calibration and speculative-round kernels (nt_spec.hip).
+// acc[0] += cosine similarity of a and b (n floats).
+int launch_cos_acc(const float* a, const float* b, int n, float* acc, hipStream_t stream);
+// d[0] = *cur, posj[j] = *pos + j (j <= K).
+int launch_spec_init(const int32_t* cur, const int32_t* pos, int K, int32_t* d, int32_t* posj, hipStream_t stream);
+// Accept drafted d[1..K] against verified a[0..K]; emit, advance pos and cur.
+int launch_spec_accept(const int32_t* d, const int32_t* a, int K, int32_t* cur, int32_t* pos, int32_t* out,
+                       int32_t* n_out, hipStream_t stream);
+
 }  // namespace nt
