@@ -24,6 +24,10 @@ Secondary workloads (`--workload`, one JSON line each; not the headline):
            of M = 1, 2, 4, 8 tokens from context 4096: verified positions/s,
            host-to-device GB/s against a copy-only run, and the overlap of
            copies with compute against an all-resident run.
+  spec     self-speculative rounds on the same stack (the 36 resident layers
+           draft K = 3 or 7 tokens, one streamed verify pass checks them):
+           round, draft-step and verify times, tokens emitted per round, and
+           plain streamed decode with 20 calibrated layers skipped.
 """
 from __future__ import annotations
 
@@ -278,42 +282,65 @@ def workload_layer8b(dev) -> dict:
             "us_per_layer": round(ms * 1e3, 2), "alg_bytes": alg, "frac_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
 
 
+class StreamedStack:
+    """80 Q6_K 70B-shaped layers, the first 36 resident in HBM and the other
+    44 in pinned host memory, streamed through two HBM staging buffers; every
+    layer is a copy of one seeded layer (the timing does not depend on the
+    weight values), with its own KV cache."""
+
+    def __init__(self, dev, max_ctx: int, n_past: int = 4096, n_layer: int = 80, fs: int = 36):
+        import torch
+
+        import quantized_decode_dequant_amd as nt
+        from quantized_decode_dequant_amd.model import DeviceLayer, cfg_of, pack_blob
+        from synth import workloads as wl
+
+        shape, vocab = wl.LLAMA70B, 128256
+        self.n_layer, self.fs, self.vocab, self.n_past = n_layer, fs, vocab, n_past
+        self.cfg = cfg = cfg_of(shape, max_ctx)
+        t0 = time.time()
+        self.li = li = wl.gen_layer(shape, wl.ALL_Q6_K, wl.W_VERIFY_70B, 0, max_ctx, n_past)
+        blob = pack_blob(cfg, li)
+        self.sb = sb = blob.size
+        self.host = host = [None] * n_layer
+        for l in range(fs, n_layer):
+            host[l] = torch.empty(sb, dtype=torch.uint8, pin_memory=True)
+            host[l].numpy()[:] = blob
+        self.stage = (torch.empty(sb, dtype=torch.uint8, device=dev), torch.empty(sb, dtype=torch.uint8, device=dev))
+        self.layers = [DeviceLayer(li, dev, weights_on_device=(l < fs)) for l in range(n_layer)]
+        log(f"[bench] streamed stack ready: {fs} resident + {n_layer - fs} streamed layers of {sb / 1e6:.1f} MB "
+            f"({time.time() - t0:.0f} s)")
+        self.emb = torch.from_numpy(wl.gen_matrix(wl.Q6_K, vocab, shape.hidden, wl.W_VERIFY_70B, 0,
+                                                  wl.T_TOK_EMB)).to(dev)
+        self.head = torch.from_numpy(wl.gen_matrix(wl.Q6_K, vocab, shape.hidden, wl.W_VERIFY_70B, 0,
+                                                   wl.T_LM_HEAD)).to(dev)
+        self.norm = torch.from_numpy(wl.gen_gains(shape, wl.W_VERIFY_70B, 0, wl.T_OUT_NORM)).to(dev)
+        self.copy_stream = torch.cuda.Stream()
+        self.h = nt.ModelHandle(cfg, [d.struct for d in self.layers], vocab, self.emb, wl.Q6_K, self.head, wl.Q6_K,
+                                self.norm, first_streamed=fs, host_layers=host, stage=self.stage, stage_bytes=sb,
+                                copy_stream=self.copy_stream)
+        self.stream_bytes = sb * (n_layer - fs)
+
+
 def workload_verify(dev, passes: int) -> dict:
-    """Config 5: streamed verify passes; every layer is a copy of one seeded
-    Q6_K layer (the timing does not depend on the weight values)."""
+    """Config 5: streamed verify passes of M = 1, 2, 4, 8 tokens."""
     import numpy as np
     import torch
 
     import quantized_decode_dequant_amd as nt
-    from quantized_decode_dequant_amd.model import DeviceLayer, cfg_of, pack_blob
+    from quantized_decode_dequant_amd.model import DeviceLayer
     from synth import workloads as wl
 
-    shape, n_layer, fs, n_past, vocab = wl.LLAMA70B, 80, 36, 4096, 128256
-    max_ctx = n_past + 8
-    cfg = cfg_of(shape, max_ctx)
-    t0 = time.time()
-    li = wl.gen_layer(shape, wl.ALL_Q6_K, wl.W_VERIFY_70B, 0, max_ctx, n_past)
-    blob = pack_blob(cfg, li)
-    sb = blob.size
-    host = [None] * n_layer
-    for l in range(fs, n_layer):
-        host[l] = torch.empty(sb, dtype=torch.uint8, pin_memory=True)
-        host[l].numpy()[:] = blob
-    stage = (torch.empty(sb, dtype=torch.uint8, device=dev), torch.empty(sb, dtype=torch.uint8, device=dev))
-    streamed = [DeviceLayer(li, dev, weights_on_device=(l < fs)) for l in range(n_layer)]
-    log(f"[bench] verify stack ready: {fs} resident + {n_layer - fs} streamed layers of {sb / 1e6:.1f} MB "
-        f"({time.time() - t0:.0f} s)")
-    emb = torch.from_numpy(wl.gen_matrix(wl.Q6_K, vocab, shape.hidden, wl.W_VERIFY_70B, 0, wl.T_TOK_EMB)).to(dev)
-    head = torch.from_numpy(wl.gen_matrix(wl.Q6_K, vocab, shape.hidden, wl.W_VERIFY_70B, 0, wl.T_LM_HEAD)).to(dev)
-    norm = torch.from_numpy(wl.gen_gains(shape, wl.W_VERIFY_70B, 0, wl.T_OUT_NORM)).to(dev)
-    copy_stream = torch.cuda.Stream()
-    hs = nt.ModelHandle(cfg, [d.struct for d in streamed], vocab, emb, wl.Q6_K, head, wl.Q6_K, norm,
-                        first_streamed=fs, host_layers=host, stage=stage, stage_bytes=sb, copy_stream=copy_stream)
+    n_past = 4096
+    S = StreamedStack(dev, n_past + 8, n_past)
+    hs, cfg, li, host, stage, sb = S.h, S.cfg, S.li, S.host, S.stage, S.sb
+    n_layer, fs, vocab = S.n_layer, S.fs, S.vocab
+    emb, head, norm = S.emb, S.head, S.norm
     stream = torch.cuda.current_stream()
     toks = torch.from_numpy(wl.gen_tokens(wl.W_VERIFY_70B, 8, vocab)).to(dev)
     pos = torch.tensor([n_past], dtype=torch.int32, device=dev)
     out = torch.zeros(8, dtype=torch.int32, device=dev)
-    stream_bytes = sb * (n_layer - fs)
+    stream_bytes = S.stream_bytes
     # copy-only: the 44 layer copies alone
     def copies():
         for l in range(fs, n_layer):
@@ -328,7 +355,7 @@ def workload_verify(dev, passes: int) -> dict:
         log(f"[bench] verify M={M}: {ms:.1f} ms per pass")
         del ws
     # compute-only: the same 80 layers all resident
-    del hs
+    del hs, S
     resident = [DeviceLayer(li, dev) for _ in range(n_layer)]
     hr = nt.ModelHandle(cfg, [d.struct for d in resident], vocab, emb, wl.Q6_K, head, wl.Q6_K, norm)
     for M in [1, 2, 4, 8]:
@@ -347,6 +374,95 @@ def workload_verify(dev, passes: int) -> dict:
             "verify": res}
 
 
+def workload_spec(dev, rounds: int) -> dict:
+    """Self-speculative rounds and layer skip on the config-5 stack: the 36
+    resident layers draft, the whole stack verifies (its 44 streamed layers
+    cross the host link once per round).  Reports the draft step, the verify
+    pass and the round, the tokens a round emitted on these seeded weights,
+    and plain streamed decode with and without 20 calibrated skipped layers.
+    Emitted tokens per round depend on how often the draft agrees with the
+    whole stack, which seeded random weights do not model: `break_even`
+    gives the tokens per round at which rounds beat plain decode."""
+    import numpy as np
+    import torch
+
+    import quantized_decode_dequant_amd as nt
+    from synth import workloads as wl
+
+    n_past = 4096
+    S = StreamedStack(dev, n_past + 64, n_past)
+    h, n_layer, fs, vocab = S.h, S.n_layer, S.fs, S.vocab
+    stream = torch.cuda.current_stream()
+    first = int(wl.gen_tokens(wl.W_VERIFY_70B, 1, vocab)[0])
+    draft_skip = [1 if l >= fs else 0 for l in range(n_layer)]
+    res = {}
+    ws1 = torch.zeros(h.workspace_bytes(1), dtype=torch.uint8, device=dev)
+    tok = torch.tensor([first], dtype=torch.int32, device=dev)
+    pos = torch.tensor([n_past], dtype=torch.int32, device=dev)
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    # plain streamed decode (every layer; 44 layer copies per token)
+    plain_ms = timed(lambda: h.decode_step(tok, pos, nxt, ws1, None, stream), 3)
+    # draft step: the resident layers and the LM head
+    h.set_skip(draft_skip)
+    draft_ms = timed(lambda: h.decode_step(tok, pos, nxt, ws1, None, stream), 10)
+    h.set_skip(None)
+    res["plain_decode_ms"] = round(plain_ms, 2)
+    res["draft_step_ms"] = round(draft_ms, 3)
+    log(f"[bench] spec: plain streamed decode {plain_ms:.1f} ms, draft step {draft_ms:.2f} ms")
+    for K in (3, 7):
+        ws = torch.zeros(h.spec_workspace_bytes(K), dtype=torch.uint8, device=dev)
+        cur = torch.tensor([first], dtype=torch.int32, device=dev)
+        p = torch.tensor([n_past], dtype=torch.int32, device=dev)
+        out = torch.zeros(K + 1, dtype=torch.int32, device=dev)
+        n_out = torch.zeros(1, dtype=torch.int32, device=dev)
+        h.spec_step(draft_skip, K, cur, p, out, n_out, ws, stream)   # warm
+        torch.cuda.synchronize()
+        emitted, t_ms = 0, 0.0
+        for r in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            h.spec_step(draft_skip, K, cur, p, out, n_out, ws, stream)
+            e1.record()
+            torch.cuda.synchronize()
+            t_ms += e0.elapsed_time(e1)
+            emitted += int(n_out.item())
+        round_ms = t_ms / rounds
+        wsv = torch.zeros(h.workspace_bytes(K + 1), dtype=torch.uint8, device=dev)
+        toks = torch.from_numpy(wl.gen_tokens(wl.W_VERIFY_70B, K + 1, vocab)).to(dev)
+        av = torch.zeros(K + 1, dtype=torch.int32, device=dev)
+        verify_ms = timed(lambda: h.verify_step(toks, K + 1, pos, av, wsv, None, stream), 2)
+        res[f"K{K}"] = {"round_ms": round(round_ms, 1), "verify_ms": round(verify_ms, 1),
+                        "tokens_per_round": round(emitted / rounds, 2),
+                        "tokens_per_s": round(emitted / rounds / (round_ms / 1e3), 3),
+                        "break_even_tokens_per_round": round(round_ms / plain_ms, 2)}
+        log(f"[bench] spec K={K}: round {round_ms:.1f} ms, {emitted / rounds:.2f} tokens per round")
+        del ws, wsv
+    # layer skip: calibrate on 4 tokens, skip the 20 most similar of layers 1..78
+    cos = torch.zeros(n_layer, dtype=torch.float32, device=dev)
+    t, p = tok.clone(), pos.clone()
+    for _ in range(4):
+        h.calibrate_step(t, p, nxt, cos, ws1, stream)
+        t.copy_(nxt)
+        p.add_(1)
+    torch.cuda.synchronize()
+    mask = nt.select_skip(cos.cpu().numpy(), 20, 1, n_layer - 1)
+    h.set_skip(mask)
+    skip_ms = timed(lambda: h.decode_step(tok, pos, nxt, ws1, None, stream), 3)
+    h.set_skip(None)
+    n_stream_skipped = int(mask[fs:].sum())
+    res["skip20"] = {"decode_ms": round(skip_ms, 2), "skipped_layers": np.nonzero(mask)[0].tolist(),
+                     "streamed_layers_skipped": n_stream_skipped,
+                     "tokens_per_s": round(1e3 / skip_ms, 3)}
+    log(f"[bench] skip20: {skip_ms:.1f} ms per token ({n_stream_skipped} of the skipped layers streamed)")
+    best = max(res[f"K{K}"]["tokens_per_s"] for K in (3, 7))
+    return {"metric": "self-speculative decode: emitted tokens/s (seeded random weights)", "unit": "tokens/s",
+            "n_gpus": 1, "value": best, "higher_is_better": True, "data": "synthetic",
+            "config": {"workload": "80 Q6_K 70B-shaped layers, 36 resident (the draft) + 44 streamed from pinned "
+                                   "host memory, K = 3 and 7 drafted tokens per round, context 4096",
+                       "stream_bytes_per_pass": S.stream_bytes},
+            "spec": res}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -359,9 +475,9 @@ def main():
                     help="also run one device copy of 256 MiB (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize", metavar="DIR", help="print per-kernel statistics of a rocprofv3 output "
                     "directory (kernel trace or counter csv) and exit")
-    ap.add_argument("--workload", choices=["decode", "gemv", "layer8b", "verify"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "gemv", "layer8b", "verify", "spec"], default="decode",
                     help="decode (the headline, default) or one of the secondary workloads")
-    ap.add_argument("--passes", type=int, default=5, help="verify workload: timed passes per M")
+    ap.add_argument("--passes", type=int, default=5, help="verify workload: timed passes per M; spec: rounds per K")
     args = ap.parse_args()
     if args.summarize:
         summarize_profile(args.summarize)
@@ -378,7 +494,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload != "decode":
         fn = {"gemv": lambda: workload_gemv(dev), "layer8b": lambda: workload_layer8b(dev),
-              "verify": lambda: workload_verify(dev, args.passes)}[args.workload]
+              "verify": lambda: workload_verify(dev, args.passes),
+              "spec": lambda: workload_spec(dev, args.passes)}[args.workload]
         print(json.dumps(fn()), flush=True)
         return
     n_past = 4096
