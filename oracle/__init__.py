@@ -28,7 +28,7 @@ _DIR = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_DIR, "oracle.c")
 _LIB = os.path.join(_DIR, "liboracle.so")
 
-Q8_0, Q4_0, Q4_K, Q6_K = 0, 1, 2, 3
+Q8_0, Q4_0, Q4_K, Q6_K, Q5_K, F16, F32 = 0, 1, 2, 3, 4, 5, 6
 
 
 def build(force: bool = True) -> str:

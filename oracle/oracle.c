@@ -9,8 +9,8 @@
  *
  * What is computed, and where the pages state it (ntransformer pages; p1 is
  * the unwiki summary, p2 the GeekNews article):
- *   - weights stored in the GGUF block formats Q8_0, Q4_0, Q4_K, Q6_K
- *     (p1 "About" format list; p2 "Présentation de NTransformer");
+ *   - weights stored in the GGUF formats Q8_0, Q4_0, Q4_K, Q5_K, Q6_K, F16
+ *     and F32 (p1 "About" format list; p2 "Présentation de NTransformer");
  *   - the Llama decoder: RMSNorm, RoPE, grouped-query attention over a KV
  *     cache, SwiGLU FFN (p1 list of Llama features; p2 "Fonctionnalités
  *     principales", last bullet);
@@ -34,7 +34,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_Q8_0 = 0, OR_Q4_0 = 1, OR_Q4_K = 2, OR_Q6_K = 3 };
+enum { OR_Q8_0 = 0, OR_Q4_0 = 1, OR_Q4_K = 2, OR_Q6_K = 3, OR_Q5_K = 4, OR_F16 = 5, OR_F32 = 6 };
 
 /* ---------------------------------------------------------------- scalars */
 
@@ -77,7 +77,8 @@ uint16_t or_to_half(double v) {
 int or_block_elems(int fmt) {
   switch (fmt) {
     case OR_Q8_0: case OR_Q4_0: return 32;
-    case OR_Q4_K: case OR_Q6_K: return 256;
+    case OR_Q4_K: case OR_Q6_K: case OR_Q5_K: return 256;
+    case OR_F16: case OR_F32: return 1;    /* unquantized: one value per "block" */
   }
   return 0;
 }
@@ -88,6 +89,9 @@ int or_block_bytes(int fmt) {
     case OR_Q4_0: return 2 + 16;            /* d, 32 nibbles                */
     case OR_Q4_K: return 2 + 2 + 12 + 128;  /* d, dmin, scales, 256 nibbles */
     case OR_Q6_K: return 128 + 64 + 16 + 2; /* ql, qh, scales, d            */
+    case OR_Q5_K: return 2 + 2 + 12 + 32 + 128; /* d, dmin, scales, qh, nibbles */
+    case OR_F16: return 2;
+    case OR_F32: return 4;
   }
   return 0;
 }
@@ -143,6 +147,32 @@ void or_dequant_block(int fmt, const uint8_t* b, double* w) {
         int q = ((e / 32) % 2) ? (byte >> 4) : (byte & 15);
         w[e] = d * (double)scale * (double)q - dmin * (double)min;
       }
+      break;
+    }
+    case OR_Q5_K: { /* w = d * scale_s * q - dmin * min_s, q 5-bit */
+      double d = or_half(rd16(b)), dmin = or_half(rd16(b + 2));
+      const uint8_t* sc = b + 4;
+      const uint8_t* qh = b + 16;
+      const uint8_t* qs = b + 48;
+      for (int e = 0; e < 256; ++e) {
+        /* READING (GGUF order; the pages only name the format): scales and
+         * mins as Q4_K, the low four bits as Q4_K's nibbles, and the fifth
+         * bit of element l (< 32) of sub-block s is bit s of qh[l]. */
+        int s = e / 32, c = e / 64, l = e % 32, scale, min;
+        q4k_scale_min(sc, s, &scale, &min);
+        uint8_t byte = qs[32 * c + l];
+        int q = ((s % 2) ? (byte >> 4) : (byte & 15)) | (((qh[l] >> s) & 1) << 4);
+        w[e] = d * (double)scale * (double)q - dmin * (double)min;
+      }
+      break;
+    }
+    case OR_F16:
+      w[0] = or_half(rd16(b));
+      break;
+    case OR_F32: { /* IEEE binary32, little endian */
+      float f;
+      memcpy(&f, b, 4);
+      w[0] = (double)f;
       break;
     }
     case OR_Q6_K: { /* w_e = d * scale[e/16] * (q_e - 32) */

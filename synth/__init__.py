@@ -21,10 +21,11 @@ _LIB = os.path.join(_DIR, "libsynth.so")
 BASE_SEED = 20261202
 
 # Format ids shared with the C ABI of the library and the oracle.
-Q8_0, Q4_0, Q4_K, Q6_K = 0, 1, 2, 3
-FMT_NAMES = {Q8_0: "q8_0", Q4_0: "q4_0", Q4_K: "q4_k", Q6_K: "q6_k"}
+Q8_0, Q4_0, Q4_K, Q6_K, Q5_K, F16, F32 = 0, 1, 2, 3, 4, 5, 6
+FMT_NAMES = {Q8_0: "q8_0", Q4_0: "q4_0", Q4_K: "q4_k", Q6_K: "q6_k", Q5_K: "q5_k", F16: "f16", F32: "f32"}
 # (weights per block, bytes per block)
-BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q4_K: (256, 144), Q6_K: (256, 210)}
+BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q4_K: (256, 144), Q6_K: (256, 210), Q5_K: (256, 176), F16: (1, 2),
+         F32: (1, 4)}
 
 
 def row_bytes(fmt: int, cols: int) -> int:

@@ -90,13 +90,14 @@ static inline uint16_t scale_f16(uint64_t w, double lo, double hi) {
   return synth_f64_to_f16(lo + (hi - lo) * sm_u01(w));
 }
 
-enum { SY_Q8_0 = 0, SY_Q4_0 = 1, SY_Q4_K = 2, SY_Q6_K = 3 };
+enum { SY_Q8_0 = 0, SY_Q4_0 = 1, SY_Q4_K = 2, SY_Q6_K = 3, SY_Q5_K = 4, SY_F16 = 5, SY_F32 = 6 };
 #define SY_WORDS_PER_BLOCK 32u
 
 int synth_block_elems(int fmt) {
   switch (fmt) {
     case SY_Q8_0: case SY_Q4_0: return 32;
-    case SY_Q4_K: case SY_Q6_K: return 256;
+    case SY_Q4_K: case SY_Q6_K: case SY_Q5_K: return 256;
+    case SY_F16: case SY_F32: return 1;
   }
   return 0;
 }
@@ -107,6 +108,9 @@ int synth_block_bytes(int fmt) {
     case SY_Q4_0: return 18;
     case SY_Q4_K: return 144;
     case SY_Q6_K: return 210;
+    case SY_Q5_K: return 176;
+    case SY_F16: return 2;
+    case SY_F32: return 4;
   }
   return 0;
 }
@@ -139,6 +143,23 @@ static void fill_block(int fmt, uint64_t key, uint64_t b, double dlo, double dhi
       put_word_bytes(out + 12, sm_word(key, w0 + 3), 4);
       for (int j = 0; j < 16; ++j) put_word_bytes(out + 16 + 8 * j, sm_word(key, w0 + 4 + j), 8);
       break;
+    case SY_Q5_K:
+      put16(out, scale_f16(sm_word(key, w0), dlo, dhi));
+      put16(out + 2, scale_f16(sm_word(key, w0 + 1), dlo, dhi));
+      put_word_bytes(out + 4, sm_word(key, w0 + 2), 8);                                  /* scales */
+      put_word_bytes(out + 12, sm_word(key, w0 + 3), 4);
+      for (int j = 0; j < 20; ++j) put_word_bytes(out + 16 + 8 * j, sm_word(key, w0 + 4 + j), 8); /* qh, qs */
+      break;
+    case SY_F16: /* unquantized weights: N(0, (10 dhi)^2), i.e. std 0.1 at the default scale range */
+      put16(out, synth_f64_to_f16(10.0 * dhi * sm_normal(key, b)));
+      break;
+    case SY_F32: {
+      float f = (float)(10.0 * dhi * sm_normal(key, b));
+      uint32_t u;
+      memcpy(&u, &f, 4);
+      put_word_bytes(out, u, 4);
+      break;
+    }
     case SY_Q6_K:
       for (int j = 0; j < 24; ++j) put_word_bytes(out + 8 * j, sm_word(key, w0 + j), 8); /* ql, qh */
       put_word_bytes(out + 192, sm_word(key, w0 + 24), 8);                              /* scales */

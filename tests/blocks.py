@@ -54,3 +54,23 @@ def enc_q6_k(d_bits: int, sc: np.ndarray, q: np.ndarray) -> bytes:
         ql[bi] |= lo << (4 * (k // 2))
         qh[32 * n + l] |= hi << (2 * k)
     return bytes(ql) + bytes(qh) + sc.astype(np.int8).tobytes() + bytes([d_bits & 255, d_bits >> 8])
+
+
+def enc_q5_k(d_bits: int, dmin_bits: int, sc: np.ndarray, mn: np.ndarray, q: np.ndarray) -> bytes:
+    """sc, mn: 8 six-bit values (packed as Q4_K); q: 256 values in 0..31.  The low four
+    bits go in the nibbles as Q4_K's; the fifth bit of element 32 s + l is bit s of qh[l]."""
+    assert q.shape == (256,) and q.min() >= 0 and q.max() <= 31
+    q4 = enc_q4_k(d_bits, dmin_bits, sc, mn, q & 15)
+    qh = [0] * 32
+    for s in range(8):
+        for l in range(32):
+            qh[l] |= ((int(q[32 * s + l]) >> 4) & 1) << s
+    return q4[:16] + bytes(qh) + q4[16:]
+
+
+def enc_f16(v: np.ndarray) -> bytes:
+    return np.asarray(v, np.float16).astype("<f2").tobytes()
+
+
+def enc_f32(v: np.ndarray) -> bytes:
+    return np.asarray(v, np.float32).astype("<f4").tobytes()

@@ -25,8 +25,8 @@ def _f16(bits):
 
 
 def test_block_sizes_match_formats():
-    assert [oracle.block_elems(f) for f in range(4)] == [32, 32, 256, 256]
-    assert [oracle.block_bytes(f) for f in range(4)] == [34, 18, 144, 210]
+    assert [oracle.block_elems(f) for f in range(7)] == [32, 32, 256, 256, 256, 1, 1]
+    assert [oracle.block_bytes(f) for f in range(7)] == [34, 18, 144, 210, 176, 2, 4]
 
 
 @pytest.mark.parametrize("trial", range(4))
@@ -93,6 +93,46 @@ def test_q6_k_element_order_distinct_values():
     assert np.array_equal(w, (q - 32).astype(np.float64))
 
 
+@pytest.mark.parametrize("trial", range(4))
+def test_q5_k_roundtrip(trial):
+    d, dmin = H(RNG.uniform(1e-3, 1e-2)), H(RNG.uniform(1e-3, 1e-2))
+    sc = RNG.integers(0, 64, 8)
+    mn = RNG.integers(0, 64, 8)
+    q = RNG.integers(0, 32, 256)
+    raw = np.frombuffer(blocks.enc_q5_k(d, dmin, sc, mn, q), np.uint8)
+    w = oracle.dequant(oracle.Q5_K, raw, 1, 256)[0]
+    s = np.repeat(sc, 32).astype(np.float64)
+    m = np.repeat(mn, 32).astype(np.float64)
+    assert np.array_equal(w, _f16(d) * s * q - _f16(dmin) * m)
+
+
+def test_q5_k_element_order_distinct_values():
+    # element e carries (e + e // 32) % 32: every sub-block sees every fifth-bit pattern
+    q = (np.arange(256) + np.arange(256) // 32) % 32
+    raw = np.frombuffer(blocks.enc_q5_k(H(1.0), H(0.0), np.ones(8, np.int64), np.zeros(8, np.int64), q), np.uint8)
+    w = oracle.dequant(oracle.Q5_K, raw, 1, 256)[0]
+    assert np.array_equal(w, q.astype(np.float64))
+
+
+def test_f16_f32_rows_decode_exactly():
+    v = RNG.normal(0, 1, 64)
+    w16 = oracle.dequant(oracle.F16, np.frombuffer(blocks.enc_f16(v), np.uint8), 1, 64)[0]
+    assert np.array_equal(w16, v.astype(np.float16).astype(np.float64))
+    w32 = oracle.dequant(oracle.F32, np.frombuffer(blocks.enc_f32(v), np.uint8), 1, 64)[0]
+    assert np.array_equal(w32, v.astype(np.float32).astype(np.float64))
+    # special values
+    sp = np.array([0.0, -0.0, np.inf, -np.inf, 65504.0, 2.0 ** -24], np.float64)
+    assert np.array_equal(oracle.dequant(oracle.F16, np.frombuffer(blocks.enc_f16(sp), np.uint8), 1, 6)[0], sp)
+
+
+def test_f32_gemv_is_dense_matmul():
+    rows, cols = 5, 96
+    Wv = RNG.normal(0, 1, (rows, cols)).astype(np.float32)
+    x = RNG.normal(0, 1, cols)
+    y = oracle.gemv(oracle.F32, np.frombuffer(blocks.enc_f32(Wv), np.uint8), x, rows, cols)
+    assert np.allclose(y, Wv.astype(np.float64) @ x, rtol=1e-13, atol=1e-13)
+
+
 def _const_row(fmt, nblocks, d, qval, extra=None):
     if fmt == oracle.Q8_0:
         b = blocks.enc_q8_0(H(d), np.full(32, qval))
@@ -101,6 +141,9 @@ def _const_row(fmt, nblocks, d, qval, extra=None):
     elif fmt == oracle.Q4_K:
         sc, mn, dmin = extra
         b = blocks.enc_q4_k(H(d), H(dmin), np.full(8, sc), np.full(8, mn), np.full(256, qval))
+    elif fmt == oracle.Q5_K:
+        sc, mn, dmin = extra
+        b = blocks.enc_q5_k(H(d), H(dmin), np.full(8, sc), np.full(8, mn), np.full(256, qval))
     else:
         b = blocks.enc_q6_k(H(d), np.full(16, extra), np.full(256, qval))
     return np.frombuffer(b * nblocks, np.uint8)
@@ -111,6 +154,7 @@ def _const_row(fmt, nblocks, d, qval, extra=None):
     (oracle.Q4_0, 0.0048828125, 3, None, lambda d, q, e: d * (q - 8)),
     (oracle.Q4_K, 0.001953125, 11, (37, 21, 0.00390625), lambda d, q, e: d * e[0] * q - e[2] * e[1]),
     (oracle.Q6_K, 0.0009765625, 50, -93, lambda d, q, e: d * e * (q - 32)),
+    (oracle.Q5_K, 0.001953125, 27, (45, 9, 0.0078125), lambda d, q, e: d * e[0] * q - e[2] * e[1]),
 ])
 def test_constant_block_gemv_closed_form(fmt, d, q, extra, coef):
     # every weight equal => y = w * sum(x); d chosen as powers of two (exact in f16)
