@@ -47,7 +47,7 @@ typedef enum nt_status {
   NT_EUNSUPPORTED = -5  /* shape outside what the kernels handle (see limits)   */
 } nt_status;
 
-/* GGUF block formats (p1 "About" format list).  Byte layouts:
+/* GGUF weight formats (p1 "About" format list).  Byte layouts:
  *   NT_Q8_0  34 B / 32 weights : f16 d, int8 q[32];          w = d*q
  *   NT_Q4_0  18 B / 32 weights : f16 d, u8 qs[16];           w = d*(q-8),
  *            q of element j<16 = low nibble of qs[j], of j+16 = high nibble.
@@ -58,12 +58,21 @@ typedef enum nt_status {
  *   NT_Q6_K 210 B / 256 weights: u8 ql[128], u8 qh[64], int8 sc[16], f16 d;
  *            w_e = d*sc[e/16]*(q_e-32), q_e 6-bit from ql nibble + qh 2 bits
  *            (GGUF order).
- * A matrix is `rows` consecutive rows, each cols/QK consecutive blocks. */
-typedef enum nt_fmt { NT_Q8_0 = 0, NT_Q4_0 = 1, NT_Q4_K = 2, NT_Q6_K = 3 } nt_fmt;
+ *   NT_Q5_K 176 B / 256 weights: f16 d, f16 dmin, u8 scales[12], u8 qh[32],
+ *            u8 qs[128]; scales, mins and nibbles as NT_Q4_K, and the fifth
+ *            bit of element l (< 32) of sub-block s is bit s of qh[l];
+ *            q in 0..31, w = d*sc*q - dmin*m.
+ *   NT_F16    2 B / weight: IEEE binary16.    NT_F32  4 B / weight: binary32.
+ * A matrix is `rows` consecutive rows, each cols/QK consecutive blocks.
+ * NT_F16 and NT_F32 are GEMV/small-M formats (nt_gemv_q, nt_gemm_q_small)
+ * and embedding rows; decoder layers and the LM head take the block formats. */
+typedef enum nt_fmt {
+  NT_Q8_0 = 0, NT_Q4_0 = 1, NT_Q4_K = 2, NT_Q6_K = 3, NT_Q5_K = 4, NT_F16 = 5, NT_F32 = 6
+} nt_fmt;
 
-/* Weights per block (32 or 256), 0 for an unknown format. */
+/* Weights per block (32, 256, or 1 for F16/F32), 0 for an unknown format. */
 int nt_block_elems(int fmt);
-/* Bytes per block (34, 18, 144, 210), 0 for an unknown format. */
+/* Bytes per block (34, 18, 144, 210, 176, 2, 4), 0 for an unknown format. */
 int nt_block_bytes(int fmt);
 /* Bytes of one row of `cols` weights; 0 if fmt is unknown or cols % QK != 0. */
 int64_t nt_row_bytes(int fmt, int64_t cols);
@@ -76,9 +85,11 @@ int64_t nt_max_cols(void);
  * y = W x (GEMV on quantized weights; p2 "Architecture et structure du code").
  *   W: device, fmt blocks, rows x cols, 16-byte aligned.
  *   x: device fp32 [cols], 16-byte aligned.   y: device fp32 [rows], overwritten.
- *   cols must be a positive multiple of the format's QK and <= nt_max_cols().
- *   rows == 0 is a no-op.  Inside the kernel x is held as 16-bit fixed point
- *   per 32-element block (relative error of y about 1e-5).
+ *   cols must be a positive multiple of the format's QK and <= nt_max_cols()
+ *   (F16: a multiple of 8, F32: of 4, so rows are whole 16-byte loads).
+ *   rows == 0 is a no-op.  For the block formats x is held inside the kernel
+ *   as 16-bit fixed point per 32-element block (relative error of y about
+ *   1e-5); F16/F32 weights multiply x in fp32.
  */
 int nt_gemv_q(int fmt, const void* W, const float* x, float* y, int64_t rows, int64_t cols, void* stream);
 
@@ -94,7 +105,8 @@ size_t nt_gemm_q_small_workspace_bytes(int M, int64_t rows, int64_t cols);
  *   X: device fp32 [M][cols], rows 16-byte aligned; Y: device fp32 [M][rows],
  *   overwritten; 1 <= M <= 8.  The weights are read once for all M tokens:
  *   int8 MFMA tiles over the same 16-bit fixed-point activation as nt_gemv_q
- *   (M == 1 is nt_gemv_q).
+ *   (M == 1 is nt_gemv_q).  F16/F32 weights: one fp32 stream over the rows,
+ *   no workspace (ws may be NULL).
  *   ws: device workspace of ws_bytes >= nt_gemm_q_small_workspace_bytes(M,
  *   rows, cols), 16-byte aligned (may be NULL when M == 1); its contents need
  *   no initialisation.  Calls that share a workspace must not overlap.

@@ -13,7 +13,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libnt.so")
 
-NT_Q8_0, NT_Q4_0, NT_Q4_K, NT_Q6_K = 0, 1, 2, 3
+NT_Q8_0, NT_Q4_0, NT_Q4_K, NT_Q6_K, NT_Q5_K, NT_F16, NT_F32 = 0, 1, 2, 3, 4, 5, 6
 STATUS = {0: "NT_OK", -1: "NT_EINVAL", -2: "NT_EALIGN", -3: "NT_EWORKSPACE", -4: "NT_EHIP", -5: "NT_EUNSUPPORTED"}
 
 

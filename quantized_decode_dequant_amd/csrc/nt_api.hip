@@ -66,6 +66,7 @@ int check_layer(const nt_layer_cfg& c, const nt_layer& L) {
   const int64_t cols[7] = {c.hidden, c.hidden, c.hidden, nq, c.hidden, c.hidden, c.ffn};
   for (int i = 0; i < 7; ++i) {
     if (!fmt_cols_ok(mats[i]->fmt, cols[i])) return NT_EINVAL;
+    if (block_elems(mats[i]->fmt) == 1) return NT_EUNSUPPORTED;  // F16/F32: GEMV only
     if (!mats[i]->data) return NT_EINVAL;
     if (!aligned16(mats[i]->data)) return NT_EALIGN;
   }
@@ -333,7 +334,9 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
   if (sa.cos_acc && M != 1) return NT_EINVAL;
   if (!fmt_cols_ok(m.tok_emb.fmt, m.cfg.hidden) || !fmt_cols_ok(m.lm_head.fmt, m.cfg.hidden)) return NT_EINVAL;
   if (!m.tok_emb.data || !m.lm_head.data || !m.out_norm) return NT_EINVAL;
+  if (block_elems(m.lm_head.fmt) == 1) return NT_EUNSUPPORTED;  // the LM head runs on the block-format engine
   if (!aligned16(m.lm_head.data) || !aligned16(m.out_norm) || !aligned16(ws_v)) return NT_EALIGN;
+  if (!aligned16(m.tok_emb.data)) return NT_EALIGN;
   const int fs = m.first_streamed;
   if (fs < 0 || fs > m.n_layer) return NT_EINVAL;
   auto skipped = [&](int l) { return (m.skip && m.skip[l]) || (sa.skip2 && sa.skip2[l]); };
@@ -500,6 +503,10 @@ int nt_gemv_q(int fmt, const void* W, const float* x, float* y, int64_t rows, in
   if (rows == 0) return NT_OK;
   if (!W || !x || !y) return NT_EINVAL;
   if (!aligned16(W) || !aligned16(x)) return NT_EALIGN;
+  if (qk == 1) {  // F16 / F32: rows of 16-byte loads
+    if ((cols * block_bytes(fmt)) % 16 != 0) return NT_EINVAL;
+    return launch_gemv_f(fmt, W, x, y, 1, (int)rows, (int)cols, static_cast<hipStream_t>(stream));
+  }
   Job job;
   const uint8_t* Wp = static_cast<const uint8_t*>(W);
   const int r = (int)rows;
@@ -526,6 +533,10 @@ int nt_gemm_q_small(int fmt, const void* W, const float* X, float* Y, int M, int
   if (!W || !X || !Y) return NT_EINVAL;
   if (!aligned16(W) || !aligned16(X) || (M > 1 && (cols * 4) % 16 != 0)) return NT_EALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (qk == 1) {  // F16 / F32: no staging, no workspace
+    if ((cols * block_bytes(fmt)) % 16 != 0) return NT_EINVAL;
+    return launch_gemv_f(fmt, W, X, Y, M, (int)rows, (int)cols, st);
+  }
   const uint8_t* Wp = static_cast<const uint8_t*>(W);
   const int r = (int)rows;
   int rc;

@@ -343,6 +343,31 @@ __global__ __launch_bounds__(256) void k_embed(int fmt, const uint8_t* __restric
       const int q = (s & 1) ? (qs[l] >> 4) : (qs[l] & 15);
       out[l] = d * (float)scale * (float)q - dmin * (float)mn;
     }
+  } else if (fmt == NT_Q5_K) {
+    const uint8_t* b = row + (int64_t)(grp / 8) * 176;
+    const int s = grp % 8;  // sub-block
+    const float d = h2f(b), dmin = h2f(b + 2);
+    const uint8_t* sc = b + 4;
+    int scale, mn;
+    if (s < 4) {
+      scale = sc[s] & 63;
+      mn = sc[s + 4] & 63;
+    } else {
+      scale = (sc[s + 4] & 15) | ((sc[s - 4] >> 6) << 4);
+      mn = (sc[s + 4] >> 4) | ((sc[s] >> 6) << 4);
+    }
+    const uint8_t* qh = b + 16;
+    const uint8_t* qs = b + 48 + 32 * (s / 2);
+    for (int l = 0; l < 32; ++l) {
+      const int q = ((s & 1) ? (qs[l] >> 4) : (qs[l] & 15)) | (((qh[l] >> s) & 1) << 4);
+      out[l] = d * (float)scale * (float)q - dmin * (float)mn;
+    }
+  } else if (fmt == NT_F16) {
+    const uint8_t* b = row + (int64_t)grp * 64;
+    for (int l = 0; l < 32; ++l) out[l] = h2f(b + 2 * l);
+  } else if (fmt == NT_F32) {
+    const float* b = reinterpret_cast<const float*>(row) + (int64_t)grp * 32;
+    for (int l = 0; l < 32; ++l) out[l] = b[l];
   } else {  // Q6_K
     const uint8_t* b = row + (int64_t)(grp / 8) * 210;
     const int e0 = 32 * (grp % 8);

@@ -99,22 +99,27 @@ __device__ __forceinline__ float unit_q4_0(uint32_t seg, int k, bool two, NT_XAR
   return acc;
 }
 
-// Q4_K: unit k is chunk c = k%4 (64 weights) of superblock k/4: quant bytes
-// 32c..32c+31, whose low nibbles are the chunk's first 32 weights (sub-block
-// 2c) and high nibbles the next 32 (sub-block 2c+1).  w = d*sc*q - dmin*m.
-// hd: the superblock's first 16 bytes (d, dmin, scales); q0, q1: the chunk's
-// 32 quant bytes.
-__device__ __forceinline__ float q4k_dot(const uint4& hd, const uint4& q0, const uint4& q1, int c, NT_XARGS) {
-  const float d = h2f(hd.x & 0xffffu), dmin = h2f(hd.x >> 16);
-  // 6-bit scales and mins of sub-blocks 2c and 2c+1, byte-parallel: bytes
-  // 0 and 1 of SC and MN (sub-blocks 0..3 sit in the low six bits of scale
-  // bytes 0..7; 4..7 take four bits from bytes 8..11 and two from the top of
-  // bytes 0..7)
+// K-quant superblock header (Q4_K, Q5_K): the 6-bit scales and mins of
+// sub-blocks 2c and 2c+1, byte-parallel in bytes 0 and 1 of SC and MN.
+// Sub-blocks 0..3 sit in the low six bits of scale bytes 0..7; 4..7 take four
+// bits from bytes 8..11 and two from the top of bytes 0..7.  hd: the
+// superblock's first 16 bytes (d, dmin, scales).
+__device__ __forceinline__ void kq_scale_min(const uint4& hd, int c, uint32_t& SC, uint32_t& MN) {
   const int h = 16 * (c & 1);
   const uint32_t a0 = hd.y >> h, a1 = hd.z >> h, a2 = hd.w >> h;
   const bool lowsb = c < 2;
-  const uint32_t SC = lowsb ? (a0 & 0x3F3Fu) : ((a2 & 0x0F0Fu) | ((a0 >> 2) & 0x3030u));
-  const uint32_t MN = lowsb ? (a1 & 0x3F3Fu) : (((a2 >> 4) & 0x0F0Fu) | ((a1 >> 2) & 0x3030u));
+  SC = lowsb ? (a0 & 0x3F3Fu) : ((a2 & 0x0F0Fu) | ((a0 >> 2) & 0x3030u));
+  MN = lowsb ? (a1 & 0x3F3Fu) : (((a2 >> 4) & 0x0F0Fu) | ((a1 >> 2) & 0x3030u));
+}
+
+// Q4_K: unit k is chunk c = k%4 (64 weights) of superblock k/4: quant bytes
+// 32c..32c+31, whose low nibbles are the chunk's first 32 weights (sub-block
+// 2c) and high nibbles the next 32 (sub-block 2c+1).  w = d*sc*q - dmin*m.
+// q0, q1: the chunk's 32 quant bytes.
+__device__ __forceinline__ float q4k_dot(const uint4& hd, const uint4& q0, const uint4& q1, int c, NT_XARGS) {
+  const float d = h2f(hd.x & 0xffffu), dmin = h2f(hd.x >> 16);
+  uint32_t SC, MN;
+  kq_scale_min(hd, c, SC, MN);
   const uint32_t qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
   int AH = 0, AL = 0, BH = 0, BL = 0;
 #pragma unroll
@@ -135,6 +140,37 @@ __device__ __forceinline__ float unit_q4_k(uint32_t seg, int k, NT_XARGS) {
   const uint32_t blk = seg + 144u * (k >> 2);
   const int c = k & 3;
   return q4k_dot(ld128(blk), ld128(blk + 16 + 32 * c), ld128(blk + 32 + 32 * c), c, xh, xl, xs, xm, xf);
+}
+
+// Q5_K: the layout of Q4_K with 32 bytes qh between the scales and the
+// nibbles (176 bytes per superblock).  Element l (< 32) of sub-block s takes
+// its fifth bit from bit s of qh[l]; for chunk c the first 32 weights use
+// bit 2c and the next 32 bit 2c+1.  q in 0..31, w = d*sc*q - dmin*m.
+__device__ __forceinline__ float unit_q5_k(uint32_t seg, int k, NT_XARGS) {
+  const uint32_t blk = seg + 176u * (k >> 2);
+  const int c = k & 3;
+  const uint4 hd = ld128(blk), h0 = ld128(blk + 16), h1 = ld128(blk + 32);
+  const uint4 q0 = ld128(blk + 48 + 32 * c), q1 = ld128(blk + 64 + 32 * c);
+  const float d = h2f(hd.x & 0xffffu), dmin = h2f(hd.x >> 16);
+  uint32_t SC, MN;
+  kq_scale_min(hd, c, SC, MN);
+  const uint32_t qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+  const uint32_t hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+  const int sa = 2 * c, sb = 2 * c + 1;
+  int AH = 0, AL = 0, BH = 0, BL = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t lo5 = (qv[i] & 0x0F0F0F0Fu) | (((hv[i] >> sa) & 0x01010101u) << 4);
+    const uint32_t hi5 = ((qv[i] >> 4) & 0x0F0F0F0Fu) | (((hv[i] >> sb) & 0x01010101u) << 4);
+    AH = i == 0 ? dot4z(lo5, xh[0]) : dot4(lo5, xh[i], AH);
+    AL = i == 0 ? dot4z(lo5, xl[0]) : dot4(lo5, xl[i], AL);
+    BH = i == 0 ? dot4z(hi5, xh[8]) : dot4(hi5, xh[8 + i], BH);
+    BL = i == 0 ? dot4z(hi5, xl[8]) : dot4(hi5, xl[8 + i], BL);
+  }
+  const int SA = (AH << 8) + AL, SB = (BH << 8) + BL;
+  const float t = xs[0] * (float)(SC & 0xffu) * (float)SA + xs[1] * (float)(SC >> 8) * (float)SB;
+  const float u = (float)(MN & 0xffu) * xf[0] + (float)(MN >> 8) * xf[1];
+  return d * t - dmin * u;
 }
 
 // Q6_K: unit k covers elements 64p..64p+63 of superblock k/4, p = k%4, i.e.
@@ -466,6 +502,7 @@ __device__ __forceinline__ float seg_compute(const Seg& sg, uint32_t slab, int l
       switch (FMT >= 0 ? FMT : (FMT == kFmtK46 ? (sg.fmt == NT_Q6_K ? NT_Q6_K : NT_Q4_K) : sg.fmt)) {
         case NT_Q4_K: acc += unit_q4_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j], xr.sf[j]); break;
         case NT_Q6_K: acc += unit_q6_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j], xr.sf[j]); break;
+        case NT_Q5_K: acc += unit_q5_k(seg, k, xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j], xr.sf[j]); break;
         case NT_Q8_0:
           acc += unit_q8_0(seg, k, !(sg.half && k == sg.nunits - 1), xr.hi[j], xr.lo[j], xr.sc[j], xr.sm[j], xr.sf[j]);
           break;

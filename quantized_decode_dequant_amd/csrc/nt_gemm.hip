@@ -254,7 +254,7 @@ __device__ __forceinline__ long pack2(uint32_t lo, uint32_t hi) { return (long)(
 
 // Scale table of the tile-slice, per (entry, row): entry = 32-block (Q6_K:
 // 16-weight group).  A block's contribution is alpha (s S) - beta (s sum X)
-// with beta = 0 (Q8_0), 8 alpha (Q4_0), 32 alpha (Q6_K); Q4_K keeps
+// with beta = 0 (Q8_0), 8 alpha (Q4_0), 32 alpha (Q6_K); Q4_K and Q5_K keep
 // (alpha, beta) pairs.  Layout: scl + 4 * (16 entry + row), pairs 8 * (...).
 __device__ __forceinline__ void scale_table(const TSeg& sg, uint32_t po, uint32_t scl, int lane) {
   const int row = lane & 15, kq = lane >> 4;
@@ -270,7 +270,8 @@ __device__ __forceinline__ void scale_table(const TSeg& sg, uint32_t po, uint32_
       }
       break;
     }
-    case NT_Q4_K: {
+    case NT_Q4_K:
+    case NT_Q5_K: {  // same superblock header
       uint32_t h[3];
       ld_unaligned<3>(po + 4, h);
       const float d = h2f(ld16(po)), dmin = h2f(ld16(po + 2));
@@ -314,6 +315,14 @@ __device__ __forceinline__ long a_operand(const TSeg& sg, uint32_t po, int kb, i
       ld_unaligned<2>(po + 16 + 32 * (kb >> 1) + 8 * kq, v);
       const int sh = 4 * (kb & 1);
       return pack2((v[0] >> sh) & 0x0F0F0F0Fu, (v[1] >> sh) & 0x0F0F0F0Fu);
+    }
+    case NT_Q5_K: {  // Q4_K nibbles (after 32 bytes qh) plus bit kb of qh[l] as the fifth bit
+      uint32_t h[2];
+      ld_unaligned<2>(po + 48 + 32 * (kb >> 1) + 8 * kq, v);
+      ld_unaligned<2>(po + 16 + 8 * kq, h);
+      const int sh = 4 * (kb & 1);
+      return pack2(((v[0] >> sh) & 0x0F0F0F0Fu) | (((h[0] >> kb) & 0x01010101u) << 4),
+                   ((v[1] >> sh) & 0x0F0F0F0Fu) | (((h[1] >> kb) & 0x01010101u) << 4));
     }
     default: {  // Q6_K: elements 32 kb + 8 kq .. +7: half n, quarter q'
       const int n = kb >> 2, qq = kb & 3;
@@ -376,7 +385,7 @@ __device__ __forceinline__ void tseg_compute(const JobM& job, const TSeg& sg, ui
     } else {
       const float2 r = *reinterpret_cast<const float2*>(nt_smem + rec);
       const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bo, zero, 0, 0, 0);
-      if (sg.fmt == NT_Q4_K) {
+      if (sg.fmt == NT_Q4_K || sg.fmt == NT_Q5_K) {
         const uint32_t e = scl + 8u * (uint32_t)(16 * kb + 4 * kq);
         const float4 p0 = *reinterpret_cast<const float4*>(nt_smem + e);
         const float4 p1 = *reinterpret_cast<const float4*>(nt_smem + e + 16);
@@ -677,6 +686,7 @@ int plan_job_m(JobM& job, int nmat, const uint8_t* const* W, const int* fmt, con
   for (int m = 0; m < nmat; ++m) {
     const int qk = block_elems(fmt[m]);
     if (qk == 0 || cols % qk != 0 || rows[m] < 0) return NT_EINVAL;
+    if (qk == 1) return NT_EUNSUPPORTED;  // F16/F32 have their own kernel
     if (pairs && (rows[m] & 1)) return NT_EINVAL;
     if (paired && rows[m] != rows[0]) return NT_EINVAL;
     job.W[m] = W[m];

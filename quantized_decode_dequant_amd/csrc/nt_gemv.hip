@@ -130,6 +130,7 @@ int launch_lpl(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_
   if constexpr (LPL == 3) {
     if (f == NT_Q4_K) return launch_k<EPI, LPL, NT_Q4_K>(job, pro, ea, stream);
     if (f == NT_Q4_0) return launch_k<EPI, LPL, NT_Q4_0>(job, pro, ea, stream);
+    if (f == NT_Q5_K) return launch_k<EPI, LPL, NT_Q5_K>(job, pro, ea, stream);
   }
   if constexpr (LPL <= 4) {
     if (f == NT_Q6_K) return launch_k<EPI, LPL, NT_Q6_K>(job, pro, ea, stream);
@@ -172,6 +173,7 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
   for (int m = 0; m < nmat; ++m) {
     const int qk = block_elems(fmt[m]);
     if (qk == 0 || cols % qk != 0) return NT_EINVAL;
+    if (qk == 1) return NT_EUNSUPPORTED;  // F16/F32 have their own GEMV kernel
     if (pairs && (rows[m] & 1)) return NT_EINVAL;
     if (paired && rows[m] != rows[0]) return NT_EINVAL;
     if (rows[m] < 0) return NT_EINVAL;

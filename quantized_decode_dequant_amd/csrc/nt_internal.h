@@ -21,7 +21,12 @@ constexpr int kMaxMats = 3;       // matrices one engine launch walks (Q, K, V)
 constexpr int64_t kMaxCols = 49152;
 
 __host__ __device__ inline int block_elems(int fmt) {
-  return fmt == NT_Q4_K || fmt == NT_Q6_K ? 256 : (fmt == NT_Q8_0 || fmt == NT_Q4_0 ? 32 : 0);
+  switch (fmt) {
+    case NT_Q8_0: case NT_Q4_0: return 32;
+    case NT_Q4_K: case NT_Q5_K: case NT_Q6_K: return 256;
+    case NT_F16: case NT_F32: return 1;
+  }
+  return 0;
 }
 __host__ __device__ inline int block_bytes(int fmt) {
   switch (fmt) {
@@ -29,6 +34,9 @@ __host__ __device__ inline int block_bytes(int fmt) {
     case NT_Q4_0: return 18;
     case NT_Q4_K: return 144;
     case NT_Q6_K: return 210;
+    case NT_Q5_K: return 176;
+    case NT_F16: return 2;
+    case NT_F32: return 4;
   }
   return 0;
 }
@@ -192,6 +200,10 @@ int launch_embed(int fmt, const void* E, const int32_t* tokens, int M, int vocab
                  hipStream_t stream);
 int argmax_parts(int n);
 int launch_argmax(const float* logits, int M, int n, float* pv, int* pi, int32_t* out, hipStream_t stream);
+
+// F16 / F32 weights (nt_gemv_f.hip): Y[t][r] = W X[t] for M <= 8 tokens,
+// Y rows `rows` apart; cols a multiple of 16 / element size, W and X 16-byte aligned.
+int launch_gemv_f(int fmt, const void* W, const float* X, float* Y, int M, int rows, int cols, hipStream_t stream);
 
 // Layer-skip calibration and speculative-round kernels (nt_spec.hip).
 // acc[0] += cosine similarity of a and b (n floats).

@@ -11,7 +11,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import BLOCK, Q4_0, Q4_K, Q6_K, Q8_0, key, matrix_bytes, normal_f16, normal_f32, quant, uint_below
+from . import BLOCK, F16, F32, Q4_0, Q4_K, Q5_K, Q6_K, Q8_0, key, matrix_bytes, normal_f16, normal_f32, quant, uint_below
 
 # stream tags
 T_WQ, T_WK, T_WV, T_WO, T_WG, T_WU, T_WD = 1, 2, 3, 4, 5, 6, 7
@@ -49,6 +49,9 @@ ALL_Q8_0 = {m: Q8_0 for m in MATS}
 ALL_Q6_K = {m: Q6_K for m in MATS}
 # Q4_K_M mix: Q4_K for Q/K/O/gate/up, Q6_K for V/down.
 Q4_K_M = dict(wq=Q4_K, wk=Q4_K, wv=Q6_K, wo=Q4_K, wg=Q4_K, wu=Q4_K, wd=Q6_K)
+# Q5_K_M mix: Q5_K for Q/K/O/gate/up, Q6_K for V/down.
+Q5_K_M = dict(wq=Q5_K, wk=Q5_K, wv=Q6_K, wo=Q5_K, wg=Q5_K, wu=Q5_K, wd=Q6_K)
+ALL_Q5_K = {m: Q5_K for m in MATS}
 
 # workload ids (first key tag)
 W_GEMV_Q8 = 1

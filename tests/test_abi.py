@@ -33,8 +33,10 @@ def test_library_exports_every_declared_symbol():
 def test_metadata_calls_without_gpu():
     import quantized_decode_dequant_amd as nt
     L = nt.lib()
-    assert [L.nt_block_elems(f) for f in range(4)] == [32, 32, 256, 256]
-    assert [L.nt_block_bytes(f) for f in range(4)] == [34, 18, 144, 210]
+    assert [L.nt_block_elems(f) for f in range(7)] == [32, 32, 256, 256, 256, 1, 1]
+    assert [L.nt_block_bytes(f) for f in range(7)] == [34, 18, 144, 210, 176, 2, 4]
+    assert L.nt_row_bytes(nt.NT_Q5_K, 8192) == 5632
+    assert L.nt_row_bytes(nt.NT_F16, 100) == 200
     assert L.nt_block_elems(9) == 0
     assert L.nt_row_bytes(nt.NT_Q4_K, 8192) == 4608
     assert L.nt_row_bytes(nt.NT_Q6_K, 28672) == 23520

@@ -13,7 +13,7 @@ from tests.gpu_util import device, rel_inf, say, to_dev
 pytestmark = pytest.mark.gpu
 
 GEMV_TOL = 2e-3
-FMTS = [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K]
+FMTS = [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K, synth.Q5_K, synth.F16, synth.F32]
 
 
 def run_gemv(fmt, rows, cols, tag, guard=64):
@@ -62,6 +62,35 @@ def test_gemv_70b_projection_shapes(name):
     err = rel_inf(y, ref)
     say(f"  70B {name} {rows}x{cols} max rel err {err:.2e}")
     assert err <= GEMV_TOL
+
+
+def test_gemv_70b_gate_q5_k_full():
+    rows, cols = wl.LLAMA70B.mat_shape("wg")
+    W, x, y = run_gemv(synth.Q5_K, rows, cols, tag=150)
+    err = rel_inf(y, oracle.gemv(synth.Q5_K, W, x, rows, cols))
+    say(f"  70B gate Q5_K {rows}x{cols} max rel err {err:.2e}")
+    assert err <= GEMV_TOL
+
+
+@pytest.mark.parametrize("fmt,cols", [(synth.F16, 8), (synth.F16, 1000), (synth.F16, 4104),
+                                      (synth.F32, 4), (synth.F32, 1004), (synth.F32, 8196)])
+@pytest.mark.parametrize("rows", [1, 3, 257])
+def test_gemv_unquantized_ragged(fmt, cols, rows):
+    W, x, y = run_gemv(fmt, rows, cols, tag=cols + rows)
+    err = rel_inf(y, oracle.gemv(fmt, W, x, rows, cols))
+    say(f"  max rel err {err:.2e}")
+    assert err <= 1e-5
+
+
+def test_gemv_unquantized_argument_errors():
+    import torch
+    import quantized_decode_dequant_amd as nt
+    L = nt.lib()
+    buf = torch.zeros(4096, dtype=torch.uint8, device=device())
+    a = buf.data_ptr()
+    assert L.nt_gemv_q(synth.F16, a, a, a, 4, 4, None) == -1     # 4 x 2 bytes: not whole 16-byte loads
+    assert L.nt_gemv_q(synth.F32, a, a, a, 4, 6, None) == -1
+    assert L.nt_gemv_q(synth.F32, a + 4, a, a, 4, 8, None) == -2
 
 
 def test_gemv_deterministic_and_empty():

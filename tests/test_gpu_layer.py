@@ -53,7 +53,8 @@ def check(got, ref, kc, vc, li, n_past, M):
                               np.delete(c_ref, range(n_past, n_past + M), axis=1))
 
 
-@pytest.mark.parametrize("fmts", [wl.ALL_Q8_0, wl.ALL_Q4_0, wl.Q4_K_M, wl.ALL_Q6_K], ids=["q8_0", "q4_0", "q4_k_m", "q6_k"])
+@pytest.mark.parametrize("fmts", [wl.ALL_Q8_0, wl.ALL_Q4_0, wl.Q4_K_M, wl.ALL_Q6_K, wl.Q5_K_M, wl.ALL_Q5_K],
+                         ids=["q8_0", "q4_0", "q4_k_m", "q6_k", "q5_k_m", "q5_k"])
 @pytest.mark.parametrize("n_past,M", [(37, 1), (0, 1), (20, 3), (63, 1)])
 def test_layer_tiny(fmts, n_past, M):
     got, ref, kc, vc, li = run_layer(wl.TINY, fmts, wl.W_TEST, 3, 64, n_past, M)
@@ -65,7 +66,8 @@ def test_layer_tiny(fmts, n_past, M):
 GROUP8 = wl.LayerShape(hidden=2048, n_head=16, n_kv_head=2, head_dim=128, ffn=4096)
 
 
-@pytest.mark.parametrize("fmts", [wl.ALL_Q8_0, wl.ALL_Q4_0, wl.Q4_K_M, wl.ALL_Q6_K], ids=["q8_0", "q4_0", "q4_k_m", "q6_k"])
+@pytest.mark.parametrize("fmts", [wl.ALL_Q8_0, wl.ALL_Q4_0, wl.Q4_K_M, wl.ALL_Q6_K, wl.Q5_K_M],
+                         ids=["q8_0", "q4_0", "q4_k_m", "q6_k", "q5_k_m"])
 @pytest.mark.parametrize("n_past", [0, 63, 64, 200, 1000])
 def test_layer_group8_batch1(fmts, n_past):
     # 1..1001 positions: one split of one round up to many splits, ragged last round

@@ -58,6 +58,20 @@ def test_stack_tiny_greedy(fmts):
     assert g_toks == o_toks
 
 
+@pytest.mark.parametrize("emb_fmt,head_fmt", [(wl.F16, wl.Q5_K), (wl.F32, wl.Q8_0), (wl.Q5_K, wl.Q4_K)],
+                         ids=["f16_q5k", "f32_q8", "q5k_q4k"])
+def test_stack_embedding_and_head_formats(emb_fmt, head_fmt):
+    hs = HostStack(wl.TINY, wl.Q5_K_M, n_layer=2, vocab=700, max_ctx=40, n_past=9, wid=wl.W_TEST + 6,
+                   emb_fmt=emb_fmt, head_fmt=head_fmt)
+    steps = 4
+    g_toks, g_lgs = greedy_gpu(hs.device_model(device()), hs.first_token, 9, steps, hs.vocab)
+    o_toks, o_lgs, margins = greedy_oracle(hs.oracle_model(), hs.first_token, 9, steps)
+    say(f"gpu {g_toks} oracle {o_toks}")
+    for s in range(steps):
+        assert rel_inf(g_lgs[s], o_lgs[s]) <= LOGIT_TOL, s
+    assert g_toks == o_toks
+
+
 def test_verify_matches_oracle_and_decode():
     import torch
     dev = device()
