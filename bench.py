@@ -219,6 +219,12 @@ def workload_gemv(dev) -> dict:
         r, c = wl.LLAMA70B.mat_shape(n)
         cases.append((f"70b_{n}_{synth.FMT_NAMES[wl.Q4_K_M[n]]}_{r}x{c}", wl.Q4_K_M[n], r, c, wl.W_GEMV_70B,
                       wl.MAT_TAG[n]))
+    # the other formats of the pages' list, at the same kinds of shape
+    for n in ["wq", "wg", "wd"]:
+        r, c = wl.LLAMA70B.mat_shape(n)
+        cases.append((f"x70b_{n}_q5_k_{r}x{c}", wl.Q5_K, r, c, wl.W_GEMV_70B, 20 + wl.MAT_TAG[n]))
+    cases.append(("xf16_4096x4096", wl.F16, 4096, 4096, wl.W_GEMV_Q8, 1))
+    cases.append(("xf32_4096x4096", wl.F32, 4096, 4096, wl.W_GEMV_Q8, 2))
     layer_bytes, layer_ms = 0, 0.0
     for name, fmt, rows, cols, wid, tag in cases:
         wbytes = rows * nt.row_bytes(fmt, cols)
@@ -244,7 +250,8 @@ def workload_gemv(dev) -> dict:
         del Ws, base
     return {"metric": "quant GEMV effective GB/s (% HBM peak)", "unit": "GB/s", "n_gpus": 1,
             "value": res["q8_0_4096x4096"]["gbs"], "higher_is_better": True, "data": "synthetic",
-            "config": {"workload": "single GEMVs: Q8_0 4096x4096 and the 70B-shaped Q4_K_M projections, "
+            "config": {"workload": "single GEMVs: Q8_0 4096x4096 and the 70B-shaped Q4_K_M projections "
+                                   "(plus, prefixed x, Q5_K 70B-shaped and F16/F32 4096x4096), "
                                    "weights rotated over distinct copies"},
             "read_ceiling_gbs": round(read_gbs, 1), "gemv": res,
             "seven_gemv_layer_gbs": round(layer_bytes / layer_ms / 1e6, 1)}
