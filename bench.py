@@ -28,6 +28,9 @@ Secondary workloads (`--workload`, one JSON line each; not the headline):
            draft K = 3 or 7 tokens, one streamed verify pass checks them):
            round, draft-step and verify times, tokens emitted per round, and
            plain streamed decode with 20 calibrated layers skipped.
+  tiers    nt_plan_tiers places the 80-layer Q4_K_M and Q6_K stacks within
+           24 and 48 GB of device memory; greedy decode time at each
+           placement.
 """
 from __future__ import annotations
 
@@ -295,7 +298,7 @@ class StreamedStack:
     layer is a copy of one seeded layer (the timing does not depend on the
     weight values), with its own KV cache."""
 
-    def __init__(self, dev, max_ctx: int, n_past: int = 4096, n_layer: int = 80, fs: int = 36):
+    def __init__(self, dev, max_ctx: int, n_past: int = 4096, n_layer: int = 80, fs: int = 36, mix=None):
         import torch
 
         import quantized_decode_dequant_amd as nt
@@ -306,14 +309,16 @@ class StreamedStack:
         self.n_layer, self.fs, self.vocab, self.n_past = n_layer, fs, vocab, n_past
         self.cfg = cfg = cfg_of(shape, max_ctx)
         t0 = time.time()
-        self.li = li = wl.gen_layer(shape, wl.ALL_Q6_K, wl.W_VERIFY_70B, 0, max_ctx, n_past)
+        self.mix = mix = wl.ALL_Q6_K if mix is None else mix
+        self.li = li = wl.gen_layer(shape, mix, wl.W_VERIFY_70B, 0, max_ctx, n_past)
         blob = pack_blob(cfg, li)
         self.sb = sb = blob.size
         self.host = host = [None] * n_layer
         for l in range(fs, n_layer):
             host[l] = torch.empty(sb, dtype=torch.uint8, pin_memory=True)
             host[l].numpy()[:] = blob
-        self.stage = (torch.empty(sb, dtype=torch.uint8, device=dev), torch.empty(sb, dtype=torch.uint8, device=dev))
+        self.stage = (torch.empty(sb, dtype=torch.uint8, device=dev), torch.empty(sb, dtype=torch.uint8, device=dev)) \
+            if fs < n_layer else (None, None)
         self.layers = [DeviceLayer(li, dev, weights_on_device=(l < fs)) for l in range(n_layer)]
         log(f"[bench] streamed stack ready: {fs} resident + {n_layer - fs} streamed layers of {sb / 1e6:.1f} MB "
             f"({time.time() - t0:.0f} s)")
@@ -327,6 +332,53 @@ class StreamedStack:
                                 self.norm, first_streamed=fs, host_layers=host, stage=self.stage, stage_bytes=sb,
                                 copy_stream=self.copy_stream)
         self.stream_bytes = sb * (n_layer - fs)
+
+
+def workload_tiers(dev) -> dict:
+    """Tier placement (p1 "3-Tier Adaptive Caching"): nt_plan_tiers places the
+    80-layer 70B-shaped stack (Q4_K_M and Q6_K, context 4096) within a device
+    budget, and greedy decode runs at that placement: the resident layers read
+    HBM, the streamed ones cross the host link once per token."""
+    import torch
+
+    import quantized_decode_dequant_amd as nt
+    from quantized_decode_dequant_amd.model import cfg_of
+    from synth import workloads as wl
+
+    n_past, vocab = 4096, 128256
+    cfg = cfg_of(wl.LLAMA70B, n_past + 16)
+    res = {}
+    for name, mix in (("q4_k_m", wl.Q4_K_M), ("q6_k", wl.ALL_Q6_K)):
+        for budget in (24 * 10**9, 48 * 10**9):
+            p = nt.plan_tiers(cfg, [mix] * 80, vocab, wl.Q6_K, wl.Q6_K, 1, budget)
+            if not p["ok"]:
+                res[f"{name}_{budget // 10**9}gb"] = {"plan": p}
+                continue
+            S = StreamedStack(dev, n_past + 16, n_past, fs=p["first_streamed"], mix=mix)
+            h = S.h
+            stream = torch.cuda.current_stream()
+            ws = torch.zeros(h.workspace_bytes(1), dtype=torch.uint8, device=dev)
+            tok = torch.tensor([int(wl.gen_tokens(wl.W_VERIFY_70B, 1, vocab)[0])], dtype=torch.int32, device=dev)
+            pos = torch.tensor([n_past], dtype=torch.int32, device=dev)
+            nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+            used = torch.cuda.memory_allocated(dev)
+            ms = timed(lambda: h.decode_step(tok, pos, nxt, ws, None, stream), 3)
+            key = f"{name}_{budget // 10**9}gb"
+            res[key] = {"resident_layers": p["first_streamed"], "streamed_layers": p["n_streamed"],
+                        "plan_device_gb": round(p["device_bytes"] / 1e9, 3),
+                        "torch_allocated_gb": round(used / 1e9, 3),
+                        "host_gb_per_token": round(p["host_bytes"] / 1e9, 3),
+                        "decode_ms": round(ms, 2), "tokens_per_s": round(1e3 / ms, 3),
+                        "h2d_gbs": round(p["host_bytes"] / ms / 1e6, 1)}
+            log(f"[bench] tiers {key}: {p['first_streamed']} resident + {p['n_streamed']} streamed, "
+                f"{ms:.1f} ms per token")
+            del S, h, ws
+            torch.cuda.empty_cache()
+    return {"metric": "decode tok/s at a planned device/pinned-host placement", "unit": "tokens/s", "n_gpus": 1,
+            "higher_is_better": True, "data": "synthetic",
+            "config": {"workload": "80-layer llama70b-shaped stacks (Q4_K_M, Q6_K), context 4096, placed by "
+                                   "nt_plan_tiers within 24 and 48 GB of device memory"},
+            "tiers": res}
 
 
 def workload_verify(dev, passes: int) -> dict:
@@ -482,7 +534,7 @@ def main():
                     help="also run one device copy of 256 MiB (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize", metavar="DIR", help="print per-kernel statistics of a rocprofv3 output "
                     "directory (kernel trace or counter csv) and exit")
-    ap.add_argument("--workload", choices=["decode", "gemv", "layer8b", "verify", "spec"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "gemv", "layer8b", "verify", "spec", "tiers"], default="decode",
                     help="decode (the headline, default) or one of the secondary workloads")
     ap.add_argument("--passes", type=int, default=5, help="verify workload: timed passes per M; spec: rounds per K")
     args = ap.parse_args()
@@ -502,7 +554,8 @@ def main():
     if args.workload != "decode":
         fn = {"gemv": lambda: workload_gemv(dev), "layer8b": lambda: workload_layer8b(dev),
               "verify": lambda: workload_verify(dev, args.passes),
-              "spec": lambda: workload_spec(dev, args.passes)}[args.workload]
+              "spec": lambda: workload_spec(dev, args.passes),
+              "tiers": lambda: workload_tiers(dev)}[args.workload]
         print(json.dumps(fn()), flush=True)
         return
     n_past = 4096

@@ -241,6 +241,46 @@ int nt_calibrate_step(const nt_model* model, const int32_t* token_dev, const int
  */
 int nt_select_skip(const float* score, int n_layer, int n_skip, int first, int last, uint8_t* mask);
 
+/*
+ * Tier placement (p1 "3-Tier Adaptive Caching": layers resident in GPU memory
+ * need no I/O, layers in pinned RAM need a host-to-device copy per pass, and
+ * the split is made automatically; p1 notes that Q4_K_M fits 36 layers of a
+ * 70B model in 24 GB where the larger format fits 26).  The NVMe/mmap tier is
+ * not part of this library.
+ *
+ * nt_plan_tiers picks the largest prefix of layers whose weights stay in
+ * device memory within `device_budget` bytes, next to what every placement
+ * keeps on the device; the rest are streamed from pinned host memory through
+ * two staging buffers (nt_model.first_streamed, stage, stage_bytes).  Byte
+ * counts (each buffer rounded up to 256 B):
+ *   fixed    = embedding + LM head + final gains + every layer's two gains and
+ *              K/V caches (cfg.max_ctx positions) + workspace (nt_decode_step
+ *              for M == 1; nt_spec_step with K = M - 1 for M >= 2, which also
+ *              covers nt_verify_step with M tokens);
+ *   resident = nt_layer_blob_bytes of the layers below first_streamed;
+ *   stage    = the largest nt_layer_blob_bytes among the streamed layers;
+ *   device   = fixed + resident + 2 * stage  (<= device_budget);
+ *   host     = nt_layer_blob_bytes summed over the streamed layers, the bytes
+ *              copied per pass (<= host_budget; pass SIZE_MAX for no limit).
+ * The largest first_streamed in 0..n_layer meeting both limits is chosen
+ * (n_layer: nothing streamed, stage 0).  Skip flags are not considered.
+ *   model: host struct; only cfg, n_layer, vocab, the formats of tok_emb and
+ *          lm_head and the formats of layers[] are read (pointers may be NULL).
+ *   M: tokens per pass the workspace must hold, 1..8.
+ * Returns NT_EINVAL for a bad model or M, NT_EUNSUPPORTED when no placement
+ * meets the limits (*plan then describes first_streamed = 0).  No GPU work.
+ */
+typedef struct nt_tier_plan {
+  int32_t first_streamed;   /* layers [0, first_streamed) resident            */
+  int32_t n_streamed;       /* n_layer - first_streamed                       */
+  uint64_t fixed_bytes;     /* device bytes every placement needs             */
+  uint64_t resident_bytes;  /* weights of the resident layers                 */
+  uint64_t stage_bytes;     /* bytes of each of the two staging buffers       */
+  uint64_t device_bytes;    /* fixed + resident + 2 * stage                   */
+  uint64_t host_bytes;      /* pinned bytes of the streamed layers (per pass) */
+} nt_tier_plan;
+int nt_plan_tiers(const nt_model* model, int M, size_t device_budget, size_t host_budget, nt_tier_plan* plan);
+
 /* Workspace bytes nt_spec_step needs for K draft tokens (0 if K is outside 1..7). */
 size_t nt_spec_workspace_bytes(const nt_model* model, int K);
 

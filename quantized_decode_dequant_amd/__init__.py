@@ -47,6 +47,13 @@ class Model(ctypes.Structure):
                 ("stage_bytes", ctypes.c_size_t), ("copy_stream", ctypes.c_void_p), ("skip", ctypes.c_void_p)]
 
 
+class TierPlan(ctypes.Structure):
+    _fields_ = [("first_streamed", ctypes.c_int32), ("n_streamed", ctypes.c_int32),
+                ("fixed_bytes", ctypes.c_uint64), ("resident_bytes", ctypes.c_uint64),
+                ("stage_bytes", ctypes.c_uint64), ("device_bytes", ctypes.c_uint64),
+                ("host_bytes", ctypes.c_uint64)]
+
+
 _lib = None
 
 EXPORTS = {
@@ -77,6 +84,8 @@ EXPORTS = {
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "nt_select_skip": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_void_p]),
+    "nt_plan_tiers": (ctypes.c_int, [ctypes.POINTER(Model), ctypes.c_int, ctypes.c_size_t, ctypes.c_size_t,
+                                     ctypes.POINTER(TierPlan)]),
     "nt_spec_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Model), ctypes.c_int]),
     "nt_spec_step": (ctypes.c_int, [ctypes.POINTER(Model), ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -187,6 +196,34 @@ def select_skip(score, n_skip: int, first: int = 0, last: int | None = None):
     _check("nt_select_skip", lib().nt_select_skip(sc.ctypes.data, n, n_skip, first, n if last is None else last,
                                                   mask.ctypes.data))
     return mask
+
+
+def plan_tiers(cfg: LayerCfg, layer_fmts: list, vocab: int, emb_fmt: int, head_fmt: int, M: int,
+               device_budget: int, host_budget: int | None = None) -> dict:
+    """Device/pinned-host placement of a stack's layers (nt_plan_tiers; host only).
+    layer_fmts: one {matrix name: format} dict per layer.  Returns the plan's fields
+    and ok (False when no placement meets the limits)."""
+    n = len(layer_fmts)
+    arr = (Layer * max(1, n))()
+    for i, f in enumerate(layer_fmts):
+        for name in MAT_NAMES:
+            setattr(arr[i], name, QMat(f[name], None))
+    m = Model()
+    m.cfg = cfg
+    m.n_layer = n
+    m.vocab = vocab
+    m.tok_emb = QMat(emb_fmt, None)
+    m.lm_head = QMat(head_fmt, None)
+    m.layers = ctypes.cast(arr, ctypes.POINTER(Layer))
+    m.first_streamed = n
+    plan = TierPlan()
+    hb = (1 << 64) - 1 if host_budget is None else host_budget
+    rc = lib().nt_plan_tiers(ctypes.byref(m), M, device_budget, hb, ctypes.byref(plan))
+    if rc not in (0, -5):
+        _check("nt_plan_tiers", rc)
+    out = {k: int(getattr(plan, k)) for k, _ in TierPlan._fields_}
+    out["ok"] = rc == 0
+    return out
 
 
 def layer_cfg(hidden, n_head, n_kv_head, head_dim, ffn, max_ctx, rope_theta=5e5, rms_eps=1e-5) -> LayerCfg:

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "nt_internal.h"
 
@@ -630,6 +631,60 @@ int nt_select_skip(const float* score, int n_layer, int n_skip, int first, int l
     mask[best] = 1;
   }
   return NT_OK;
+}
+
+int nt_plan_tiers(const nt_model* model, int M, size_t device_budget, size_t host_budget, nt_tier_plan* plan) {
+  if (!model || !plan || M < 1 || M > 8) return NT_EINVAL;
+  const nt_model& m = *model;
+  if (!cfg_ok(m.cfg) || m.n_layer < 0 || m.vocab <= 0 || (m.n_layer > 0 && !m.layers)) return NT_EINVAL;
+  const nt_layer_cfg& c = m.cfg;
+  if (!fmt_cols_ok(m.tok_emb.fmt, c.hidden) || !fmt_cols_ok(m.lm_head.fmt, c.hidden)) return NT_EINVAL;
+  const int n = m.n_layer;
+  std::vector<size_t> blob(n);
+  for (int l = 0; l < n; ++l) {
+    const nt_layer& L = m.layers[l];
+    const int64_t nq = (int64_t)c.n_head * c.head_dim;
+    const nt_qmat* mats[7] = {&L.wq, &L.wk, &L.wv, &L.wo, &L.wg, &L.wu, &L.wd};
+    const int64_t cols[7] = {c.hidden, c.hidden, c.hidden, nq, c.hidden, c.hidden, c.ffn};
+    for (int i = 0; i < 7; ++i)
+      if (!fmt_cols_ok(mats[i]->fmt, cols[i]) || block_elems(mats[i]->fmt) == 1) return NT_EINVAL;
+    size_t off[8];
+    blob_offsets(c, L, off);
+    blob[l] = off[7];
+  }
+  // what every placement keeps on the device
+  const size_t gains = up256((size_t)c.hidden * 4);
+  const size_t kv = up256((size_t)c.n_kv_head * c.max_ctx * c.head_dim * 2);
+  size_t fixed = up256((size_t)qmat_bytes(m.tok_emb.fmt, m.vocab, c.hidden)) +
+                 up256((size_t)qmat_bytes(m.lm_head.fmt, m.vocab, c.hidden)) + gains;
+  fixed += (size_t)n * (2 * gains + 2 * kv);
+  fixed += M == 1 ? step_ws(m, 1).total : spec_ws(m, M - 1).total;
+  // streamed suffix sums and their largest blob, for every first_streamed k
+  std::vector<size_t> host(n + 1, 0), stage(n + 1, 0);
+  for (int k = n - 1; k >= 0; --k) {
+    host[k] = host[k + 1] + blob[k];
+    stage[k] = std::max(stage[k + 1], blob[k]);
+  }
+  size_t resident = 0;
+  for (int l = 0; l < n; ++l) resident += blob[l];
+  int best = -1;
+  nt_tier_plan p{};
+  for (int k = n; k >= 0; --k) {
+    if (k < n) resident -= blob[k];
+    p.first_streamed = k;
+    p.n_streamed = n - k;
+    p.fixed_bytes = fixed;
+    p.resident_bytes = resident;
+    p.stage_bytes = stage[k];
+    p.device_bytes = fixed + resident + 2 * stage[k];
+    p.host_bytes = host[k];
+    if (p.device_bytes <= device_budget && p.host_bytes <= host_budget) {
+      best = k;
+      break;
+    }
+  }
+  *plan = p;
+  return best >= 0 ? NT_OK : NT_EUNSUPPORTED;
 }
 
 size_t nt_spec_workspace_bytes(const nt_model* model, int K) {
