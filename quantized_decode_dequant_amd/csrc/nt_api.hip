@@ -30,7 +30,7 @@ bool cfg_ok(const nt_layer_cfg& c) {
   if (c.hidden % 32 || c.ffn % 32 || (c.n_head * c.head_dim) % 32) return false;
   if (c.hidden > kMaxCols || c.ffn > kMaxCols || c.n_head * c.head_dim > kMaxCols) return false;
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return false;
-  if ((int64_t)c.max_ctx > 1024LL * std::min(256, 16384 / c.head_dim)) return false;  // at most 1024 attention splits
+  if ((int64_t)c.max_ctx > 1024LL * std::min(256, std::max(64, 8192 / c.head_dim))) return false;  // <= 1024 attention splits
   return true;
 }
 

@@ -28,9 +28,11 @@ constexpr int kMaxSplits = 1024;  // position splits of one attention
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Positions per split for a head size: K and V tiles of at most 32 KB each.
+// Positions per split for a head size: K and V tiles of 16 KB each (64 to
+// 256 positions), so a 4096-position cache of 8 kv heads makes ~520
+// workgroups, two per CU.
 template <int HD>
-constexpr int attn_chunk() { return 16384 / HD < 256 ? 16384 / HD : 256; }
+constexpr int attn_chunk() { return 8192 / HD < 64 ? 64 : (8192 / HD > 256 ? 256 : 8192 / HD); }
 
 // q: fp32 [n_query][n_head][HD] (query i at position pos+i attends to
 // 0..pos+i).  Partials: part_o [n_query][nsplit][n_head][HD],
@@ -77,6 +79,20 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
   const int G = n_head / n_kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
+  // the query rows do not depend on the position: their loads go out first,
+  // beside the position's, and are converted once the K/V loads are issued
+  const bool hv = r16 < G;
+  float4 qa[KS], qb[KS];
+  {
+    const float* qp = q + ((int64_t)query * n_head + g * G + (hv ? r16 : 0)) * HD + 8 * q4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qa[ks] = *reinterpret_cast<const float4*>(qp + 32 * ks);
+      qb[ks] = *reinterpret_cast<const float4*>(qp + 32 * ks + 4);
+    }
+  }
+  // the position's load (and its wait) may not move above the query's loads
+  __builtin_amdgcn_sched_barrier(0);
   const int pos = *pos_ptr;
   const int n_pos = pos + query + 1;
   const bool ok = pos >= 0 && pos + query < max_ctx;
@@ -103,6 +119,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
       const int c = tid + kAttnThreads * r, t = c / CPR, d8 = c % CPR;
       vr[r] = *reinterpret_cast<const uint4*>(vg + (int64_t)(t < nt ? t : 0) * HD + 8 * d8);
     }
+    // every K and V load is issued before the first wait for V
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
       const int c = tid + kAttnThreads * r, t = c / CPR, d8 = c % CPR;
@@ -113,12 +131,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
   v8h qh[KS], ql[KS];
   {
     const float scale = 1.0f / sqrtf((float)HD);
-    const bool hv = r16 < G;
-    const float* qp = q + ((int64_t)query * n_head + g * G + (hv ? r16 : 0)) * HD + 8 * q4;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const float4 a = *reinterpret_cast<const float4*>(qp + 32 * ks);
-      const float4 b = *reinterpret_cast<const float4*>(qp + 32 * ks + 4);
+      const float4 a = qa[ks], b = qb[ks];
       const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -172,7 +187,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
 
   // o = P V over this split
   const int tg = wave % (4 / KSPLIT), kp = wave / (4 / KSPLIT);
-  const bool hv = r16 < G;
   const int hr = hv ? r16 : 0;
   v4f oacc[TPW];
 #pragma unroll
@@ -233,31 +247,36 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                       const int32_t* pos_ptr, int n_head, int head_dim, int chunk,
                                                       int nsplit, int max_ctx, float* __restrict__ o) {
-  constexpr int kPre = 8;  // splits per thread held in registers
+  constexpr int kPre = 12;  // splits per thread held in registers
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[8];
   __shared__ float s_acc[8][32];
   const int nch = head_dim / 32;
   const int h = blockIdx.x / nch, d0 = 32 * (blockIdx.x % nch), query = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int pos = *pos_ptr;
-  const bool ok = pos >= 0 && pos + query < max_ctx;
-  const int n_pos = pos + query + 1;
-  const int ns = ok ? min(nsplit, (n_pos + chunk - 1) / chunk) : 0;
   const float* ml = part_ml + ((int64_t)query * nsplit * n_head + h) * 2;
   const int dl = tid & 31, j = tid >> 5;
   const float* po = part_o + ((int64_t)query * nsplit * n_head + h) * head_dim + d0 + dl;
   const int64_t sst = (int64_t)n_head * head_dim;
+  // every split's partials were written by this attention's split kernel, so
+  // their loads go out with the position's; splits past the position are
+  // masked by selects below
+  // (indices clamped to the last split rather than branched around, so all
+  // loads issue back to back)
   float ov[kPre];
 #pragma unroll
-  for (int k = 0; k < kPre; ++k) {
-    const int s = j + 8 * k;
-    ov[k] = s < ns ? po[s * sst] : 0.f;
-  }
-  float m0 = -FLT_MAX, l0 = 0.f;
-  if (tid < ns) {
-    m0 = ml[(int64_t)tid * n_head * 2];
-    l0 = ml[(int64_t)tid * n_head * 2 + 1];
+  for (int k = 0; k < kPre; ++k) ov[k] = po[min(j + 8 * k, nsplit - 1) * sst];
+  const int sm = min(tid, nsplit - 1);
+  float m0 = ml[(int64_t)sm * n_head * 2];
+  float l0 = ml[(int64_t)sm * n_head * 2 + 1];
+  __builtin_amdgcn_sched_barrier(0);
+  const int pos = *pos_ptr;
+  const bool ok = pos >= 0 && pos + query < max_ctx;
+  const int n_pos = pos + query + 1;
+  const int ns = ok ? min(nsplit, (n_pos + chunk - 1) / chunk) : 0;
+  if (tid >= ns) {
+    m0 = -FLT_MAX;
+    l0 = 0.f;
   }
   // M = max over splits
   float m = m0;
@@ -428,10 +447,10 @@ __global__ __launch_bounds__(64) void k_argmax_final(const float* __restrict__ p
 
 }  // namespace
 
-// Split geometry: 16384/head_dim positions per split (K and V tiles of
-// 32 KB).  Independent of the device, so workspace sizes are.
+// Split geometry: attn_chunk positions per split.  Independent of the
+// device, so workspace sizes are.
 void attn_plan(int head_dim, int max_ctx, int& chunk, int& nsplit) {
-  chunk = std::min(256, 16384 / head_dim);
+  chunk = std::min(256, std::max(64, 8192 / head_dim));
   nsplit = (max_ctx + chunk - 1) / chunk;
 }
 
