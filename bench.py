@@ -16,7 +16,8 @@ timed with HIP events on its launch stream inside the timed region;
 Secondary workloads (`--workload`, one JSON line each; not the headline):
   gemv     the single Q8_0 4096x4096 GEMV and the seven 70B-shaped Q4_K_M
            projections, each rotated over distinct weight copies (more than
-           the 256 MB last-level cache): effective GB/s per GEMV.
+           the 256 MB last-level cache), timed as HIP graph replays of
+           back-to-back launches: effective GB/s per GEMV.
   layer8b  one 8B-shaped Q4_0 decoder layer at position 512, over 32 distinct
            layers: GB/s per layer.
   verify   80 Q6_K 70B-shaped layers, 36 resident and 44 streamed from
@@ -206,6 +207,34 @@ def timed(fn, n: int) -> float:
     return e0.elapsed_time(e1) / n
 
 
+def timed_graph(fn, n: int, reps: int = 5) -> float:
+    """Mean milliseconds per fn() call with n calls captured in one HIP graph
+    and the graph replayed `reps` times (after one eager warm call and one
+    warm replay): the launches run back to back on the device, without the
+    host's per-call cost between them."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(n):
+                fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / (reps * n)
+
+
 def workload_gemv(dev) -> dict:
     """Configs 1 and 3: effective GB/s of each GEMV, weights rotated over
     distinct copies so no launch finds them in the last-level cache."""
@@ -242,20 +271,25 @@ def workload_gemv(dev) -> dict:
             nt.gemv_q(fmt, Ws[it[0] % ncopy], x, y, rows, cols)
             it[0] += 1
 
-        ms = timed(one, max(100, 2 * ncopy))
+        n_calls = max(100, 2 * ncopy)
+        ms_eager = timed(one, n_calls)
+        ms = timed_graph(one, n_calls)
         alg = wbytes + 4 * cols + 4 * rows
         res[name] = dict(us=round(ms * 1e3, 2), gbs=round(alg / ms / 1e6, 1),
-                         frac_peak=round(alg / ms / 1e6 / HBM_PEAK_GBS, 4), copies=ncopy, alg_bytes=alg)
+                         frac_peak=round(alg / ms / 1e6 / HBM_PEAK_GBS, 4), copies=ncopy, alg_bytes=alg,
+                         us_eager_launches=round(ms_eager * 1e3, 2))
         if name.startswith("70b"):
             layer_bytes += alg
             layer_ms += ms
-        log(f"[bench] {name}: {ms * 1e3:.1f} us, {alg / ms / 1e6:.0f} GB/s")
+        log(f"[bench] {name}: {ms * 1e3:.1f} us ({ms_eager * 1e3:.1f} us launched one by one from the host), "
+            f"{alg / ms / 1e6:.0f} GB/s")
         del Ws, base
     return {"metric": "quant GEMV effective GB/s (% HBM peak)", "unit": "GB/s", "n_gpus": 1,
             "value": res["q8_0_4096x4096"]["gbs"], "higher_is_better": True, "data": "synthetic",
             "config": {"workload": "single GEMVs: Q8_0 4096x4096 and the 70B-shaped Q4_K_M projections "
                                    "(plus, prefixed x, Q5_K 70B-shaped and F16/F32 4096x4096), "
-                                   "weights rotated over distinct copies"},
+                                   "weights rotated over distinct copies; times are HIP graph replays of "
+                                   "back-to-back launches"},
             "read_ceiling_gbs": round(read_gbs, 1), "gemv": res,
             "seven_gemv_layer_gbs": round(layer_bytes / layer_ms / 1e6, 1)}
 
@@ -537,6 +571,8 @@ def main():
     ap.add_argument("--workload", choices=["decode", "gemv", "layer8b", "verify", "spec", "tiers"], default="decode",
                     help="decode (the headline, default) or one of the secondary workloads")
     ap.add_argument("--passes", type=int, default=5, help="verify workload: timed passes per M; spec: rounds per K")
+    ap.add_argument("--graph-steps", action="store_true",
+                    help="decode: also time the steps as replays of one captured step (reported beside value)")
     args = ap.parse_args()
     if args.summarize:
         summarize_profile(args.summarize)
@@ -625,6 +661,35 @@ def main():
     achieved = ffn_bytes / ffn_avg_s / 1e9
     traffic = counter_traffic("ffn_gate_up", ffn_bytes)
 
+    graph_ms = None
+    if args.graph_steps:
+        # one decode step (with the token hand-off and the position increment)
+        # captured in a HIP graph, replayed from context 4096 again
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                h.decode_step(tok, pos, nxt, ws, None, side)
+                tok.copy_(nxt)
+                pos.add_(1)
+        stream.wait_stream(side)
+        tok.fill_(first)
+        pos.fill_(n_past)
+        g.replay()
+        torch.cuda.synchronize()
+        tok.fill_(first)
+        pos.fill_(n_past)
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        log(f"[bench] graph replays: {graph_ms:.3f} ms/token")
+        del g
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (oracle, {args.cpu_sample_layers} layers)")
@@ -662,6 +727,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "tokens_head": toks[:8],
+        **({"ms_per_step_graph_replay": round(graph_ms, 4)} if graph_ms is not None else {}),
     }
     print(json.dumps(out), flush=True)
 
