@@ -47,7 +47,15 @@ namespace {
 
 
 template <int EPI, int LPL, int FMT>
-__global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, EpiArgs ea) {
+__global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro_in, EpiArgs ea) {
+  constexpr bool kBurst = EPI == EPI_STORE_BURST;
+  // a burst launch has no RMSNorm and no RoPE (the host checks): with the
+  // gains known absent, their registers stay free for the weight buffers
+  ProArgs pro = pro_in;
+  if constexpr (kBurst) {
+    pro.gain = nullptr;
+    pro.rope_hd = 0;
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform: keep everything derived from it (segment ids
   // and addresses) in scalar registers
@@ -57,16 +65,26 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, Epi
   if (tid == 0) sti32(job.ctl, 0);  // claim counter; the prologue's barrier publishes it
   XStage xst;
   stage_load(job, pro, tid, xst);
-  const float ss = stage_norm(job, pro, tid, xst);  // the activation has arrived
-  const float r = stage_scale(job, pro, tid, ss);
   uint4 pa[LPL], pb[LPL];
   Seg sa, sb;
   int k_cur = wave, k_nxt = wave + job.nwaves;
-  // two segments in flight before the prologue (unconditional loads: see seg_null)
-  sa = k_cur < sh.nseg ? seg_at(job, sh, k_cur) : seg_null(job);
-  seg_load(sa, lane, pa);
-  sb = k_nxt < sh.nseg ? seg_at(job, sh, k_nxt) : seg_null(job);
-  seg_load(sb, lane, pb);
+  // two segments in flight before the prologue (unconditional loads: see
+  // seg_null); a burst launch issues them behind the activation's loads, so
+  // the activation's wait below leaves them in flight
+  if constexpr (kBurst) {
+    sa = k_cur < sh.nseg ? seg_at(job, sh, k_cur) : seg_null(job);
+    seg_load(sa, lane, pa);
+    sb = k_nxt < sh.nseg ? seg_at(job, sh, k_nxt) : seg_null(job);
+    seg_load(sb, lane, pb);
+  }
+  const float ss = stage_norm(job, pro, tid, xst);  // the activation has arrived
+  const float r = stage_scale(job, pro, tid, ss);
+  if constexpr (!kBurst) {
+    sa = k_cur < sh.nseg ? seg_at(job, sh, k_cur) : seg_null(job);
+    seg_load(sa, lane, pa);
+    sb = k_nxt < sh.nseg ? seg_at(job, sh, k_nxt) : seg_null(job);
+    seg_load(sb, lane, pb);
+  }
   stage_finish(job, pro, tid, xst, r);  // ends with a workgroup barrier
   if (k_cur < sh.nseg) {
     XR xr;
@@ -79,7 +97,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro, Epi
     } while (k_cur < sh.nseg);
   }
   __syncthreads();
-  share_epilogue<EPI>(job, sh, tid, job.nwaves * 64, ea);
+  share_epilogue<kBurst ? EPI_STORE : EPI>(job, sh, tid, job.nwaves * 64, ea);
 }
 
 struct DevInfo {
@@ -108,11 +126,12 @@ int launch_k(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t 
       return NT_EHIP;
     attr_set = true;
   }
-  trace_before(EPI, stream);
+  constexpr int kind = EPI == EPI_STORE_BURST ? EPI_STORE : EPI;  // trace kinds are the epilogues
+  trace_before(kind, stream);
   hipLaunchKernelGGL((k_qgemv<EPI, LPL, FMT>), dim3(job.grid), dim3(64 * job.nwaves), job.lds_bytes, stream, job, pro,
                      ea);
   const bool ok = hipGetLastError() == hipSuccess;
-  trace_after(EPI, stream);
+  trace_after(kind, stream);
   return ok ? NT_OK : NT_EHIP;
 }
 
@@ -246,7 +265,14 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
 
 int launch_gemv(const Job& job, const ProArgs& pro, int epi, const EpiArgs& ea, hipStream_t stream) {
   switch (epi) {
-    case EPI_STORE: return launch_epi<EPI_STORE>(job, pro, ea, stream);
+    case EPI_STORE: {
+      // every share's segments fit the two buffers of its waves: one burst
+      const int vper = job.paired ? 2 : 1;
+      const int64_t nseg_max = (int64_t)(job.wg_base + (job.wg_rem ? 1 : 0)) * job.unit * vper * job.nslice;
+      if (!pro.gain && pro.rope_hd == 0 && nseg_max <= 2 * job.nwaves)
+        return launch_epi<EPI_STORE_BURST>(job, pro, ea, stream);
+      return launch_epi<EPI_STORE>(job, pro, ea, stream);
+    }
     case EPI_RESID: return launch_epi<EPI_RESID>(job, pro, ea, stream);
     case EPI_QKV: return launch_epi<EPI_QKV>(job, pro, ea, stream);
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(job, pro, ea, stream);

@@ -103,6 +103,10 @@ enum Epi : int {
   EPI_RESID = 1,   // y[r] += acc              (residual add, in place)
   EPI_QKV = 2,     // RoPE + q store + f16 K/V append
   EPI_SWIGLU = 3,  // y[r] = silu(acc_gate) * acc_up
+  // EPI_STORE for a launch whose whole share is in flight at once (at most
+  // two segments per wave) and has no RMSNorm: the weight loads are issued
+  // right behind the activation's, without waiting for it
+  EPI_STORE_BURST = 4,
 };
 
 struct EpiArgs {
