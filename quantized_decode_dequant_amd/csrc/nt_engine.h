@@ -332,7 +332,8 @@ __device__ __forceinline__ float stage_scale(const Job& job, const ProArgs& pro,
   return 1.0f / sqrtf(tot / (float)job.cols + pro.eps);
 }
 
-// r: the factor from stage_scale.
+// r: the factor from stage_scale.  The caller ends the staging with a
+// workgroup barrier.
 __device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro, int tid, XStage& st, float r) {
   const int NT = job.nwaves * 64, lane = tid & 63;
   const int nround = (job.cols + 4 * NT - 1) / (4 * NT);
@@ -360,7 +361,6 @@ __device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro,
       stf(job.rope + 8u * i + 4, (float)sin(ang));
     }
   }
-  __syncthreads();
 }
 
 // ----------------------------------------------------------- segment stream

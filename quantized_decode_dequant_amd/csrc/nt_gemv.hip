@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro_in, 
   uint4 pa[LPL], pb[LPL];
   Seg sa, sb;
   int k_cur = wave, k_nxt = wave + job.nwaves;
-  // two segments in flight before the prologue (unconditional loads: see
+  // two segments in flight before the stream (unconditional loads: see
   // seg_null); a burst launch issues them behind the activation's loads, so
   // the activation's wait below leaves them in flight
   if constexpr (kBurst) {
@@ -79,13 +79,21 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro_in, 
   }
   const float ss = stage_norm(job, pro, tid, xst);  // the activation has arrived
   const float r = stage_scale(job, pro, tid, ss);
-  if constexpr (!kBurst) {
+  if constexpr (kBurst) {
+    stage_finish(job, pro, tid, xst, r);
+  } else {
+    // The first segment's loads go out before the quantization and the
+    // second's after it.  A wave cannot issue loads faster than the memory
+    // system drains them, so with both issued first the quantization waited
+    // behind the whole first burst (and the compute behind the quantization):
+    // this way it runs while the first segment is in flight.
     sa = k_cur < sh.nseg ? seg_at(job, sh, k_cur) : seg_null(job);
     seg_load(sa, lane, pa);
+    stage_finish(job, pro, tid, xst, r);
     sb = k_nxt < sh.nseg ? seg_at(job, sh, k_nxt) : seg_null(job);
     seg_load(sb, lane, pb);
   }
-  stage_finish(job, pro, tid, xst, r);  // ends with a workgroup barrier
+  __syncthreads();  // the staged activation is complete
   if (k_cur < sh.nseg) {
     XR xr;
     int xslice = -1;
