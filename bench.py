@@ -20,6 +20,8 @@ Secondary workloads (`--workload`, one JSON line each; not the headline):
            back-to-back launches: effective GB/s per GEMV.
   layer8b  one 8B-shaped Q4_0 decoder layer at position 512, over 32 distinct
            layers: GB/s per layer.
+  gemm_small  the verify pass's small-M GEMM on the 70B-shaped gate (Q4_K)
+           and down (Q6_K) matrices for M = 1, 2, 4, 8: weight GB/s per pass.
   verify   80 Q6_K 70B-shaped layers, 36 resident and 44 streamed from
            pinned host memory through two HBM staging buffers, verify passes
            of M = 1, 2, 4, 8 tokens from context 4096: verified positions/s,
@@ -326,6 +328,50 @@ def workload_layer8b(dev) -> dict:
             "us_per_layer": round(ms * 1e3, 2), "alg_bytes": alg, "frac_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
 
 
+def workload_gemm_small(dev) -> dict:
+    """Small-M GEMMs of the verify pass (nt_gemm_q_small): the 70B-shaped
+    Q4_K gate (28672 x 8192) and Q6_K down (8192 x 28672) matrices for M = 1,
+    2, 4, 8 tokens, weights rotated over distinct copies, timed as HIP graph
+    replays.  M = 1 is the GEMV engine; M >= 2 reads the weights once for all
+    tokens on int8 MFMA."""
+    import torch
+
+    import quantized_decode_dequant_amd as nt
+    from synth import workloads as wl
+
+    res = {}
+    for n in ("wg", "wd"):
+        fmt = wl.Q4_K_M[n]
+        rows, cols = wl.LLAMA70B.mat_shape(n)
+        wbytes = rows * nt.row_bytes(fmt, cols)
+        ncopy = max(2, -(-512_000_000 // wbytes))
+        base = torch.from_numpy(wl.gen_matrix(fmt, rows, cols, wl.W_GEMV_70B, 0, wl.MAT_TAG[n])).to(dev)
+        Ws = [base.clone() for _ in range(ncopy)]
+        X = torch.from_numpy(wl.gen_x(8 * cols, wl.W_GEMV_70B)).to(dev).view(8, cols)
+        Y = torch.empty(8, rows, dtype=torch.float32, device=dev)
+        for M in (1, 2, 4, 8):
+            ws_bytes = nt.gemm_q_small_workspace_bytes(M, rows, cols)
+            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+            it = [0]
+
+            def one():
+                nt.gemm_q_small(fmt, Ws[it[0] % ncopy], X, Y, M, rows, cols, ws)
+                it[0] += 1
+
+            ms = timed_graph(one, max(20, 2 * ncopy))
+            alg = wbytes + 4 * M * (rows + cols)
+            key = f"70b_{n}_{'q4_k' if fmt == wl.Q4_K else 'q6_k'}_{rows}x{cols}_M{M}"
+            res[key] = {"us": round(ms * 1e3, 2), "weight_gbs": round(wbytes / ms / 1e6, 1),
+                        "token_rows_per_us": round(M * rows / (ms * 1e3), 1), "alg_bytes": alg}
+            log(f"[bench] {key}: {ms * 1e3:.1f} us, weights at {wbytes / ms / 1e6:.0f} GB/s")
+        del Ws, base
+    return {"metric": "small-M GEMM: weight GB/s per pass of M tokens", "unit": "GB/s", "n_gpus": 1,
+            "higher_is_better": True, "data": "synthetic",
+            "config": {"workload": "70B-shaped Q4_K gate and Q6_K down matrices, M = 1, 2, 4, 8 tokens, weights "
+                                   "rotated over distinct copies, HIP graph replays"},
+            "gemm_small": res}
+
+
 class StreamedStack:
     """80 Q6_K 70B-shaped layers, the first 36 resident in HBM and the other
     44 in pinned host memory, streamed through two HBM staging buffers; every
@@ -568,7 +614,7 @@ def main():
                     help="also run one device copy of 256 MiB (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize", metavar="DIR", help="print per-kernel statistics of a rocprofv3 output "
                     "directory (kernel trace or counter csv) and exit")
-    ap.add_argument("--workload", choices=["decode", "gemv", "layer8b", "verify", "spec", "tiers"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "gemv", "layer8b", "gemm_small", "verify", "spec", "tiers"], default="decode",
                     help="decode (the headline, default) or one of the secondary workloads")
     ap.add_argument("--passes", type=int, default=5, help="verify workload: timed passes per M; spec: rounds per K")
     ap.add_argument("--graph-steps", action="store_true",
@@ -591,7 +637,7 @@ def main():
         fn = {"gemv": lambda: workload_gemv(dev), "layer8b": lambda: workload_layer8b(dev),
               "verify": lambda: workload_verify(dev, args.passes),
               "spec": lambda: workload_spec(dev, args.passes),
-              "tiers": lambda: workload_tiers(dev)}[args.workload]
+              "tiers": lambda: workload_tiers(dev), "gemm_small": lambda: workload_gemm_small(dev)}[args.workload]
         print(json.dumps(fn()), flush=True)
         return
     n_past = 4096
