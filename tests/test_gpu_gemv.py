@@ -43,6 +43,19 @@ def test_gemv_parity_small(fmt, rows, cols):
     assert err <= GEMV_TOL
 
 
+@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_K, synth.Q6_K])
+@pytest.mark.parametrize("rows", [8192, 8448])
+def test_gemv_burst_boundary(fmt, rows):
+    # 4096 columns (one slice) over 256 workgroups of 16 waves: 8192 rows give
+    # every workgroup 32 segments (the whole share in flight at once, the burst
+    # launch), 8448 give some 33 (the streaming launch)
+    W, x, y = run_gemv(fmt, rows, 4096, tag=rows + fmt)
+    ref = oracle.gemv(fmt, W, x, rows, 4096)
+    err = rel_inf(y, ref)
+    say(f"  max rel err {err:.2e}")
+    assert err <= GEMV_TOL
+
+
 def test_gemv_q8_0_4096_full():
     # the single-GEMV workload: Q8_0 4096 x 4096
     W, x, y = run_gemv(synth.Q8_0, 4096, 4096, tag=1)

@@ -127,3 +127,45 @@ def test_streamed_layers_bitwise_equal_resident(M):
         assert torch.equal(r[1], res[0][1])
         for a, b in zip(r[2], res[0][2]):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("M", [2, 3])
+def test_verify_few_tokens_equals_sequential_decode(M):
+    # up to two tokens per layer (three for the LM head) run the GEMV engine
+    # once per token: a verify pass of M tokens then equals M decode steps
+    # bitwise in the layers that took that path; M = 3 layers use the small-M
+    # GEMM and are held to the oracle bar instead
+    import torch
+    dev = device()
+    hs = HostStack(wl.TINY, wl.Q4_K_M, n_layer=3, vocab=901, max_ctx=40, n_past=13, wid=wl.W_TEST + 8)
+    toks = wl.gen_tokens(wl.W_TEST + 8, M, hs.vocab)
+    hv = hs.device_model(dev)
+    out = torch.zeros(M, dtype=torch.int32, device=dev)
+    logits = torch.zeros(M * hs.vocab, dtype=torch.float32, device=dev)
+    pos = torch.tensor([13], dtype=torch.int32, device=dev)
+    hv.verify_step(torch.from_numpy(toks).to(dev), M, pos, out,
+                   torch.zeros(hv.workspace_bytes(M), dtype=torch.uint8, device=dev), logits)
+    hd = hs.device_model(dev)
+    ws = torch.zeros(hd.workspace_bytes(1), dtype=torch.uint8, device=dev)
+    seq_out, seq_lg, keep = [], [], []
+    for i in range(M):
+        b = torch.zeros(1, dtype=torch.int32, device=dev)
+        lb = torch.zeros(hs.vocab, device=dev)
+        t_i = torch.from_numpy(toks[i:i + 1]).to(dev)
+        p_i = torch.tensor([13 + i], dtype=torch.int32, device=dev)
+        hd.decode_step(t_i, p_i, b, ws, lb)
+        seq_out.append(b)
+        seq_lg.append(lb)
+        keep += [t_i, p_i]
+    torch.cuda.synchronize()
+    g = logits.view(M, hs.vocab)
+    if M == 2:
+        assert torch.equal(out, torch.cat(seq_out))
+        for i in range(M):
+            assert torch.equal(g[i], seq_lg[i]), i
+        for a, b in zip(hv.keep["dls"], hd.keep["dls"]):
+            assert torch.equal(a.k_cache, b.k_cache) and torch.equal(a.v_cache, b.v_cache)
+    nxt, _, ref, _ = hs.oracle_model().decode(toks, 13, want_logits=True)
+    for i in range(M):
+        assert rel_inf(g[i].cpu().numpy(), ref[i]) <= LOGIT_TOL
+    assert out.cpu().numpy().tolist() == nxt.tolist()
