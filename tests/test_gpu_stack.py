@@ -169,3 +169,31 @@ def test_verify_few_tokens_equals_sequential_decode(M):
     for i in range(M):
         assert rel_inf(g[i].cpu().numpy(), ref[i]) <= LOGIT_TOL
     assert out.cpu().numpy().tolist() == nxt.tolist()
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_streamed_70b_shape_bitwise_equal_resident(M):
+    # Llama-70B-shaped Q6_K layers (701,890,560-byte blobs), two of four
+    # streamed from pinned host memory through the staging buffers
+    import torch
+    dev = device()
+    hs = HostStack(wl.LLAMA70B, wl.ALL_Q6_K, n_layer=4, vocab=2048, max_ctx=64, n_past=40, wid=wl.W_TEST + 9)
+    toks = torch.from_numpy(wl.gen_tokens(wl.W_TEST + 9, M, hs.vocab)).to(dev)
+    pos = torch.tensor([40], dtype=torch.int32, device=dev)
+    copy_stream = torch.cuda.Stream()
+    res = []
+    for fs in (None, 2):
+        h = hs.device_model(dev, first_streamed=fs, copy_stream=copy_stream if fs is not None else None)
+        ws = torch.zeros(h.workspace_bytes(M), dtype=torch.uint8, device=dev)
+        out = torch.zeros(M, dtype=torch.int32, device=dev)
+        logits = torch.zeros(M * hs.vocab, device=dev)
+        h.verify_step(toks, M, pos, out, ws, logits)
+        torch.cuda.synchronize()
+        res.append((out.clone(), logits.clone(), [d.k_cache.clone() for d in h.keep["dls"]]))
+        del h, ws
+        torch.cuda.empty_cache()
+    assert torch.equal(res[1][0], res[0][0])
+    assert torch.equal(res[1][1], res[0][1])
+    for a, b in zip(res[1][2], res[0][2]):
+        assert torch.equal(a, b)
+    say(f"streamed 70B-shaped stack, M={M}: tokens {res[0][0].tolist()} bitwise equal to resident")
