@@ -20,6 +20,8 @@ Secondary workloads (`--workload`, one JSON line each; not the headline):
            back-to-back launches: effective GB/s per GEMV.
   layer8b  one 8B-shaped Q4_0 decoder layer at position 512, over 32 distinct
            layers: GB/s per layer.
+  decode8b greedy decode of a 32-layer Llama-8B-shaped Q8_0 stack from
+           context 512 (the pages' one decode figure is for Llama 8B Q8_0).
   gemm_small  the verify pass's small-M GEMM on the 70B-shaped gate (Q4_K)
            and down (Q6_K) matrices for M = 1, 2, 4, 8: weight GB/s per pass.
   verify   80 Q6_K 70B-shaped layers, 36 resident and 44 streamed from
@@ -372,6 +374,55 @@ def workload_gemm_small(dev) -> dict:
             "gemm_small": res}
 
 
+def workload_decode8b(dev, steps: int) -> dict:
+    """Greedy decode of a 32-layer Llama-8B-shaped stack in Q8_0 (hidden 4096,
+    32/8 heads, FFN 14336, Q8_0 embeddings and LM head of 128256 x 4096), from
+    context 512: the configuration behind the only decode figure the pages
+    give (Llama 8B Q8_0 on an RTX 3090; context not stated there)."""
+    import torch
+
+    import quantized_decode_dequant_amd as nt
+    from quantized_decode_dequant_amd.model import DeviceLayer, cfg_of
+    from synth import workloads as wl
+
+    shape, fmts, wid, n_layer, vocab, n_past = wl.LLAMA8B, wl.ALL_Q8_0, wl.W_LAYER_8B, 32, 128256, 512
+    max_ctx = n_past + steps + 1
+    layers = [DeviceLayer(wl.gen_layer(shape, fmts, wid, l, max_ctx, n_past), dev) for l in range(n_layer)]
+    emb = torch.from_numpy(wl.gen_matrix(wl.Q8_0, vocab, shape.hidden, wid, 0, wl.T_TOK_EMB)).to(dev)
+    head = torch.from_numpy(wl.gen_matrix(wl.Q8_0, vocab, shape.hidden, wid, 0, wl.T_LM_HEAD)).to(dev)
+    norm = torch.from_numpy(wl.gen_gains(shape, wid, 0, wl.T_OUT_NORM)).to(dev)
+    h = nt.ModelHandle(cfg_of(shape, max_ctx), [d.struct for d in layers], vocab, emb, wl.Q8_0, head, wl.Q8_0, norm)
+    wbytes = sum(d.weight_bytes() for d in layers) + head.numel() + emb.numel() // vocab
+    ws = torch.zeros(h.workspace_bytes(1), dtype=torch.uint8, device=dev)
+    first = int(wl.gen_tokens(wid, 1, vocab)[0])
+    tok = torch.tensor([first], dtype=torch.int32, device=dev)
+    pos = torch.tensor([n_past], dtype=torch.int32, device=dev)
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    h.decode_step(tok, pos, nxt, ws, None, stream)  # warm
+    torch.cuda.synchronize()
+    tok.fill_(first)
+    pos.fill_(n_past)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        h.decode_step(tok, pos, nxt, ws, None, stream)
+        tok.copy_(nxt)
+        pos.add_(1)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    log(f"[bench] decode8b: {ms:.3f} ms per token, {1e3 / ms:.1f} tok/s, {wbytes / ms / 1e6:.0f} GB/s of weights")
+    return {"metric": "decode tok/s, Llama-8B-shaped Q8_0", "unit": "tokens/s", "n_gpus": 1,
+            "value": round(1e3 / ms, 2), "higher_is_better": True, "data": "synthetic",
+            "config": {"workload": "32-layer llama8b-shaped Q8_0 greedy decode (Q8_0 embeddings and LM head), "
+                                   "f16 KV from context 512", "steps": steps},
+            "ms_per_token": round(ms, 4), "weight_bytes_per_token": wbytes,
+            "weight_gbs": round(wbytes / ms / 1e6, 1),
+            "pages_figure_for_context": {"value": 48.9, "unit": "tokens/s", "hardware": "RTX 3090",
+                                         "note": "Llama 8B Q8_0; context not stated on the pages"}}
+
+
 class StreamedStack:
     """80 Q6_K 70B-shaped layers, the first 36 resident in HBM and the other
     44 in pinned host memory, streamed through two HBM staging buffers; every
@@ -614,7 +665,7 @@ def main():
                     help="also run one device copy of 256 MiB (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize", metavar="DIR", help="print per-kernel statistics of a rocprofv3 output "
                     "directory (kernel trace or counter csv) and exit")
-    ap.add_argument("--workload", choices=["decode", "gemv", "layer8b", "gemm_small", "verify", "spec", "tiers"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "decode8b", "gemv", "layer8b", "gemm_small", "verify", "spec", "tiers"], default="decode",
                     help="decode (the headline, default) or one of the secondary workloads")
     ap.add_argument("--passes", type=int, default=5, help="verify workload: timed passes per M; spec: rounds per K")
     ap.add_argument("--graph-steps", action="store_true",
@@ -637,7 +688,8 @@ def main():
         fn = {"gemv": lambda: workload_gemv(dev), "layer8b": lambda: workload_layer8b(dev),
               "verify": lambda: workload_verify(dev, args.passes),
               "spec": lambda: workload_spec(dev, args.passes),
-              "tiers": lambda: workload_tiers(dev), "gemm_small": lambda: workload_gemm_small(dev)}[args.workload]
+              "tiers": lambda: workload_tiers(dev), "gemm_small": lambda: workload_gemm_small(dev),
+              "decode8b": lambda: workload_decode8b(dev, args.steps)}[args.workload]
         print(json.dumps(fn()), flush=True)
         return
     n_past = 4096
