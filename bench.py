@@ -240,8 +240,9 @@ def timed_graph(fn, n: int, reps: int = 5) -> float:
 
 
 def workload_gemv(dev) -> dict:
-    """Configs 1 and 3: effective GB/s of each GEMV, weights rotated over
-    distinct copies so no launch finds them in the last-level cache."""
+    """The single Q8_0 4096x4096 GEMV and the 70B-shaped projections:
+    effective GB/s of each GEMV, weights rotated over distinct copies so no
+    launch finds them in the last-level cache."""
     import torch
 
     import quantized_decode_dequant_amd as nt
@@ -299,7 +300,7 @@ def workload_gemv(dev) -> dict:
 
 
 def workload_layer8b(dev) -> dict:
-    """Config 2: one 8B-shaped Q4_0 layer at position 512, timed over 32
+    """One 8B-shaped Q4_0 layer at position 512, timed over 32
     distinct layers (3.9 GB of weights, more than the last-level cache)."""
     import torch
 
@@ -513,7 +514,7 @@ def workload_tiers(dev) -> dict:
 
 
 def workload_verify(dev, passes: int) -> dict:
-    """Config 5: streamed verify passes of M = 1, 2, 4, 8 tokens."""
+    """Streamed verify passes (80 Q6_K 70B-shaped layers, 44 streamed) of M = 1, 2, 4, 8 tokens."""
     import numpy as np
     import torch
 
@@ -565,7 +566,7 @@ def workload_verify(dev, passes: int) -> dict:
 
 
 def workload_spec(dev, rounds: int) -> dict:
-    """Self-speculative rounds and layer skip on the config-5 stack: the 36
+    """Self-speculative rounds and layer skip on the streamed 80-layer Q6_K stack: the 36
     resident layers draft, the whole stack verifies (its 44 streamed layers
     cross the host link once per round).  Reports the draft step, the verify
     pass and the round, the tokens a round emitted on these seeded weights,
