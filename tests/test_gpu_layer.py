@@ -55,7 +55,7 @@ def check(got, ref, kc, vc, li, n_past, M):
 
 @pytest.mark.parametrize("fmts", [wl.ALL_Q8_0, wl.ALL_Q4_0, wl.Q4_K_M, wl.ALL_Q6_K, wl.Q5_K_M, wl.ALL_Q5_K],
                          ids=["q8_0", "q4_0", "q4_k_m", "q6_k", "q5_k_m", "q5_k"])
-@pytest.mark.parametrize("n_past,M", [(37, 1), (0, 1), (20, 3), (63, 1)])
+@pytest.mark.parametrize("n_past,M", [(37, 1), (0, 1), (20, 3), (63, 1), (30, 2)])
 def test_layer_tiny(fmts, n_past, M):
     got, ref, kc, vc, li = run_layer(wl.TINY, fmts, wl.W_TEST, 3, 64, n_past, M)
     check(got, ref, kc, vc, li, n_past, M)
