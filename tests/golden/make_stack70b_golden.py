@@ -1,25 +1,39 @@
-"""Writes tests/golden/stack70b_q4km_greedy.json: the fp64 oracle's greedy
-decode of the 80-layer Llama-70B-shaped Q4_K_M stack (hidden 8192, FFN 28672,
-64/8 heads, f16 KV at context 4096, Q6_K embeddings and LM head of
-128256 x 8192) from the seeded inputs the GPU test builds.
+"""Stored oracle values for the 80-layer Llama-70B-shaped Q4_K_M stack (hidden
+8192, FFN 28672, 64/8 heads, f16 KV at context 4096, Q6_K embeddings and LM
+head of 128256 x 8192), built from the seeded inputs the GPU tests build.
 
-Calls only the oracle (and the seeded input generator).  Per step it stores
-the input token and position, the greedy token, the top-1/top-2 margin, the
-largest |logit|, the top five (index, logit) pairs and the logits at 256
-fixed indices, so that a GPU run can be checked token by token and on sampled
-logits without recomputing the oracle (~45 s per token on 16 cores).
+Calls only the oracle (and the seeded input generator).  The oracle takes
+~45 s per token on 16 cores, so the GPU tests compare against these files
+instead of recomputing it.  Three modes:
 
-With --perturb-seed S it instead reruns the stored steps (same input tokens)
-with one f16 ulp added to or taken from a random 10% of every layer's past
-K/V cache entries -- the size of the differences between the GPU's cache
-entries (rounded from fp32) and the oracle's (rounded from fp64) -- and
-stores, per step, how far the oracle's own sampled logits move
-(perturbed_err, relative to the largest |logit|).  Steps where the stack
-amplifies such a perturbation are where the GPU's logits may differ by more
-than the rounding bar while the tokens still agree.
+  (default) teacher data, --steps 64: the oracle's own greedy decode from
+      the first token.  Per step it stores the input token and position, the
+      greedy token, the top-1/top-2 margin, the largest |logit| and the top
+      five (index, logit) pairs (stack70b_q4km_teacher.json), and in
+      stack70b_q4km_teacher.npz the full logit vector (float32) and the f16
+      K/V rows the step appended to every layer's caches (uint16 bits,
+      [step][layer][K, V][kv head][head_dim]).  With those rows a GPU run can
+      start every step from the oracle's state (teacher forcing): the step's
+      input token and every cached entry equal the oracle's, so the step is
+      compared on its own and the rounding of earlier steps cannot carry over.
 
-usage: python tests/golden/make_stack70b_golden.py --steps 22
-       python tests/golden/make_stack70b_golden.py --perturb-seed 5
+  --cond-rel D: conditioning of each stored step.  The step is rerun from the
+      stored state with the residual stream entering every layer moved by
+      D * max|x| * u, u uniform in [-1, 1] per element (seeded per step and
+      layer) -- a deviation of the size a GPU layer introduces -- and the
+      relative movement of the full logit vector, max|dlogit| / max|logit|,
+      and the perturbed greedy token are stored per step (cond_err,
+      cond_next).  A step where cond_err is large amplifies deviations of
+      that size; the layer composition used here equals the plain decode
+      bit for bit when D = 0 (tests/test_oracle_layer_parts.py).
+
+  --free-running: the earlier record stack70b_q4km_greedy.json (token,
+      margin, top five and 256 sampled logits per step, 22 steps), and with
+      --perturb-seed S the oracle's movement under one f16 ulp on 10% of its
+      past cache entries.  Kept as the record of the free-running trajectory.
+
+usage: python tests/golden/make_stack70b_golden.py --steps 64
+       python tests/golden/make_stack70b_golden.py --cond-rel 1e-4
 """
 import argparse
 import json
@@ -35,15 +49,135 @@ sys.path.insert(0, ROOT)
 from synth import workloads as wl  # noqa: E402
 from tests.stack_util import HostStack  # noqa: E402
 
-OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "stack70b_q4km_greedy.json")
+HERE = os.path.dirname(os.path.abspath(__file__))
+OUT_FREE = os.path.join(HERE, "stack70b_q4km_greedy.json")
+OUT_TEACHER = os.path.join(HERE, "stack70b_q4km_teacher.json")
+OUT_TEACHER_NPZ = os.path.join(HERE, "stack70b_q4km_teacher.npz")
 N_PAST = 4096
 VOCAB = 128256
 N_SAMPLE = 256
+N_LAYER = 80
 
 
 def sample_indices() -> list:
     """256 distinct logit indices spread over the vocabulary (fixed, not random)."""
     return [int(i) for i in np.linspace(0, VOCAB - 1, N_SAMPLE).round().astype(np.int64)]
+
+
+def build_stack(steps: int) -> HostStack:
+    return HostStack(wl.LLAMA70B, wl.Q4_K_M, n_layer=N_LAYER, vocab=VOCAB, max_ctx=N_PAST + steps, n_past=N_PAST,
+                     wid=wl.W_STACK_70B)
+
+
+def appended_rows(om, pos: int) -> np.ndarray:
+    """The f16 K/V rows at `pos` of every layer of the oracle's caches: [layer][2][n_kv][head_dim]."""
+    return np.stack([np.stack([li.k_cache[:, pos, :], li.v_cache[:, pos, :]]) for li in om.layers_in])
+
+
+def write_rows(om, pos: int, rows: np.ndarray) -> None:
+    for li, r in zip(om.layers_in, rows):
+        li.k_cache[:, pos, :] = r[0]
+        li.v_cache[:, pos, :] = r[1]
+
+
+def step_record(token_in, pos, nxt, margin, l0) -> dict:
+    top = np.argsort(-l0, kind="stable")[:5]
+    return {"token_in": int(token_in), "pos": int(pos), "next": int(nxt), "margin": float(margin),
+            "logit_max_abs": float(np.abs(l0).max()), "top5": [[int(i), float(l0[i])] for i in top]}
+
+
+def teacher(args):
+    t0 = time.time()
+    print("generating the 80-layer 70B-shaped stack", flush=True)
+    hs = build_stack(args.steps)
+    om = hs.oracle_model()
+    steps, rows, logits = [], [], []
+    t = hs.first_token
+    for s in range(args.steps):
+        pos = N_PAST + s
+        nxt, margin, lg, _ = om.decode([t], pos, want_logits=True)
+        steps.append(step_record(t, pos, nxt[0], margin[0], lg[0]))
+        rows.append(appended_rows(om, pos))
+        logits.append(lg[0].astype(np.float32))
+        print(f"step {s}: token {int(t)} -> {int(nxt[0])} (margin {float(margin[0]):.4g}) "
+              f"after {time.time() - t0:.0f} s", flush=True)
+        t = int(nxt[0])
+        # written after every step, so a run cut short still leaves its steps
+        np.savez(OUT_TEACHER_NPZ + ".tmp.npz", kv_rows=np.stack(rows), logits=np.stack(logits))
+        os.replace(OUT_TEACHER_NPZ + ".tmp.npz", OUT_TEACHER_NPZ)
+        with open(OUT_TEACHER, "w") as f:
+            json.dump({"what": "fp64 oracle greedy decode of the 80-layer Llama-70B-shaped Q4_K_M stack, "
+                               "context 4096, seeded inputs (synth workload W_STACK_70B); per step the input "
+                               "token, greedy token, margin and top five; full logits (float32) and the "
+                               "appended f16 K/V rows of every layer in the .npz beside this file",
+                       "script": "tests/golden/make_stack70b_golden.py", "first_token": hs.first_token,
+                       "n_past": N_PAST, "vocab": VOCAB, "n_layer": N_LAYER, "steps": steps}, f)
+    print(f"wrote {len(steps)} steps to {OUT_TEACHER} and {OUT_TEACHER_NPZ}", flush=True)
+
+
+def perturbed_decode(om, hs, token: int, pos: int, rel: float, seed: int) -> np.ndarray:
+    """The decode of one token composed from the oracle's parts (embedding row,
+    layers, output norm, LM head), with the residual stream entering layer l
+    moved by rel * max|x| * u, u ~ U[-1, 1] seeded by (seed, l).  Returns the
+    logits.  rel = 0 gives the plain decode's logits exactly."""
+    import oracle
+    sh = hs.shape
+    rb = sh.hidden // oracle.block_elems(hs.emb_fmt) * oracle.block_bytes(hs.emb_fmt)
+    x = oracle.dequant(hs.emb_fmt, hs.tok_emb[token * rb:(token + 1) * rb], 1, sh.hidden)
+    for l, li in enumerate(om.layers_in):
+        if rel > 0:
+            u = np.random.default_rng([seed, l]).uniform(-1.0, 1.0, x.shape)
+            x = x + rel * np.abs(x).max() * u
+        x = oracle.layer(li, x, pos)
+    xn = oracle.rmsnorm(x[0], hs.out_norm, sh.rms_eps)
+    return oracle.gemv(hs.head_fmt, hs.lm_head, xn, hs.vocab, sh.hidden)
+
+
+def conditioning(args):
+    g = json.load(open(OUT_TEACHER))
+    z = np.load(OUT_TEACHER_NPZ)
+    kv, ref = z["kv_rows"], z["logits"]
+    n = min(len(g["steps"]), kv.shape[0])
+    t0 = time.time()
+    hs = build_stack(n)
+    om = hs.oracle_model()
+    for s in range(n):
+        st = g["steps"][s]
+        pos = st["pos"]
+        for p in range(s):  # the oracle's state before step s
+            write_rows(om, N_PAST + p, kv[p])
+        lg = perturbed_decode(om, hs, st["token_in"], pos, args.cond_rel, 1000 + s)
+        err = float(np.abs(lg - ref[s].astype(np.float64)).max() / np.abs(ref[s]).max())
+        st["cond_err"] = err
+        st["cond_next"] = int(np.argmax(lg))
+        g["cond_rel"] = args.cond_rel
+        print(f"step {s}: perturbed logits moved {err:.2e}, token {st['cond_next']} (stored {st['next']}) "
+              f"after {time.time() - t0:.0f} s", flush=True)
+        with open(OUT_TEACHER, "w") as f:
+            json.dump(g, f)
+
+
+def free_running(args):
+    if args.perturb_seed is not None:
+        return free_running_perturbed(args)
+    t0 = time.time()
+    hs = build_stack(args.steps)
+    om = hs.oracle_model()
+    idx = sample_indices()
+    steps = []
+    t = hs.first_token
+    for s in range(args.steps):
+        nxt, margin, lg, _ = om.decode([t], N_PAST + s, want_logits=True)
+        rec = step_record(t, N_PAST + s, nxt[0], margin[0], lg[0])
+        rec["sample_logits"] = [float(lg[0][i]) for i in idx]
+        steps.append(rec)
+        print(f"step {s}: token {int(t)} -> {int(nxt[0])} after {time.time() - t0:.0f} s", flush=True)
+        t = int(nxt[0])
+        with open(OUT_FREE, "w") as f:
+            json.dump({"what": "fp64 oracle greedy decode of the 80-layer Llama-70B-shaped Q4_K_M stack, "
+                               "context 4096, seeded inputs (synth workload W_STACK_70B)",
+                       "script": "tests/golden/make_stack70b_golden.py", "first_token": hs.first_token,
+                       "n_past": N_PAST, "vocab": VOCAB, "sample_idx": idx, "steps": steps}, f)
 
 
 def perturb_past(om, n_past: int, seed: int) -> None:
@@ -59,62 +193,37 @@ def perturb_past(om, n_past: int, seed: int) -> None:
             bits[ok] = nb[ok].astype(np.uint16)
 
 
-def perturbed(args):
-    g = json.load(open(args.out))
+def free_running_perturbed(args):
+    g = json.load(open(OUT_FREE))
     steps = g["steps"]
     t0 = time.time()
-    hs = HostStack(wl.LLAMA70B, wl.Q4_K_M, n_layer=80, vocab=VOCAB, max_ctx=N_PAST + len(steps), n_past=N_PAST,
-                   wid=wl.W_STACK_70B)
+    hs = build_stack(len(steps))
     om = hs.oracle_model()
     perturb_past(om, N_PAST, args.perturb_seed)
     idx = np.asarray(g["sample_idx"])
     for s, st in enumerate(steps):
         nxt, margin, lg, _ = om.decode([st["token_in"]], st["pos"], want_logits=True)
-        err = float(np.abs(lg[0][idx] - np.asarray(st["sample_logits"])).max() / st["logit_max_abs"])
-        st["perturbed_err"] = err
+        st["perturbed_err"] = float(np.abs(lg[0][idx] - np.asarray(st["sample_logits"])).max() / st["logit_max_abs"])
         st["perturbed_next"] = int(nxt[0])
-        print(f"step {s}: perturbed oracle {int(nxt[0])} (stored {st['next']}), sampled logits moved {err:.2e} "
-              f"after {time.time() - t0:.0f} s", flush=True)
+        print(f"step {s}: perturbed oracle {int(nxt[0])} after {time.time() - t0:.0f} s", flush=True)
         g["perturb_seed"] = args.perturb_seed
-        with open(args.out, "w") as f:
+        with open(OUT_FREE, "w") as f:
             json.dump(g, f)
 
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--steps", type=int, default=16)
-    ap.add_argument("--out", default=OUT)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--cond-rel", type=float, default=None)
+    ap.add_argument("--free-running", action="store_true")
     ap.add_argument("--perturb-seed", type=int, default=None)
     args = ap.parse_args()
-    if args.perturb_seed is not None:
-        perturbed(args)
-        return
-    t0 = time.time()
-    print("generating the 80-layer 70B-shaped stack", flush=True)
-    hs = HostStack(wl.LLAMA70B, wl.Q4_K_M, n_layer=80, vocab=VOCAB, max_ctx=N_PAST + args.steps, n_past=N_PAST,
-                   wid=wl.W_STACK_70B)
-    om = hs.oracle_model()
-    idx = sample_indices()
-    steps = []
-    t = hs.first_token
-    for s in range(args.steps):
-        nxt, margin, lg, _ = om.decode([t], N_PAST + s, want_logits=True)
-        l0 = lg[0]
-        top = np.argsort(-l0, kind="stable")[:5]
-        steps.append({"token_in": int(t), "pos": N_PAST + s, "next": int(nxt[0]), "margin": float(margin[0]),
-                      "logit_max_abs": float(np.abs(l0).max()),
-                      "top5": [[int(i), float(l0[i])] for i in top],
-                      "sample_logits": [float(l0[i]) for i in idx]})
-        print(f"step {s}: token {int(t)} -> {int(nxt[0])} (margin {float(margin[0]):.4g}) "
-              f"after {time.time() - t0:.0f} s", flush=True)
-        t = int(nxt[0])
-        # written after every step, so a run cut short still leaves its steps
-        with open(args.out, "w") as f:
-            json.dump({"what": "fp64 oracle greedy decode of the 80-layer Llama-70B-shaped Q4_K_M stack, "
-                               "context 4096, seeded inputs (synth workload W_STACK_70B)",
-                       "script": "tests/golden/make_stack70b_golden.py", "first_token": hs.first_token,
-                       "n_past": N_PAST, "vocab": VOCAB, "sample_idx": idx, "steps": steps}, f)
-    print(f"wrote {len(steps)} steps to {args.out}", flush=True)
+    if args.free_running:
+        free_running(args)
+    elif args.cond_rel is not None:
+        conditioning(args)
+    else:
+        teacher(args)
 
 
 if __name__ == "__main__":

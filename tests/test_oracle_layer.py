@@ -160,3 +160,70 @@ def test_stack_verify_equals_sequential_decode():
         b, _, lb, _ = mb.decode(toks[i:i + 1], pos + i, want_logits=True)
         assert b[0] == a[i]
         assert np.array_equal(lb[0], la[i])
+
+
+def test_query_rope_inside_layer_closed_form():
+    # Wq = 4 I (q = 4 xn), Wk = Wv = 0 (the new key and value are zero), Wo = I,
+    # FFN zero.  The cache is zero except, in kv group 0, the key at position
+    # t0 is the unit vector along dimension 2i (first of pair i) and the value
+    # at t0 is e_0.  Query head h of group 0 then scores t0 with
+    # s_h = qr_h[2i] / sqrt(hd), where qr is q turned by pos * theta^(-2i/hd)
+    # (pair (2i, 2i+1)), and every other position 0..pos scores 0; so
+    # out - x at dim 0 of head h is e^s / (e^s + pos) and zero elsewhere.
+    # An unrotated query, or one turned at pos +- 1, gives another value.
+    mats = zero_mats(SHP)
+    mats["wq"] = q8_matrix(64, 64, [(r, r) for r in range(64)], d_bits=blocks.f16_bits(4.0))
+    mats["wo"] = q8_matrix(64, 64, [(r, r) for r in range(64)])
+    hd, i, pos, t0 = SHP.head_dim, 1, 9, 3
+    li = make_layer(SHP, mats, 12, pos)
+    li.k_cache[...] = 0
+    li.v_cache[...] = 0
+    li.k_cache[0, t0, 2 * i] = blocks.f16_bits(1.0)
+    li.v_cache[0, t0, 0] = blocks.f16_bits(1.0)
+    x = wl.gen_x(SHP.hidden, wl.W_TEST, 6).astype(np.float64) * 2.0
+    out = oracle.layer(li, x, pos=pos)[0]
+    g = li.attn_norm.astype(np.float64)
+    xn = x / math.sqrt(np.mean(x * x) + SHP.rms_eps) * g
+    q = 4.0 * xn
+    ang = pos * SHP.rope_theta ** (-2.0 * i / hd)
+    expect = np.zeros(64)
+    for h in range(2):  # the two query heads of kv group 0
+        a, b = q[h * hd + 2 * i], q[h * hd + 2 * i + 1]
+        s = (a * math.cos(ang) - b * math.sin(ang)) / math.sqrt(hd)
+        expect[h * hd] = math.exp(s) / (math.exp(s) + pos)
+    assert np.allclose(out - x, expect, rtol=1e-12, atol=1e-14)
+    # the same layer with the query unrotated, or turned one position off,
+    # lands measurably elsewhere (the pin separates those mistakes)
+    for wrong in (0.0, (pos - 1) * SHP.rope_theta ** (-2.0 * i / hd), (pos + 1) * SHP.rope_theta ** (-2.0 * i / hd)):
+        a, b = q[2 * i], q[2 * i + 1]
+        s = (a * math.cos(wrong) - b * math.sin(wrong)) / math.sqrt(hd)
+        assert abs(math.exp(s) / (math.exp(s) + pos) - expect[0]) > 1e-3
+
+
+def test_stack_output_norm_logit_values():
+    # Zero layers (the final hidden state is the embedding row), a Q8_0
+    # embedding with distinct, non-unit rows and an identity LM head: the
+    # logits are the output RMSNorm of the embedding row, e / sqrt(mean(e^2)
+    # + eps) * g, value for value.
+    shp = SHP
+    vocab = shp.hidden
+    layers = [make_layer(shp, zero_mats(shp), 8, 2, layer=l) for l in range(2)]
+    rng = np.random.default_rng(21)
+    q = rng.integers(-127, 128, size=(vocab, shp.hidden))
+    d = blocks.f16_bits(1.0 / 16.0)
+    emb_rows = bytearray()
+    for r in range(vocab):
+        for b in range(shp.hidden // 32):
+            emb_rows += blocks.enc_q8_0(d, q[r, 32 * b:32 * b + 32])
+    emb = np.frombuffer(bytes(emb_rows), np.uint8).copy()
+    lm = q8_matrix(vocab, shp.hidden, [(i, i) for i in range(vocab)])
+    g = wl.gen_gains(shp, wl.W_TEST, 0, wl.T_OUT_NORM)
+    m = oracle.OracleModel(shp, layers, oracle.Q8_0, emb, oracle.Q8_0, lm, g, vocab)
+    for t in [0, 17, 63]:
+        nxt, margin, logits, hidden = m.decode([t], pos=2, want_logits=True, want_hidden=True)
+        e = q[t].astype(np.float64) / 16.0
+        assert np.array_equal(hidden[0], e)
+        expect = e / math.sqrt(np.mean(e * e) + shp.rms_eps) * g.astype(np.float64)
+        assert np.allclose(logits[0], expect, rtol=1e-13, atol=0)
+        assert nxt[0] == int(np.argmax(expect))
+        assert abs(math.sqrt(np.mean(e * e)) - 1.0) > 0.5  # the norm is far from a no-op here
