@@ -23,10 +23,18 @@
  *  - Errors: arguments are validated before anything is enqueued; a negative
  *    nt_status is returned and nothing runs.  A failed launch returns
  *    NT_EHIP.  Faults inside kernels surface at the caller's next sync.
+ *    The decode position lives in device memory (so a captured graph can be
+ *    replayed), so a position out of range (pos < 0 or pos + M > max_ctx)
+ *    can only be seen on the device: the kernels then leave the KV cache
+ *    untouched and skip attention, the residual stream x of a layer call
+ *    comes out NaN, and a step writes -1 as its token (see each call).
  *  - Alignment: weight matrices, activation vectors and workspaces must be
  *    16-byte aligned (NT_EALIGN otherwise).
- *  - Calls are re-entrant; concurrent calls on different streams must not
- *    share output, cache or workspace buffers.
+ *  - Calls are re-entrant, except the tracing calls (nt_trace_*), which are
+ *    per process; concurrent calls on different streams must not share
+ *    output, cache, workspace or staging buffers.  The streaming pipeline
+ *    keeps one set of HIP events per staging buffer, so steps of models
+ *    with different staging buffers may run concurrently.
  */
 #ifndef NT_H
 #define NT_H
@@ -157,7 +165,8 @@ size_t nt_layer_workspace_bytes(const nt_layer_cfg* cfg, int M);
  *   x: device fp32 [M][hidden], updated in place.
  *   pos_dev: device int32 holding pos (read by the kernels, so a captured
  *            graph can be replayed with a new position); if pos < 0 or
- *            pos + M > max_ctx the kernels skip the cache write and attention.
+ *            pos + M > max_ctx no token writes the cache, attention is
+ *            skipped and every row of x comes out as NaN.
  *   ws: device workspace of ws_bytes >= nt_layer_workspace_bytes(cfg, M);
  *       its contents need no initialisation.  Calls that share a workspace
  *       must not overlap.
@@ -200,19 +209,41 @@ size_t nt_step_workspace_bytes(const nt_model* model, int M);
 size_t nt_layer_blob_bytes(const nt_layer_cfg* cfg, const nt_layer* fmts_only);
 
 /*
- * One greedy decode step: embedding row of *token_dev -> n_layer layers at
- * *pos_dev -> final RMSNorm -> LM head -> argmax (lowest index on ties)
- * written to *next_token_dev.  logits_dev (fp32 [vocab]) may be NULL.
- * Token and position live on the device so the step can be captured in a
- * graph and replayed.
+ * One greedy decode step of the whole stack (p1 "About": a Llama 70B model
+ * run token by token; p1 "Llama architecture support" and p2 "Architecture
+ * et structure du code": the model composed of attention, FFN and
+ * normalisation, with a sampler and an engine on top):
+ *   embedding row of *token_dev -> n_layer layers at *pos_dev (nt_decode_layer
+ *   with M = 1; layers >= first_streamed streamed, flagged layers skipped) ->
+ *   final RMSNorm (out_norm) -> LM head -> argmax (lowest index on ties)
+ *   written to *next_token_dev.
+ *   token_dev, pos_dev: device int32, read by the kernels (the token is
+ *     clamped to [0, vocab)); they live on the device so the step can be
+ *     captured in a graph and replayed.  The call does not advance pos.
+ *   next_token_dev: device int32; -1 when the position is out of range
+ *     (pos < 0 or pos >= max_ctx; the caches are then left untouched).
+ *   logits_dev: device fp32 [vocab] or NULL.
+ *   ws: device workspace of ws_bytes >= nt_step_workspace_bytes(model, 1),
+ *     16-byte aligned, no initialisation needed; steps sharing it must not
+ *     overlap.
+ * Errors as for every call (validated before anything is enqueued:
+ * NT_EINVAL, NT_EALIGN, NT_EWORKSPACE, NT_EUNSUPPORTED; NT_EHIP on a failed
+ * launch or copy).
  */
 int nt_decode_step(const nt_model* model, const int32_t* token_dev, const int32_t* pos_dev,
                    int32_t* next_token_dev, float* logits_dev, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Verify pass of self-speculative decoding: M (1..8) tokens at positions
- * pos..pos+M-1 through the whole stack in one pass; argmax_dev[i] is the
- * greedy token after token i.  logits_dev (fp32 [M][vocab]) may be NULL.
+ * Verify pass of self-speculative decoding (p1 "About" and feature list:
+ * self-speculative decoding with the resident layers as the draft model;
+ * p2 "Fonctionnalites principales"; the drafted tokens are checked by one
+ * pass of the whole model): M (1..8) tokens at positions pos..pos+M-1
+ * through the whole stack in one pass, token i attending to 0..pos+i;
+ * argmax_dev[i] (device int32 [M]) is the greedy token after token i, or -1
+ * for every i when pos < 0 or pos + M > max_ctx.  tokens_dev: device int32
+ * [M].  logits_dev (fp32 [M][vocab]) may be NULL.  ws: ws_bytes >=
+ * nt_step_workspace_bytes(model, M).  Ownership, errors and pos as
+ * nt_decode_step.  M == 1 is nt_decode_step.
  */
 int nt_verify_step(const nt_model* model, const int32_t* tokens_dev, int M, const int32_t* pos_dev,
                    int32_t* argmax_dev, float* logits_dev, void* ws, size_t ws_bytes, void* stream);
@@ -225,7 +256,8 @@ int nt_verify_step(const nt_model* model, const int32_t* tokens_dev, int M, cons
  * to cos_dev[l].  cos_dev: device fp32 [n_layer]; the caller zeroes it before
  * the first calibration token, so that after T tokens cos_dev[l] / T is the
  * layer's mean similarity.  Entries of skipped layers are not touched.  Other
- * arguments as nt_decode_step (same workspace size).
+ * arguments as nt_decode_step (same workspace size); with the position out
+ * of range the token is -1 and NaN is added.
  */
 int nt_calibrate_step(const nt_model* model, const int32_t* token_dev, const int32_t* pos_dev,
                       int32_t* next_token_dev, float* cos_dev, void* ws, size_t ws_bytes, void* stream);
@@ -303,8 +335,8 @@ size_t nt_spec_workspace_bytes(const nt_model* model, int K);
  * cur_dev, pos_dev, out_dev ([K + 1]) and n_out_dev are device int32; the
  * state stays on the device, so rounds can be queued back to back.
  * ws: nt_spec_workspace_bytes(model, K).  The draft steps and the verify pass
- * must fit the cache: pos + K + 1 <= max_ctx (else, as for nt_decode_layer,
- * the kernels skip the cache write and attention).
+ * must fit the cache: pos + K + 1 <= max_ctx.  Otherwise the round emits
+ * nothing: out_dev[0..K] = -1, *n_out_dev = 0, and pos and cur stay.
  */
 int nt_spec_step(const nt_model* model, const uint8_t* draft_skip, int K, int32_t* cur_dev, int32_t* pos_dev,
                  int32_t* out_dev, int32_t* n_out_dev, void* ws, size_t ws_bytes, void* stream);
@@ -332,6 +364,18 @@ typedef enum nt_trace_kind {
 int nt_trace_begin(int kind);
 int nt_trace_begin_every(int kind, int every);
 int nt_trace_end(int* launches, double* total_ms);
+
+/*
+ * Test hook for the streaming pipeline's failure path: the next streamed
+ * pass (nt_decode_step, nt_verify_step, nt_calibrate_step or a pass of
+ * nt_spec_step) returns NT_EHIP where it would issue the copy of its j-th
+ * streamed layer (0-based among the streamed layers that run), as if that
+ * copy had failed; the hook then disarms itself.  Work already enqueued
+ * (the layers before it) still runs, writing only cache entries at the
+ * pass's own positions, so the caller repeats the pass at the same position.
+ * j == -1 disarms.  NT_EINVAL for j < -1.  Per process; no GPU work.
+ */
+int nt_test_fail_stream_copy(int j);
 
 /*
  * Measurement aid: a pure streaming read of `bytes` (a multiple of 16) from

@@ -94,9 +94,15 @@ EXPORTS = {
     "nt_trace_begin_every": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "nt_trace_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]),
     "nt_read_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    "nt_test_fail_stream_copy": (ctypes.c_int, [ctypes.c_int]),
 }
 
 TRACE_GEMV, TRACE_GEMV_RESID, TRACE_QKV, TRACE_FFN_UP, TRACE_ATTN = 0, 1, 2, 3, 4
+
+
+def test_fail_stream_copy(j: int) -> None:
+    """Arm the streaming pipeline's failure hook (nt_test_fail_stream_copy)."""
+    _check("nt_test_fail_stream_copy", lib().nt_test_fail_stream_copy(int(j)))
 
 
 def read_probe(buf, out, stream=None) -> None:

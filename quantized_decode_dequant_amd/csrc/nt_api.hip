@@ -3,6 +3,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -160,6 +161,7 @@ int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const
     EpiArgs ea{};
     ea.y = x;
     ea.ld = c.hidden;
+    ea.err = err;  // NaN out when a position was out of range
     if ((rc = launch_gemm_m(job, stage, part, none, EPI_RESID, ea, st)) != NT_OK) return rc;
   }
   return NT_OK;
@@ -206,6 +208,7 @@ int run_layer(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const i
       ea.q_rows = nq;
       ea.kv_rows = nkv;
       ea.pos_add = i;
+      ea.n_tok = M;
       if ((rc = launch_gemv(job, pro, EPI_QKV, ea, st)) != NT_OK) return rc;
     }
   }
@@ -253,6 +256,7 @@ int run_layer(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const i
       ProArgs pro{a, nullptr, 0.f, 0, 0, 0.f, nullptr, 0};
       EpiArgs ea{};
       ea.y = xi;
+      ea.err = err;  // NaN out when a position was out of range
       if ((rc = launch_gemv(jd, pro, EPI_RESID, ea, st)) != NT_OK) return rc;
     }
   }
@@ -302,30 +306,44 @@ StepWs step_ws(const nt_model& m, int M) {
   return w;
 }
 
-// Events of the streaming pipeline, one set per device, made on first use.
+// Events of the streaming pipeline: one set per (device, staging buffer),
+// made on first use and kept for the process.  Steps of models with
+// different staging buffers can therefore run concurrently on different
+// streams; steps that share staging buffers must not overlap (they share
+// the buffers themselves).
 struct StreamEvents {
+  int dev = -1;
+  const void* stage = nullptr;
   hipEvent_t ready[2] = {nullptr, nullptr};
   hipEvent_t freed[2] = {nullptr, nullptr};
-  bool init = false;
 };
 
 std::mutex g_ev_mu;
 
-StreamEvents* stream_events() {
-  static StreamEvents ev[64];
+StreamEvents* stream_events(const void* stage0) {
+  static std::vector<StreamEvents*> sets;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return nullptr;
   std::lock_guard<std::mutex> lk(g_ev_mu);
-  StreamEvents& e = ev[dev & 63];
-  if (!e.init) {
-    for (int i = 0; i < 2; ++i) {
-      if (hipEventCreateWithFlags(&e.ready[i], hipEventDisableTiming) != hipSuccess) return nullptr;
-      if (hipEventCreateWithFlags(&e.freed[i], hipEventDisableTiming) != hipSuccess) return nullptr;
+  for (StreamEvents* e : sets)
+    if (e->dev == dev && e->stage == stage0) return e;
+  StreamEvents* e = new StreamEvents;
+  for (int i = 0; i < 2; ++i) {
+    if (hipEventCreateWithFlags(&e->ready[i], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&e->freed[i], hipEventDisableTiming) != hipSuccess) {
+      delete e;
+      return nullptr;
     }
-    e.init = true;
   }
-  return &e;
+  e->dev = dev;
+  e->stage = stage0;
+  sets.push_back(e);
+  return e;
 }
+
+// Test hook (nt_test_fail_stream_copy): the next streamed pass fails, with
+// NT_EHIP, where it would issue the copy of this streamed layer (-1: off).
+std::atomic<int> g_fail_copy{-1};
 
 // Arguments of one pass through the stack beyond the model itself.
 struct StepArgs {
@@ -381,13 +399,19 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
   float* x = reinterpret_cast<float*>(ws + w.x);
   float* x_in = reinterpret_cast<float*>(ws + w.x_in);
   float* logits = logits_user ? logits_user : reinterpret_cast<float*>(ws + w.logits);
-  int rc = launch_embed(m.tok_emb.fmt, m.tok_emb.data, tokens, M, m.vocab, m.cfg.hidden, x, st);
+  // the layers' status word (one for the whole step: every layer writes it
+  // from the same position); the embedding clears it, so a step without
+  // layers reports no error
+  int* err = reinterpret_cast<int*>(ws + w.layer + w.lw.err);
+  int rc = launch_embed(m.tok_emb.fmt, m.tok_emb.data, tokens, M, m.vocab, m.cfg.hidden, x, err, st);
   if (rc != NT_OK) return rc;
   StreamEvents* ev = nullptr;
   hipStream_t cs = static_cast<hipStream_t>(m.copy_stream);
   auto issue_copy = [&](int j) -> int {
     // streamed layer j (0-based among the streamed layers that run) into stage[j % 2]
     const int l = streamed_layer(j), b = j & 1;
+    int armed = j;
+    if (g_fail_copy.load() == j && g_fail_copy.compare_exchange_strong(armed, -1)) return NT_EHIP;
     nt_layer L = m.layers[l];
     blob_offsets(m.cfg, L, boff);
     if (j >= 2 && hipStreamWaitEvent(cs, ev->freed[b], 0) != hipSuccess) return NT_EHIP;
@@ -396,7 +420,7 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
     return NT_OK;
   };
   if (streaming) {
-    if (!(ev = stream_events())) return NT_EHIP;
+    if (!(ev = stream_events(m.stage[0]))) return NT_EHIP;
     // the copies may only start once everything queued before this step on
     // the compute stream (e.g. a previous step still reading the staging
     // buffers) is done
@@ -458,8 +482,8 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
       if ((rc = launch_gemv(jl, pro, EPI_STORE, ea, st)) != NT_OK) return rc;
     }
   }
-  return launch_argmax(logits, M, m.vocab, reinterpret_cast<float*>(ws + w.pv), reinterpret_cast<int*>(ws + w.pi), out,
-                       st);
+  return launch_argmax(logits, M, m.vocab, reinterpret_cast<float*>(ws + w.pv), reinterpret_cast<int*>(ws + w.pi), err,
+                       out, st);
 }
 
 // Workspace of a speculative round: one pass's workspace (the draft steps
@@ -625,6 +649,12 @@ int nt_calibrate_step(const nt_model* model, const int32_t* token_dev, const int
   sa.cos_acc = cos_dev;
   return run_step(*model, token_dev, 1, pos_dev, next_token_dev, nullptr, ws, ws_bytes,
                   static_cast<hipStream_t>(stream), sa);
+}
+
+int nt_test_fail_stream_copy(int j) {
+  if (j < -1) return NT_EINVAL;
+  g_fail_copy.store(j);
+  return NT_OK;
 }
 
 int nt_select_skip(const float* score, int n_layer, int n_skip, int first, int last, uint8_t* mask) {

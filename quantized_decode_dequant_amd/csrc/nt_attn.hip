@@ -322,9 +322,12 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 // ------------------------------------------------------------ embedding row
 // x[m][:] = decoded row tokens[m] of an embedding matrix (fp32).  One thread
 // per 32-weight group; the formulas are the block definitions of nt.h.
+// It also clears the step's status word (err), which the layers set when a
+// position is out of range.
 __global__ __launch_bounds__(256) void k_embed(int fmt, const uint8_t* __restrict__ E, const int32_t* tokens, int vocab,
-                                               int cols, float* __restrict__ x) {
+                                               int cols, float* __restrict__ x, int* __restrict__ err) {
   const int m = blockIdx.y;
+  if (err && m == 0 && blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
   int tok = tokens[m];
   tok = min(max(tok, 0), vocab - 1);
   const int grp = blockIdx.x * blockDim.x + threadIdx.x;  // 32-weight group
@@ -435,14 +438,15 @@ __global__ __launch_bounds__(256) void k_argmax_part(const float* __restrict__ l
   }
 }
 
+// A step whose status word is set (a position out of range) writes -1.
 __global__ __launch_bounds__(64) void k_argmax_final(const float* __restrict__ pv, const int* __restrict__ pi, int nparts,
-                                                     int32_t* __restrict__ out) {
+                                                     const int* __restrict__ err, int32_t* __restrict__ out) {
   const int m = blockIdx.x;
   float v = -INFINITY;
   int idx = INT32_MAX;
   for (int i = threadIdx.x; i < nparts; i += 64) better(v, idx, pv[(int64_t)m * nparts + i], pi[(int64_t)m * nparts + i]);
   for (int o = 32; o > 0; o >>= 1) better(v, idx, __shfl_xor(v, o, 64), __shfl_xor(idx, o, 64));
-  if (threadIdx.x == 0) out[m] = idx == INT32_MAX ? 0 : idx;
+  if (threadIdx.x == 0) out[m] = (err && *err != 0) ? -1 : (idx == INT32_MAX ? 0 : idx);
 }
 
 }  // namespace
@@ -475,21 +479,22 @@ int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, con
   return ok ? NT_OK : NT_EHIP;
 }
 
-int launch_embed(int fmt, const void* E, const int32_t* tokens, int M, int vocab, int cols, float* x,
+int launch_embed(int fmt, const void* E, const int32_t* tokens, int M, int vocab, int cols, float* x, int* err,
                  hipStream_t stream) {
   const int groups = cols / 32;
   hipLaunchKernelGGL(k_embed, dim3((groups + 255) / 256, M), dim3(256), 0, stream, fmt,
-                     static_cast<const uint8_t*>(E), tokens, vocab, cols, x);
+                     static_cast<const uint8_t*>(E), tokens, vocab, cols, x, err);
   return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
 }
 
 int argmax_parts(int n) { return std::min(256, (n + 1023) / 1024); }
 
-int launch_argmax(const float* logits, int M, int n, float* pv, int* pi, int32_t* out, hipStream_t stream) {
+int launch_argmax(const float* logits, int M, int n, float* pv, int* pi, const int* err, int32_t* out,
+                  hipStream_t stream) {
   const int parts = argmax_parts(n);
   const int per = (n + parts - 1) / parts;
   hipLaunchKernelGGL(k_argmax_part, dim3(parts, M), dim3(256), 0, stream, logits, n, per, pv, pi);
-  hipLaunchKernelGGL(k_argmax_final, dim3(M), dim3(64), 0, stream, pv, pi, parts, out);
+  hipLaunchKernelGGL(k_argmax_final, dim3(M), dim3(64), 0, stream, pv, pi, parts, err, out);
   return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
 }
 

@@ -1,5 +1,4 @@
-// The GEMV engine's device code, shared by the single-GEMV kernel
-// (nt_gemv.hip) and the persistent decoder-layer kernel (nt_layer.hip): the
+// The GEMV engine's device code (kernel and launch in nt_gemv.hip): the
 // staged activation, the format units, the segment stream and the
 // epilogues.  The design is described at the top of nt_gemv.hip.
 //
@@ -529,10 +528,13 @@ template <int EPI>
 __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, int tid, int nthreads,
                                                const EpiArgs& ea) {
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
+    // a residual launch given the layer's status word turns the stream into
+    // NaN when the layer's position was out of range
+    const bool bad = EPI == EPI_RESID && ea.err && *ea.err != 0;
     for (int t = tid; t < sh.no; t += nthreads) {
       const float s = row_total(job, t);
       float* y = ea.y + srow(job, sh, t);
-      if constexpr (EPI == EPI_RESID) *y += s;
+      if constexpr (EPI == EPI_RESID) *y = bad ? __builtin_nanf("") : *y + s;
       else *y = s;
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
@@ -540,8 +542,11 @@ __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, 
       ea.y[srow(job, sh, t)] = silu(row_total(job, t)) * row_total(job, sh.no + t);
   } else if constexpr (EPI == EPI_QKV) {
     const int pos = *ea.pos + ea.pos_add;
-    const bool pos_ok = pos >= ea.pos_add && pos < ea.max_ctx;
-    if (!pos_ok && ea.err && tid == 0) *ea.err = 1;
+    // every position of the call (*pos .. *pos + n_tok - 1) must fit the
+    // cache, or no token of the call writes its entries
+    const bool pos_ok = *ea.pos >= 0 && *ea.pos + max(ea.n_tok, 1) - 1 < ea.max_ctx;
+    // the layer's status word: every workgroup writes the same value
+    if (ea.err && tid == 0) *ea.err = pos_ok ? 0 : 1;
     for (int t = tid; 2 * t < sh.no; t += nthreads) {
       const int R = srow(job, sh, 2 * t);  // even row of an adjacent pair (concatenated Q, K, V rows)
       float a = row_total(job, 2 * t), b = row_total(job, 2 * t + 1);

@@ -568,8 +568,10 @@ __global__ __launch_bounds__(256) void k_reduce_m(const float* __restrict__ part
     if (i >= (int64_t)npr * M) return;
     const int t = (int)(i / npr), R = 2 * (int)(i - (int64_t)t * npr);
     const int pos = *ea.pos + t;
-    const bool pos_ok = *ea.pos >= 0 && pos < ea.max_ctx;
-    if (!pos_ok && ea.err) *ea.err = 1;
+    // all M positions must fit the cache, or no token writes its entries;
+    // the layer's status word says which
+    const bool pos_ok = *ea.pos >= 0 && *ea.pos + M - 1 < ea.max_ctx;
+    if (ea.err && i == 0) *ea.err = pos_ok ? 0 : 1;
     float a = total(t, R), b = total(t, R + 1);
     const int dd = R % ea.head_dim;
     if (R < ea.q_rows + ea.kv_rows) {
@@ -600,7 +602,9 @@ __global__ __launch_bounds__(256) void k_reduce_m(const float* __restrict__ part
     if constexpr (EPI == EPI_SWIGLU) {
       ea.y[t * ea.ld + R] = silu(total(t, R)) * total(t, (int64_t)orows + R);
     } else if constexpr (EPI == EPI_RESID) {
-      ea.y[t * ea.ld + R] += total(t, R);
+      // NaN when the layer's status word says a position was out of range
+      const bool bad = ea.err && *ea.err != 0;
+      ea.y[t * ea.ld + R] = bad ? __builtin_nanf("") : ea.y[t * ea.ld + R] + total(t, R);
     } else {
       ea.y[t * ea.ld + R] = total(t, R);
     }

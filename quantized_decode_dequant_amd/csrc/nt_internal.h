@@ -117,13 +117,15 @@ struct EpiArgs {
   uint16_t* k_cache;
   uint16_t* v_cache;
   const int32_t* pos;
-  int* err;            // set to 1 when pos is out of range
+  int* err;            // layer status word: EPI_QKV writes 1 when a position is out of range, else 0;
+                       // an EPI_RESID launch given it writes NaN when it is set
   int head_dim;
   int max_ctx;
   float rope_theta;
   int q_rows;          // n_head*head_dim
   int kv_rows;         // n_kv_head*head_dim
   int pos_add;         // this token sits at *pos + pos_add
+  int n_tok;           // tokens of the layer call (positions *pos .. *pos + n_tok - 1)
 };
 
 // Planner: fills job geometry for `nmat` matrices; returns NT_OK or an error.
@@ -200,10 +202,14 @@ void attn_plan(int head_dim, int max_ctx, int& chunk, int& nsplit);
 int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, const int32_t* pos, int n_query,
                      int n_head, int n_kv, int head_dim, int max_ctx, int chunk, int nsplit, float* part_o,
                      float* part_ml, float* o, hipStream_t stream);
-int launch_embed(int fmt, const void* E, const int32_t* tokens, int M, int vocab, int cols, float* x,
+// Embedding rows of tokens[0..M) into x; also clears the status word *err
+// (may be null).
+int launch_embed(int fmt, const void* E, const int32_t* tokens, int M, int vocab, int cols, float* x, int* err,
                  hipStream_t stream);
 int argmax_parts(int n);
-int launch_argmax(const float* logits, int M, int n, float* pv, int* pi, int32_t* out, hipStream_t stream);
+// Greedy tokens of M logit rows; -1 for every row when *err (may be null) is set.
+int launch_argmax(const float* logits, int M, int n, float* pv, int* pi, const int* err, int32_t* out,
+                  hipStream_t stream);
 
 // F16 / F32 weights (nt_gemv_f.hip): Y[t][r] = W X[t] for M <= 8 tokens,
 // Y rows `rows` apart; cols a multiple of 16 / element size, W and X 16-byte aligned.

@@ -51,6 +51,13 @@ __global__ void k_spec_accept(const int32_t* __restrict__ d, const int32_t* __re
                               int32_t* __restrict__ cur, int32_t* __restrict__ pos, int32_t* __restrict__ out,
                               int32_t* __restrict__ n_out) {
   if (threadIdx.x != 0) return;
+  if (a[0] < 0) {
+    // the verify pass met a position out of range: nothing is emitted and
+    // the position and current token stay
+    for (int i = 0; i <= K; ++i) out[i] = -1;
+    *n_out = 0;
+    return;
+  }
   int n = 0;
   while (n < K && d[n + 1] == a[n]) ++n;
   for (int i = 0; i <= K; ++i) out[i] = i <= n ? a[i] : -1;

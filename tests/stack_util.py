@@ -40,7 +40,10 @@ class HostStack:
             blobs = [pack_blob(cfg, li) for li in self.layers[fs:]]
             sb = blobs[0].size
             host[fs:] = [torch.from_numpy(b).pin_memory() for b in blobs]
-            stage = (torch.empty(sb, dtype=torch.uint8, device=device), torch.empty(sb, dtype=torch.uint8, device=device))
+            # staging buffers start as 0xFF bytes: f16 scales of NaN, so a
+            # layer computed from a buffer before its copy landed gives NaN
+            stage = (torch.full((sb,), 0xFF, dtype=torch.uint8, device=device),
+                     torch.full((sb,), 0xFF, dtype=torch.uint8, device=device))
         keep = dict(
             dls=dls, host=host, stage=stage,
             emb=torch.from_numpy(self.tok_emb).to(device), head=torch.from_numpy(self.lm_head).to(device),

@@ -61,8 +61,7 @@ def test_layer_tiny(fmts, n_past, M):
     check(got, ref, kc, vc, li, n_past, M)
 
 
-# 8 query heads per kv head, head_dim 128: the batch-1 layer runs attention,
-# O, gate/up and down as one persistent launch (grid barriers between them)
+# 8 query heads per kv head, head_dim 128 (the 70B group size)
 GROUP8 = wl.LayerShape(hidden=2048, n_head=16, n_kv_head=2, head_dim=128, ffn=4096)
 
 
@@ -105,8 +104,9 @@ def test_layer_attention_shapes_verify_tokens(name):
 
 
 def test_layer_group8_repeat_calls_share_workspace():
-    # the launch leaves its barrier counters at zero: consecutive calls on one
-    # workspace give identical results, and a new workspace gives the same
+    # consecutive calls on one workspace give identical results, and a
+    # workspace filled with other bytes gives the same (its contents need no
+    # initialisation)
     import torch
     import quantized_decode_dequant_amd as nt
     from quantized_decode_dequant_amd.model import DeviceLayer, cfg_of
@@ -140,7 +140,21 @@ def test_layer_70b_q4_k_m_full():
     check(got, ref, kc, vc, li, 4096, 1)
 
 
-def test_layer_position_out_of_range_leaves_cache_alone():
+@pytest.mark.parametrize("fmts", [wl.Q4_K_M, wl.ALL_Q6_K], ids=["q4_k_m", "q6_k"])
+@pytest.mark.parametrize("M", [4, 8])
+def test_layer_70b_verify_full(fmts, M):
+    # the verify pass's layer at full Llama-70B shape: M drafted tokens at
+    # positions 4096..4096+M-1 through one layer (small-M GEMM for every
+    # projection), every output value of every token against the oracle
+    got, ref, kc, vc, li = run_layer(wl.LLAMA70B, fmts, wl.W_VERIFY_70B, 1, 4104, 4096, M)
+    check(got, ref, kc, vc, li, 4096, M)
+
+
+@pytest.mark.parametrize("M,bad", [(1, 16), (1, 116), (1, -1), (2, 15), (3, 14), (3, -2)])
+def test_layer_position_out_of_range_leaves_cache_alone(M, bad):
+    # pos < 0 or pos + M > max_ctx: no token writes the cache and x comes out
+    # NaN (M = 2 runs the engine per token, M = 3 the small-M GEMM); a later
+    # call at a valid position on the same workspace is unaffected
     import torch
     import quantized_decode_dequant_amd as nt
     from quantized_decode_dequant_amd.model import DeviceLayer, cfg_of
@@ -150,16 +164,23 @@ def test_layer_position_out_of_range_leaves_cache_alone():
     k0 = dl.k_cache.clone()
     v0 = dl.v_cache.clone()
     cfg = cfg_of(shape, max_ctx)
-    ws = torch.zeros(nt.layer_workspace_bytes(cfg, 2), dtype=torch.uint8, device=device())
-    xd = to_dev(np.ones(2 * shape.hidden, np.float32))
-    for bad in (max_ctx, max_ctx + 100, -1):
-        pos = torch.tensor([bad], dtype=torch.int32, device=device())
-        nt.decode_layer(cfg, dl.struct, xd, 1, pos, ws)
-    pos = torch.tensor([max_ctx - 1], dtype=torch.int32, device=device())
-    nt.decode_layer(cfg, dl.struct, xd, 2, pos, ws)  # second token would land past the end
+    ws = torch.zeros(nt.layer_workspace_bytes(cfg, M), dtype=torch.uint8, device=device())
+    x = np.stack([wl.gen_x(shape.hidden, wl.W_TEST, 4, 300 + i) for i in range(M)]).astype(np.float32)
+    xd = to_dev(x.reshape(-1))
+    pos = torch.tensor([bad], dtype=torch.int32, device=device())
+    nt.decode_layer(cfg, dl.struct, xd, M, pos, ws)
     torch.cuda.synchronize()
-    assert torch.equal(dl.v_cache[:, :max_ctx - 1], v0[:, :max_ctx - 1])
-    assert torch.equal(dl.k_cache[:, :max_ctx - 1], k0[:, :max_ctx - 1])
+    assert torch.equal(dl.k_cache, k0) and torch.equal(dl.v_cache, v0)
+    assert torch.isnan(xd).all()
+    # the same workspace at a valid position: the oracle's layer
+    xd = to_dev(x.reshape(-1))
+    pos = torch.tensor([10], dtype=torch.int32, device=device())
+    nt.decode_layer(cfg, dl.struct, xd, M, pos, ws)
+    torch.cuda.synchronize()
+    ref = oracle.layer(li, x, 10, M)
+    got = xd.cpu().numpy().reshape(M, shape.hidden)
+    for i in range(M):
+        assert rel_inf(got[i], ref[i]) <= LAYER_TOL
 
 
 def test_layer_argument_errors():

@@ -173,16 +173,19 @@ def test_verify_few_tokens_equals_sequential_decode(M):
 
 @pytest.mark.parametrize("M", [1, 4])
 def test_streamed_70b_shape_bitwise_equal_resident(M):
-    # Llama-70B-shaped Q6_K layers (701,890,560-byte blobs), two of four
-    # streamed from pinned host memory through the staging buffers
+    # Llama-70B-shaped Q6_K layers (701,890,560-byte blobs), three of five
+    # streamed from pinned host memory through the two staging buffers (the
+    # third copy waits for the first buffer to be freed); the buffers start
+    # as NaN bytes, so a layer read before its copy landed would show
     import torch
     dev = device()
-    hs = HostStack(wl.LLAMA70B, wl.ALL_Q6_K, n_layer=4, vocab=2048, max_ctx=64, n_past=40, wid=wl.W_TEST + 9)
+    hs = HostStack(wl.LLAMA70B, wl.ALL_Q6_K, n_layer=5, vocab=2048, max_ctx=64, n_past=40, wid=wl.W_TEST + 9)
     toks = torch.from_numpy(wl.gen_tokens(wl.W_TEST + 9, M, hs.vocab)).to(dev)
     pos = torch.tensor([40], dtype=torch.int32, device=dev)
     copy_stream = torch.cuda.Stream()
     res = []
     for fs in (None, 2):
+        say(f"70B-shaped stack of 5 Q6_K layers, first streamed {fs}, M={M}")
         h = hs.device_model(dev, first_streamed=fs, copy_stream=copy_stream if fs is not None else None)
         ws = torch.zeros(h.workspace_bytes(M), dtype=torch.uint8, device=dev)
         out = torch.zeros(M, dtype=torch.int32, device=dev)
@@ -192,6 +195,7 @@ def test_streamed_70b_shape_bitwise_equal_resident(M):
         res.append((out.clone(), logits.clone(), [d.k_cache.clone() for d in h.keep["dls"]]))
         del h, ws
         torch.cuda.empty_cache()
+    assert not torch.isnan(res[0][1]).any()
     assert torch.equal(res[1][0], res[0][0])
     assert torch.equal(res[1][1], res[0][1])
     for a, b in zip(res[1][2], res[0][2]):
