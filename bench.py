@@ -12,6 +12,10 @@ Prints one JSON line.  `value` is decode tokens/s with every input resident
 in HBM; `roofline` is the dominant kernel (the fused gate/up + SwiGLU GEMV)
 timed with HIP events on its launch stream inside the timed region;
 `cpu_baseline` is the fp64 oracle timed on this host on a bounded sample.
+`gemv` carries the GEMV half of the metric: the single Q8_0 4096x4096 GEMV
+and the seven 70B-shaped Q4_K_M projections, each timed as HIP graph replays
+over distinct weight copies (effective GB/s and fraction of 8 TB/s), with
+the oracle's GB/s for the same GEMVs on this host's cores beside them.
 
 Secondary workloads (`--workload`, one JSON line each; not the headline):
   gemv     the single Q8_0 4096x4096 GEMV and the seven 70B-shaped Q4_K_M
@@ -110,10 +114,27 @@ def build_stack(n_layer: int, max_ctx: int, n_past: int, dev):
     return h, first, vocab, wbytes, shape, fmts
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(sample_layers: int, n_layer_full: int, n_past: int):
     """The oracle (as it stands) on one decode token through `sample_layers`
     layers of the same shapes plus the LM head, scaled to tokens/s of the
-    full stack."""
+    full stack: the layers all have the same shapes and work, so the
+    80-layer time is the sampled layers' time times 80 / sample_layers."""
     import numpy as np
 
     import oracle
@@ -128,8 +149,6 @@ def cpu_baseline(sample_layers: int, n_layer_full: int, n_past: int):
     norm = wl.gen_gains(shape, wid, 0, wl.T_OUT_NORM)
     first = int(wl.gen_tokens(wid, 1, vocab)[0])
     m = oracle.OracleModel(shape, layers, wl.Q6_K, emb, wl.Q6_K, head, norm, vocab)
-    t0 = time.time()
-    x = np.zeros((1, shape.hidden))
     oracle.lib()  # load before timing
     t0 = time.time()
     m.decode([first], n_past)
@@ -141,8 +160,8 @@ def cpu_baseline(sample_layers: int, n_layer_full: int, n_past: int):
     t_head = time.time() - t1
     t_layers = max(t_all - t_head, 1e-9)
     per_token = t_layers * n_layer_full / sample_layers + t_head
-    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    return dict(value=1.0 / per_token, unit="tokens/s", cores=cores, kind="oracle",
+    return dict(value=1.0 / per_token, unit="tokens/s", cores=oracle_threads(), kind="oracle",
+                cpu=cpu_model(),
                 sample=f"one decode token through {sample_layers} of {n_layer_full} 70B-shaped Q4_K_M layers "
                        f"(context {n_past}) plus the 128256x8192 Q6_K LM head, fp64; {t_all:.1f} s measured, "
                        f"layer time scaled x{n_layer_full / sample_layers:.0f}")
@@ -239,30 +258,53 @@ def timed_graph(fn, n: int, reps: int = 5) -> float:
     return e0.elapsed_time(e1) / (reps * n)
 
 
-def workload_gemv(dev) -> dict:
-    """The single Q8_0 4096x4096 GEMV and the 70B-shaped projections:
-    effective GB/s of each GEMV, weights rotated over distinct copies so no
-    launch finds them in the last-level cache."""
-    import torch
-
-    import quantized_decode_dequant_amd as nt
+def gemv_cases(extra: bool):
+    """(name, format, rows, cols, workload id, tensor tag): the single Q8_0
+    4096x4096 GEMV and the seven 70B-shaped Q4_K_M projections; with
+    `extra`, the pages' other formats at the same kinds of shape."""
     import synth
     from synth import workloads as wl
-
-    read_gbs = read_ceiling(dev)
-    res = {}
     cases = [("q8_0_4096x4096", wl.Q8_0, 4096, 4096, wl.W_GEMV_Q8, 0)]
     for n in ["wq", "wk", "wv", "wo", "wg", "wu", "wd"]:
         r, c = wl.LLAMA70B.mat_shape(n)
         cases.append((f"70b_{n}_{synth.FMT_NAMES[wl.Q4_K_M[n]]}_{r}x{c}", wl.Q4_K_M[n], r, c, wl.W_GEMV_70B,
                       wl.MAT_TAG[n]))
-    # the other formats of the pages' list, at the same kinds of shape
-    for n in ["wq", "wg", "wd"]:
-        r, c = wl.LLAMA70B.mat_shape(n)
-        cases.append((f"x70b_{n}_q5_k_{r}x{c}", wl.Q5_K, r, c, wl.W_GEMV_70B, 20 + wl.MAT_TAG[n]))
-    cases.append(("xf16_4096x4096", wl.F16, 4096, 4096, wl.W_GEMV_Q8, 1))
-    cases.append(("xf32_4096x4096", wl.F32, 4096, 4096, wl.W_GEMV_Q8, 2))
-    layer_bytes, layer_ms = 0, 0.0
+    if extra:
+        for n in ["wq", "wg", "wd"]:
+            r, c = wl.LLAMA70B.mat_shape(n)
+            cases.append((f"x70b_{n}_q5_k_{r}x{c}", wl.Q5_K, r, c, wl.W_GEMV_70B, 20 + wl.MAT_TAG[n]))
+        cases.append(("xf16_4096x4096", wl.F16, 4096, 4096, wl.W_GEMV_Q8, 1))
+        cases.append(("xf32_4096x4096", wl.F32, 4096, 4096, wl.W_GEMV_Q8, 2))
+    return cases
+
+
+def oracle_gemv_gbs(cases) -> dict:
+    """The oracle's GEMV (fp64, as it stands) on the same weights and
+    activation as each case: weight GB/s on this host's cores."""
+    import oracle
+    from synth import workloads as wl
+    oracle.lib()
+    out = {}
+    for name, fmt, rows, cols, wid, tag in cases:
+        W = wl.gen_matrix(fmt, rows, cols, wid, 0, tag)
+        x = wl.gen_x(cols, wid)
+        t0 = time.perf_counter()
+        oracle.gemv(fmt, W, x, rows, cols)
+        dt = time.perf_counter() - t0
+        out[name] = round((W.nbytes + 4 * cols + 4 * rows) / dt / 1e9, 3)
+    return out
+
+
+def time_gemvs(dev, cases) -> dict:
+    """Effective GB/s of each GEMV case, weights rotated over distinct copies
+    so no launch finds them in the last-level cache; times are HIP graph
+    replays of back-to-back launches (eager launches beside them)."""
+    import torch
+
+    import quantized_decode_dequant_amd as nt
+    from synth import workloads as wl
+
+    res = {}
     for name, fmt, rows, cols, wid, tag in cases:
         wbytes = rows * nt.row_bytes(fmt, cols)
         ncopy = 32 if name.startswith("q8_0") else max(2, -(-512_000_000 // wbytes))
@@ -283,12 +325,25 @@ def workload_gemv(dev) -> dict:
         res[name] = dict(us=round(ms * 1e3, 2), gbs=round(alg / ms / 1e6, 1),
                          frac_peak=round(alg / ms / 1e6 / HBM_PEAK_GBS, 4), copies=ncopy, alg_bytes=alg,
                          us_eager_launches=round(ms_eager * 1e3, 2))
-        if name.startswith("70b"):
-            layer_bytes += alg
-            layer_ms += ms
         log(f"[bench] {name}: {ms * 1e3:.1f} us ({ms_eager * 1e3:.1f} us launched one by one from the host), "
             f"{alg / ms / 1e6:.0f} GB/s")
         del Ws, base
+        torch.cuda.empty_cache()
+    return res
+
+
+def seven_gemv_gbs(res: dict) -> float:
+    """Effective GB/s of the seven 70B projections run one after the other."""
+    b = sum(v["alg_bytes"] for k, v in res.items() if k.startswith("70b"))
+    us = sum(v["us"] for k, v in res.items() if k.startswith("70b"))
+    return round(b / us / 1e3, 1)
+
+
+def workload_gemv(dev) -> dict:
+    """The single Q8_0 4096x4096 GEMV and the 70B-shaped projections (and the
+    pages' other formats): effective GB/s of each GEMV."""
+    read_gbs = read_ceiling(dev)
+    res = time_gemvs(dev, gemv_cases(extra=True))
     return {"metric": "quant GEMV effective GB/s (% HBM peak)", "unit": "GB/s", "n_gpus": 1,
             "value": res["q8_0_4096x4096"]["gbs"], "higher_is_better": True, "data": "synthetic",
             "config": {"workload": "single GEMVs: Q8_0 4096x4096 and the 70B-shaped Q4_K_M projections "
@@ -296,7 +351,7 @@ def workload_gemv(dev) -> dict:
                                    "weights rotated over distinct copies; times are HIP graph replays of "
                                    "back-to-back launches"},
             "read_ceiling_gbs": round(read_gbs, 1), "gemv": res,
-            "seven_gemv_layer_gbs": round(layer_bytes / layer_ms / 1e6, 1)}
+            "seven_gemv_layer_gbs": seven_gemv_gbs(res)}
 
 
 def workload_layer8b(dev) -> dict:
@@ -789,8 +844,20 @@ def main():
         log(f"[bench] graph replays: {graph_ms:.3f} ms/token")
         del g
 
+    # the GEMV half of the metric: the single Q8_0 4096x4096 GEMV and the
+    # seven 70B-shaped projections, alone (graph replays, rotated copies)
+    cases = gemv_cases(extra=False)
+    gres = time_gemvs(dev, cases)
+    gemv = {"timing": "HIP graph replays of back-to-back launches, weights rotated over distinct copies "
+                      "larger than the 256 MB last-level cache",
+            "q8_0_4096x4096": gres["q8_0_4096x4096"],
+            "llama70b_q4_k_m": {k: v for k, v in gres.items() if k.startswith("70b")},
+            "llama70b_seven_gemvs_gbs": seven_gemv_gbs(gres)}
     cpu = None
     if not args.no_cpu_baseline:
+        log("[bench] oracle GEMVs")
+        gemv["cpu_oracle"] = {"gbs": oracle_gemv_gbs(cases), "cores": oracle_threads(), "cpu": cpu_model(),
+                              "kind": "oracle", "what": "the oracle's fp64 GEMV on the same weights, one call each"}
         log(f"[bench] cpu baseline (oracle, {args.cpu_sample_layers} layers)")
         cpu = cpu_baseline(args.cpu_sample_layers, args.layers, n_past)
 
@@ -805,7 +872,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4_k/q6_k weights, i8 dot products, f32 accumulate",
+        "dtype": "q4_k/q6_k weights; activations as 16-bit fixed point per 32-block, split into two int8 "
+                 "planes for i8 dot products; f32 accumulate",
         "data": "synthetic",
         "config": {
             "workload": "llama70b-shaped Q4_K_M 80-layer greedy decode, f16 KV at context 4096",
@@ -825,6 +893,7 @@ def main():
             "bytes_per_launch": ffn_bytes,
         },
         "cpu_baseline": cpu,
+        "gemv": gemv,
         "tokens_head": toks[:8],
         **({"ms_per_step_graph_replay": round(graph_ms, 4)} if graph_ms is not None else {}),
     }

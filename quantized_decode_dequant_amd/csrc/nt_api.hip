@@ -31,7 +31,9 @@ bool cfg_ok(const nt_layer_cfg& c) {
   if (c.hidden % 32 || c.ffn % 32 || (c.n_head * c.head_dim) % 32) return false;
   if (c.hidden > kMaxCols || c.ffn > kMaxCols || c.n_head * c.head_dim > kMaxCols) return false;
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return false;
-  if ((int64_t)c.max_ctx > 1024LL * std::min(256, std::max(64, 8192 / c.head_dim))) return false;  // <= 1024 attention splits
+  int chunk = 0, nsplit = 0;
+  attn_plan(c.head_dim, c.max_ctx, chunk, nsplit);
+  if (nsplit > 1024) return false;  // the combine merges at most 1024 splits
   return true;
 }
 

@@ -21,18 +21,22 @@
 namespace nt {
 namespace {
 
-constexpr int kAttnThreads = 256;
 constexpr int kMaxGroup = 8;  // query heads per kv head
 constexpr int kMaxSplits = 1024;  // position splits of one attention
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Positions per split for a head size: K and V tiles of 16 KB each (64 to
-// 256 positions), so a 4096-position cache of 8 kv heads makes ~520
-// workgroups, two per CU.
+// Split shape per head size: positions per split (K and V tiles of 16 KB
+// each, 64 to 256 positions) over four waves, so a 4096-position cache of
+// 8 kv heads makes ~520 workgroups, two per CU.  (Tiles of 256 positions
+// over 16 waves at head_dim 128 -- 136 workgroups, a quarter of the
+// partials -- took the split from 8.3 to 10.5 us per 70B layer and left
+// the combine unchanged.)
 template <int HD>
 constexpr int attn_chunk() { return 8192 / HD < 64 ? 64 : (8192 / HD > 256 ? 256 : 8192 / HD); }
+template <int HD>
+constexpr int attn_waves() { return 4; }
 
 // q: fp32 [n_query][n_head][HD] (query i at position pos+i attends to
 // 0..pos+i).  Partials: part_o [n_query][nsplit][n_head][HD],
@@ -43,31 +47,36 @@ constexpr int attn_chunk() { return 8192 / HD < 64 ? 64 : (8192 / HD > 256 ? 256
 // cache, so they enter exactly; q and the softmax numerators p are split as
 // x = hi + lo (hi = f16(x), lo = f16(x - hi), about 22 significant bits) and
 // each product is two MFMAs accumulating in fp32.
-//   scores  S = Q K^T: wave w takes positions [w C/4, (w+1) C/4) in 16-column
-//           tiles, K loaded straight from HBM in the B-operand layout;
-//   P V     the V tile is staged position-major in LDS; wave w takes output
-//           columns (16 dims per tile) over all positions (head_dim 32: two
-//           waves per tile, one per half of the positions, summed in LDS).
+//   scores  S = Q K^T: of the NW waves, wave w takes positions
+//           [w C/NW, (w+1) C/NW) in 16-column tiles, K loaded straight from
+//           HBM in the B-operand layout;
+//   P V     the V tile is staged position-major in LDS; each wave takes
+//           output columns (16 dims per tile), over all positions, or over
+//           one half of them when there are twice as many waves as tiles (the
+//           two halves summed in LDS).
 // Operand layout (16x16x32): A[i][k] in lane i + 16 (k / 8), element k % 8;
 // B[k][n] in lane n + 16 (k / 8), element k % 8; C[i][n] in lane
 // n + 16 (i / 4), element i % 4.
 template <int HD>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __restrict__ q, const uint16_t* __restrict__ kc,
-                                                             const uint16_t* __restrict__ vc, const int32_t* pos_ptr,
-                                                             int query, int n_head, int n_kv, int max_ctx, int nsplit,
-                                                             float* __restrict__ part_o, float* __restrict__ part_ml) {
+__global__ __launch_bounds__(64 * attn_waves<HD>()) void k_attn_split(
+    const float* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* pos_ptr, int query, int n_head, int n_kv, int max_ctx, int nsplit, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
   constexpr int C = attn_chunk<HD>();
+  constexpr int NW = attn_waves<HD>();           // waves per workgroup
+  constexpr int NT = 64 * NW;                    // threads
   constexpr int KS = HD / 32;                    // k-steps of a score tile
-  constexpr int PW = C / 4;                      // positions per wave (scores)
+  constexpr int PW = C / NW;                     // positions per wave (scores)
   constexpr int TW = PW / 16;                    // score tiles per wave
   constexpr int NTT = HD / 16;                   // output tiles
-  constexpr int TPW = NTT >= 4 ? NTT / 4 : 1;    // output tiles per wave
-  constexpr int KSPLIT = 4 * TPW / NTT;          // waves per output tile (over position parts)
+  constexpr int TPW = NTT >= NW ? NTT / NW : 1;  // output tiles per wave
+  constexpr int KSPLIT = NW * TPW / NTT;         // waves per output tile (over position parts)
   constexpr int PKS = C / 32 / KSPLIT;           // P.V k-steps per wave
   constexpr int VST = HD + 8;                    // V row stride in LDS (f16), rows 16-byte aligned
-  constexpr int NV = C * HD / 8 / kAttnThreads;  // 16-byte V chunks per thread
+  constexpr int NV = C * HD / 8 / NT;            // 16-byte V chunks per thread
   constexpr int CPR = HD / 8;                    // 16-byte chunks per row
-  static_assert(TW >= 1 && NV >= 1 && PKS >= 1 && KSPLIT <= 2, "attention tile shape");
+  static_assert(TW >= 1 && NV >= 1 && PKS >= 1 && KSPLIT <= 2 && NV * NT * 8 == C * HD && TW * 16 * NW == C,
+                "attention tile shape");
   __shared__ __attribute__((aligned(16))) _Float16 s_v[C * VST];
   __shared__ __attribute__((aligned(16))) _Float16 s_ph[kMaxGroup][C];
   __shared__ __attribute__((aligned(16))) _Float16 s_pl[kMaxGroup][C];
@@ -116,14 +125,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
     uint4 vr[NV];
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
-      const int c = tid + kAttnThreads * r, t = c / CPR, d8 = c % CPR;
+      const int c = tid + NT * r, t = c / CPR, d8 = c % CPR;
       vr[r] = *reinterpret_cast<const uint4*>(vg + (int64_t)(t < nt ? t : 0) * HD + 8 * d8);
     }
     // every K and V load is issued before the first wait for V
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
-      const int c = tid + kAttnThreads * r, t = c / CPR, d8 = c % CPR;
+      const int c = tid + NT * r, t = c / CPR, d8 = c % CPR;
       *reinterpret_cast<uint4*>(s_v + t * VST + 8 * d8) = vr[r];
     }
   }
@@ -165,7 +174,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
   __syncthreads();
 
   // softmax numerators (as hi + lo f16) and sums over this split, one wave per head
-  for (int h = wave; h < G; h += kAttnThreads / 64) {
+  for (int h = wave; h < G; h += NW) {
     float m = -FLT_MAX;
     for (int t = lane; t < nt; t += 64) m = fmaxf(m, s_s[h][t]);
     m = fmaxf(wave_max(m), -FLT_MAX);
@@ -186,7 +195,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(const float* __rest
   __syncthreads();
 
   // o = P V over this split
-  const int tg = wave % (4 / KSPLIT), kp = wave / (4 / KSPLIT);
+  const int tg = wave % (NW / KSPLIT), kp = wave / (NW / KSPLIT);
   const int hr = hv ? r16 : 0;
   v4f oacc[TPW];
 #pragma unroll
@@ -454,7 +463,12 @@ __global__ __launch_bounds__(64) void k_argmax_final(const float* __restrict__ p
 // Split geometry: attn_chunk positions per split.  Independent of the
 // device, so workspace sizes are.
 void attn_plan(int head_dim, int max_ctx, int& chunk, int& nsplit) {
-  chunk = std::min(256, std::max(64, 8192 / head_dim));
+  switch (head_dim) {
+    case 32: chunk = attn_chunk<32>(); break;
+    case 64: chunk = attn_chunk<64>(); break;
+    case 128: chunk = attn_chunk<128>(); break;
+    default: chunk = attn_chunk<256>(); break;
+  }
   nsplit = (max_ctx + chunk - 1) / chunk;
 }
 
@@ -464,13 +478,19 @@ int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, con
   trace_before(NT_TRACE_ATTN, stream);
   for (int qi = 0; qi < n_query; ++qi) {
     const dim3 grid(n_kv, nsplit);
+#define NT_ATTN_CASE(HD)                                                                                      \
+  case HD:                                                                                                    \
+    hipLaunchKernelGGL(k_attn_split<HD>, grid, dim3(64 * attn_waves<HD>()), 0, stream, q, kc, vc, pos, qi, n_head, \
+                       n_kv, max_ctx, nsplit, part_o, part_ml);                                               \
+    break;
     switch (head_dim) {
-      case 32: hipLaunchKernelGGL(k_attn_split<32>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, nsplit, part_o, part_ml); break;
-      case 64: hipLaunchKernelGGL(k_attn_split<64>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, nsplit, part_o, part_ml); break;
-      case 128: hipLaunchKernelGGL(k_attn_split<128>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, nsplit, part_o, part_ml); break;
-      case 256: hipLaunchKernelGGL(k_attn_split<256>, grid, dim3(kAttnThreads), 0, stream, q, kc, vc, pos, qi, n_head, n_kv, max_ctx, nsplit, part_o, part_ml); break;
+      NT_ATTN_CASE(32)
+      NT_ATTN_CASE(64)
+      NT_ATTN_CASE(128)
+      NT_ATTN_CASE(256)
       default: return NT_EUNSUPPORTED;
     }
+#undef NT_ATTN_CASE
   }
   hipLaunchKernelGGL(k_attn_combine, dim3(n_head * (head_dim / 32), n_query), dim3(256), 0, stream, part_o, part_ml,
                      pos, n_head, head_dim, chunk, nsplit, max_ctx, o);
