@@ -234,6 +234,27 @@ int nt_decode_step(const nt_model* model, const int32_t* token_dev, const int32_
                    int32_t* next_token_dev, float* logits_dev, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * nt_decode_step for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * step with no ws argument.  Its workspace is a file-scope device array of
+ * nt_decode_step_noalloc_max_bytes() bytes (32 MiB) that each device holds
+ * from the first call until the process ends; the call itself allocates
+ * nothing.  Arguments, results and errors are nt_decode_step's, plus:
+ *   NT_EWORKSPACE when nt_step_workspace_bytes(model, 1) exceeds the array
+ *     (e.g. a 70B-shaped model with max_ctx beyond ~60000 positions);
+ *   NT_EUNSUPPORTED for a model with streamed layers (first_streamed <
+ *     n_layer: the pipeline makes HIP events on first use);
+ *   NT_EHIP if the array's device address cannot be looked up.
+ * Every call on one device shares that device's array: calls that overlap
+ * on one device (different streams or host threads) race and must not be
+ * made.  The array's contents are left from the last call; the step needs
+ * none of them.
+ */
+int nt_decode_step_noalloc(const nt_model* model, const int32_t* token_dev, const int32_t* pos_dev,
+                           int32_t* next_token_dev, float* logits_dev, void* stream);
+size_t nt_decode_step_noalloc_max_bytes(void);
+
+/*
  * Verify pass of self-speculative decoding (p1 "About" and feature list:
  * self-speculative decoding with the resident layers as the draft model;
  * p2 "Fonctionnalites principales"; the drafted tokens are checked by one

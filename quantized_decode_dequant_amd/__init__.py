@@ -95,6 +95,9 @@ EXPORTS = {
     "nt_trace_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]),
     "nt_read_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "nt_test_fail_stream_copy": (ctypes.c_int, [ctypes.c_int]),
+    "nt_decode_step_noalloc": (ctypes.c_int, [ctypes.POINTER(Model), ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "nt_decode_step_noalloc_max_bytes": (ctypes.c_size_t, []),
 }
 
 TRACE_GEMV, TRACE_GEMV_RESID, TRACE_QKV, TRACE_FFN_UP, TRACE_ATTN = 0, 1, 2, 3, 4
@@ -332,6 +335,12 @@ class ModelHandle:
         _check("nt_decode_step", lib().nt_decode_step(ctypes.byref(self.m), _ptr(token_dev), _ptr(pos_dev),
                                                       _ptr(next_dev), _ptr(logits_dev), _ptr(ws),
                                                       ws.numel() * ws.element_size(), _stream(stream)))
+
+    def decode_step_noalloc(self, token_dev, pos_dev, next_dev, logits_dev=None, stream=None) -> None:
+        """nt_decode_step_noalloc: the decode step on the library's own device workspace."""
+        _check("nt_decode_step_noalloc", lib().nt_decode_step_noalloc(ctypes.byref(self.m), _ptr(token_dev),
+                                                                      _ptr(pos_dev), _ptr(next_dev),
+                                                                      _ptr(logits_dev), _stream(stream)))
 
     def verify_step(self, tokens_dev, M: int, pos_dev, argmax_dev, ws, logits_dev=None, stream=None) -> None:
         """nt_verify_step."""

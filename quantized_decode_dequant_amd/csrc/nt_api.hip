@@ -505,6 +505,32 @@ SpecWs spec_ws(const nt_model& m, int K) {
   return s;
 }
 
+// Workspace of nt_decode_step_noalloc: a file-scope device array, so that
+// callers that cannot allocate (graph capture, tight serving loops) need no
+// buffer of their own.  Each device that runs the entry point holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: kernels and copies take the address that
+// hipGetSymbolAddress gives, kept per device.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64] = {};
+
+// The device address of `scratch` on the current device (looked up once per
+// device, with that device current); null if the lookup fails.
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_dev[dev] = p;
+  }
+  return g_scratch_dev[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -634,6 +660,26 @@ int nt_decode_step(const nt_model* model, const int32_t* token_dev, const int32_
                    float* logits_dev, void* ws, size_t ws_bytes, void* stream) {
   if (!model) return NT_EINVAL;
   return run_step(*model, token_dev, 1, pos_dev, next_token_dev, logits_dev, ws, ws_bytes,
+                  static_cast<hipStream_t>(stream));
+}
+
+size_t nt_decode_step_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int nt_decode_step_noalloc(const nt_model* model, const int32_t* token_dev, const int32_t* pos_dev,
+                           int32_t* next_token_dev, float* logits_dev, void* stream) {
+  if (!model) return NT_EINVAL;
+  // streamed layers need the pipeline's events, which are made on first use
+  if (model->first_streamed != model->n_layer) return NT_EUNSUPPORTED;
+  const size_t need = nt_step_workspace_bytes(model, 1);
+  if (need == 0) return NT_EINVAL;
+  if (need > kScratchBytes) return NT_EWORKSPACE;
+  // validate everything before the first call on a device looks the array up
+  int rc = run_step(*model, token_dev, 1, pos_dev, next_token_dev, logits_dev, reinterpret_cast<void*>(256), need,
+                    nullptr, StepArgs(), true);
+  if (rc != NT_OK) return rc;
+  void* ws = scratch_ptr();
+  if (!ws) return NT_EHIP;
+  return run_step(*model, token_dev, 1, pos_dev, next_token_dev, logits_dev, ws, kScratchBytes,
                   static_cast<hipStream_t>(stream));
 }
 
