@@ -1,33 +1,38 @@
 """Full-size parity: the 80-layer Llama-70B-shaped Q4_K_M stack (hidden 8192,
 FFN 28672, 64/8 heads, f16 KV at context 4096, Q6_K embeddings and LM head of
-128256 x 8192) decoded greedily on the GPU, in the bench's launch
-configuration (nt_decode_step), against the fp64 oracle on the same seeded
-inputs.  Bar: identical greedy tokens; logits within 5e-3 of the largest
-|logit|.
+128256 x 8192) decoded greedily on the GPU through nt_decode_step, the
+bench's launch configuration, against the fp64 oracle on the same seeded
+inputs.
 
-The oracle's tokens and sampled logits for the first steps are stored in
-tests/golden/stack70b_q4km_greedy.json (written by make_stack70b_golden.py,
-which calls only the oracle; ~45 s per token on 16 cores), so the test
-checks every stored step without recomputing it.  Without that file, or with
-NT_STACK70B_LIVE=1, the oracle also runs here for NT_STACK70B_STEPS steps
-(default 1; needs ~45 GB of host memory).
+Teacher forcing (the bar).  tests/golden/stack70b_q4km_teacher.{json,npz},
+written by make_stack70b_golden.py from the oracle alone (~45 s per token on
+16 cores), hold the oracle's own greedy decode of 64 steps from context 4096:
+per step the input token, the greedy token, the full logit vector and the
+f16 K/V rows the step appended to every layer.  Before GPU step s the rows
+of oracle steps 0..s-1 are in the GPU caches (each step's rows are written
+over the GPU's own right after it) and the input is the oracle's token, so
+every step starts from the oracle's state and is compared on its own:
+  - the greedy token equals the oracle's, at every step;
+  - the full logit vector is within 5e-3 of the largest |logit|;
+  - the K/V rows the GPU appended, per layer, agree with the oracle's within
+    5e-3 of their largest magnitude (the layer bar: inside the stack each
+    layer's input already carries the deviation of the layers before it).
+The conditioning estimate stored with each step (cond_err: how far the
+oracle's own logits move when the residual stream entering every layer moves
+by 1.5e-5 of its largest magnitude, the half step of the fixed point the GPU
+holds activations in) says which steps are posed at the bar.  Where it
+exceeds a tenth of the bar, the oracle itself cannot fix the logits to 5e-3
+under deviations of the GPU's size, and the step is held to the token (and
+the logit and K/V checks are reported, not asserted); those steps are listed
+with their numbers in the design notes.  A step without a stored estimate is
+held to every check.
 
-On these random weights the residual stream grows through the 80 layers
-(logits of ~3400) and attention is close to a one-position choice, so at some
-steps the stack amplifies rounding: the stored file also holds, per step, how
-far the oracle's own logits move when 10% of its past cache entries change by
-one f16 ulp (perturbed_err).  Logits are held to the bar at the steps where
-that movement stays under a tenth of the bar, where the bar is meaningful.
-
-The decode is a trajectory: each step appends K/V entries that the GPU
-rounds from fp32 and the oracle from fp64, and the amplifying steps grow
-those differences.  Tokens are identical for the first TRAJECTORY_STEPS
-steps; at step 16 the two trajectories part (the GPU emits 123785, the
-stored oracle 83067).  The oracle run on the GPU's own caches after step 15
-gives the GPU's token with logits within 8.4e-4, and the oracle's own
-trajectory flips a token at step 18 under the one-ulp perturbation, so the
-parting is the stack's sensitivity, not a step the GPU computes wrongly.
-The later stored steps are kept as the record and not compared.
+Free-running (a record, not the bar).  Without teacher forcing each step
+appends K/V rows that the GPU rounds from fp32 and the oracle from fp64, and
+this random-weight stack amplifies such differences at some steps, so the two
+trajectories part after some steps (the stored record,
+stack70b_q4km_greedy.json, shows where).  That test checks the first step,
+where both start from the same state, and prints the rest.
 """
 import json
 import os
@@ -41,73 +46,108 @@ from tests.stack_util import HostStack
 
 pytestmark = pytest.mark.gpu
 
-GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "stack70b_q4km_greedy.json")
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TEACHER_JSON = os.path.join(GOLDEN, "stack70b_q4km_teacher.json")
+TEACHER_NPZ = os.path.join(GOLDEN, "stack70b_q4km_teacher.npz")
+FREE_JSON = os.path.join(GOLDEN, "stack70b_q4km_greedy.json")
 TOL = 5e-3
-STABLE = TOL / 10  # oracle's own logit movement under a one-ulp cache perturbation
-TRAJECTORY_STEPS = 16  # stored steps before the GPU and oracle trajectories part
+KV_TOL = 5e-3
+N_PAST = 4096
 
 
-def gpu_greedy(hs, n_past, steps, dev):
-    import torch
-    h = hs.device_model(dev)
-    ws = torch.zeros(h.workspace_bytes(1), dtype=torch.uint8, device=dev)
-    tok = torch.tensor([hs.first_token], dtype=torch.int32, device=dev)
-    pos = torch.tensor([n_past], dtype=torch.int32, device=dev)
-    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
-    logits = torch.zeros(hs.vocab, dtype=torch.float32, device=dev)
-    toks, lgs = [], []
-    for s in range(steps):
-        h.decode_step(tok, pos, nxt, ws, logits)
-        torch.cuda.synchronize()
-        toks.append(int(nxt.item()))
-        lgs.append(logits.cpu().numpy())
-        tok.copy_(nxt)
-        pos += 1
-    del h
-    torch.cuda.empty_cache()
-    return toks, lgs
+def load_teacher():
+    g = json.load(open(TEACHER_JSON))
+    z = np.load(TEACHER_NPZ)
+    n = min(len(g["steps"]), z["kv_rows"].shape[0], z["logits"].shape[0])
+    return g, z["kv_rows"][:n], z["logits"][:n], n
 
 
 @pytest.mark.timeout(900)
-def test_stack_70b_q4_k_m_greedy():
+def test_stack_70b_q4_k_m_teacher_forced():
+    import torch
     dev = device()  # before the 45 GB of host inputs are generated
-    golden = json.load(open(GOLDEN)) if os.path.exists(GOLDEN) else None
-    live = golden is None or os.environ.get("NT_STACK70B_LIVE") == "1"
-    n_live = int(os.environ.get("NT_STACK70B_STEPS", "1")) if live else 0
-    n_gold = min(len(golden["steps"]), TRAJECTORY_STEPS) if golden else 0
-    steps = max(n_live, n_gold)
-    n_past = 4096
-    say(f"generating the 80-layer 70B-shaped stack ({steps} steps: {n_gold} stored, {n_live} live)")
-    hs = HostStack(wl.LLAMA70B, wl.Q4_K_M, n_layer=80, vocab=128256, max_ctx=n_past + steps, n_past=n_past,
+    g, kv, ref_logits, n = load_teacher()
+    say(f"teacher-forced 70B stack: {n} stored oracle steps")
+    assert n >= 1
+    hs = HostStack(wl.LLAMA70B, wl.Q4_K_M, n_layer=80, vocab=128256, max_ctx=N_PAST + n, n_past=N_PAST,
                    wid=wl.W_STACK_70B)
-    g_toks, g_lgs = gpu_greedy(hs, n_past, steps, dev)
-    if golden:
-        assert golden["first_token"] == hs.first_token and golden["n_past"] == n_past
-        idx = np.asarray(golden["sample_idx"])
-        n_checked = 0
-        for s, st in enumerate(golden["steps"][:n_gold]):
-            got = g_lgs[s]
-            err = float(np.abs(got[idx] - np.asarray(st["sample_logits"])).max() / st["logit_max_abs"])
-            top = np.abs(np.array([got[i] - v for i, v in st["top5"]])).max() / st["logit_max_abs"]
-            moved = st.get("perturbed_err", 0.0)
-            stable = moved <= STABLE
-            say(f"step {s}: gpu {g_toks[s]} oracle {st['next']} margin {st['margin']:.4g} "
-                f"sampled logits err {err:.2e}, top-5 err {top:.2e}; oracle under perturbation {moved:.2e}"
-                f"{'' if stable else ' (amplifying step: token only)'}")
-            assert st["token_in"] == (hs.first_token if s == 0 else g_toks[s - 1])
-            assert g_toks[s] == st["next"]
-            if stable:
-                assert err <= TOL and top <= TOL
-                n_checked += 1
-        assert n_checked >= n_gold // 2
-    if n_live:
-        om = hs.oracle_model()
-        t = hs.first_token
-        for s in range(n_live):
-            say(f"oracle step {s}")
-            nxt_o, margin, lg, _ = om.decode([t], n_past + s, want_logits=True)
-            err = rel_inf(g_lgs[s], lg[0])
-            say(f"step {s}: gpu {g_toks[s]} oracle {int(nxt_o[0])} margin {margin[0]:.4g} logits rel err {err:.2e}")
-            assert err <= TOL
-            assert g_toks[s] == int(nxt_o[0])
-            t = int(nxt_o[0])
+    assert g["first_token"] == hs.first_token and g["n_past"] == N_PAST
+    h = hs.device_model(dev)
+    dls = h.keep["dls"]
+    ws = torch.zeros(h.workspace_bytes(1), dtype=torch.uint8, device=dev)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+    pos = torch.zeros(1, dtype=torch.int32, device=dev)
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    logits = torch.zeros(hs.vocab, dtype=torch.float32, device=dev)
+    token_only = []
+    worst, kv_worst = 0.0, 0.0
+    for s, st in enumerate(g["steps"][:n]):
+        p = N_PAST + s
+        assert st["pos"] == p and st["token_in"] == (hs.first_token if s == 0 else g["steps"][s - 1]["next"])
+        tok.fill_(st["token_in"])
+        pos.fill_(p)
+        h.decode_step(tok, pos, nxt, ws, logits)
+        torch.cuda.synchronize()
+        got = logits.cpu().numpy().astype(np.float64)
+        err = rel_inf(got, ref_logits[s])
+        # the rows this step appended, against the oracle's, then replaced by them
+        kv_err, kv_at = 0.0, None
+        for l, d in enumerate(dls):
+            for c, cache in enumerate((d.k_cache, d.v_cache)):
+                mine = cache[:, p, :].cpu().numpy().view(np.float16).astype(np.float64)
+                e = rel_inf(mine, kv[s, l, c].view(np.float16).astype(np.float64))
+                if e > kv_err:
+                    kv_err, kv_at = e, (l, "KV"[c])
+                cache[:, p, :] = torch.from_numpy(kv[s, l, c].view(np.int16)).to(dev)
+        cond = st.get("cond_err")
+        ill = cond is not None and cond > TOL / 10
+        say(f"step {s}: gpu {int(nxt.item())} oracle {st['next']} margin {st['margin']:.4g} logits err {err:.2e} "
+            f"appended K/V err {kv_err:.2e} (layer {kv_at[0]} {kv_at[1]})" + (f"; conditioning {cond:.2e}" if cond is not None else "")
+            + (" (token only)" if ill else ""))
+        assert int(nxt.item()) == st["next"], s
+        if ill:
+            token_only.append(s)
+        else:
+            assert err <= TOL, s
+            assert kv_err <= KV_TOL, s
+            worst = max(worst, err)
+            kv_worst = max(kv_worst, kv_err)
+    say(f"teacher-forced: {n} steps, tokens identical; at the {n - len(token_only)} steps posed at the bar, logits "
+        f"within {worst:.2e} of the largest |logit| (bar {TOL}) and appended K/V rows within {kv_worst:.2e}; "
+        f"token-only steps {token_only}")
+
+
+@pytest.mark.timeout(600)
+def test_stack_70b_q4_k_m_free_running_record():
+    import torch
+    dev = device()
+    g = json.load(open(FREE_JSON))
+    steps = len(g["steps"])
+    hs = HostStack(wl.LLAMA70B, wl.Q4_K_M, n_layer=80, vocab=128256, max_ctx=N_PAST + steps, n_past=N_PAST,
+                   wid=wl.W_STACK_70B)
+    assert g["first_token"] == hs.first_token
+    h = hs.device_model(dev)
+    ws = torch.zeros(h.workspace_bytes(1), dtype=torch.uint8, device=dev)
+    tok = torch.tensor([hs.first_token], dtype=torch.int32, device=dev)
+    pos = torch.tensor([N_PAST], dtype=torch.int32, device=dev)
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    logits = torch.zeros(hs.vocab, dtype=torch.float32, device=dev)
+    idx = np.asarray(g["sample_idx"])
+    parted = None
+    for s, st in enumerate(g["steps"]):
+        h.decode_step(tok, pos, nxt, ws, logits)
+        torch.cuda.synchronize()
+        got = logits.cpu().numpy()
+        err = float(np.abs(got[idx] - np.asarray(st["sample_logits"])).max() / st["logit_max_abs"])
+        same = int(nxt.item()) == st["next"]
+        say(f"free-running step {s}: gpu {int(nxt.item())} oracle {st['next']} sampled logits err {err:.2e}")
+        if s == 0:
+            # both start from the same state here
+            assert same and err <= TOL
+        if not same:
+            parted = s
+            break
+        tok.copy_(nxt)
+        pos += 1
+    say(f"free-running trajectories " + (f"part at step {parted}" if parted is not None else
+                                         f"agree over all {steps} stored steps"))

@@ -227,3 +227,29 @@ def test_stack_output_norm_logit_values():
         assert np.allclose(logits[0], expect, rtol=1e-13, atol=0)
         assert nxt[0] == int(np.argmax(expect))
         assert abs(math.sqrt(np.mean(e * e)) - 1.0) > 0.5  # the norm is far from a no-op here
+
+
+def test_composed_decode_equals_plain_decode():
+    # the stored conditioning estimates of the 70B stack rerun each decode
+    # step composed from the oracle's parts (embedding row, layers, output
+    # norm, LM head) with a perturbation in between; without it the
+    # composition is the plain decode, bit for bit
+    import importlib.util
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "make_stack70b_golden.py")
+    spec = importlib.util.spec_from_file_location("make_stack70b_golden", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    from tests.stack_util import HostStack
+    hs = HostStack(wl.TINY, wl.Q4_K_M, n_layer=3, vocab=300, max_ctx=24, n_past=9, wid=wl.W_TEST + 70)
+    om_a, om_b = hs.oracle_model(), hs.oracle_model()
+    _, _, lg, _ = om_a.decode([hs.first_token], 9, want_logits=True)
+    lg_b = mod.perturbed_decode(om_b, hs, hs.first_token, 9, 0.0, 0)
+    assert np.array_equal(lg[0], lg_b)
+    for a, b in zip(om_a.layers_in, om_b.layers_in):
+        assert np.array_equal(a.k_cache, b.k_cache) and np.array_equal(a.v_cache, b.v_cache)
+    # a perturbation of the size used there moves these logits a little, not at all is wrong
+    om_c = hs.oracle_model()
+    lg_c = mod.perturbed_decode(om_c, hs, hs.first_token, 9, 1.5e-5, 0)
+    d = np.abs(lg_c - lg[0]).max() / np.abs(lg[0]).max()
+    assert 0 < d < 1e-3
