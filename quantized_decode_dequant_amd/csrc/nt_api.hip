@@ -19,8 +19,10 @@ size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Workspace of one decode layer for M tokens (offsets from the base).  With
 // M >= 2 it also holds the small-M GEMM's staged activation and partial sums.
+// qx_o, qx_h, qx_a: the quantized activations (qx_bytes each per token) that
+// the attention, O and gate/up launches hand to the next launch.
 struct LayerWs {
-  size_t q, part_o, part_ml, o, a, err, stage, part, total;
+  size_t q, part_o, part_ml, o, a, err, qx_o, qx_h, qx_a, stage, part, total;
   int chunk, nsplit;
 };
 
@@ -48,6 +50,9 @@ LayerWs layer_ws(const nt_layer_cfg& c, int M) {
   w.o = off; off += up256((size_t)M * nq * 4);
   w.a = off; off += up256((size_t)M * c.ffn * 4);
   w.err = off; off += 256;
+  w.qx_o = off; off += up256((size_t)M * qx_bytes(nq));
+  w.qx_h = off; off += up256((size_t)M * qx_bytes(c.hidden));
+  w.qx_a = off; off += up256((size_t)M * qx_bytes(c.ffn));
   if (M >= 2) {
     const int64_t nkv = (int64_t)c.n_kv_head * c.head_dim;
     w.stage = off; off += up256(stage_m_bytes(std::max<int>(std::max<int>(c.hidden, (int)nq), c.ffn)));
@@ -124,7 +129,7 @@ int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const
   }
   // 2. attention over the cache (token t sees positions 0..pos+t)
   if ((rc = launch_attention(q, L.k_cache, L.v_cache, pos, M, c.n_head, c.n_kv_head, c.head_dim, c.max_ctx, w.chunk,
-                             w.nsplit, part_o, part_ml, o, st)) != NT_OK)
+                             w.nsplit, part_o, part_ml, o, nullptr, st)) != NT_OK)
     return rc;
   // 3. h = x + Wo o
   {
@@ -177,9 +182,19 @@ int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const
 constexpr int kEngineLayerTokens = 2;
 constexpr int kEngineHeadTokens = 3;
 
+// How a layer hands its input and output on as quantized activations
+// (qx_bytes(hidden) per token).
+struct LayerQx {
+  const uint8_t* x_in = nullptr;    // the layer's input times attn_norm, quantized by the launch before; or null
+  uint8_t* x_out = nullptr;         // where the down projection quantizes the output for the next launch, or null
+  const float* next_gain = nullptr; // the gains the next launch normalizes with (null: none)
+  bool x_out_written = false;       // set when the down projection did write x_out
+};
+
 // The launches of one layer (arguments already validated).
 int run_layer(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const int32_t* pos, uint8_t* ws,
-              const LayerWs& w, hipStream_t st) {
+              const LayerWs& w, hipStream_t st, LayerQx* lq = nullptr) {
+  if (lq) lq->x_out_written = false;
   if (M > kEngineLayerTokens) return run_layer_m(c, L, x, M, pos, ws, w, st);
   const int nq = c.n_head * c.head_dim, nkv = c.n_kv_head * c.head_dim;
   float* q = reinterpret_cast<float*>(ws + w.q);
@@ -198,6 +213,12 @@ int run_layer(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const i
     if ((rc = plan_job(job, 3, W, fmt, rows, c.hidden, 0, 1)) != NT_OK) return rc;
     for (int i = 0; i < M; ++i) {
       ProArgs pro{x + (int64_t)i * c.hidden, L.attn_norm, c.rms_eps, 0, c.head_dim, c.rope_theta, pos, i};
+      if (lq && lq->x_in) {  // already normalized-and-quantized by the launch before
+        pro.src = nullptr;
+        pro.gain = nullptr;
+        pro.qx = lq->x_in + (int64_t)i * qx_bytes(c.hidden);
+        pro.qx_norm = 1;
+      }
       EpiArgs ea{};
       ea.q_out = q + (int64_t)i * nq;
       ea.k_cache = L.k_cache;
@@ -214,60 +235,89 @@ int run_layer(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const i
       if ((rc = launch_gemv(job, pro, EPI_QKV, ea, st)) != NT_OK) return rc;
     }
   }
-  // 2. attention over the cache (split over positions) and combine
+  // 2. attention over the cache (split over positions) and combine; the
+  // combine also hands o on quantized (each of its workgroups is one block)
+  const size_t qo = qx_bytes(nq), qh = qx_bytes(c.hidden), qa = qx_bytes(c.ffn);
+  uint8_t* qx_o = qx_ok(nq) ? ws + w.qx_o : nullptr;
   if ((rc = launch_attention(q, L.k_cache, L.v_cache, pos, M, c.n_head, c.n_kv_head, c.head_dim, c.max_ctx, w.chunk,
-                             w.nsplit, part_o, part_ml, o, st)) != NT_OK)
+                             w.nsplit, part_o, part_ml, o, qx_o, st)) != NT_OK)
     return rc;
+  // O, gate/up and down hand their outputs on quantized where their rows
+  // split into whole 32-row blocks per workgroup (Job::qblock)
   Job jo, jf, jd;
   {
     const uint8_t* W[1] = {u8(L.wo.data)};
     const int fmt[1] = {L.wo.fmt};
     const int rows[1] = {c.hidden};
-    if ((rc = plan_job(jo, 1, W, fmt, rows, nq, 0, 0)) != NT_OK) return rc;
+    if ((rc = plan_job(jo, 1, W, fmt, rows, nq, 0, 0, 1)) != NT_OK) return rc;
   }
   {
     const uint8_t* W[2] = {u8(L.wg.data), u8(L.wu.data)};
     const int fmt[2] = {L.wg.fmt, L.wu.fmt};
     const int rows[2] = {c.ffn, c.ffn};
-    if ((rc = plan_job(jf, 2, W, fmt, rows, c.hidden, 1, 0)) != NT_OK) return rc;
+    if ((rc = plan_job(jf, 2, W, fmt, rows, c.hidden, 1, 0, 1)) != NT_OK) return rc;
   }
   {
     const uint8_t* W[1] = {u8(L.wd.data)};
     const int fmt[1] = {L.wd.fmt};
     const int rows[1] = {c.hidden};
-    if ((rc = plan_job(jd, 1, W, fmt, rows, c.ffn, 0, 0)) != NT_OK) return rc;
+    if ((rc = plan_job(jd, 1, W, fmt, rows, c.ffn, 0, 0, lq && lq->x_out ? 1 : 0)) != NT_OK) return rc;
   }
   for (int i = 0; i < M; ++i) {
     float* xi = x + (int64_t)i * c.hidden;
     // 3. h = x + Wo o
     {
       ProArgs pro{o + (int64_t)i * nq, nullptr, 0.f, 0, 0, 0.f, nullptr, 0};
+      if (qx_o) {
+        pro.src = nullptr;
+        pro.qx = qx_o + i * qo;
+      }
       EpiArgs ea{};
       ea.y = xi;
+      if (jo.qblock) {
+        ea.qx_out = ws + w.qx_h + i * qh;
+        ea.qx_gain = L.ffn_norm;
+      }
       if ((rc = launch_gemv(jo, pro, EPI_RESID, ea, st)) != NT_OK) return rc;
     }
     // 4. a = silu(Wg hn) * (Wu hn), hn = RMSNorm(h)
     {
       ProArgs pro{xi, L.ffn_norm, c.rms_eps, 0, 0, 0.f, nullptr, 0};
+      if (jo.qblock) {
+        pro.src = nullptr;
+        pro.gain = nullptr;
+        pro.qx = ws + w.qx_h + i * qh;
+        pro.qx_norm = 1;
+      }
       EpiArgs ea{};
       ea.y = a;
+      if (jf.qblock) ea.qx_out = ws + w.qx_a + i * qa;
       if ((rc = launch_gemv(jf, pro, EPI_SWIGLU, ea, st)) != NT_OK) return rc;
     }
     // 5. x = h + Wd a
     {
       ProArgs pro{a, nullptr, 0.f, 0, 0, 0.f, nullptr, 0};
+      if (jf.qblock) {
+        pro.src = nullptr;
+        pro.qx = ws + w.qx_a + i * qa;
+      }
       EpiArgs ea{};
       ea.y = xi;
       ea.err = err;  // NaN out when a position was out of range
+      if (jd.qblock) {
+        ea.qx_out = lq->x_out + i * qh;
+        ea.qx_gain = lq->next_gain;
+      }
       if ((rc = launch_gemv(jd, pro, EPI_RESID, ea, st)) != NT_OK) return rc;
     }
   }
+  if (lq) lq->x_out_written = jd.qblock != 0;
   return NT_OK;
 }
 
 // ---- decode step
 struct StepWs {
-  size_t x, x_in, layer, logits, pv, pi, part_lm, total;
+  size_t x, x_in, qx_x, layer, logits, pv, pi, part_lm, total;
   LayerWs lw;
 };
 
@@ -296,6 +346,7 @@ StepWs step_ws(const nt_model& m, int M) {
   size_t off = 0;
   w.x = off; off += up256((size_t)M * m.cfg.hidden * 4);
   w.x_in = off; off += up256((size_t)m.cfg.hidden * 4);  // a layer's input, for the similarity of calibration
+  w.qx_x = off; off += up256((size_t)M * qx_bytes(m.cfg.hidden));  // the next layer's input, quantized
   w.layer = off; off += w.lw.total;
   w.logits = off; off += up256((size_t)M * m.vocab * 4);
   w.pv = off; off += up256((size_t)M * 256 * 4);
@@ -405,8 +456,22 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
   // from the same position); the embedding clears it, so a step without
   // layers reports no error
   int* err = reinterpret_cast<int*>(ws + w.layer + w.lw.err);
-  int rc = launch_embed(m.tok_emb.fmt, m.tok_emb.data, tokens, M, m.vocab, m.cfg.hidden, x, err, st);
+  // Each launch hands the residual stream on to the next normalizing launch
+  // as a quantized activation (times that launch's RMSNorm gains) where the
+  // layers run the GEMV engine: the embedding to the first layer, each
+  // layer's down projection to the next layer that runs, the last one to the
+  // LM head.
+  const bool qx_step = M <= kEngineLayerTokens && qx_ok(m.cfg.hidden);
+  uint8_t* qx_x = ws + w.qx_x;
+  auto gain_after = [&](int l) {  // the gains of the first launch after layer l that normalizes
+    for (int k = l + 1; k < m.n_layer; ++k)
+      if (!skipped(k)) return m.layers[k].attn_norm;
+    return m.out_norm;
+  };
+  int rc = launch_embed(m.tok_emb.fmt, m.tok_emb.data, tokens, M, m.vocab, m.cfg.hidden, x, err,
+                        qx_step ? qx_x : nullptr, qx_step ? gain_after(-1) : nullptr, st);
   if (rc != NT_OK) return rc;
+  bool x_quantized = qx_step;
   StreamEvents* ev = nullptr;
   hipStream_t cs = static_cast<hipStream_t>(m.copy_stream);
   auto issue_copy = [&](int j) -> int {
@@ -451,7 +516,12 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
     if (sa.cos_acc &&
         hipMemcpyAsync(x_in, x, (size_t)m.cfg.hidden * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
       return NT_EHIP;
-    if ((rc = run_layer(m.cfg, L, x, M, pos, ws + w.layer, w.lw, st)) != NT_OK) return rc;
+    LayerQx lq;
+    lq.x_in = x_quantized ? qx_x : nullptr;
+    lq.x_out = qx_step ? qx_x : nullptr;
+    lq.next_gain = gain_after(l);
+    if ((rc = run_layer(m.cfg, L, x, M, pos, ws + w.layer, w.lw, st, &lq)) != NT_OK) return rc;
+    x_quantized = lq.x_out_written;
     if (sa.cos_acc && (rc = launch_cos_acc(x_in, x, m.cfg.hidden, sa.cos_acc + l, st)) != NT_OK) return rc;
     if (l >= fs) {
       if (hipEventRecord(ev->freed[b], st) != hipSuccess) return NT_EHIP;
@@ -479,6 +549,12 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
     if ((rc = plan_job(jl, 1, Wl, fmtl, rowsl, m.cfg.hidden, 0, 0)) != NT_OK) return rc;
     for (int i = 0; i < M; ++i) {
       ProArgs pro{x + (int64_t)i * m.cfg.hidden, m.out_norm, m.cfg.rms_eps, 0, 0, 0.f, nullptr, 0};
+      if (x_quantized) {
+        pro.src = nullptr;
+        pro.gain = nullptr;
+        pro.qx = qx_x + (int64_t)i * qx_bytes(m.cfg.hidden);
+        pro.qx_norm = 1;
+      }
       EpiArgs ea{};
       ea.y = logits + (int64_t)i * m.vocab;
       if ((rc = launch_gemv(jl, pro, EPI_STORE, ea, st)) != NT_OK) return rc;

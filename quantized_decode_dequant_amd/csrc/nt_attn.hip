@@ -253,9 +253,12 @@ __global__ __launch_bounds__(64 * attn_waves<HD>()) void k_attn_split(
 // partial sums are added in order.  Once the position is known every load
 // is issued at once (each thread's first eight splits of o with the (m, l)
 // pairs), so the kernel waits on memory twice.
+// With qx_o the 32 values of the workgroup (one 32-block of the output) also
+// go out as a quantized activation of n_head * head_dim values per query.
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                       const int32_t* pos_ptr, int n_head, int head_dim, int chunk,
-                                                      int nsplit, int max_ctx, float* __restrict__ o) {
+                                                      int nsplit, int max_ctx, float* __restrict__ o,
+                                                      uint8_t* __restrict__ qx_o) {
   constexpr int kPre = 12;  // splits per thread held in registers
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[8];
@@ -324,7 +327,12 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
     float t = s_acc[0][tid];
 #pragma unroll
     for (int k = 1; k < 8; ++k) t += s_acc[k][tid];
-    o[((int64_t)query * n_head + h) * head_dim + d0 + tid] = t * inv;
+    const float v = t * inv;
+    o[((int64_t)query * n_head + h) * head_dim + d0 + tid] = v;
+    if (qx_o) {
+      const int64_t n = (int64_t)n_head * head_dim;
+      qx_store_block32(qx_o + query * qx_bytes(n), n, (h * head_dim + d0) >> 5, tid, v, v);
+    }
   }
 }
 
@@ -333,8 +341,11 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 // per 32-weight group; the formulas are the block definitions of nt.h.
 // It also clears the step's status word (err), which the layers set when a
 // position is out of range.
+// With qx the row times qx_gain also goes out as a quantized activation
+// (qx_bytes(cols) per token); each thread holds one 32-block.
 __global__ __launch_bounds__(256) void k_embed(int fmt, const uint8_t* __restrict__ E, const int32_t* tokens, int vocab,
-                                               int cols, float* __restrict__ x, int* __restrict__ err) {
+                                               int cols, float* __restrict__ x, int* __restrict__ err,
+                                               uint8_t* __restrict__ qx, const float* __restrict__ qx_gain) {
   const int m = blockIdx.y;
   if (err && m == 0 && blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
   int tok = tokens[m];
@@ -412,6 +423,27 @@ __global__ __launch_bounds__(256) void k_embed(int fmt, const uint8_t* __restric
       out[l] = d * (float)(int8_t)b[192 + e / 16] * (float)((nib | (hi << 4)) - 32);
     }
   }
+  if (qx) {
+    uint8_t* q = qx + (int64_t)m * qx_bytes(cols);
+    float v[32], amax = 0.f, ss = 0.f;
+    for (int l = 0; l < 32; ++l) {
+      const float y = out[l];
+      v[l] = qx_gain ? y * qx_gain[32 * grp + l] : y;
+      amax = fmaxf(amax, fabsf(v[l]));
+      ss += y * y;
+    }
+    int s16[2] = {0, 0};
+    for (int l = 0; l < 32; ++l) {
+      const int X = fx_quant(v[l], amax);
+      q[32 * grp + l] = (uint8_t)(fx_hi(X) & 255);
+      q[qx_lo_off(cols) + 32 * grp + l] = (uint8_t)(fx_lo(X) & 255);
+      s16[l >> 4] += X;
+    }
+    reinterpret_cast<int*>(q + qx_sum_off(cols))[2 * grp] = s16[0];
+    reinterpret_cast<int*>(q + qx_sum_off(cols))[2 * grp + 1] = s16[1];
+    reinterpret_cast<float*>(q + qx_sc_off(cols))[grp] = amax / kXMax;
+    reinterpret_cast<float*>(q + qx_ss_off(cols))[grp] = ss;
+  }
 }
 
 // ------------------------------------------------------------------ argmax
@@ -474,7 +506,7 @@ void attn_plan(int head_dim, int max_ctx, int& chunk, int& nsplit) {
 
 int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, const int32_t* pos, int n_query,
                      int n_head, int n_kv, int head_dim, int max_ctx, int chunk, int nsplit, float* part_o,
-                     float* part_ml, float* o, hipStream_t stream) {
+                     float* part_ml, float* o, uint8_t* qx_o, hipStream_t stream) {
   trace_before(NT_TRACE_ATTN, stream);
   for (int qi = 0; qi < n_query; ++qi) {
     const dim3 grid(n_kv, nsplit);
@@ -493,17 +525,17 @@ int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, con
 #undef NT_ATTN_CASE
   }
   hipLaunchKernelGGL(k_attn_combine, dim3(n_head * (head_dim / 32), n_query), dim3(256), 0, stream, part_o, part_ml,
-                     pos, n_head, head_dim, chunk, nsplit, max_ctx, o);
+                     pos, n_head, head_dim, chunk, nsplit, max_ctx, o, qx_o);
   const bool ok = hipGetLastError() == hipSuccess;
   trace_after(NT_TRACE_ATTN, stream);
   return ok ? NT_OK : NT_EHIP;
 }
 
 int launch_embed(int fmt, const void* E, const int32_t* tokens, int M, int vocab, int cols, float* x, int* err,
-                 hipStream_t stream) {
+                 uint8_t* qx, const float* qx_gain, hipStream_t stream) {
   const int groups = cols / 32;
   hipLaunchKernelGGL(k_embed, dim3((groups + 255) / 256, M), dim3(256), 0, stream, fmt,
-                     static_cast<const uint8_t*>(E), tokens, vocab, cols, x, err);
+                     static_cast<const uint8_t*>(E), tokens, vocab, cols, x, err, qx, qx_gain);
   return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
 }
 

@@ -128,5 +128,42 @@ __device__ __forceinline__ uint4 load_chunk(const uint8_t* p) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// The 16-bit fixed point of the activations: a 32-block with largest
+// magnitude amax has scale amax / 32639 and X = rint(v * 32639 / amax),
+// clamped to [-32639, 32639]; X = 256 hi + lo with hi = (X + 128) >> 8, so
+// both planes fit int8.  (A zero block has X = 0 and scale 0.)
+__device__ __forceinline__ int fx_quant(float v, float amax) {
+  const float inv = amax > 0.f ? kXMax / amax : 0.f;
+  const int X = __float2int_rn(v * inv);
+  return max(-32639, min(32639, X));
+}
+__device__ __forceinline__ int fx_hi(int X) { return (X + 128) >> 8; }
+__device__ __forceinline__ int fx_lo(int X) { return X - (fx_hi(X) << 8); }
+
+// Quantized-activation output of one 32-block held by 32 consecutive lanes
+// (lanes 0-31 or 32-63 of a wave, all active): lane l has value v (already
+// times the gains) and y (the value whose square goes into the block's sum
+// of squares); b is the block's index in the n-value vector at q.
+__device__ __forceinline__ void qx_store_block32(uint8_t* q, int64_t n, int b, int l, float v, float y) {
+  float amax = fabsf(v);
+#pragma unroll
+  for (int m = 16; m > 0; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
+  const int X = fx_quant(v, amax);
+  int s16 = X;
+#pragma unroll
+  for (int m = 8; m > 0; m >>= 1) s16 += __shfl_xor(s16, m, 16);
+  float ss = y * y;
+#pragma unroll
+  for (int m = 16; m > 0; m >>= 1) ss += __shfl_xor(ss, m, 32);
+  const int64_t e = 32 * (int64_t)b + l;
+  q[e] = (uint8_t)(fx_hi(X) & 255);
+  q[qx_lo_off(n) + e] = (uint8_t)(fx_lo(X) & 255);
+  if ((l & 15) == 0) reinterpret_cast<int*>(q + qx_sum_off(n))[2 * b + (l >> 4)] = s16;
+  if (l == 0) {
+    reinterpret_cast<float*>(q + qx_sc_off(n))[b] = amax / kXMax;
+    reinterpret_cast<float*>(q + qx_ss_off(n))[b] = ss;
+  }
+}
+
 }  // namespace
 }  // namespace nt

@@ -212,9 +212,16 @@ __device__ __forceinline__ float unit_q6_k(uint32_t seg, int k, NT_XARGS) {
 #undef NT_XARGS
 
 // ----------------------------------------------------------------- prologue
-// Stage the activation: v = src (or RMSNorm(src) * gain), then per 32-block
-// s = max|v| / 32639, X = rint(v / s), hi = (X + 128) >> 8, lo = X - 256 hi.
-// For the QKV launch it also tabulates the RoPE rotation of this position.
+// Stage the activation: v = src (times the RMSNorm gains where the launch
+// normalizes), then per 32-block s = max|v| / 32639, X = rint(v / s),
+// hi = (X + 128) >> 8, lo = X - 256 hi.  Quantizing v rather than the
+// normalized vector changes nothing but the block scales (a block's X do not
+// depend on a common factor), so the normalization factor r is applied to
+// the row sums in the epilogue, and no barrier is needed before the first
+// weight loads.  A launch given an already quantized activation (ProArgs::qx,
+// written by the epilogue of the launch before it) copies it instead.  For
+// the QKV launch the prologue also tabulates the RoPE rotation of this
+// position.
 //
 // Loads are coalesced: in round r thread t holds elements 4(NT r + t) ..
 // +3, so the 8 lanes of an aligned lane group hold one 32-block and a
@@ -227,10 +234,34 @@ __device__ __forceinline__ float unit_q6_k(uint32_t seg, int k, NT_XARGS) {
 constexpr int kXRounds = 8;  // rounds held in registers: inputs up to 4 * 1024 * 8 = 32768 wide
 
 struct XStage {
-  float4 v[kXRounds];  // src (times the gains once stage_norm has run)
+  float4 v[kXRounds];  // src (times the gains once stage_norm has run); or the chunks of a quantized activation
   float4 g[kXRounds];  // RMSNorm gains
   int pos;             // RoPE position
 };
+
+// A quantized activation is copied with 16-byte loads, kXRounds per thread.
+__device__ __forceinline__ int qx_chunks(const Job& job) { return (int)(qx_bytes(job.cols) / 16); }
+
+__device__ __forceinline__ void qstage_load(const Job& job, const ProArgs& pro, int tid, XStage& st) {
+  const int NT = job.nwaves * 64, nch = qx_chunks(job);
+#pragma unroll
+  for (int r = 0; r < kXRounds; ++r) {
+    const int c = tid + NT * r;
+    if (c < nch) st.v[r] = *reinterpret_cast<const float4*>(pro.qx + 16 * (int64_t)c);
+  }
+  st.pos = pro.rope_hd > 0 ? __builtin_nontemporal_load(pro.pos) + pro.pos_add : 0;
+}
+
+// The quantized activation's layout in memory is the staging area's in LDS
+// (x_hi at 0, then x_lo, x_sc, x_sum, x_ss).
+__device__ __forceinline__ void qstage_store(const Job& job, int tid, const XStage& st) {
+  const int NT = job.nwaves * 64, nch = qx_chunks(job);
+#pragma unroll
+  for (int r = 0; r < kXRounds; ++r) {
+    const int c = tid + NT * r;
+    if (c < nch) st128(job.x_hi + 16u * (uint32_t)c, __builtin_bit_cast(uint4, st.v[r]));
+  }
+}
 
 __device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
@@ -286,18 +317,14 @@ __device__ __forceinline__ float stage_norm(const Job& job, const ProArgs& pro, 
 __device__ __forceinline__ void quant4(const Job& job, int lane, int e, float4 w) {
   float amax = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
   amax = max8(amax);
-  const float inv = amax > 0.f ? kXMax / amax : 0.f;
   const float f[4] = {w.x, w.y, w.z, w.w};
   uint32_t H = 0, L = 0;
   int sum = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    int X = __float2int_rn(f[k] * inv);
-    X = max(-32639, min(32639, X));
-    const int hi = (X + 128) >> 8;
-    const int lo = X - (hi << 8);
-    H |= (uint32_t)(hi & 255) << (8 * k);
-    L |= (uint32_t)(lo & 255) << (8 * k);
+    const int X = fx_quant(f[k], amax);
+    H |= (uint32_t)(fx_hi(X) & 255) << (8 * k);
+    L |= (uint32_t)(fx_lo(X) & 255) << (8 * k);
     sum += X;
   }
   *reinterpret_cast<uint32_t*>(nt_smem + job.x_hi + e) = H;
@@ -308,14 +335,11 @@ __device__ __forceinline__ void quant4(const Job& job, int lane, int e, float4 w
 }
 
 
-// ss: this thread's sum of squares from stage_norm.
-// The RMSNorm factor r = 1/sqrt(mean(src^2) + eps), or 1 without norm.  It
-// runs before the wave issues any weight load: the workgroup barrier of the
-// reduction then waits for no wave that is stalled issuing its weight
-// requests behind the launch's burst (measured ~2 us per launch when it ran
-// after the prefetch).
-__device__ __forceinline__ float stage_scale(const Job& job, const ProArgs& pro, int tid, float ss) {
-  if (!pro.gain) return 1.0f;
+// ss: this thread's sum of squares from stage_norm.  The wave's part of the
+// sum of squares of the source goes to the workgroup's table for the
+// epilogue's normalization factor (norm_factor); no barrier here.
+__device__ __forceinline__ void stage_ss(const Job& job, const ProArgs& pro, int tid, float ss) {
+  if (!pro.gain) return;
   const int NT = job.nwaves * 64, lane = tid & 63;
   const int nround = (job.cols + 4 * NT - 1) / (4 * NT);
   // rounds past the registers (inputs wider than 4 * 64 * nwaves * kXRounds)
@@ -325,39 +349,55 @@ __device__ __forceinline__ float stage_scale(const Job& job, const ProArgs& pro,
   }
   ss = wave_sum(ss);
   if (lane == 0) stf(job.red + 4u * (tid >> 6), ss);
-  __syncthreads();
+}
+
+// The RMSNorm factor r = 1/sqrt(mean(src^2) + eps) of a normalizing launch
+// (1 otherwise), after the barrier that ends the stream: from the waves'
+// sums of squares (staged from fp32) or the blocks' (a quantized activation).
+// Every wave adds the same values in the same order.
+__device__ __forceinline__ float norm_factor(const Job& job, const ProArgs& pro, int lane) {
   float tot = 0.f;
-  for (int w = 0; w < job.nwaves; ++w) tot += ldf(job.red + 4u * w);
+  if (pro.qx) {
+    if (!pro.qx_norm) return 1.0f;
+    for (int b = lane; b < job.cols / 32; b += 64) tot += ldf(job.x_ss + 4u * (uint32_t)b);
+    tot = wave_sum(tot);
+  } else {
+    if (!pro.gain) return 1.0f;
+    for (int w = 0; w < job.nwaves; ++w) tot += ldf(job.red + 4u * w);
+  }
   return 1.0f / sqrtf(tot / (float)job.cols + pro.eps);
 }
 
-// r: the factor from stage_scale.  The caller ends the staging with a
-// workgroup barrier.
-__device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro, int tid, XStage& st, float r) {
+// Cos and sin of the RoPE rotation of this position for the QKV epilogue.
+__device__ __forceinline__ void rope_table(const Job& job, const ProArgs& pro, int tid, int pos) {
+  if (pro.rope_hd <= 0) return;
+  const int NT = job.nwaves * 64;
+  // pair i turns by pos * theta^(-2i/head_dim); the angle is formed in
+  // double so large positions keep fp32 accuracy
+  for (int i = tid; i < pro.rope_hd / 2; i += NT) {
+    const double freq = exp2(-(double)(2 * i) / (double)pro.rope_hd * log2((double)pro.rope_theta));
+    const double ang = (double)pos * freq;
+    stf(job.rope + 8u * i, (float)cos(ang));
+    stf(job.rope + 8u * i + 4, (float)sin(ang));
+  }
+}
+
+// Quantize the staged source (times the gains) into the LDS planes.  The
+// caller ends the staging with a workgroup barrier.
+__device__ __forceinline__ void stage_finish(const Job& job, const ProArgs& pro, int tid, XStage& st) {
   const int NT = job.nwaves * 64, lane = tid & 63;
   const int nround = (job.cols + 4 * NT - 1) / (4 * NT);
 #pragma unroll
   for (int k = 0; k < kXRounds; ++k) {
     const int e = 4 * (NT * k + tid);
-    if (e < job.cols) quant4(job, lane, e, scale4(st.v[k], r));
+    if (e < job.cols) quant4(job, lane, e, st.v[k]);
   }
   for (int k = kXRounds; k < nround; ++k) {
     const int e = 4 * (NT * k + tid);
     if (e < job.cols) {
       float4 v = ld_f4(pro.src + e);
       if (pro.gain) v = mul4(v, ld_f4(pro.gain + e));
-      quant4(job, lane, e, scale4(v, r));
-    }
-  }
-  if (pro.rope_hd > 0) {
-    // pair i turns by pos * theta^(-2i/head_dim); the angle is formed in
-    // double so large positions keep fp32 accuracy
-    for (int i = tid; i < pro.rope_hd / 2; i += NT) {
-      const int pos = st.pos;
-      const double freq = exp2(-(double)(2 * i) / (double)pro.rope_hd * log2((double)pro.rope_theta));
-      const double ang = (double)pos * freq;
-      stf(job.rope + 8u * i, (float)cos(ang));
-      stf(job.rope + 8u * i + 4, (float)sin(ang));
+      quant4(job, lane, e, v);
     }
   }
 }
@@ -384,8 +424,14 @@ __device__ __forceinline__ Share share_of(const Job& job, int b) {
   Share sh;
   const bool big = b < job.wg_rem;
   const int nu = job.wg_base + (big ? 1 : 0);
-  sh.o0 = b * job.unit;
-  sh.ostep = job.grid * job.unit;
+  if (job.qblock) {
+    // whole 32-row blocks, one contiguous range per workgroup
+    sh.o0 = (b * job.wg_base + min(b, job.wg_rem)) * job.unit;
+    sh.ostep = 1;
+  } else {
+    sh.o0 = b * job.unit;
+    sh.ostep = job.grid * job.unit;
+  }
   sh.no = nu * job.unit;
   sh.nv = job.paired ? 2 * sh.no : sh.no;
   sh.nseg = sh.nv * job.nslice;
@@ -523,23 +569,33 @@ __device__ __forceinline__ float row_total(const Job& job, int v) {
 }
 
 // Finish the workgroup's rows (after the barrier that follows the stream):
-// thread t of `nthreads` handles output rows (or row pairs) t, t + nthreads, ...
+// thread t of `nthreads` handles output rows (or row pairs) t, t + nthreads,
+// ...; r is the RMSNorm factor of the launch's input (norm_factor).
 template <int EPI>
 __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, int tid, int nthreads,
-                                               const EpiArgs& ea) {
+                                               const EpiArgs& ea, float r) {
+  const bool qout = (EPI == EPI_RESID || EPI == EPI_SWIGLU) && ea.qx_out != nullptr;  // uniform
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
     // a residual launch given the layer's status word turns the stream into
     // NaN when the layer's position was out of range
     const bool bad = EPI == EPI_RESID && ea.err && *ea.err != 0;
     for (int t = tid; t < sh.no; t += nthreads) {
-      const float s = row_total(job, t);
+      const float s = r * row_total(job, t);
       float* y = ea.y + srow(job, sh, t);
-      if constexpr (EPI == EPI_RESID) *y = bad ? __builtin_nanf("") : *y + s;
-      else *y = s;
+      if constexpr (EPI == EPI_RESID) {
+        const float v = bad ? __builtin_nanf("") : *y + s;
+        *y = v;
+        if (qout) stf(job.qo + 4u * (uint32_t)t, v);
+      } else {
+        *y = s;
+      }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    for (int t = tid; t < sh.no; t += nthreads)
-      ea.y[srow(job, sh, t)] = silu(row_total(job, t)) * row_total(job, sh.no + t);
+    for (int t = tid; t < sh.no; t += nthreads) {
+      const float v = silu(r * row_total(job, t)) * (r * row_total(job, sh.no + t));
+      ea.y[srow(job, sh, t)] = v;
+      if (qout) stf(job.qo + 4u * (uint32_t)t, v);
+    }
   } else if constexpr (EPI == EPI_QKV) {
     const int pos = *ea.pos + ea.pos_add;
     // every position of the call (*pos .. *pos + n_tok - 1) must fit the
@@ -549,7 +605,7 @@ __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, 
     if (ea.err && tid == 0) *ea.err = pos_ok ? 0 : 1;
     for (int t = tid; 2 * t < sh.no; t += nthreads) {
       const int R = srow(job, sh, 2 * t);  // even row of an adjacent pair (concatenated Q, K, V rows)
-      float a = row_total(job, 2 * t), b = row_total(job, 2 * t + 1);
+      float a = r * row_total(job, 2 * t), b = r * row_total(job, 2 * t + 1);
       const int dd = R % ea.head_dim;
       if (R < ea.q_rows + ea.kv_rows) {
         // RoPE: pair (2i, 2i+1) of a head turns by pos * theta^(-2i/head_dim)
@@ -572,6 +628,17 @@ __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, 
         *reinterpret_cast<uint32_t*>(cache + off) =
             (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
       }
+    }
+  }
+  if (qout) {
+    // the share is whole 32-row blocks (qblock): half-waves quantize one
+    // block each into the next launch's activation (times ea.qx_gain)
+    __syncthreads();
+    const int l = tid & 31;
+    for (int blk = tid >> 5; blk < (sh.no >> 5); blk += nthreads >> 5) {
+      const int t = 32 * blk + l, R = srow(job, sh, t);
+      const float y = ldf(job.qo + 4u * (uint32_t)t);
+      qx_store_block32(ea.qx_out, job.orows, R >> 5, l, ea.qx_gain ? y * ea.qx_gain[R] : y, y);
     }
   }
 }

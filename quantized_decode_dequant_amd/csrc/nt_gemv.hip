@@ -55,7 +55,9 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro_in, 
   if constexpr (kBurst) {
     pro.gain = nullptr;
     pro.rope_hd = 0;
+    pro.qx_norm = 0;
   }
+  const bool qin = pro.qx != nullptr;  // a quantized activation to copy (uniform)
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform: keep everything derived from it (segment ids
   // and addresses) in scalar registers
@@ -64,7 +66,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro_in, 
   const uint32_t slab = job.slab + (uint32_t)wave * (uint32_t)(LPL * 1024);
   if (tid == 0) sti32(job.ctl, 0);  // claim counter; the prologue's barrier publishes it
   XStage xst;
-  stage_load(job, pro, tid, xst);
+  if (qin) qstage_load(job, pro, tid, xst);
+  else stage_load(job, pro, tid, xst);
   uint4 pa[LPL], pb[LPL];
   Seg sa, sb;
   int k_cur = wave, k_nxt = wave + job.nwaves;
@@ -77,19 +80,22 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro_in, 
     sb = k_nxt < sh.nseg ? seg_at(job, sh, k_nxt) : seg_null(job);
     seg_load(sb, lane, pb);
   }
-  const float ss = stage_norm(job, pro, tid, xst);  // the activation has arrived
-  const float r = stage_scale(job, pro, tid, ss);
+  if (!qin) stage_ss(job, pro, tid, stage_norm(job, pro, tid, xst));  // the activation has arrived
   if constexpr (kBurst) {
-    stage_finish(job, pro, tid, xst, r);
+    if (qin) qstage_store(job, tid, xst);
+    else stage_finish(job, pro, tid, xst);
   } else {
-    // The first segment's loads go out before the quantization and the
-    // second's after it.  A wave cannot issue loads faster than the memory
-    // system drains them, so with both issued first the quantization waited
-    // behind the whole first burst (and the compute behind the quantization):
-    // this way it runs while the first segment is in flight.
+    // The first segment's loads go out before the quantization (or the copy
+    // of a quantized activation) and the second's after it.  A wave cannot
+    // issue loads faster than the memory system drains them, so with both
+    // issued first the quantization waited behind the whole first burst (and
+    // the compute behind the quantization): this way it runs while the first
+    // segment is in flight.
     sa = k_cur < sh.nseg ? seg_at(job, sh, k_cur) : seg_null(job);
     seg_load(sa, lane, pa);
-    stage_finish(job, pro, tid, xst, r);
+    if (qin) qstage_store(job, tid, xst);
+    else stage_finish(job, pro, tid, xst);
+    rope_table(job, pro, tid, xst.pos);
     sb = k_nxt < sh.nseg ? seg_at(job, sh, k_nxt) : seg_null(job);
     seg_load(sb, lane, pb);
   }
@@ -105,7 +111,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro_in, 
     } while (k_cur < sh.nseg);
   }
   __syncthreads();
-  share_epilogue<kBurst ? EPI_STORE : EPI>(job, sh, tid, job.nwaves * 64, ea);
+  share_epilogue<kBurst ? EPI_STORE : EPI>(job, sh, tid, job.nwaves * 64, ea, norm_factor(job, pro, lane));
 }
 
 struct DevInfo {
@@ -187,7 +193,7 @@ int launch_epi(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_
 // grid (one workgroup per CU, fewer when there is little work, more when a
 // share's partial-sum table would not fit).
 int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const int* rows, int cols, int paired,
-             int pairs) {
+             int pairs, int qblock) {
   if (nmat < 1 || nmat > kMaxMats || (paired && nmat != 2)) return NT_EINVAL;
   if (cols <= 0 || cols > kMaxCols) return NT_EUNSUPPORTED;
   job = Job{};
@@ -215,6 +221,15 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
   if (orows > INT32_MAX / 2) return NT_EUNSUPPORTED;
   job.orows = (int)orows;
   job.unit = pairs ? 2 : 1;
+  // whole 32-row blocks per workgroup, when one launch's rows make enough of
+  // them to keep nearly every CU busy (p blocks each on ceil(blocks / p)
+  // workgroups, at least 7/8 of the CUs)
+  const int cus = dev_info().cus;
+  if (qblock && !pairs && (nmat == 1 || paired) && orows % 32 == 0 && qx_ok(orows)) {
+    const int64_t nb = orows / 32, per = (nb + cus - 1) / cus, g = (nb + per - 1) / per;
+    if (8 * g >= 7 * (int64_t)cus && nb % g == 0) job.qblock = 1;
+  }
+  if (job.qblock) job.unit = 32;
   const int units = (cols + 63) / 64;
   job.nslice = (units + kSliceUnits - 1) / kSliceUnits;
   int ups = (units + job.nslice - 1) / job.nslice;
@@ -233,7 +248,6 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
   job.lpl = need <= 3 ? 3 : need;
   if (need > kSlabLoads) return NT_EUNSUPPORTED;
   job.nwaves = kMaxWaves;
-  const int cus = dev_info().cus;
   // workgroups: about one per CU, no more than one per wave's worth of
   // segments, and enough that a share's (row, slice) table fits kAccFloats
   const int vper = paired ? 2 : 1;  // segment rows per output row
@@ -241,6 +255,12 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
   const int64_t segs = orows * vper * job.nslice;
   int64_t grid = std::min<int64_t>(cus, (segs + job.nwaves - 1) / job.nwaves);
   const int64_t units_cap = kAccFloats / ((int64_t)job.nslice * job.unit * vper);
+  if (job.qblock) {
+    const int64_t per = (nu + cus - 1) / cus;
+    grid = nu / per;  // whole blocks, the same number in every share
+    if (per > units_cap) job.qblock = 0;
+  }
+  if (!job.qblock && job.unit == 32) return plan_job(job, nmat, W, fmt, rows, cols, paired, pairs, 0);
   if (units_cap < 1) return NT_EUNSUPPORTED;
   grid = std::max<int64_t>(grid, (nu + units_cap - 1) / units_cap);
   grid = std::max<int64_t>(1, std::min<int64_t>(grid, std::max<int64_t>(nu, 1)));
@@ -253,16 +273,24 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
     job.magic[i] = nv > 0 ? (uint32_t)(0xffffffffull / (uint64_t)nv) : 0u;
   }
   const int64_t nv_max = (int64_t)(job.wg_base + (job.wg_rem ? 1 : 0)) * job.unit * vper;
+  // the staged activation in the layout of a quantized activation in memory
+  // (a copy of one is a straight copy), then 256 bytes of slack for the
+  // last unit's reads past the end (a unit of a 32-weight format may hold
+  // only one block)
   uint32_t off = 0;
-  job.x_hi = off; off += cols + 64;
-  job.x_lo = off; off += cols + 64;
+  job.x_hi = off;
+  job.x_lo = off + (uint32_t)qx_lo_off(cols);
+  job.x_sc = off + (uint32_t)qx_sc_off(cols);
+  job.x_sum = off + (uint32_t)qx_sum_off(cols);
+  job.x_ss = off + (uint32_t)qx_ss_off(cols);
+  off += (uint32_t)qx_bytes(cols) + 256;
   off = (off + 15) & ~15u;
-  job.x_sc = off; off += (cols / 32 + 2) * 4;
-  job.x_sum = off; off += (cols / 16 + 4) * 4;
   job.red = off; off += 16 * 4;
   job.ctl = off; off += 16;
   job.rope = off; off += 128 * 8;  // cos/sin of up to 128 rotation pairs (head_dim <= 256)
   job.acc = off; off += (uint32_t)(nv_max * job.nslice * 4);
+  job.qo = off;
+  if (job.qblock) off += (uint32_t)(nv_max / vper * 4);  // the share's outputs, for their quantization
   off = (off + 15) & ~15u;
   job.slab = off;
   off += (uint32_t)(job.nwaves * job.lpl * 1024);
@@ -277,7 +305,7 @@ int launch_gemv(const Job& job, const ProArgs& pro, int epi, const EpiArgs& ea, 
       // every share's segments fit the two buffers of its waves: one burst
       const int vper = job.paired ? 2 : 1;
       const int64_t nseg_max = (int64_t)(job.wg_base + (job.wg_rem ? 1 : 0)) * job.unit * vper * job.nslice;
-      if (!pro.gain && pro.rope_hd == 0 && nseg_max <= 2 * job.nwaves)
+      if (!pro.gain && !pro.qx_norm && pro.rope_hd == 0 && nseg_max <= 2 * job.nwaves)
         return launch_epi<EPI_STORE_BURST>(job, pro, ea, stream);
       return launch_epi<EPI_STORE>(job, pro, ea, stream);
     }

@@ -79,10 +79,30 @@ struct Job {
   int wg_base, wg_rem;        // workgroup b owns wg_base (+1 if b < wg_rem) units of `unit` output rows
   uint32_t magic[2];          // floor((2^32-1)/nv) for the two segment-row counts nv of a workgroup
   int lpl;                    // 16-B loads per lane per segment (3, 4 or 5)
-  // dynamic LDS layout (byte offsets)
-  uint32_t x_hi, x_lo, x_sc, x_sum, red, slab, acc, ctl, rope;
+  // With qblock, workgroup b's rows are one contiguous range of whole
+  // 32-row blocks (unit == 32), so its epilogue can quantize its outputs
+  // into the activation layout the next launch copies (EpiArgs::qx_out).
+  int qblock;
+  // dynamic LDS layout (byte offsets); the staged activation is laid out as
+  // a quantized activation in memory (x_hi .. x_ss, see qx_bytes)
+  uint32_t x_hi, x_lo, x_sc, x_sum, x_ss, red, slab, acc, ctl, rope, qo;
   uint32_t lds_bytes;
 };
+
+// A quantized activation of n values (n a multiple of 32), as launches hand
+// it to each other: per 32-block a scale s = max|v| / 32639 and integers
+// X = rint(v / s), split X = 256 hi + lo into two int8 planes; v is the
+// vector times its RMSNorm gains where the consumer normalizes, and the
+// block's sum of squares of the unscaled vector is kept for the
+// normalization factor.  Bytes: hi [n], lo [n], s (f32) [n/32], sums of X
+// over 16 values (i32) [n/16], sums of squares (f32) [n/32].  Launches copy
+// it with 16-byte loads, which needs n to be a multiple of 128.
+__host__ __device__ inline size_t qx_bytes(int64_t n) { return (size_t)n * 5 / 2; }
+__host__ __device__ inline size_t qx_lo_off(int64_t n) { return (size_t)n; }
+__host__ __device__ inline size_t qx_sc_off(int64_t n) { return (size_t)n * 2; }
+__host__ __device__ inline size_t qx_sum_off(int64_t n) { return (size_t)n * 2 + (size_t)n / 8; }
+__host__ __device__ inline size_t qx_ss_off(int64_t n) { return (size_t)n * 2 + (size_t)n * 3 / 8; }
+inline bool qx_ok(int64_t n) { return n > 0 && n % 128 == 0; }
 
 // Activation source of the engine prologue.
 struct ProArgs {
@@ -96,6 +116,11 @@ struct ProArgs {
   float rope_theta;
   const int32_t* pos;
   int pos_add;
+  // A quantized activation (see qx_bytes) to copy instead of src; with
+  // qx_norm the launch applies RMSNorm through the stored sums of squares
+  // (the gains are already in it).
+  const uint8_t* qx;
+  int qx_norm;
 };
 
 enum Epi : int {
@@ -126,11 +151,17 @@ struct EpiArgs {
   int kv_rows;         // n_kv_head*head_dim
   int pos_add;         // this token sits at *pos + pos_add
   int n_tok;           // tokens of the layer call (positions *pos .. *pos + n_tok - 1)
+  // EPI_RESID / EPI_SWIGLU on a qblock launch: the outputs (times qx_gain,
+  // when given) also go out as a quantized activation of orows values
+  uint8_t* qx_out;
+  const float* qx_gain;
 };
 
 // Planner: fills job geometry for `nmat` matrices; returns NT_OK or an error.
+// With qblock, the shares are whole 32-row blocks when the rows split into
+// enough of them to keep the chip busy (job.qblock says whether they do).
 int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const int* rows, int cols, int paired,
-             int pairs);
+             int pairs, int qblock = 0);
 
 // Launch the engine (prologue: optional RMSNorm; epilogue: epi).
 int launch_gemv(const Job& job, const ProArgs& pro, int epi, const EpiArgs& ea, hipStream_t stream);
@@ -199,13 +230,17 @@ void trace_after(int kind, hipStream_t stream);
 
 // Attention and step kernels (nt_attn.hip).
 void attn_plan(int head_dim, int max_ctx, int& chunk, int& nsplit);
+// o [n_query][n_head * head_dim] fp32; with qx_o (may be null) each query's
+// output also goes out as a quantized activation of n_head * head_dim values
+// (qx_bytes apart per query).
 int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, const int32_t* pos, int n_query,
                      int n_head, int n_kv, int head_dim, int max_ctx, int chunk, int nsplit, float* part_o,
-                     float* part_ml, float* o, hipStream_t stream);
+                     float* part_ml, float* o, uint8_t* qx_o, hipStream_t stream);
 // Embedding rows of tokens[0..M) into x; also clears the status word *err
-// (may be null).
+// (may be null).  With qx (may be null) each row, times qx_gain, also goes
+// out as a quantized activation (qx_bytes(cols) apart per token).
 int launch_embed(int fmt, const void* E, const int32_t* tokens, int M, int vocab, int cols, float* x, int* err,
-                 hipStream_t stream);
+                 uint8_t* qx, const float* qx_gain, hipStream_t stream);
 int argmax_parts(int n);
 // Greedy tokens of M logit rows; -1 for every row when *err (may be null) is set.
 int launch_argmax(const float* logits, int M, int n, float* pv, int* pi, const int* err, int32_t* out,

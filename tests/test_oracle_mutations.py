@@ -76,7 +76,8 @@ def _run(name, reps, tmp):
         if os.path.exists(p):
             shutil.copy(p, os.path.join(d, "tests", f))
     for f in os.listdir(os.path.join(ROOT, "tests", "golden")):
-        if f.endswith(".json") and os.path.getsize(os.path.join(ROOT, "tests", "golden", f)) < 1 << 20:
+        small = os.path.getsize(os.path.join(ROOT, "tests", "golden", f)) < 1 << 20
+        if (f.endswith(".json") and small) or f.endswith(".py"):
             shutil.copy(os.path.join(ROOT, "tests", "golden", f), os.path.join(d, "tests", "golden", f))
     shutil.copy(os.path.join(ROOT, "pytest.ini"), d)
     open(os.path.join(d, "oracle", "oracle.c"), "w").write(src)
