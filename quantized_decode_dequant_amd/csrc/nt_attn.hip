@@ -337,12 +337,59 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 }
 
 // ------------------------------------------------------------ embedding row
-// x[m][:] = decoded row tokens[m] of an embedding matrix (fp32).  One thread
-// per 32-weight group; the formulas are the block definitions of nt.h.
-// It also clears the step's status word (err), which the layers set when a
-// position is out of range.
+// Element e of an embedding row: the block definitions of nt.h.
+__device__ __forceinline__ float embed_elem(int fmt, const uint8_t* __restrict__ row, int e) {
+  auto h2f = [](const uint8_t* p) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(p[0] | (p[1] << 8))); };
+  const int j = e & 31;
+  if (fmt == NT_Q8_0) {
+    const uint8_t* b = row + (int64_t)(e >> 5) * 34;
+    return h2f(b) * (float)(int8_t)b[2 + j];
+  }
+  if (fmt == NT_Q4_0) {
+    const uint8_t* b = row + (int64_t)(e >> 5) * 18;
+    const int q = j < 16 ? (b[2 + j] & 15) : (b[2 + j - 16] >> 4);
+    return h2f(b) * (float)(q - 8);
+  }
+  if (fmt == NT_F16) return h2f(row + 2 * (int64_t)e);
+  if (fmt == NT_F32) return reinterpret_cast<const float*>(row)[e];
+  if (fmt == NT_Q6_K) {
+    const uint8_t* b = row + (int64_t)(e >> 8) * 210;
+    const int i = e & 255, n = i >> 7, k = (i & 127) >> 5;
+    const uint8_t lo = b[64 * n + 32 * (k & 1) + j];
+    const int nib = (k >> 1) ? (lo >> 4) : (lo & 15);
+    const int hi = (b[128 + 32 * n + j] >> (2 * k)) & 3;
+    return h2f(b + 208) * (float)(int8_t)b[192 + i / 16] * (float)((nib | (hi << 4)) - 32);
+  }
+  // Q4_K and Q5_K: sub-block s of a 256-element superblock with 6-bit scale and min
+  const int bb = fmt == NT_Q4_K ? 144 : 176;
+  const uint8_t* b = row + (int64_t)(e >> 8) * bb;
+  const int s = (e & 255) >> 5;
+  const uint8_t* sc = b + 4;
+  int scale, mn;
+  if (s < 4) {
+    scale = sc[s] & 63;
+    mn = sc[s + 4] & 63;
+  } else {
+    scale = (sc[s + 4] & 15) | ((sc[s - 4] >> 6) << 4);
+    mn = (sc[s + 4] >> 4) | ((sc[s] >> 6) << 4);
+  }
+  int q;
+  if (fmt == NT_Q4_K) {
+    const uint8_t v = b[16 + 32 * (s / 2) + j];
+    q = (s & 1) ? (v >> 4) : (v & 15);
+  } else {
+    const uint8_t v = b[48 + 32 * (s / 2) + j];
+    q = ((s & 1) ? (v >> 4) : (v & 15)) | (((b[16 + j] >> s) & 1) << 4);
+  }
+  return h2f(b) * (float)scale * (float)q - h2f(b + 2) * (float)mn;
+}
+
+// x[m][:] = decoded row tokens[m] of an embedding matrix (fp32), one thread
+// per element.  It also clears the step's status word (err), which the layers
+// set when a position is out of range.
 // With qx the row times qx_gain also goes out as a quantized activation
-// (qx_bytes(cols) per token); each thread holds one 32-block.
+// (qx_bytes(cols) per token; cols is then a multiple of 128, so the 32 lanes
+// of a block are all active).
 __global__ __launch_bounds__(256) void k_embed(int fmt, const uint8_t* __restrict__ E, const int32_t* tokens, int vocab,
                                                int cols, float* __restrict__ x, int* __restrict__ err,
                                                uint8_t* __restrict__ qx, const float* __restrict__ qx_gain) {
@@ -350,100 +397,12 @@ __global__ __launch_bounds__(256) void k_embed(int fmt, const uint8_t* __restric
   if (err && m == 0 && blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
   int tok = tokens[m];
   tok = min(max(tok, 0), vocab - 1);
-  const int grp = blockIdx.x * blockDim.x + threadIdx.x;  // 32-weight group
-  if (grp >= cols / 32) return;
-  const int qk = block_elems(fmt), bb = block_bytes(fmt);
-  const uint8_t* row = E + (int64_t)tok * (cols / qk) * bb;
-  float* out = x + (int64_t)m * cols + 32 * grp;
-  auto h2f = [](const uint8_t* p) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(p[0] | (p[1] << 8))); };
-  if (fmt == NT_Q8_0) {
-    const uint8_t* b = row + (int64_t)grp * 34;
-    const float d = h2f(b);
-    for (int j = 0; j < 32; ++j) out[j] = d * (float)(int8_t)b[2 + j];
-  } else if (fmt == NT_Q4_0) {
-    const uint8_t* b = row + (int64_t)grp * 18;
-    const float d = h2f(b);
-    for (int j = 0; j < 16; ++j) {
-      out[j] = d * (float)((b[2 + j] & 15) - 8);
-      out[j + 16] = d * (float)((b[2 + j] >> 4) - 8);
-    }
-  } else if (fmt == NT_Q4_K) {
-    const uint8_t* b = row + (int64_t)(grp / 8) * 144;
-    const int s = grp % 8;  // sub-block
-    const float d = h2f(b), dmin = h2f(b + 2);
-    const uint8_t* sc = b + 4;
-    int scale, mn;
-    if (s < 4) {
-      scale = sc[s] & 63;
-      mn = sc[s + 4] & 63;
-    } else {
-      scale = (sc[s + 4] & 15) | ((sc[s - 4] >> 6) << 4);
-      mn = (sc[s + 4] >> 4) | ((sc[s] >> 6) << 4);
-    }
-    const uint8_t* qs = b + 16 + 32 * (s / 2);
-    for (int l = 0; l < 32; ++l) {
-      const int q = (s & 1) ? (qs[l] >> 4) : (qs[l] & 15);
-      out[l] = d * (float)scale * (float)q - dmin * (float)mn;
-    }
-  } else if (fmt == NT_Q5_K) {
-    const uint8_t* b = row + (int64_t)(grp / 8) * 176;
-    const int s = grp % 8;  // sub-block
-    const float d = h2f(b), dmin = h2f(b + 2);
-    const uint8_t* sc = b + 4;
-    int scale, mn;
-    if (s < 4) {
-      scale = sc[s] & 63;
-      mn = sc[s + 4] & 63;
-    } else {
-      scale = (sc[s + 4] & 15) | ((sc[s - 4] >> 6) << 4);
-      mn = (sc[s + 4] >> 4) | ((sc[s] >> 6) << 4);
-    }
-    const uint8_t* qh = b + 16;
-    const uint8_t* qs = b + 48 + 32 * (s / 2);
-    for (int l = 0; l < 32; ++l) {
-      const int q = ((s & 1) ? (qs[l] >> 4) : (qs[l] & 15)) | (((qh[l] >> s) & 1) << 4);
-      out[l] = d * (float)scale * (float)q - dmin * (float)mn;
-    }
-  } else if (fmt == NT_F16) {
-    const uint8_t* b = row + (int64_t)grp * 64;
-    for (int l = 0; l < 32; ++l) out[l] = h2f(b + 2 * l);
-  } else if (fmt == NT_F32) {
-    const float* b = reinterpret_cast<const float*>(row) + (int64_t)grp * 32;
-    for (int l = 0; l < 32; ++l) out[l] = b[l];
-  } else {  // Q6_K
-    const uint8_t* b = row + (int64_t)(grp / 8) * 210;
-    const int e0 = 32 * (grp % 8);
-    const float d = h2f(b + 208);
-    for (int l = 0; l < 32; ++l) {
-      const int e = e0 + l;
-      const int n = e / 128, k = (e % 128) / 32, ll = e % 32;
-      const uint8_t lo = b[64 * n + 32 * (k % 2) + ll];
-      const int nib = (k / 2) ? (lo >> 4) : (lo & 15);
-      const int hi = (b[128 + 32 * n + ll] >> (2 * k)) & 3;
-      out[l] = d * (float)(int8_t)b[192 + e / 16] * (float)((nib | (hi << 4)) - 32);
-    }
-  }
-  if (qx) {
-    uint8_t* q = qx + (int64_t)m * qx_bytes(cols);
-    float v[32], amax = 0.f, ss = 0.f;
-    for (int l = 0; l < 32; ++l) {
-      const float y = out[l];
-      v[l] = qx_gain ? y * qx_gain[32 * grp + l] : y;
-      amax = fmaxf(amax, fabsf(v[l]));
-      ss += y * y;
-    }
-    int s16[2] = {0, 0};
-    for (int l = 0; l < 32; ++l) {
-      const int X = fx_quant(v[l], amax);
-      q[32 * grp + l] = (uint8_t)(fx_hi(X) & 255);
-      q[qx_lo_off(cols) + 32 * grp + l] = (uint8_t)(fx_lo(X) & 255);
-      s16[l >> 4] += X;
-    }
-    reinterpret_cast<int*>(q + qx_sum_off(cols))[2 * grp] = s16[0];
-    reinterpret_cast<int*>(q + qx_sum_off(cols))[2 * grp + 1] = s16[1];
-    reinterpret_cast<float*>(q + qx_sc_off(cols))[grp] = amax / kXMax;
-    reinterpret_cast<float*>(q + qx_ss_off(cols))[grp] = ss;
-  }
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= cols) return;
+  const uint8_t* row = E + (int64_t)tok * (cols / block_elems(fmt)) * block_bytes(fmt);
+  const float y = embed_elem(fmt, row, e);
+  x[(int64_t)m * cols + e] = y;
+  if (qx) qx_store_block32(qx + (int64_t)m * qx_bytes(cols), cols, e >> 5, e & 31, qx_gain ? y * qx_gain[e] : y, y);
 }
 
 // ------------------------------------------------------------------ argmax
@@ -533,8 +492,7 @@ int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, con
 
 int launch_embed(int fmt, const void* E, const int32_t* tokens, int M, int vocab, int cols, float* x, int* err,
                  uint8_t* qx, const float* qx_gain, hipStream_t stream) {
-  const int groups = cols / 32;
-  hipLaunchKernelGGL(k_embed, dim3((groups + 255) / 256, M), dim3(256), 0, stream, fmt,
+  hipLaunchKernelGGL(k_embed, dim3((cols + 255) / 256, M), dim3(256), 0, stream, fmt,
                      static_cast<const uint8_t*>(E), tokens, vocab, cols, x, err, qx, qx_gain);
   return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
 }
