@@ -126,6 +126,19 @@ __device__ __forceinline__ uint4 load_chunk(const uint8_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// A segment of weights as a raw buffer: 16-byte loads at byte offsets
+// below `bytes` read memory, loads at or past it return zeros without a
+// memory access (the buffer instructions' range check), non-temporal like
+// load_chunk.  The resource's last word is the gfx9 raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seg_rsrc(const uint8_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kAuxNt = 2;  // cache-policy bits of a non-temporal load
+__device__ __forceinline__ uint4 load_seg_chunk(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kAuxNt);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // The 16-bit fixed point of the activations: a 32-block with largest

@@ -495,14 +495,15 @@ __device__ __forceinline__ Seg seg_at(const Job& job, const Share& sh, int k) {
   return sg;
 }
 
-// Stand-in when a wave has no segment to load: one chunk at the start of the
-// first matrix.  Loads are still issued for it, so every path through the
-// stream issues the same number of loads and the waits before a slab store
-// count exactly the older segment (waits merge across paths pessimistically).
+// Stand-in when a wave has no segment to load: an empty range at the start
+// of the first matrix.  Loads are still issued for it (they return zeros
+// without a memory access), so every path through the stream issues the
+// same number of loads and the waits before a slab store count exactly the
+// older segment (waits merge across paths pessimistically).
 __device__ __forceinline__ Seg seg_null(const Job& job) {
   Seg sg;
   sg.a = job.W[0];
-  sg.nchunks = 1;
+  sg.nchunks = 0;
   sg.d = 0;
   sg.fmt = job.fmt[0];
   sg.nunits = 0;
@@ -512,19 +513,20 @@ __device__ __forceinline__ Seg seg_null(const Job& job) {
   return sg;
 }
 
-// Every lane issues exactly LPL loads (lanes past the segment's end re-read
-// its last chunk), so the number of loads in flight is the same on every
-// path and the waits before the slab store count exactly the older segment.
+// Every lane issues exactly LPL loads (those past the segment's end return
+// zeros without a memory access), so the number of loads in flight is the
+// same on every path and the waits before the slab store count exactly the
+// older segment.  A stand-in's loads complete at once: the epilogue, whose
+// registers overlap the buffers, does not wait for memory behind them.
 template <int LPL>
 __device__ __forceinline__ void seg_load(const Seg& sg, int lane, uint4 (&pre)[LPL]) {
-  const uint32_t last = 16u * (uint32_t)(sg.nchunks - 1);
+  const __amdgpu_buffer_rsrc_t r = seg_rsrc(sg.a, 16u * (uint32_t)sg.nchunks);
 #pragma unroll
-  for (int i = 0; i < LPL; ++i) pre[i] = load_chunk(sg.a + min(16u * (uint32_t)(lane + 64 * i), last));
+  for (int i = 0; i < LPL; ++i) pre[i] = load_seg_chunk(r, 16u * (uint32_t)(lane + 64 * i));
 }
 
 // The slab holds LPL KB, so every chunk slot is written (slots past the
-// segment's end get the re-read last chunk, which nothing reads): no
-// divergent branch.
+// segment's end get zeros, which nothing reads): no divergent branch.
 template <int LPL>
 __device__ __forceinline__ void seg_store(uint32_t slab, int lane, const uint4 (&pre)[LPL]) {
 #pragma unroll
@@ -568,22 +570,68 @@ __device__ __forceinline__ float row_total(const Job& job, int v) {
   return t;
 }
 
+// A struct in the engine's LDS (the argument copies).
+template <class T>
+__device__ __forceinline__ const T& lds_ref(uint32_t off) {
+  return *reinterpret_cast<const T*>(nt_smem + off);
+}
+
+// Copy the launch's argument structs into LDS (threads 0 .. ~110, one word
+// each); the prologue's barrier publishes them.
+template <class T>
+__device__ __forceinline__ void copy_words(const T& v, uint32_t off, int i) {
+  constexpr int n = (int)(sizeof(T) / 4);
+  if (i >= 0 && i < n) sti32(off + 4u * (uint32_t)i, reinterpret_cast<const int*>(&v)[i]);
+}
+__device__ __forceinline__ void args_to_lds(const Job& job, const ProArgs& pro, const EpiArgs& ea, int tid) {
+  constexpr int nj = (int)(sizeof(Job) / 4), np = (int)(sizeof(ProArgs) / 4);
+  copy_words(job, kLdsJob, tid);
+  copy_words(pro, kLdsPro, tid - nj);
+  copy_words(ea, kLdsEpi, tid - nj - np);
+}
+
+// The epilogue's values from memory, loaded at the start so they have
+// arrived when the stream ends: the residual and the gain of this thread's
+// first output row, the layer's status word, the position.
+struct EpiPre {
+  float y = 0.f, g = 1.f;
+  int err = 0, pos = 0;
+};
+template <int EPI>
+__device__ __forceinline__ EpiPre epi_prefetch(const Job& job, const Share& sh, int tid, const EpiArgs& ea) {
+  EpiPre p;
+  if constexpr (EPI == EPI_RESID || EPI == EPI_SWIGLU) {
+    if (tid < sh.no) {
+      const int R = srow(job, sh, tid);
+      if constexpr (EPI == EPI_RESID) p.y = ea.y[R];
+      if (ea.qx_out && ea.qx_gain) p.g = ea.qx_gain[R];
+    }
+    if constexpr (EPI == EPI_RESID) {
+      if (ea.err) p.err = *ea.err;
+    }
+  } else if constexpr (EPI == EPI_QKV) {
+    p.pos = *ea.pos;
+  }
+  return p;
+}
+
 // Finish the workgroup's rows (after the barrier that follows the stream):
 // thread t of `nthreads` handles output rows (or row pairs) t, t + nthreads,
-// ...; r is the RMSNorm factor of the launch's input (norm_factor).
+// ...; r is the RMSNorm factor of the launch's input (norm_factor); pre
+// holds what epi_prefetch loaded for the first of them.
 template <int EPI>
 __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, int tid, int nthreads,
-                                               const EpiArgs& ea, float r) {
+                                               const EpiArgs& ea, float r, const EpiPre& pre) {
   const bool qout = (EPI == EPI_RESID || EPI == EPI_SWIGLU) && ea.qx_out != nullptr;  // uniform
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
     // a residual launch given the layer's status word turns the stream into
     // NaN when the layer's position was out of range
-    const bool bad = EPI == EPI_RESID && ea.err && *ea.err != 0;
+    const bool bad = EPI == EPI_RESID && pre.err != 0;
     for (int t = tid; t < sh.no; t += nthreads) {
       const float s = r * row_total(job, t);
       float* y = ea.y + srow(job, sh, t);
       if constexpr (EPI == EPI_RESID) {
-        const float v = bad ? __builtin_nanf("") : *y + s;
+        const float v = bad ? __builtin_nanf("") : (t == tid ? pre.y : *y) + s;
         *y = v;
         if (qout) stf(job.qo + 4u * (uint32_t)t, v);
       } else {
@@ -597,10 +645,10 @@ __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, 
       if (qout) stf(job.qo + 4u * (uint32_t)t, v);
     }
   } else if constexpr (EPI == EPI_QKV) {
-    const int pos = *ea.pos + ea.pos_add;
+    const int pos = pre.pos + ea.pos_add;
     // every position of the call (*pos .. *pos + n_tok - 1) must fit the
     // cache, or no token of the call writes its entries
-    const bool pos_ok = *ea.pos >= 0 && *ea.pos + max(ea.n_tok, 1) - 1 < ea.max_ctx;
+    const bool pos_ok = pre.pos >= 0 && pre.pos + max(ea.n_tok, 1) - 1 < ea.max_ctx;
     // the layer's status word: every workgroup writes the same value
     if (ea.err && tid == 0) *ea.err = pos_ok ? 0 : 1;
     for (int t = tid; 2 * t < sh.no; t += nthreads) {
@@ -638,7 +686,8 @@ __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, 
     for (int blk = tid >> 5; blk < (sh.no >> 5); blk += nthreads >> 5) {
       const int t = 32 * blk + l, R = srow(job, sh, t);
       const float y = ldf(job.qo + 4u * (uint32_t)t);
-      qx_store_block32(ea.qx_out, job.orows, R >> 5, l, ea.qx_gain ? y * ea.qx_gain[R] : y, y);
+      const float g = ea.qx_gain ? (t == tid ? pre.g : ea.qx_gain[R]) : 1.0f;
+      qx_store_block32(ea.qx_out, job.orows, R >> 5, l, y * g, y);
     }
   }
 }

@@ -65,9 +65,12 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro_in, 
   const Share sh = share_of(job, blockIdx.x);
   const uint32_t slab = job.slab + (uint32_t)wave * (uint32_t)(LPL * 1024);
   if (tid == 0) sti32(job.ctl, 0);  // claim counter; the prologue's barrier publishes it
+  args_to_lds(job, pro_in, ea, tid);   // for the epilogue; the prologue's barrier publishes them
   XStage xst;
   if (qin) qstage_load(job, pro, tid, xst);
   else stage_load(job, pro, tid, xst);
+  // the epilogue's loads from memory (residual, gains, position), issued now
+  const EpiPre pre = epi_prefetch<kBurst ? EPI_STORE : EPI>(job, sh, tid, ea);
   uint4 pa[LPL], pb[LPL];
   Seg sa, sb;
   int k_cur = wave, k_nxt = wave + job.nwaves;
@@ -111,7 +114,10 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro_in, 
     } while (k_cur < sh.nseg);
   }
   __syncthreads();
-  share_epilogue<kBurst ? EPI_STORE : EPI>(job, sh, tid, job.nwaves * 64, ea, norm_factor(job, pro, lane));
+  const Job& J = lds_ref<Job>(kLdsJob);
+  const float r = kBurst ? 1.0f : norm_factor(J, lds_ref<ProArgs>(kLdsPro), lane);
+  share_epilogue<kBurst ? EPI_STORE : EPI>(J, share_of(J, blockIdx.x), tid, J.nwaves * 64, lds_ref<EpiArgs>(kLdsEpi),
+                                          r, pre);
 }
 
 struct DevInfo {
@@ -277,7 +283,7 @@ int plan_job(Job& job, int nmat, const uint8_t* const* W, const int* fmt, const 
   // (a copy of one is a straight copy), then 256 bytes of slack for the
   // last unit's reads past the end (a unit of a 32-weight format may hold
   // only one block)
-  uint32_t off = 0;
+  uint32_t off = kArgsLds;
   job.x_hi = off;
   job.x_lo = off + (uint32_t)qx_lo_off(cols);
   job.x_sc = off + (uint32_t)qx_sc_off(cols);

@@ -157,6 +157,18 @@ struct EpiArgs {
   const float* qx_gain;
 };
 
+// The engine's LDS starts with copies of its three argument structs, made
+// by the first threads at the start: the epilogue reads its arguments from
+// there (argument loads issued after the stream miss the scalar cache and
+// each costs a memory round trip).
+constexpr uint32_t lds_align16(size_t n) { return (uint32_t)((n + 15) & ~size_t(15)); }
+constexpr uint32_t kLdsJob = 0;
+constexpr uint32_t kLdsPro = kLdsJob + lds_align16(sizeof(Job));
+constexpr uint32_t kLdsEpi = kLdsPro + lds_align16(sizeof(ProArgs));
+constexpr uint32_t kArgsLds = kLdsEpi + lds_align16(sizeof(EpiArgs));
+static_assert(kArgsLds <= 1024, "engine argument copies");
+static_assert(sizeof(Job) % 4 == 0 && sizeof(ProArgs) % 4 == 0 && sizeof(EpiArgs) % 4 == 0, "copied as words");
+
 // Planner: fills job geometry for `nmat` matrices; returns NT_OK or an error.
 // With qblock, the shares are whole 32-row blocks when the rows split into
 // enough of them to keep the chip busy (job.qblock says whether they do).
