@@ -352,8 +352,8 @@ __device__ __forceinline__ void stage_ss(const Job& job, const ProArgs& pro, int
 }
 
 // The RMSNorm factor r = 1/sqrt(mean(src^2) + eps) of a normalizing launch
-// (1 otherwise), after the barrier that ends the stream: from the waves'
-// sums of squares (staged from fp32) or the blocks' (a quantized activation).
+// (1 otherwise), after the prologue's barrier: from the waves' sums of
+// squares (staged from fp32) or the blocks' (a quantized activation).
 // Every wave adds the same values in the same order.
 __device__ __forceinline__ float norm_factor(const Job& job, const ProArgs& pro, int lane) {
   float tot = 0.f;

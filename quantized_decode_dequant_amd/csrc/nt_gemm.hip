@@ -300,9 +300,10 @@ __device__ __forceinline__ void scale_table(const TSeg& sg, uint32_t po, uint32_
 
 // A operand: 8 quants (one byte each) of row lane%16, weights 8*(lane/16)..+7
 // of block kb of the tile-slice.
+template <int F>
 __device__ __forceinline__ long a_operand(const TSeg& sg, uint32_t po, int kb, int kq) {
   uint32_t v[2];
-  switch (sg.fmt) {
+  switch (F >= 0 ? F : sg.fmt) {
     case NT_Q8_0:
       ld_unaligned<2>(po + 34u * kb + 2 + 8 * kq, v);
       return pack2(v[0], v[1]);
@@ -354,7 +355,8 @@ __device__ __forceinline__ void alphas(uint32_t scl, int e, int kq, float (&al)[
   al[0] = a.x; al[1] = a.y; al[2] = a.z; al[3] = a.w;
 }
 
-__device__ __forceinline__ void tseg_compute(const JobM& job, const TSeg& sg, uint32_t slab, uint32_t scl, int lane,
+template <int F>
+__device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, uint32_t slab, uint32_t scl, int lane,
                                              float (&acc)[4]) {
   const int kq = lane >> 4, t = (lane & 15) >> 1;
   const uint32_t po = piece_off(sg, slab, lane & 15);
@@ -364,13 +366,13 @@ __device__ __forceinline__ void tseg_compute(const JobM& job, const TSeg& sg, ui
     for (int j = 0; j < 4; ++j) acc[j] = 0.f;
   }
   const v4i zero = {0, 0, 0, 0};
-  for (int kb = 0; kb < sg.nblk; ++kb) {
+  auto block = [&](int kb) {
     const int lb = sg.lb0 + kb;
-    const long a = a_operand(sg, po, kb, kq);
+    const long a = a_operand<F>(sg, po, kb, kq);
     const long bo = *reinterpret_cast<const long*>(nt_smem + job.xbl + 512u * (uint32_t)lb + 8u * lane);
     const uint32_t rec = job.xsl + 16u * (uint32_t)(lb * kMaxTokens + t);
     float al[4], be[4];
-    if (sg.fmt == NT_Q6_K) {
+    if (F == NT_Q6_K) {
       const float4 r = *reinterpret_cast<const float4*>(nt_smem + rec);
       const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? a : 0l, bo, zero, 0, 0, 0);
       const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? 0l : a, bo, zero, 0, 0, 0);
@@ -385,7 +387,7 @@ __device__ __forceinline__ void tseg_compute(const JobM& job, const TSeg& sg, ui
     } else {
       const float2 r = *reinterpret_cast<const float2*>(nt_smem + rec);
       const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bo, zero, 0, 0, 0);
-      if (sg.fmt == NT_Q4_K || sg.fmt == NT_Q5_K) {
+      if (F == NT_Q4_K || F == NT_Q5_K) {
         const uint32_t e = scl + 8u * (uint32_t)(16 * kb + 4 * kq);
         const float4 p0 = *reinterpret_cast<const float4*>(nt_smem + e);
         const float4 p1 = *reinterpret_cast<const float4*>(nt_smem + e + 16);
@@ -393,12 +395,18 @@ __device__ __forceinline__ void tseg_compute(const JobM& job, const TSeg& sg, ui
         al[2] = p1.x; be[2] = p1.y; al[3] = p1.z; be[3] = p1.w;
       } else {
         alphas(scl, kb, kq, al);
-        const float f = sg.fmt == NT_Q4_0 ? 8.f : 0.f;
+        const float f = F == NT_Q4_0 ? 8.f : 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) be[j] = f * al[j];
       }
       accumulate(c, al, be, r.x, r.y, acc);
     }
+  };
+  if (sg.nblk == kTS / 32) {
+#pragma unroll
+    for (int kb = 0; kb < kTS / 32; ++kb) block(kb);
+  } else {
+    for (int kb = 0; kb < sg.nblk; ++kb) block(kb);
   }
   if (sg.last && (lane & 1) == 0 && t < job.M) {
 #pragma unroll
@@ -406,6 +414,17 @@ __device__ __forceinline__ void tseg_compute(const JobM& job, const TSeg& sg, ui
       const int v = kTileRows * sg.vt + 4 * kq + j;
       stf(job.acc + 4u * (uint32_t)((v * job.nsub + sg.sub) * job.M + t), acc[j]);
     }
+  }
+}
+
+__device__ __forceinline__ void tseg_compute(const JobM& job, const TSeg& sg, uint32_t slab, uint32_t scl, int lane,
+                                             float (&acc)[4]) {
+  switch (sg.fmt) {
+    case NT_Q4_K: tseg_compute_f<NT_Q4_K>(job, sg, slab, scl, lane, acc); break;
+    case NT_Q6_K: tseg_compute_f<NT_Q6_K>(job, sg, slab, scl, lane, acc); break;
+    case NT_Q8_0: tseg_compute_f<NT_Q8_0>(job, sg, slab, scl, lane, acc); break;
+    case NT_Q4_0: tseg_compute_f<NT_Q4_0>(job, sg, slab, scl, lane, acc); break;
+    default: tseg_compute_f<NT_Q5_K>(job, sg, slab, scl, lane, acc); break;
   }
 }
 

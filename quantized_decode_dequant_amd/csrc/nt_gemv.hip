@@ -103,6 +103,9 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro_in, 
     seg_load(sb, lane, pb);
   }
   __syncthreads();  // the staged activation is complete
+  // the RMSNorm factor, from sums of squares the barrier published; formed
+  // here so the epilogue does not wait for its LDS round trips
+  const float r = kBurst ? 1.0f : norm_factor(job, pro, lane);
   if (k_cur < sh.nseg) {
     XR xr;
     int xslice = -1;
@@ -115,7 +118,6 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemv(Job job, ProArgs pro_in, 
   }
   __syncthreads();
   const Job& J = lds_ref<Job>(kLdsJob);
-  const float r = kBurst ? 1.0f : norm_factor(J, lds_ref<ProArgs>(kLdsPro), lane);
   share_epilogue<kBurst ? EPI_STORE : EPI>(J, share_of(J, blockIdx.x), tid, J.nwaves * 64, lds_ref<EpiArgs>(kLdsEpi),
                                           r, pre);
 }
