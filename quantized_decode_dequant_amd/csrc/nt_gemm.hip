@@ -44,10 +44,12 @@ constexpr int kStageThreads = 1024;
 
 // ------------------------------------------------------------------ staging
 // Token t = blockIdx.x.  Thread groups of 8 lanes hold one 32-block (4
-// elements each, coalesced as in the GEMV prologue).
+// elements each, coalesced as in the GEMV prologue); a wave holds one
+// 256-block, which shares one fixed-point scale (every lane takes part in
+// the wave's maximum: lanes past the end hold zeros).
 __global__ __launch_bounds__(kStageThreads) void k_stage_m(const float* __restrict__ src, int64_t stride,
                                                            const float* __restrict__ gain, float eps, int cols,
-                                                           uint8_t* __restrict__ xb, float4* __restrict__ xs) {
+                                                           uint8_t* __restrict__ xb, int4* __restrict__ xs) {
   __shared__ float red[kStageThreads / 64];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const float* x = src + (int64_t)t * stride;
@@ -65,15 +67,16 @@ __global__ __launch_bounds__(kStageThreads) void k_stage_m(const float* __restri
     for (int w = 0; w < kStageThreads / 64; ++w) tot += red[w];
     r = 1.0f / sqrtf(tot / (float)cols + eps);
   }
-  for (int e = 4 * tid; e < cols; e += 4 * kStageThreads) {
-    float4 v = *reinterpret_cast<const float4*>(x + e);
-    if (gain) {
+  for (int base = 0; base < cols; base += 4 * kStageThreads) {
+    const int e = base + 4 * tid;
+    const bool ok = e < cols;
+    float4 v = ok ? *reinterpret_cast<const float4*>(x + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (gain && ok) {
       const float4 g = *reinterpret_cast<const float4*>(gain + e);
       v = make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w);
     }
     v = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
-    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    amax = max8(amax);
+    const float amax = wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     const float inv = amax > 0.f ? kXMax / amax : 0.f;
     const float f[4] = {v.x, v.y, v.z, v.w};
     uint32_t H = 0, L = 0;
@@ -91,14 +94,13 @@ __global__ __launch_bounds__(kStageThreads) void k_stage_m(const float* __restri
     // elements k = 4g..4g+3 of block b (g = lane's place in its group):
     // B-layout lane n + 16*(k/8), byte k%8, for n = 2t (hi) and 2t + 1 (lo)
     const int b = e >> 5, g = (e >> 2) & 7;
-    uint8_t* blk = xb + 512 * (int64_t)b + 128 * (g >> 1) + 4 * (g & 1);
-    *reinterpret_cast<uint32_t*>(blk + 8 * (2 * t)) = H;
-    *reinterpret_cast<uint32_t*>(blk + 8 * (2 * t + 1)) = L;
-    const int s16 = sum4(sum);                            // lanes g<4: first half, g>=4: second half
-    const int other = dpp_i<0x141>(s16);                  // row_half_mirror: the other half's sum
-    if (g == 0) {
-      const float s = amax / kXMax;
-      xs[(int64_t)b * kMaxTokens + t] = make_float4(s, s * (float)(s16 + other), s * (float)s16, s * (float)other);
+    const int s16 = sum4(sum);            // lanes g<4: first half, g>=4: second half
+    const int other = dpp_i<0x141>(s16);  // row_half_mirror: the other half's sum
+    if (ok) {
+      uint8_t* blk = xb + 512 * (int64_t)b + 128 * (g >> 1) + 4 * (g & 1);
+      *reinterpret_cast<uint32_t*>(blk + 8 * (2 * t)) = H;
+      *reinterpret_cast<uint32_t*>(blk + 8 * (2 * t + 1)) = L;
+      if (g == 0) xs[(int64_t)b * kMaxTokens + t] = make_int4(s16, other, __float_as_int(amax / kXMax), 0);
     }
   }
 }
@@ -252,11 +254,12 @@ __device__ __forceinline__ uint32_t piece_off(const TSeg& sg, uint32_t slab, int
 
 __device__ __forceinline__ long pack2(uint32_t lo, uint32_t hi) { return (long)(((uint64_t)hi << 32) | lo); }
 
-// Scale table of the tile-slice, per (entry, row): entry = 32-block (Q6_K:
-// 16-weight group).  A block's contribution is alpha (s S) - beta (s sum X)
-// with beta = 0 (Q8_0), 8 alpha (Q4_0), 32 alpha (Q6_K); Q4_K and Q5_K keep
-// (alpha, beta) pairs.  Layout: scl + 4 * (16 entry + row), pairs 8 * (...).
-__device__ __forceinline__ void scale_table(const TSeg& sg, uint32_t po, uint32_t scl, int lane) {
+// Scale table of the tile-slice, per (entry, row), from the lanes that read
+// row lane % 16: Q8_0 / Q4_0 the block's d (float, scl + 4 (16 block + row));
+// Q4_K / Q5_K the sub-block's six-bit scale and min (int2, scl + 8 (16 j +
+// row)); Q6_K the 16-weight group's signed scale (int, scl + 4 (16 g +
+// row)).  Returns the row's superblock d (and dmin), K-quants only.
+__device__ __forceinline__ float2 scale_table(const TSeg& sg, uint32_t po, uint32_t scl, int lane) {
   const int row = lane & 15, kq = lane >> 4;
   switch (sg.fmt) {
     case NT_Q8_0:
@@ -268,32 +271,28 @@ __device__ __forceinline__ void scale_table(const TSeg& sg, uint32_t po, uint32_
         const float a = e < sg.nblk ? h2f(ld16(po + bb * e)) : 0.f;
         stf(scl + 4u * (uint32_t)(16 * e + row), a);
       }
-      break;
+      return make_float2(0.f, 0.f);
     }
     case NT_Q4_K:
     case NT_Q5_K: {  // same superblock header
       uint32_t h[3];
       ld_unaligned<3>(po + 4, h);
-      const float d = h2f(ld16(po)), dmin = h2f(ld16(po + 2));
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int e = kq + 4 * q;
         int sc, m;
         q4k_scale_min(h[0], h[1], h[2], e, sc, m);
-        *reinterpret_cast<float2*>(nt_smem + scl + 8u * (uint32_t)(16 * e + row)) =
-            make_float2(d * (float)sc, dmin * (float)m);
+        *reinterpret_cast<int2*>(nt_smem + scl + 8u * (uint32_t)(16 * e + row)) = make_int2(sc, m);
       }
-      break;
+      return make_float2(h2f(ld16(po)), h2f(ld16(po + 2)));
     }
     default: {  // Q6_K: 16 scales of 16 weights
-      const float d = h2f(ld16(po + 208));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int e = kq + 4 * q;
-        const int sc = (int)(int8_t)nt_smem[po + 192 + e];
-        stf(scl + 4u * (uint32_t)(16 * e + row), d * (float)sc);
+        sti32(scl + 4u * (uint32_t)(16 * e + row), (int)(int8_t)nt_smem[po + 192 + e]);
       }
-      break;
+      return make_float2(h2f(ld16(po + 208)), 0.f);
     }
   }
 }
@@ -338,75 +337,104 @@ __device__ __forceinline__ long a_operand(const TSeg& sg, uint32_t po, int kb, i
   }
 }
 
-// Combine the hi (even column) and lo (odd column) sums of each token and add
-// alpha_j (s S) - beta_j sx for C rows j = 0..3.
-__device__ __forceinline__ void accumulate(v4i c, const float (&al)[4], const float (&be)[4], float s, float sx,
-                                           float (&acc)[4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int lo = dpp_i<0xB1>(c[j]);  // quad_perm 1,0,3,2: the odd neighbour's (lo plane) sum
-    const float S = (float)((c[j] << 8) + lo);
-    acc[j] += al[j] * (s * S) - be[j] * sx;
-  }
-}
+__device__ __forceinline__ int mad24(int a, int b, int c) { return __mul24(a, b) + c; }
 
-__device__ __forceinline__ void alphas(uint32_t scl, int e, int kq, float (&al)[4]) {
-  const float4 a = *reinterpret_cast<const float4*>(nt_smem + scl + 4u * (uint32_t)(16 * e + 4 * kq));
-  al[0] = a.x; al[1] = a.y; al[2] = a.z; al[3] = a.w;
-}
-
-template <int F>
+// One tile-slice (16 rows x 256 columns, one superblock of the K-quants)
+// into this lane's accumulators: rows 4 kq .. 4 kq + 3 of the tile, token t,
+// plane p (column 2 t + p of the products).  The activation's 256-block
+// shares one scale s, so a K-quant superblock is summed exactly in integers
+// first: AI = sum_j sc_j C_j over its sub-blocks (C_j the MFMA's sums of
+// q X in this lane's plane) and, on the lo-plane lane only, MI = sum_j m_j
+// SX_j (SX_j the sub-block's sum of X); with X = 256 hi + lo the
+// superblock's contribution is s (256 P_hi + P_lo), P = d AI - dmin MI
+// (Q6_K: d (AI - 32 MI) with the signed 16-weight scales).  Q8_0 / Q4_0
+// blocks carry their own fp16 d: P = sum_b d_b (C_b - off SX_b), off 8 for
+// Q4_0.  Every bound: |AI| < 2^26 (Q5_K), |MI| < 2^30 (Q6_K, sixteen
+// 16-sums of |X| <= 32639 times |sc| <= 128).
+template <int F, int LPL>
 __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, uint32_t slab, uint32_t scl, int lane,
-                                             float (&acc)[4]) {
+                                               float (&acc)[4]) {
   const int kq = lane >> 4, t = (lane & 15) >> 1;
+  const bool lo_lane = lane & 1;
   const uint32_t po = piece_off(sg, slab, lane & 15);
-  scale_table(sg, po, scl, lane);
+  const float2 dd = scale_table(sg, po, scl, lane);
   if (sg.first) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = 0.f;
   }
   const v4i zero = {0, 0, 0, 0};
+  constexpr bool kq_fmt = F == NT_Q4_K || F == NT_Q5_K || F == NT_Q6_K;
+  int ai[4] = {0, 0, 0, 0}, mi[4] = {0, 0, 0, 0};
+  float af[4] = {0.f, 0.f, 0.f, 0.f};
   auto block = [&](int kb) {
     const int lb = sg.lb0 + kb;
     const long a = a_operand<F>(sg, po, kb, kq);
     const long bo = *reinterpret_cast<const long*>(nt_smem + job.xbl + 512u * (uint32_t)lb + 8u * lane);
-    const uint32_t rec = job.xsl + 16u * (uint32_t)(lb * kMaxTokens + t);
-    float al[4], be[4];
-    if (F == NT_Q6_K) {
-      const float4 r = *reinterpret_cast<const float4*>(nt_smem + rec);
+    const int2 sx = *reinterpret_cast<const int2*>(nt_smem + job.xsl + 16u * (uint32_t)(lb * kMaxTokens + t));
+    const int sxa = lo_lane ? sx.x : 0, sxb = lo_lane ? sx.y : 0;  // X sums enter on the lo-plane lane
+    if constexpr (F == NT_Q6_K) {
       const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? a : 0l, bo, zero, 0, 0, 0);
       const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? 0l : a, bo, zero, 0, 0, 0);
-      alphas(scl, 2 * kb, kq, al);
+      const int4 g0 = *reinterpret_cast<const int4*>(nt_smem + scl + 4u * (uint32_t)(16 * (2 * kb) + 4 * kq));
+      const int4 g1 = *reinterpret_cast<const int4*>(nt_smem + scl + 4u * (uint32_t)(16 * (2 * kb + 1) + 4 * kq));
+      const int s0[4] = {g0.x, g0.y, g0.z, g0.w}, s1[4] = {g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) be[j] = 32.f * al[j];
-      accumulate(c0, al, be, r.x, r.z, acc);
-      alphas(scl, 2 * kb + 1, kq, al);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) be[j] = 32.f * al[j];
-      accumulate(c1, al, be, r.x, r.w, acc);
-    } else {
-      const float2 r = *reinterpret_cast<const float2*>(nt_smem + rec);
-      const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bo, zero, 0, 0, 0);
-      if (F == NT_Q4_K || F == NT_Q5_K) {
-        const uint32_t e = scl + 8u * (uint32_t)(16 * kb + 4 * kq);
-        const float4 p0 = *reinterpret_cast<const float4*>(nt_smem + e);
-        const float4 p1 = *reinterpret_cast<const float4*>(nt_smem + e + 16);
-        al[0] = p0.x; be[0] = p0.y; al[1] = p0.z; be[1] = p0.w;
-        al[2] = p1.x; be[2] = p1.y; al[3] = p1.z; be[3] = p1.w;
-      } else {
-        alphas(scl, kb, kq, al);
-        const float f = F == NT_Q4_0 ? 8.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) be[j] = f * al[j];
+      for (int j = 0; j < 4; ++j) {
+        ai[j] = mad24(s1[j], c1[j], mad24(s0[j], c0[j], ai[j]));
+        mi[j] = mad24(s1[j], sxb, mad24(s0[j], sxa, mi[j]));
       }
-      accumulate(c, al, be, r.x, r.y, acc);
+    } else if constexpr (kq_fmt) {
+      const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bo, zero, 0, 0, 0);
+      const uint32_t e = scl + 8u * (uint32_t)(16 * kb + 4 * kq);
+      const int4 p0 = *reinterpret_cast<const int4*>(nt_smem + e);
+      const int4 p1 = *reinterpret_cast<const int4*>(nt_smem + e + 16);
+      const int sc[4] = {p0.x, p0.z, p1.x, p1.z}, m[4] = {p0.y, p0.w, p1.y, p1.w};
+      const int sxs = sxa + sxb;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ai[j] = mad24(sc[j], c[j], ai[j]);
+        mi[j] = mad24(m[j], sxs, mi[j]);
+      }
+    } else {
+      const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bo, zero, 0, 0, 0);
+      const float4 d4 = *reinterpret_cast<const float4*>(nt_smem + scl + 4u * (uint32_t)(16 * kb + 4 * kq));
+      const float d[4] = {d4.x, d4.y, d4.z, d4.w};
+      const int off = F == NT_Q4_0 ? 8 * (sxa + sxb) : 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) af[j] = fmaf(d[j], (float)(c[j] - off), af[j]);
     }
   };
   if (sg.nblk == kTS / 32) {
+    // blocks unrolled U at a time (more spill)
+    constexpr int U = LPL >= 5 ? 1 : (F == NT_Q6_K ? 2 : 4);
+#pragma unroll 1
+    for (int h = 0; h < kTS / 32; h += U) {
 #pragma unroll
-    for (int kb = 0; kb < kTS / 32; ++kb) block(kb);
+      for (int kb = 0; kb < U; ++kb) block(h + kb);
+    }
   } else {
     for (int kb = 0; kb < sg.nblk; ++kb) block(kb);
+  }
+  // the activation's scale of this 256-block, and the rows' d (dmin)
+  const float s = __int_as_float(
+      *reinterpret_cast<const int*>(nt_smem + job.xsl + 16u * (uint32_t)(sg.lb0 * kMaxTokens + t) + 8u));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float P;
+    if constexpr (kq_fmt) {
+      const int src = 4 * (4 * kq + j);  // a lane holding row 4 kq + j in scale_table
+      const float d = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(dd.x)));
+      if constexpr (F == NT_Q6_K) {
+        P = d * ((float)ai[j] - 32.f * (float)mi[j]);
+      } else {
+        const float dmin = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(dd.y)));
+        P = d * (float)ai[j] - dmin * (float)mi[j];
+      }
+    } else {
+      P = af[j];
+    }
+    const float Pl = __int_as_float(dpp_i<0xB1>(__float_as_int(P)));  // quad_perm 1,0,3,2: the lo-plane lane's
+    acc[j] = fmaf(s, fmaf(256.f, P, Pl), acc[j]);
   }
   if (sg.last && (lane & 1) == 0 && t < job.M) {
 #pragma unroll
@@ -417,14 +445,15 @@ __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, 
   }
 }
 
+template <int LPL>
 __device__ __forceinline__ void tseg_compute(const JobM& job, const TSeg& sg, uint32_t slab, uint32_t scl, int lane,
                                              float (&acc)[4]) {
   switch (sg.fmt) {
-    case NT_Q4_K: tseg_compute_f<NT_Q4_K>(job, sg, slab, scl, lane, acc); break;
-    case NT_Q6_K: tseg_compute_f<NT_Q6_K>(job, sg, slab, scl, lane, acc); break;
-    case NT_Q8_0: tseg_compute_f<NT_Q8_0>(job, sg, slab, scl, lane, acc); break;
-    case NT_Q4_0: tseg_compute_f<NT_Q4_0>(job, sg, slab, scl, lane, acc); break;
-    default: tseg_compute_f<NT_Q5_K>(job, sg, slab, scl, lane, acc); break;
+    case NT_Q4_K: tseg_compute_f<NT_Q4_K, LPL>(job, sg, slab, scl, lane, acc); break;
+    case NT_Q6_K: tseg_compute_f<NT_Q6_K, LPL>(job, sg, slab, scl, lane, acc); break;
+    case NT_Q8_0: tseg_compute_f<NT_Q8_0, LPL>(job, sg, slab, scl, lane, acc); break;
+    case NT_Q4_0: tseg_compute_f<NT_Q4_0, LPL>(job, sg, slab, scl, lane, acc); break;
+    default: tseg_compute_f<NT_Q5_K, LPL>(job, sg, slab, scl, lane, acc); break;
   }
 }
 
@@ -487,7 +516,7 @@ __device__ __forceinline__ void stream_m(const JobM& job, const ShareM& sh, int 
   sg = issue ? tseg_at(job, sh, ah.u, ah.j) : tseg_null(job);
   tseg_load(sg, lane, pre);
   if (issue) ucur_next(job, sh, ah, wave, lane, true);
-  if (valid) tseg_compute(job, cur, slab, scl, lane, acc);
+  if (valid) tseg_compute<LPL>(job, cur, slab, scl, lane, acc);
   cur_valid = nxt_valid;
   nxt_valid = issue;
 }
@@ -685,7 +714,7 @@ int launch_stage_m(const float* src, int64_t stride, const float* gain, float ep
                    hipStream_t stream) {
   if (M < 1 || M > kMaxTokens || cols <= 0 || cols % 32) return NT_EINVAL;
   uint8_t* xb = static_cast<uint8_t*>(stage);
-  float4* xs = reinterpret_cast<float4*>(xb + (size_t)(cols / 32) * 512);
+  int4* xs = reinterpret_cast<int4*>(xb + (size_t)(cols / 32) * 512);
   hipLaunchKernelGGL(k_stage_m, dim3(M), dim3(kStageThreads), 0, stream, src, stride, gain, eps, cols, xb, xs);
   return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
 }
@@ -774,7 +803,7 @@ int launch_gemm_m(JobM& job, const void* stage, void* part, const ProArgs& pro, 
                   hipStream_t stream) {
   if (job.otiles <= 0) return NT_OK;
   job.xb = static_cast<const uint8_t*>(stage);
-  job.xs = reinterpret_cast<const float4*>(job.xb + (size_t)(job.cols / 32) * 512);
+  job.xs = reinterpret_cast<const int4*>(job.xb + (size_t)(job.cols / 32) * 512);
   job.part = static_cast<float*>(part);
   int rc = NT_EUNSUPPORTED;
   switch (job.lpl) {

@@ -214,7 +214,7 @@ struct JobM {
   uint32_t magicV[2];         // floor((2^32-1)/nvt) for the two tile counts of a workgroup
   int nwaves, grid, lpl;
   const uint8_t* xb;          // staged activation in MFMA B layout [cols/32][64 lanes][8 B]
-  const float4* xs;           // [cols/32][8 tokens]: s, s*sum(X), s*sum(X first 16), s*sum(X last 16)
+  const int4* xs;             // [cols/32][8 tokens]: sum(X first 16), sum(X last 16), s of its 256-block (f32 bits), 0
   float* part;                // partial sums [nsup][M][ldp]
   int64_t ldp;                // (paired ? 2 : 1) * orows
   uint32_t xbl, xsl, slab, scl, acc, ctl, lds_bytes;
