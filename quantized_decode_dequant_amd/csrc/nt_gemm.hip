@@ -299,7 +299,21 @@ __device__ __forceinline__ float2 scale_table(const TSeg& sg, uint32_t po, uint3
 
 // A operand: 8 quants (one byte each) of row lane%16, weights 8*(lane/16)..+7
 // of block kb of the tile-slice.
-template <int F>
+// Two dwords at an 8-byte aligned LDS offset (AL) or at any 2-byte aligned one.
+template <bool AL>
+__device__ __forceinline__ void ld_pair(uint32_t off, uint32_t (&v)[2]) {
+  if constexpr (AL) {
+    const uint2 w = *reinterpret_cast<const uint2*>(nt_smem + off);
+    v[0] = w.x;
+    v[1] = w.y;
+  } else {
+    ld_unaligned<2>(off, v);
+  }
+}
+
+// AL: the row pieces start 16-byte aligned (K-quant offsets below are then
+// 8-byte aligned).
+template <int F, bool AL = false>
 __device__ __forceinline__ long a_operand(const TSeg& sg, uint32_t po, int kb, int kq) {
   uint32_t v[2];
   switch (F >= 0 ? F : sg.fmt) {
@@ -312,14 +326,14 @@ __device__ __forceinline__ long a_operand(const TSeg& sg, uint32_t po, int kb, i
       return pack2((v[0] >> sh) & 0x0F0F0F0Fu, (v[1] >> sh) & 0x0F0F0F0Fu);
     }
     case NT_Q4_K: {
-      ld_unaligned<2>(po + 16 + 32 * (kb >> 1) + 8 * kq, v);
+      ld_pair<AL>(po + 16 + 32 * (kb >> 1) + 8 * kq, v);
       const int sh = 4 * (kb & 1);
       return pack2((v[0] >> sh) & 0x0F0F0F0Fu, (v[1] >> sh) & 0x0F0F0F0Fu);
     }
     case NT_Q5_K: {  // Q4_K nibbles (after 32 bytes qh) plus bit kb of qh[l] as the fifth bit
       uint32_t h[2];
-      ld_unaligned<2>(po + 48 + 32 * (kb >> 1) + 8 * kq, v);
-      ld_unaligned<2>(po + 16 + 8 * kq, h);
+      ld_pair<AL>(po + 48 + 32 * (kb >> 1) + 8 * kq, v);
+      ld_pair<AL>(po + 16 + 8 * kq, h);
       const int sh = 4 * (kb & 1);
       return pack2(((v[0] >> sh) & 0x0F0F0F0Fu) | (((h[0] >> kb) & 0x01010101u) << 4),
                    ((v[1] >> sh) & 0x0F0F0F0Fu) | (((h[1] >> kb) & 0x01010101u) << 4));
@@ -351,7 +365,7 @@ __device__ __forceinline__ int mad24(int a, int b, int c) { return __mul24(a, b)
 // blocks carry their own fp16 d: P = sum_b d_b (C_b - off SX_b), off 8 for
 // Q4_0.  Every bound: |AI| < 2^26 (Q5_K), |MI| < 2^30 (Q6_K, sixteen
 // 16-sums of |X| <= 32639 times |sc| <= 128).
-template <int F, int LPL>
+template <int F, int LPL, bool AL>
 __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, uint32_t slab, uint32_t scl, int lane,
                                                float (&acc)[4]) {
   const int kq = lane >> 4, t = (lane & 15) >> 1;
@@ -368,7 +382,7 @@ __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, 
   float af[4] = {0.f, 0.f, 0.f, 0.f};
   auto block = [&](int kb) {
     const int lb = sg.lb0 + kb;
-    const long a = a_operand<F>(sg, po, kb, kq);
+    const long a = a_operand<F, AL>(sg, po, kb, kq);
     const long bo = *reinterpret_cast<const long*>(nt_smem + job.xbl + 512u * (uint32_t)lb + 8u * lane);
     const int2 sx = *reinterpret_cast<const int2*>(nt_smem + job.xsl + 16u * (uint32_t)(lb * kMaxTokens + t));
     const int sxa = lo_lane ? sx.x : 0, sxb = lo_lane ? sx.y : 0;  // X sums enter on the lo-plane lane
@@ -448,12 +462,21 @@ __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, 
 template <int LPL>
 __device__ __forceinline__ void tseg_compute(const JobM& job, const TSeg& sg, uint32_t slab, uint32_t scl, int lane,
                                              float (&acc)[4]) {
+  // row pieces laid out without alignment slack (the planner's exact P)
+  // start 16-byte aligned
+  const bool al = sg.P * 16 == sg.piece;
   switch (sg.fmt) {
-    case NT_Q4_K: tseg_compute_f<NT_Q4_K, LPL>(job, sg, slab, scl, lane, acc); break;
-    case NT_Q6_K: tseg_compute_f<NT_Q6_K, LPL>(job, sg, slab, scl, lane, acc); break;
-    case NT_Q8_0: tseg_compute_f<NT_Q8_0, LPL>(job, sg, slab, scl, lane, acc); break;
-    case NT_Q4_0: tseg_compute_f<NT_Q4_0, LPL>(job, sg, slab, scl, lane, acc); break;
-    default: tseg_compute_f<NT_Q5_K, LPL>(job, sg, slab, scl, lane, acc); break;
+    case NT_Q4_K:
+      if (al) tseg_compute_f<NT_Q4_K, LPL, true>(job, sg, slab, scl, lane, acc);
+      else tseg_compute_f<NT_Q4_K, LPL, false>(job, sg, slab, scl, lane, acc);
+      break;
+    case NT_Q6_K: tseg_compute_f<NT_Q6_K, LPL, false>(job, sg, slab, scl, lane, acc); break;
+    case NT_Q8_0: tseg_compute_f<NT_Q8_0, LPL, false>(job, sg, slab, scl, lane, acc); break;
+    case NT_Q4_0: tseg_compute_f<NT_Q4_0, LPL, false>(job, sg, slab, scl, lane, acc); break;
+    default:
+      if (al) tseg_compute_f<NT_Q5_K, LPL, true>(job, sg, slab, scl, lane, acc);
+      else tseg_compute_f<NT_Q5_K, LPL, false>(job, sg, slab, scl, lane, acc);
+      break;
   }
 }
 
@@ -748,7 +771,11 @@ int plan_job_m(JobM& job, int nmat, const uint8_t* const* W, const int* fmt, con
     job.row_base[m] = paired ? 0 : (int)orows;
     job.tile_base[m] = paired ? 0 : (int)otiles;
     job.tsb[m] = (kTS / qk) * block_bytes(fmt[m]);
-    job.P[m] = (job.tsb[m] + 15 + 15) / 16;
+    // chunks per row piece: exact when every piece starts 16-byte aligned
+    // (the rows' stride then keeps the 16 rows' reads on distinct LDS
+    // banks), else room for the worst alignment
+    const bool al16 = job.tsb[m] % 16 == 0 && job.rb[m] % 16 == 0 && (reinterpret_cast<uintptr_t>(W[m]) & 15) == 0;
+    job.P[m] = al16 ? job.tsb[m] / 16 : (job.tsb[m] + 15 + 15) / 16;
     job.magicP[m] = (65536u + (uint32_t)job.P[m] - 1) / (uint32_t)job.P[m];
     lpl = std::max(lpl, (kTileRows * job.P[m] + 63) / 64);
     if (!paired || m == 0) {
