@@ -27,17 +27,21 @@ instead of recomputing it.  Three modes:
       that size; the layer composition used here equals the plain decode
       bit for bit when D = 0 (tests/test_oracle_layer.py).  D = 1.5e-5 is
       the half step of the 16-bit fixed point the GPU holds activations in
-      (1 / (2 * 32639) of a block's largest magnitude).  --first/--last run
-      a range of steps, --cond-out writes elsewhere, --merge-cond copies
-      such runs' results into the teacher json.
+      (1 / (2 * 32639) of a block's largest magnitude).  Where the perturbed
+      token differs from the stored one, --cond-seeds K reruns the step under
+      K - 1 further perturbations (other seeds) and stores the set of greedy
+      tokens seen, the stored one included (cond_tokens): the tokens the
+      oracle itself gives at that step under deviations of the GPU's size.
+      --first/--last run a range of steps, --cond-out writes elsewhere,
+      --merge-cond copies such runs' results into the teacher json.
 
   --free-running: the earlier record stack70b_q4km_greedy.json (token,
       margin, top five and 256 sampled logits per step, 22 steps), and with
       --perturb-seed S the oracle's movement under one f16 ulp on 10% of its
       past cache entries.  Kept as the record of the free-running trajectory.
 
-usage: python tests/golden/make_stack70b_golden.py --steps 64
-       python tests/golden/make_stack70b_golden.py --cond-rel 1.5e-5
+usage: python tests/golden/make_stack70b_golden.py --steps 64 [--resume]
+       python tests/golden/make_stack70b_golden.py --cond-rel 1.5e-5 --cond-seeds 6
 """
 import argparse
 import json
@@ -97,7 +101,20 @@ def teacher(args):
     om = hs.oracle_model()
     steps, rows, logits = [], [], []
     t = hs.first_token
-    for s in range(args.steps):
+    if args.resume and os.path.exists(OUT_TEACHER) and os.path.exists(OUT_TEACHER_NPZ):
+        # continue a run that was cut short: the stored rows are the oracle's
+        # own appended entries, so writing them back restores its state
+        g = json.load(open(OUT_TEACHER))
+        z = np.load(OUT_TEACHER_NPZ)
+        assert g["first_token"] == hs.first_token
+        n = min(len(g["steps"]), z["kv_rows"].shape[0], z["logits"].shape[0])
+        steps, rows, logits = g["steps"][:n], list(z["kv_rows"][:n]), list(z["logits"][:n])
+        for p in range(n):
+            write_rows(om, N_PAST + p, rows[p])
+        if n:
+            t = steps[-1]["next"]
+        print(f"resuming after {n} stored steps", flush=True)
+    for s in range(len(steps), args.steps):
         pos = N_PAST + s
         nxt, margin, lg, _ = om.decode([t], pos, want_logits=True)
         steps.append(step_record(t, pos, nxt[0], margin[0], lg[0]))
@@ -154,13 +171,26 @@ def conditioning(args):
         st = g["steps"][s]
         pos = st["pos"]
         lg = perturbed_decode(om, hs, st["token_in"], pos, args.cond_rel, 1000 + s)
-        write_rows(om, pos, kv[s])  # the oracle's state before step s + 1
         err = float(np.abs(lg - ref[s].astype(np.float64)).max() / np.abs(ref[s]).max())
         st["cond_err"] = err
         st["cond_next"] = int(np.argmax(lg))
+        if st["cond_next"] != st["next"] and args.cond_seeds > 1:
+            # the token is not fixed at this precision: the tokens the oracle
+            # gives under further perturbations of the same size
+            toks = {st["next"], st["cond_next"]}
+            for k in range(1, args.cond_seeds):
+                lk = perturbed_decode(om, hs, st["token_in"], pos, args.cond_rel, 1000 + s + 100000 * k)
+                toks.add(int(np.argmax(lk)))
+                print(f"step {s}: perturbation {k + 1} of {args.cond_seeds}: token {int(np.argmax(lk))} "
+                      f"after {time.time() - t0:.0f} s", flush=True)
+                st["cond_err"] = max(st["cond_err"], float(np.abs(lk - ref[s].astype(np.float64)).max()
+                                                           / np.abs(ref[s]).max()))
+            st["cond_tokens"] = sorted(toks)
+        write_rows(om, pos, kv[s])  # the oracle's state before step s + 1
         g["cond_rel"] = args.cond_rel
-        print(f"step {s}: perturbed logits moved {err:.2e}, token {st['cond_next']} (stored {st['next']}) "
-              f"after {time.time() - t0:.0f} s", flush=True)
+        print(f"step {s}: perturbed logits moved {st['cond_err']:.2e}, token {st['cond_next']} (stored {st['next']})"
+              + (f", tokens under {args.cond_seeds} perturbations {st['cond_tokens']}" if "cond_tokens" in st else "")
+              + f" after {time.time() - t0:.0f} s", flush=True)
         with open(out, "w") as f:
             json.dump(g, f)
 
@@ -175,8 +205,9 @@ def merge_conditioning(paths) -> None:
         for s, st in enumerate(part["steps"]):
             if "cond_err" in st and s < len(g["steps"]):
                 assert st["next"] == g["steps"][s]["next"]
-                g["steps"][s]["cond_err"] = st["cond_err"]
-                g["steps"][s]["cond_next"] = st["cond_next"]
+                for k in ("cond_err", "cond_next", "cond_tokens"):
+                    if k in st:
+                        g["steps"][s][k] = st[k]
         g["cond_rel"] = part["cond_rel"]
     with open(OUT_TEACHER, "w") as f:
         json.dump(g, f)
@@ -240,10 +271,13 @@ def free_running_perturbed(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--resume", action="store_true", help="teacher: continue after the stored steps")
     ap.add_argument("--cond-rel", type=float, default=None)
     ap.add_argument("--first", type=int, default=0, help="conditioning: first step")
     ap.add_argument("--last", type=int, default=None, help="conditioning: one past the last step")
     ap.add_argument("--cond-out", default=None, help="conditioning: write the json here")
+    ap.add_argument("--cond-seeds", type=int, default=1,
+                    help="conditioning: perturbations tried where the perturbed token differs")
     ap.add_argument("--free-running", action="store_true")
     ap.add_argument("--perturb-seed", type=int, default=None)
     ap.add_argument("--merge-cond", nargs="+", default=None, help="json files of conditioning runs to merge")
