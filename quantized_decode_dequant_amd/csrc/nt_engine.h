@@ -623,6 +623,7 @@ template <int EPI>
 __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, int tid, int nthreads,
                                                const EpiArgs& ea, float r, const EpiPre& pre) {
   const bool qout = (EPI == EPI_RESID || EPI == EPI_SWIGLU) && ea.qx_out != nullptr;  // uniform
+  float qv = 0.f;  // this thread's first output (row tid), for the quantized output
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
     // a residual launch given the layer's status word turns the stream into
     // NaN when the layer's position was out of range
@@ -633,7 +634,8 @@ __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, 
       if constexpr (EPI == EPI_RESID) {
         const float v = bad ? __builtin_nanf("") : (t == tid ? pre.y : *y) + s;
         *y = v;
-        if (qout) stf(job.qo + 4u * (uint32_t)t, v);
+        if (t == tid) qv = v;
+        if (qout && sh.no > nthreads) stf(job.qo + 4u * (uint32_t)t, v);
       } else {
         *y = s;
       }
@@ -642,7 +644,8 @@ __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, 
     for (int t = tid; t < sh.no; t += nthreads) {
       const float v = silu(r * row_total(job, t)) * (r * row_total(job, sh.no + t));
       ea.y[srow(job, sh, t)] = v;
-      if (qout) stf(job.qo + 4u * (uint32_t)t, v);
+      if (t == tid) qv = v;
+      if (qout && sh.no > nthreads) stf(job.qo + 4u * (uint32_t)t, v);
     }
   } else if constexpr (EPI == EPI_QKV) {
     const int pos = pre.pos + ea.pos_add;
@@ -678,9 +681,16 @@ __device__ __forceinline__ void share_epilogue(const Job& job, const Share& sh, 
       }
     }
   }
-  if (qout) {
-    // the share is whole 32-row blocks (qblock): half-waves quantize one
-    // block each into the next launch's activation (times ea.qx_gain)
+  if (qout && sh.no <= nthreads) {
+    // the share is whole 32-row blocks (qblock), one output per thread: the
+    // half-waves of threads 0 .. no-1 quantize their block from registers
+    // into the next launch's activation (times ea.qx_gain)
+    if (tid < sh.no) {
+      const int R = srow(job, sh, tid);
+      qx_store_block32(ea.qx_out, job.orows, R >> 5, tid & 31, qv * (ea.qx_gain ? pre.g : 1.0f), qv);
+    }
+  } else if (qout) {
+    // more rows than threads: through LDS, half-waves one block at a time
     __syncthreads();
     const int l = tid & 31;
     for (int blk = tid >> 5; blk < (sh.no >> 5); blk += nthreads >> 5) {
