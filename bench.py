@@ -717,6 +717,9 @@ def main():
     ap.add_argument("--layers", type=int, default=80, help="stack depth (80 is the workload)")
     ap.add_argument("--cpu-sample-layers", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace-every", type=int, default=41,
+                    help="decode: time one gate/up launch in this many with kernel-stamped HIP events "
+                         "(prime to the 80 layers, so every layer is sampled)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one device copy of 256 MiB (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize", metavar="DIR", help="print per-kernel statistics of a rocprofv3 output "
@@ -780,10 +783,13 @@ def main():
     tok.fill_(first)
     pos.fill_(n_past)
     torch.cuda.synchronize()
-    # the roofline kernel's launches are timed with HIP events inside the timed
-    # region; one launch in ten, since each event record costs the stream a
-    # few microseconds (all of them would add ~4% to the step time)
-    trace_every = 10
+    # the roofline kernel's launches are timed inside the timed region with
+    # HIP events that the runtime stamps with the kernel's own start and end
+    # (nt_trace_*).  One launch in --trace-every (41) is sampled: a traced
+    # launch costs the host ~16 us to enqueue, and timing all of them slowed
+    # the decode by 3.5%, one in ten by 0.3%; 41 is prime to the layer count,
+    # so the samples cycle through every layer
+    trace_every = args.trace_every
     nt.trace_begin(nt.TRACE_FFN_UP, trace_every)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)

@@ -363,17 +363,16 @@ int nt_spec_step(const nt_model* model, const uint8_t* draft_skip, int K, int32_
                  int32_t* out_dev, int32_t* n_out_dev, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Instrumentation.  nt_trace_begin(kind) makes the library record a HIP event
- * pair, on the launch stream, around every following launch of one kernel
- * kind (up to 16384 launches); nt_trace_end waits for those events and returns
- * the number of launches traced and their summed duration in milliseconds
- * (*total_ms).  Kinds: 0 plain GEMV, 1 GEMV + residual add (O and down
- * projections), 2 QKV + RoPE + KV append, 3 gate/up + SwiGLU, 4 attention.
+ * Instrumentation.  nt_trace_begin(kind) makes the library time every
+ * following launch of one kernel kind (up to 16384 launches) with a pair of
+ * HIP events that the runtime stamps with the kernel's own start and end on
+ * the launch stream (hipExtLaunchKernel); nt_trace_end waits for those events
+ * and returns the number of launches traced and their summed duration in
+ * milliseconds (*total_ms).  Kinds: 0 plain GEMV, 1 GEMV + residual add (O
+ * and down projections), 2 QKV + RoPE + KV append, 3 gate/up + SwiGLU,
+ * 4 attention (the first split launch's start to the combine's end).
  * nt_trace_begin_every(kind, k) records only launches 0, k, 2k, ... of the
- * kind (k >= 1), so that a long run can be sampled at a fraction of the
- * event cost (each record costs the stream a few microseconds).
- * Tracing is per process and not thread safe; it adds two event records per
- * traced launch.
+ * kind (k >= 1).  Tracing is per process and not thread safe.
  */
 typedef enum nt_trace_kind {
   NT_TRACE_GEMV = 0,

@@ -466,13 +466,17 @@ void attn_plan(int head_dim, int max_ctx, int& chunk, int& nsplit) {
 int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, const int32_t* pos, int n_query,
                      int n_head, int n_kv, int head_dim, int max_ctx, int chunk, int nsplit, float* part_o,
                      float* part_ml, float* o, uint8_t* qx_o, hipStream_t stream) {
-  trace_before(NT_TRACE_ATTN, stream);
+  // traced: the interval from the first split launch's start to the
+  // combine's end
+  hipEvent_t t0, t1;
+  (void)trace_events(NT_TRACE_ATTN, &t0, &t1);
   for (int qi = 0; qi < n_query; ++qi) {
     const dim3 grid(n_kv, nsplit);
+    hipEvent_t ts = qi == 0 ? t0 : nullptr;
 #define NT_ATTN_CASE(HD)                                                                                      \
   case HD:                                                                                                    \
-    hipLaunchKernelGGL(k_attn_split<HD>, grid, dim3(64 * attn_waves<HD>()), 0, stream, q, kc, vc, pos, qi, n_head, \
-                       n_kv, max_ctx, nsplit, part_o, part_ml);                                               \
+    hipExtLaunchKernelGGL(k_attn_split<HD>, grid, dim3(64 * attn_waves<HD>()), 0, stream, ts, nullptr, 0, q, kc, vc, \
+                          pos, qi, n_head, n_kv, max_ctx, nsplit, part_o, part_ml);                          \
     break;
     switch (head_dim) {
       NT_ATTN_CASE(32)
@@ -483,11 +487,9 @@ int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, con
     }
 #undef NT_ATTN_CASE
   }
-  hipLaunchKernelGGL(k_attn_combine, dim3(n_head * (head_dim / 32), n_query), dim3(256), 0, stream, part_o, part_ml,
-                     pos, n_head, head_dim, chunk, nsplit, max_ctx, o, qx_o);
-  const bool ok = hipGetLastError() == hipSuccess;
-  trace_after(NT_TRACE_ATTN, stream);
-  return ok ? NT_OK : NT_EHIP;
+  hipExtLaunchKernelGGL(k_attn_combine, dim3(n_head * (head_dim / 32), n_query), dim3(256), 0, stream, nullptr, t1, 0,
+                        part_o, part_ml, pos, n_head, head_dim, chunk, nsplit, max_ctx, o, qx_o);
+  return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
 }
 
 int launch_embed(int fmt, const void* E, const int32_t* tokens, int M, int vocab, int cols, float* x, int* err,

@@ -149,12 +149,11 @@ int launch_k(const Job& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t 
     attr_set = true;
   }
   constexpr int kind = EPI == EPI_STORE_BURST ? EPI_STORE : EPI;  // trace kinds are the epilogues
-  trace_before(kind, stream);
-  hipLaunchKernelGGL((k_qgemv<EPI, LPL, FMT>), dim3(job.grid), dim3(64 * job.nwaves), job.lds_bytes, stream, job, pro,
-                     ea);
-  const bool ok = hipGetLastError() == hipSuccess;
-  trace_after(kind, stream);
-  return ok ? NT_OK : NT_EHIP;
+  hipEvent_t t0, t1;
+  (void)trace_events(kind, &t0, &t1);
+  hipExtLaunchKernelGGL((k_qgemv<EPI, LPL, FMT>), dim3(job.grid), dim3(64 * job.nwaves), job.lds_bytes, stream, t0,
+                        t1, 0, job, pro, ea);
+  return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
 }
 
 // A launch whose matrices share one format runs a kernel compiled for that

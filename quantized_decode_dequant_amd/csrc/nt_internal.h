@@ -1,6 +1,7 @@
 // Internal declarations shared by the HIP translation units of libnt.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -235,10 +236,10 @@ int launch_stage_m(const float* src, int64_t stride, const float* gain, float ep
 int launch_gemm_m(JobM& job, const void* stage, void* part, const ProArgs& pro, int epi, const EpiArgs& ea,
                   hipStream_t stream);
 
-// Launch tracing (nt_trace.hip): wraps one launch of `kind` in events when
-// tracing that kind.
-void trace_before(int kind, hipStream_t stream);
-void trace_after(int kind, hipStream_t stream);
+// Launch tracing (nt_trace.hip): true when this launch of `kind` is
+// recorded, with the events to hand to hipExtLaunchKernel (start: the first
+// kernel of the launch, stop: its last); both null otherwise.
+bool trace_events(int kind, hipEvent_t* start, hipEvent_t* stop);
 
 // Attention and step kernels (nt_attn.hip).
 void attn_plan(int head_dim, int max_ctx, int& chunk, int& nsplit);

@@ -1,6 +1,8 @@
 // nt_trace.hip -- optional event timing of one kernel kind (instrumentation
-// for benchmarks: the measured durations come from HIP events on the stream
-// the kernels are launched on).
+// for benchmarks).  A recorded launch goes out through hipExtLaunchKernel
+// with a pair of HIP events, which the runtime stamps with that dispatch's
+// own start and end on the stream it runs on: the interval is the kernel's
+// execution, without the queue's other packets or the gap before it.
 #include <vector>
 
 #include "nt_internal.h"
@@ -15,7 +17,6 @@ struct Trace {
   int n = 0;            // launches recorded
   int every = 1;        // record one launch in `every`
   int seen = 0;         // launches of the kind since trace_begin
-  bool open = false;    // the current launch is being recorded
   std::vector<hipEvent_t> start, stop;
 };
 
@@ -23,19 +24,14 @@ Trace g_trace;
 
 }  // namespace
 
-void trace_before(int kind, hipStream_t stream) {
-  g_trace.open = false;
-  if (kind != g_trace.kind || g_trace.n >= kTraceCap) return;
-  if (g_trace.seen++ % g_trace.every != 0) return;
-  g_trace.open = true;
-  (void)hipEventRecord(g_trace.start[g_trace.n], stream);
-}
-
-void trace_after(int kind, hipStream_t stream) {
-  if (kind != g_trace.kind || !g_trace.open) return;
-  g_trace.open = false;
-  (void)hipEventRecord(g_trace.stop[g_trace.n], stream);
+bool trace_events(int kind, hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
+  if (kind != g_trace.kind || g_trace.n >= kTraceCap) return false;
+  if (g_trace.seen++ % g_trace.every != 0) return false;
+  *start = g_trace.start[g_trace.n];
+  *stop = g_trace.stop[g_trace.n];
   ++g_trace.n;
+  return true;
 }
 
 }  // namespace nt
@@ -59,7 +55,6 @@ int nt_trace_begin_every(int kind, int every) {
   g_trace.n = 0;
   g_trace.every = every;
   g_trace.seen = 0;
-  g_trace.open = false;
   return NT_OK;
 }
 

@@ -145,3 +145,34 @@ def test_gemv_special_inputs():
                 assert not got.any()
             else:
                 assert rel_inf(got, ref) <= GEMV_TOL, (fmt, kind)
+
+
+def test_trace_times_each_launch_inside_the_stream_interval():
+    # nt_trace_*: every launch of the kind (or one in `every`) is timed by
+    # events stamped with the kernel's own start and end, so the summed
+    # durations are positive and fit inside an event pair around all of them;
+    # the traced launches still give the oracle's result
+    import torch
+    import quantized_decode_dequant_amd as nt
+    rows, cols, n = 4096, 4096, 12
+    W = synth.quant(synth.Q8_0, rows, cols, synth.key(wl.W_TEST, 91, synth.Q8_0))
+    x = wl.gen_x(cols, wl.W_TEST, 91)
+    Wd, xd = to_dev(W), to_dev(x)
+    y = torch.empty(rows, dtype=torch.float32, device=device())
+    for every, expect in ((1, n), (5, 3)):
+        torch.cuda.synchronize()
+        nt.trace_begin(nt.TRACE_GEMV, every)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            nt.gemv_q(synth.Q8_0, Wd, xd, y, rows, cols)
+        e1.record()
+        torch.cuda.synchronize()
+        launches, ms = nt.trace_end()
+        outer = e0.elapsed_time(e1)
+        say(f"  every {every}: {launches} launches, {ms * 1e3 / max(launches, 1):.2f} us each, "
+            f"{outer * 1e3 / n:.2f} us per launch between outer events")
+        assert launches == expect
+        assert 0.0 < ms < outer
+    err = rel_inf(y.cpu().numpy(), oracle.gemv(synth.Q8_0, W, x, rows, cols))
+    assert err <= GEMV_TOL
