@@ -107,6 +107,10 @@ __global__ __launch_bounds__(64 * attn_waves<HD>()) void k_attn_split(
   const bool ok = pos >= 0 && pos + query < max_ctx;
   const int t0 = split * C;
   const int nt = ok ? max(0, min(C, n_pos - t0)) : 0;
+  // a split past the position (a cache longer than the context so far, or an
+  // out-of-range position) has nothing to do: the combine uses no partial of
+  // it (nt is uniform, and no barrier has been reached)
+  if (nt == 0) return;
   const uint16_t* kg = kc + ((int64_t)g * max_ctx + t0) * HD;
   const uint16_t* vg = vc + ((int64_t)g * max_ctx + t0) * HD;
 
@@ -242,8 +246,8 @@ __global__ __launch_bounds__(64 * attn_waves<HD>()) void k_attn_split(
   }
   if (tid < G) {
     const int64_t mi = (((int64_t)query * nsplit + split) * n_head + g * G + tid) * 2;
-    part_ml[mi] = nt > 0 ? s_m[tid] : -FLT_MAX;
-    part_ml[mi + 1] = nt > 0 ? s_l[tid] : 0.f;
+    part_ml[mi] = s_m[tid];
+    part_ml[mi + 1] = s_l[tid];
   }
 }
 
@@ -270,9 +274,10 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   const int dl = tid & 31, j = tid >> 5;
   const float* po = part_o + ((int64_t)query * nsplit * n_head + h) * head_dim + d0 + dl;
   const int64_t sst = (int64_t)n_head * head_dim;
-  // every split's partials were written by this attention's split kernel, so
-  // their loads go out with the position's; splits past the position are
-  // masked by selects below
+  // the partials of every split that holds positions were written by this
+  // attention's split kernel, so their loads go out with the position's;
+  // splits past the position (their slots hold whatever an earlier call left)
+  // are masked by selects below
   // (indices clamped to the last split rather than branched around, so all
   // loads issue back to back)
   float ov[kPre];

@@ -106,7 +106,9 @@ def test_layer_attention_shapes_verify_tokens(name):
 def test_layer_group8_repeat_calls_share_workspace():
     # consecutive calls on one workspace give identical results, and a
     # workspace filled with other bytes gives the same (its contents need no
-    # initialisation)
+    # initialisation); with 0xFF bytes (NaN floats) the partial slots of the
+    # attention splits past the position (3 of the cache's 8 here) hold NaN,
+    # which the combine must mask by selection, not by weights of zero
     import torch
     import quantized_decode_dequant_amd as nt
     from quantized_decode_dequant_amd.model import DeviceLayer, cfg_of
@@ -118,9 +120,9 @@ def test_layer_group8_repeat_calls_share_workspace():
     pos = torch.tensor([n_past], dtype=torch.int32, device=device())
     ws = torch.zeros(nt.layer_workspace_bytes(cfg, 1), dtype=torch.uint8, device=device())
     outs = []
-    for i in range(4):
+    for i in range(5):
         xd = x0.clone()
-        w = ws if i < 3 else torch.full_like(ws, 0x5A)  # contents need no initialisation
+        w = ws if i < 3 else torch.full_like(ws, 0x5A if i == 3 else 0xFF)  # contents need no initialisation
         nt.decode_layer(cfg, dl.struct, xd, 1, pos, w)
         torch.cuda.synchronize()
         outs.append(xd.cpu().numpy())
