@@ -5,12 +5,12 @@
 // for all M tokens.
 //
 //   staging   k_stage_m puts the M activation rows (optionally RMSNorm'ed)
-//             into the GEMV engine's 16-bit fixed point: per token and
-//             32-block a scale s and integers X = 256 hi + lo.  The int8
-//             planes are laid out as the B operand of v_mfma_i32_16x16x32_i8
-//             (column n = 2t + plane: hi, lo), 512 contiguous bytes per
-//             32-block, plus a record (s, s*sum X, s*sum X over each half) per
-//             block and token.
+//             into 16-bit fixed point: per token and 256-block a scale s and
+//             integers X = 256 hi + lo.  The int8 planes are laid out as the
+//             B operand of v_mfma_i32_16x16x32_i8 (column n = 2t + plane: hi,
+//             lo), 512 contiguous bytes per 32-block, followed by the X sums
+//             of each block's two 16-element halves per B column (zero in the
+//             hi-plane column) and the scales.
 //   product   One MFMA multiplies a 16-row x 32-weight tile of raw quants by
 //             every token and plane with exact int32 sums.  Adjacent columns
 //             are combined, S = 256 C_hi + C_lo (exact), and scaled:
@@ -43,22 +43,33 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kStageThreads = 1024;
 
 // ------------------------------------------------------------------ staging
-// Token t = blockIdx.x.  Thread groups of 8 lanes hold one 32-block (4
-// elements each, coalesced as in the GEMV prologue); a wave holds one
-// 256-block, which shares one fixed-point scale (every lane takes part in
-// the wave's maximum: lanes past the end hold zeros).
+// Workgroup (c, t) stages columns 4096 c .. 4096 c + 4095 of token t: thread
+// groups of 8 lanes hold one 32-block (4 elements each, coalesced as in the
+// GEMV prologue); a wave holds one 256-block, which shares one fixed-point
+// scale (every lane takes part in the wave's maximum: lanes past the end hold
+// zeros).  With gains, each workgroup first forms the token's sum of squares
+// over the whole row, in the same order in every workgroup (the RMSNorm
+// factor is the same everywhere); its own elements are among those loads.
 __global__ __launch_bounds__(kStageThreads) void k_stage_m(const float* __restrict__ src, int64_t stride,
                                                            const float* __restrict__ gain, float eps, int cols,
-                                                           uint8_t* __restrict__ xb, int4* __restrict__ xs) {
+                                                           uint8_t* __restrict__ xb, int4* __restrict__ xs,
+                                                           float* __restrict__ xsc) {
   __shared__ float red[kStageThreads / 64];
-  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int t = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const float* x = src + (int64_t)t * stride;
+  const int base = 4 * kStageThreads * (int)blockIdx.x;
+  const int e = base + 4 * tid;
+  const bool ok = e < cols;
+  float4 v = ok ? *reinterpret_cast<const float4*>(x + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
+  if (gain && ok) g = *reinterpret_cast<const float4*>(gain + e);
   float r = 1.0f;
   if (gain) {
     float ss = 0.f;
-    for (int e = 4 * tid; e < cols; e += 4 * kStageThreads) {
-      const float4 v = *reinterpret_cast<const float4*>(x + e);
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll 4
+    for (int e2 = 4 * tid; e2 < cols; e2 += 4 * kStageThreads) {
+      const float4 w = e2 == e ? v : *reinterpret_cast<const float4*>(x + e2);
+      ss += w.x * w.x + w.y * w.y + w.z * w.z + w.w * w.w;
     }
     ss = wave_sum(ss);
     if (lane == 0) red[tid >> 6] = ss;
@@ -67,40 +78,37 @@ __global__ __launch_bounds__(kStageThreads) void k_stage_m(const float* __restri
     for (int w = 0; w < kStageThreads / 64; ++w) tot += red[w];
     r = 1.0f / sqrtf(tot / (float)cols + eps);
   }
-  for (int base = 0; base < cols; base += 4 * kStageThreads) {
-    const int e = base + 4 * tid;
-    const bool ok = e < cols;
-    float4 v = ok ? *reinterpret_cast<const float4*>(x + e) : make_float4(0.f, 0.f, 0.f, 0.f);
-    if (gain && ok) {
-      const float4 g = *reinterpret_cast<const float4*>(gain + e);
-      v = make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w);
-    }
-    v = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
-    const float amax = wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    const float inv = amax > 0.f ? kXMax / amax : 0.f;
-    const float f[4] = {v.x, v.y, v.z, v.w};
-    uint32_t H = 0, L = 0;
-    int sum = 0;
+  if (gain) v = make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w);
+  v = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
+  const float amax = wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  const float inv = amax > 0.f ? kXMax / amax : 0.f;
+  const float f[4] = {v.x, v.y, v.z, v.w};
+  uint32_t H = 0, L = 0;
+  int sum = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      int X = __float2int_rn(f[k] * inv);
-      X = max(-32639, min(32639, X));
-      const int hi = (X + 128) >> 8;
-      const int lo = X - (hi << 8);
-      H |= (uint32_t)(hi & 255) << (8 * k);
-      L |= (uint32_t)(lo & 255) << (8 * k);
-      sum += X;
-    }
-    // elements k = 4g..4g+3 of block b (g = lane's place in its group):
-    // B-layout lane n + 16*(k/8), byte k%8, for n = 2t (hi) and 2t + 1 (lo)
-    const int b = e >> 5, g = (e >> 2) & 7;
-    const int s16 = sum4(sum);            // lanes g<4: first half, g>=4: second half
-    const int other = dpp_i<0x141>(s16);  // row_half_mirror: the other half's sum
-    if (ok) {
-      uint8_t* blk = xb + 512 * (int64_t)b + 128 * (g >> 1) + 4 * (g & 1);
-      *reinterpret_cast<uint32_t*>(blk + 8 * (2 * t)) = H;
-      *reinterpret_cast<uint32_t*>(blk + 8 * (2 * t + 1)) = L;
-      if (g == 0) xs[(int64_t)b * kMaxTokens + t] = make_int4(s16, other, __float_as_int(amax / kXMax), 0);
+  for (int k = 0; k < 4; ++k) {
+    int X = __float2int_rn(f[k] * inv);
+    X = max(-32639, min(32639, X));
+    const int hi = (X + 128) >> 8;
+    const int lo = X - (hi << 8);
+    H |= (uint32_t)(hi & 255) << (8 * k);
+    L |= (uint32_t)(lo & 255) << (8 * k);
+    sum += X;
+  }
+  // elements k = 4g..4g+3 of block b (g = lane's place in its group):
+  // B-layout lane n + 16*(k/8), byte k%8, for n = 2t (hi) and 2t + 1 (lo)
+  const int b = e >> 5, gi = (e >> 2) & 7;
+  const int s16 = sum4(sum);            // lanes gi<4: first half, gi>=4: second half
+  const int other = dpp_i<0x141>(s16);  // row_half_mirror: the other half's sum
+  if (ok) {
+    uint8_t* blk = xb + 512 * (int64_t)b + 128 * (gi >> 1) + 4 * (gi & 1);
+    *reinterpret_cast<uint32_t*>(blk + 8 * (2 * t)) = H;
+    *reinterpret_cast<uint32_t*>(blk + 8 * (2 * t + 1)) = L;
+    if (gi == 0) {
+      // column 2t (hi plane) carries no X sums, column 2t + 1 (lo plane)
+      // the block's two halves; the scale once per 256-block
+      xs[(int64_t)b * kMaxTokens + t] = make_int4(0, 0, s16, other);
+      if ((b & 7) == 0) xsc[(int64_t)(b >> 3) * kMaxTokens + t] = amax / kXMax;
     }
   }
 }
@@ -137,6 +145,9 @@ __device__ __forceinline__ ShareM share_m(const JobM& job, int b) {
 // where it sits in that unit.  Wave-uniform (scalar registers).
 struct TSeg {
   const uint8_t* base;  // first byte of row 0's piece
+  const uint8_t* ab;    // its 16-byte aligned start (row strides of whole chunks)
+  uint32_t nrec;        // bytes from ab to the matrix's end (0: a stand-in)
+  uint32_t d;           // offset of the pieces in their first chunk (row strides of whole chunks)
   int64_t rb;
   int fmt, P, piece;    // chunks per piece (worst alignment), bytes per piece
   uint32_t magicP;
@@ -198,7 +209,11 @@ __device__ __forceinline__ TSeg tseg_at(const JobM& job, const ShareM& sh, int u
   sg.nblk = kq ? 8 : min(8, (job.cols - kTS * ts) >> 5);
   sg.piece = kq ? tsb : sg.nblk * block_bytes(sg.fmt);
   sg.lb0 = 8 * lts;
-  sg.base = W + (int64_t)(kTileRows * lt) * sg.rb + (int64_t)ts * tsb;
+  const int64_t r0 = (int64_t)(kTileRows * lt) * sg.rb, o = (int64_t)ts * tsb;
+  sg.base = W + r0 + o;
+  sg.d = (uint32_t)(o & 15);
+  sg.ab = W + r0 + (o & ~(int64_t)15);
+  sg.nrec = (uint32_t)((int64_t)rows * sg.rb - r0 - (o & ~(int64_t)15));
   return sg;
 }
 
@@ -207,6 +222,9 @@ __device__ __forceinline__ TSeg tseg_at(const JobM& job, const ShareM& sh, int u
 __device__ __forceinline__ TSeg tseg_null(const JobM& job) {
   TSeg sg{};
   sg.base = job.W[0];
+  sg.ab = job.W[0];
+  sg.nrec = 0;
+  sg.d = 0;
   sg.rb = 0;
   sg.fmt = job.fmt[0];
   sg.P = 1;
@@ -238,6 +256,46 @@ __device__ __forceinline__ void tseg_load(const TSeg& sg, int lane, uint4 (&pre)
   }
 }
 
+// Matrices whose rows are whole 16-byte chunks apart (job.fast): every tile-
+// slice's row pieces sit at the same offsets from its aligned start, so a
+// lane's LPL chunk offsets (chunk c = lane + 64 i is chunk c % P of row
+// c / P; past 16 P, chunk 0 of row 0) are kept while the matrix geometry
+// (P, row stride) stays, and each tile-slice's loads are raw buffer loads
+// from its aligned start whose range ends at the matrix's end: rows past the
+// matrix read zeros (their results are never stored), a stand-in reads
+// nothing.  The loads are cached (not non-temporal): a row piece (144 bytes
+// of Q4_K, 210 of Q6_K) is not a whole number of 128-byte cache lines, so
+// neighbouring tile-slices of a row share a line, and the wave that reads
+// the next tile-slice a step later finds it in L2 (HBM bytes fetched per
+// weight byte: 1.53 -> 1.16 for Q4_K, 1.58 -> 1.26 for Q6_K).
+template <int LPL>
+struct TLoad {
+  int P = -1;
+  int64_t rb = -1;
+  uint32_t off[LPL];
+};
+
+template <int LPL>
+__device__ __forceinline__ void tseg_load_fast(const TSeg& sg, TLoad<LPL>& tl, int lane, uint4 (&pre)[LPL]) {
+  if (sg.nrec != 0 && (sg.P != tl.P || sg.rb != tl.rb)) {
+    tl.P = sg.P;
+    tl.rb = sg.rb;
+#pragma unroll
+    for (int i = 0; i < LPL; ++i) {
+      const int c = lane + 64 * i;
+      const int r = (int)(((uint32_t)c * sg.magicP) >> 16);
+      const int k = c - r * sg.P;
+      tl.off[i] = r < kTileRows ? (uint32_t)r * (uint32_t)sg.rb + 16u * (uint32_t)k : 0u;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t rs = seg_rsrc(sg.ab, sg.nrec);
+#pragma unroll
+  for (int i = 0; i < LPL; ++i) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)tl.off[i], 0, 0);
+    pre[i] = make_uint4(v.x, v.y, v.z, v.w);
+  }
+}
+
 template <int LPL>
 __device__ __forceinline__ void tseg_store(uint32_t slab, int lane, const uint4 (&pre)[LPL]) {
 #pragma unroll
@@ -246,7 +304,9 @@ __device__ __forceinline__ void tseg_store(uint32_t slab, int lane, const uint4 
 
 // LDS offset of row r's piece data in the slab (rows past the tile re-read
 // the last row: their results are never stored).
+template <bool FAST>
 __device__ __forceinline__ uint32_t piece_off(const TSeg& sg, uint32_t slab, int r) {
+  if constexpr (FAST) return slab + 16u * (uint32_t)(sg.P * r) + sg.d;
   const int rr = min(r, sg.nrow - 1);
   const uint32_t d = (uint32_t)(reinterpret_cast<uintptr_t>(sg.base + (int64_t)rr * sg.rb) & 15);
   return slab + 16u * (uint32_t)(sg.P * r) + d;
@@ -365,12 +425,11 @@ __device__ __forceinline__ int mad24(int a, int b, int c) { return __mul24(a, b)
 // blocks carry their own fp16 d: P = sum_b d_b (C_b - off SX_b), off 8 for
 // Q4_0.  Every bound: |AI| < 2^26 (Q5_K), |MI| < 2^30 (Q6_K, sixteen
 // 16-sums of |X| <= 32639 times |sc| <= 128).
-template <int F, int LPL, bool AL>
+template <int F, int LPL, bool AL, bool FAST>
 __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, uint32_t slab, uint32_t scl, int lane,
                                                float (&acc)[4]) {
   const int kq = lane >> 4, t = (lane & 15) >> 1;
-  const bool lo_lane = lane & 1;
-  const uint32_t po = piece_off(sg, slab, lane & 15);
+  const uint32_t po = piece_off<FAST>(sg, slab, lane & 15);
   const float2 dd = scale_table(sg, po, scl, lane);
   if (sg.first) {
 #pragma unroll
@@ -384,8 +443,9 @@ __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, 
     const int lb = sg.lb0 + kb;
     const long a = a_operand<F, AL>(sg, po, kb, kq);
     const long bo = *reinterpret_cast<const long*>(nt_smem + job.xbl + 512u * (uint32_t)lb + 8u * lane);
-    const int2 sx = *reinterpret_cast<const int2*>(nt_smem + job.xsl + 16u * (uint32_t)(lb * kMaxTokens + t));
-    const int sxa = lo_lane ? sx.x : 0, sxb = lo_lane ? sx.y : 0;  // X sums enter on the lo-plane lane
+    // the X sums of this lane's column: zero on the hi plane, so they enter once
+    const int2 sx = *reinterpret_cast<const int2*>(nt_smem + job.xsl + 8u * (uint32_t)(16 * lb + (lane & 15)));
+    const int sxa = sx.x, sxb = sx.y;
     if constexpr (F == NT_Q6_K) {
       const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? a : 0l, bo, zero, 0, 0, 0);
       const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? 0l : a, bo, zero, 0, 0, 0);
@@ -430,8 +490,7 @@ __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, 
     for (int kb = 0; kb < sg.nblk; ++kb) block(kb);
   }
   // the activation's scale of this 256-block, and the rows' d (dmin)
-  const float s = __int_as_float(
-      *reinterpret_cast<const int*>(nt_smem + job.xsl + 16u * (uint32_t)(sg.lb0 * kMaxTokens + t) + 8u));
+  const float s = ldf(job.xscl + 4u * (uint32_t)((sg.lb0 >> 3) * kMaxTokens + t));
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float P;
@@ -459,7 +518,7 @@ __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, 
   }
 }
 
-template <int LPL>
+template <int LPL, bool FAST>
 __device__ __forceinline__ void tseg_compute(const JobM& job, const TSeg& sg, uint32_t slab, uint32_t scl, int lane,
                                              float (&acc)[4]) {
   // row pieces laid out without alignment slack (the planner's exact P)
@@ -467,15 +526,15 @@ __device__ __forceinline__ void tseg_compute(const JobM& job, const TSeg& sg, ui
   const bool al = sg.P * 16 == sg.piece;
   switch (sg.fmt) {
     case NT_Q4_K:
-      if (al) tseg_compute_f<NT_Q4_K, LPL, true>(job, sg, slab, scl, lane, acc);
-      else tseg_compute_f<NT_Q4_K, LPL, false>(job, sg, slab, scl, lane, acc);
+      if (al) tseg_compute_f<NT_Q4_K, LPL, true, FAST>(job, sg, slab, scl, lane, acc);
+      else tseg_compute_f<NT_Q4_K, LPL, false, FAST>(job, sg, slab, scl, lane, acc);
       break;
-    case NT_Q6_K: tseg_compute_f<NT_Q6_K, LPL, false>(job, sg, slab, scl, lane, acc); break;
-    case NT_Q8_0: tseg_compute_f<NT_Q8_0, LPL, false>(job, sg, slab, scl, lane, acc); break;
-    case NT_Q4_0: tseg_compute_f<NT_Q4_0, LPL, false>(job, sg, slab, scl, lane, acc); break;
+    case NT_Q6_K: tseg_compute_f<NT_Q6_K, LPL, false, FAST>(job, sg, slab, scl, lane, acc); break;
+    case NT_Q8_0: tseg_compute_f<NT_Q8_0, LPL, false, FAST>(job, sg, slab, scl, lane, acc); break;
+    case NT_Q4_0: tseg_compute_f<NT_Q4_0, LPL, false, FAST>(job, sg, slab, scl, lane, acc); break;
     default:
-      if (al) tseg_compute_f<NT_Q5_K, LPL, true>(job, sg, slab, scl, lane, acc);
-      else tseg_compute_f<NT_Q5_K, LPL, false>(job, sg, slab, scl, lane, acc);
+      if (al) tseg_compute_f<NT_Q5_K, LPL, true, FAST>(job, sg, slab, scl, lane, acc);
+      else tseg_compute_f<NT_Q5_K, LPL, false, FAST>(job, sg, slab, scl, lane, acc);
       break;
   }
 }
@@ -527,19 +586,25 @@ __device__ __forceinline__ void ucur_next(const JobM& job, const ShareM& sh, UCu
 // One step: store the tile-slice in `pre`, issue the next one's loads into
 // `pre`, compute the stored one.  A step with nothing to compute only issues
 // stand-in loads: the loop has a single exit (see the GEMV engine).
-template <int LPL>
+template <int LPL, bool FAST>
+__device__ __forceinline__ void tseg_issue(const TSeg& sg, TLoad<LPL>& tl, int lane, uint4 (&pre)[LPL]) {
+  if constexpr (FAST) tseg_load_fast(sg, tl, lane, pre);
+  else tseg_load(sg, lane, pre);
+}
+
+template <int LPL, bool FAST>
 __device__ __forceinline__ void stream_m(const JobM& job, const ShareM& sh, int wave, int lane, uint32_t slab,
                                          uint32_t scl, UCur& ah, float (&acc)[4], uint4 (&pre)[LPL], TSeg& sg,
-                                         bool& cur_valid, bool& nxt_valid) {
+                                         TLoad<LPL>& tl, bool& cur_valid, bool& nxt_valid) {
   const TSeg cur = sg;
   const bool valid = cur_valid;
   tseg_store(slab, lane, pre);
   if (!ah.done && ah.u < 0) ucur_set(job, sh, ah, claim_m(job, lane));  // claim left pending before the barrier
   const bool issue = !ah.done;
   sg = issue ? tseg_at(job, sh, ah.u, ah.j) : tseg_null(job);
-  tseg_load(sg, lane, pre);
+  tseg_issue<LPL, FAST>(sg, tl, lane, pre);
   if (issue) ucur_next(job, sh, ah, wave, lane, true);
-  if (valid) tseg_compute<LPL>(job, cur, slab, scl, lane, acc);
+  if (valid) tseg_compute<LPL, FAST>(job, cur, slab, scl, lane, acc);
   cur_valid = nxt_valid;
   nxt_valid = issue;
 }
@@ -559,7 +624,7 @@ __device__ __forceinline__ int64_t part_row(const JobM& job, const ShareM& sh, i
   return (int64_t)up * job.orows + job.row_base[m] + lr;
 }
 
-template <int LPL>
+template <int LPL, bool FAST>
 __global__ __launch_bounds__(kMaxThreads) void k_qgemm_m(JobM job) {
   const int tid = threadIdx.x, lane = tid & 63, NT = job.nwaves * 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -569,7 +634,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemm_m(JobM job) {
   if (tid == 0) sti32(job.ctl, 0);
   // the range's staged activation (B operands, then records), loaded before
   // any weight so waiting for it does not wait for the weights
-  const int cb = 32 * sh.nb, cr = 8 * sh.nb;  // 16-byte chunks
+  const int cb = 32 * sh.nb, cr = 8 * sh.nb, cs = 2 * ((sh.nb + 7) >> 3);  // 16-byte chunks
   uint4 xa[3];
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
@@ -578,6 +643,9 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemm_m(JobM job) {
     else if (c < cb + cr)
       xa[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(job.xs) + 128 * (int64_t)sh.gb0 +
                                               16 * (c - cb));
+    else if (c < cb + cr + cs)
+      xa[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(job.xsc) + 4 * (int64_t)sh.gb0 +
+                                              16 * (c - cb - cr));
   }
   // two tile-slices in flight before the barrier (static units only)
   UCur ah{};
@@ -585,27 +653,29 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemm_m(JobM job) {
   ucur_set(job, sh, ah, wave);
   uint4 pa[LPL], pb[LPL];
   TSeg sa, sb;
+  TLoad<LPL> tl;
   const bool va = !ah.done;
   sa = va ? tseg_at(job, sh, ah.u, ah.j) : tseg_null(job);
-  tseg_load(sa, lane, pa);
+  tseg_issue<LPL, FAST>(sa, tl, lane, pa);
   if (va) ucur_next(job, sh, ah, wave, lane, false);
   const bool vb = !ah.done && ah.u >= 0;
   sb = vb ? tseg_at(job, sh, ah.u, ah.j) : tseg_null(job);
-  tseg_load(sb, lane, pb);
+  tseg_issue<LPL, FAST>(sb, tl, lane, pb);
   if (vb) ucur_next(job, sh, ah, wave, lane, false);
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
     const int c = tid + NT * i;
     if (c < cb) st128(job.xbl + 16u * c, xa[i]);
     else if (c < cb + cr) st128(job.xsl + 16u * (c - cb), xa[i]);
+    else if (c < cb + cr + cs) st128(job.xscl + 16u * (c - cb - cr), xa[i]);
   }
   __syncthreads();
   if (va) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     bool cur_valid = va, nxt_valid = vb;
     do {
-      stream_m<LPL>(job, sh, wave, lane, slab, scl, ah, acc, pa, sa, cur_valid, nxt_valid);
-      stream_m<LPL>(job, sh, wave, lane, slab, scl, ah, acc, pb, sb, cur_valid, nxt_valid);
+      stream_m<LPL, FAST>(job, sh, wave, lane, slab, scl, ah, acc, pa, sa, tl, cur_valid, nxt_valid);
+      stream_m<LPL, FAST>(job, sh, wave, lane, slab, scl, ah, acc, pb, sb, tl, cur_valid, nxt_valid);
     } while (cur_valid);
   }
   __syncthreads();
@@ -689,17 +759,22 @@ int gemm_cus() {
   return v > 0 ? v : 256;
 }
 
-template <int LPL>
-int launch_m_lpl(const JobM& job, hipStream_t stream) {
+template <int LPL, bool FAST>
+int launch_m_kernel(const JobM& job, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_qgemm_m<LPL>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
-        hipSuccess)
+    if (hipFuncSetAttribute((const void*)k_qgemm_m<LPL, FAST>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024) != hipSuccess)
       return NT_EHIP;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_qgemm_m<LPL>), dim3(job.grid), dim3(64 * job.nwaves), job.lds_bytes, stream, job);
+  hipLaunchKernelGGL((k_qgemm_m<LPL, FAST>), dim3(job.grid), dim3(64 * job.nwaves), job.lds_bytes, stream, job);
   return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
+}
+
+template <int LPL>
+int launch_m_lpl(const JobM& job, hipStream_t stream) {
+  return job.fast ? launch_m_kernel<LPL, true>(job, stream) : launch_m_kernel<LPL, false>(job, stream);
 }
 
 template <int EPI>
@@ -716,7 +791,7 @@ int launch_reduce(const JobM& job, const ProArgs& pro, const EpiArgs& ea, hipStr
 
 size_t stage_m_bytes(int cols) {
   const size_t nb = (size_t)(cols + 31) / 32;
-  return nb * 512 + nb * kMaxTokens * 16;
+  return nb * 512 + nb * kMaxTokens * 16 + (nb + 7) / 8 * kMaxTokens * 4;
 }
 
 // Column ranges of a launch: as few as the per-workgroup LDS allows.
@@ -736,9 +811,12 @@ size_t part_m_bytes(int64_t orows, int paired, int cols, int M) {
 int launch_stage_m(const float* src, int64_t stride, const float* gain, float eps, int M, int cols, void* stage,
                    hipStream_t stream) {
   if (M < 1 || M > kMaxTokens || cols <= 0 || cols % 32) return NT_EINVAL;
+  const size_t nb = (size_t)cols / 32;
   uint8_t* xb = static_cast<uint8_t*>(stage);
-  int4* xs = reinterpret_cast<int4*>(xb + (size_t)(cols / 32) * 512);
-  hipLaunchKernelGGL(k_stage_m, dim3(M), dim3(kStageThreads), 0, stream, src, stride, gain, eps, cols, xb, xs);
+  int4* xs = reinterpret_cast<int4*>(xb + nb * 512);
+  float* xsc = reinterpret_cast<float*>(xb + nb * 512 + nb * kMaxTokens * 16);
+  const dim3 grid((unsigned)((cols + 4 * kStageThreads - 1) / (4 * kStageThreads)), (unsigned)M);
+  hipLaunchKernelGGL(k_stage_m, grid, dim3(kStageThreads), 0, stream, src, stride, gain, eps, cols, xb, xs, xsc);
   return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
 }
 
@@ -784,6 +862,14 @@ int plan_job_m(JobM& job, int nmat, const uint8_t* const* W, const int* fmt, con
     }
   }
   job.tile_base[nmat] = (int)otiles;
+  // rows whole 16-byte chunks apart (and each matrix under 4 GB, the reach
+  // of a buffer load's offset): the kernel's fixed-offset tile loads
+  job.fast = 1;
+  for (int m = 0; m < nmat; ++m) {
+    if (job.rb[m] % 16 != 0 || (reinterpret_cast<uintptr_t>(W[m]) & 15) != 0 ||
+        (int64_t)rows[m] * job.rb[m] >= ((int64_t)1 << 32))
+      job.fast = 0;
+  }
   if (lpl > kSlabLoads) return NT_EUNSUPPORTED;
   if (orows > INT32_MAX / 16) return NT_EUNSUPPORTED;
   job.lpl = lpl;
@@ -817,6 +903,7 @@ int plan_job_m(JobM& job, int nmat, const uint8_t* const* W, const int* fmt, con
   job.ctl = off; off += 16;
   job.xbl = off; off += (uint32_t)(8 * job.tsper * 512);
   job.xsl = off; off += (uint32_t)(8 * job.tsper * kMaxTokens * 16);
+  job.xscl = off; off += (uint32_t)(job.tsper * kMaxTokens * 4);
   job.acc = off; off += (uint32_t)(nvt * kTileRows * job.nsub * M * 4);
   off = (off + 15) & ~15u;
   job.scl = off; off += (uint32_t)job.nwaves * 1024u;  // per wave: 16 entries x 16 rows x alpha (Q4_K: 8 x 16 x pairs)
@@ -831,6 +918,7 @@ int launch_gemm_m(JobM& job, const void* stage, void* part, const ProArgs& pro, 
   if (job.otiles <= 0) return NT_OK;
   job.xb = static_cast<const uint8_t*>(stage);
   job.xs = reinterpret_cast<const int4*>(job.xb + (size_t)(job.cols / 32) * 512);
+  job.xsc = reinterpret_cast<const float*>(job.xb + (size_t)(job.cols / 32) * (512 + kMaxTokens * 16));
   job.part = static_cast<float*>(part);
   int rc = NT_EUNSUPPORTED;
   switch (job.lpl) {

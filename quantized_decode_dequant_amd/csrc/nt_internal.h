@@ -205,6 +205,7 @@ struct JobM {
   int P[kMaxMats];            // 16-B chunks per row piece (worst alignment)
   uint32_t magicP[kMaxMats];  // ceil(65536 / P): chunk -> row by a multiply
   int nmat, paired, pairs, cols, M;
+  int fast;                   // every matrix's rows are whole 16-byte chunks apart (fixed-offset tile loads)
   int orows;                  // output rows (paired: of each matrix)
   int nts;                    // tile-slices per row
   int tsper, nsup;            // tile-slices per column range, column ranges
@@ -215,10 +216,12 @@ struct JobM {
   uint32_t magicV[2];         // floor((2^32-1)/nvt) for the two tile counts of a workgroup
   int nwaves, grid, lpl;
   const uint8_t* xb;          // staged activation in MFMA B layout [cols/32][64 lanes][8 B]
-  const int4* xs;             // [cols/32][8 tokens]: sum(X first 16), sum(X last 16), s of its 256-block (f32 bits), 0
+  const int4* xs;             // [cols/32][8 tokens]: per B column (hi plane, lo plane) the X sums of the
+                              // block's two halves (zero on the hi plane)
+  const float* xsc;           // [cols/256][8 tokens]: scale s of each 256-block
   float* part;                // partial sums [nsup][M][ldp]
   int64_t ldp;                // (paired ? 2 : 1) * orows
-  uint32_t xbl, xsl, slab, scl, acc, ctl, lds_bytes;
+  uint32_t xbl, xsl, xscl, slab, scl, acc, ctl, lds_bytes;
 };
 
 int plan_job_m(JobM& job, int nmat, const uint8_t* const* W, const int* fmt, const int* rows, int cols, int paired,
