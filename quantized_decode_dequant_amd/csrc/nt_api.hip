@@ -175,10 +175,12 @@ int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const
 }
 
 // Up to this many tokens a layer runs the GEMV engine once per token rather
-// than the small-M GEMM: at two tokens two streaming passes take less time
-// than one pass whose per-(row, block, token) scale work is on the vector ALU
-// (70B-shaped gate matrix: 2 x 30.4 us against 87.4 us).  For the LM head,
-// whose single launch is long, the engine wins up to three tokens.
+// than the small-M GEMM: at two tokens two streaming passes of the 70B-shaped
+// gate matrix take about as long as one small-M pass (2 x 28.4 against
+// 54.7 us), the engine's fused gate/up launch streams both matrices for one
+// token in 46.3 us, and the two tokens come out bitwise as two decode steps.
+// For the LM head, whose single launch is long, the engine wins up to three
+// tokens.
 constexpr int kEngineLayerTokens = 2;
 constexpr int kEngineHeadTokens = 3;
 
