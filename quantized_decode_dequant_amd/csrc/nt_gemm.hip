@@ -272,7 +272,7 @@ template <int LPL>
 struct TLoad {
   int P = -1;
   int64_t rb = -1;
-  uint32_t off[LPL];
+  uint32_t off[LPL] = {};
 };
 
 template <int LPL>
