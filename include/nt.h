@@ -372,7 +372,9 @@ int nt_spec_step(const nt_model* model, const uint8_t* draft_skip, int K, int32_
  * and down projections), 2 QKV + RoPE + KV append, 3 gate/up + SwiGLU,
  * 4 attention (the first split launch's start to the combine's end).
  * nt_trace_begin_every(kind, k) records only launches 0, k, 2k, ... of the
- * kind (k >= 1).  Tracing is per process and not thread safe.
+ * kind (k >= 1).  Tracing is per process and not thread safe, and is for
+ * eager launches: a traced launch made under HIP stream capture is not
+ * supported (end tracing before capturing).
  */
 typedef enum nt_trace_kind {
   NT_TRACE_GEMV = 0,

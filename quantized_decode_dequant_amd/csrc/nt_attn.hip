@@ -39,8 +39,11 @@ template <int HD>
 constexpr int attn_waves() { return 4; }
 
 // q: fp32 [n_query][n_head][HD] (query i at position pos+i attends to
-// 0..pos+i).  Partials: part_o [n_query][nsplit][n_head][HD],
-// part_ml [n_query][nsplit][n_head][2].
+// 0..pos+i).  Workgroup (g, s, i) takes split s of kv head g for query i:
+// one launch covers every query of a verify pass, and the queries' reads of
+// one K/V tile run at the same time (the later ones find it in the caches).
+// Partials: part_o [n_query][nsplit][n_head][HD], part_ml
+// [n_query][nsplit][n_head][2].
 //
 // Both products run on v_mfma_f32_16x16x32_f16 with the group's query heads
 // as the 16 rows (rows past the group are zero).  K and V are f16 in the
@@ -60,7 +63,7 @@ constexpr int attn_waves() { return 4; }
 template <int HD>
 __global__ __launch_bounds__(64 * attn_waves<HD>()) void k_attn_split(
     const float* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const int32_t* pos_ptr, int query, int n_head, int n_kv, int max_ctx, int nsplit, float* __restrict__ part_o,
+    const int32_t* pos_ptr, int n_head, int n_kv, int max_ctx, int nsplit, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
   constexpr int C = attn_chunk<HD>();
   constexpr int NW = attn_waves<HD>();           // waves per workgroup
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(64 * attn_waves<HD>()) void k_attn_split(
   __shared__ float s_m[kMaxGroup], s_l[kMaxGroup];
   __shared__ v4f s_red[KSPLIT > 1 ? NTT * 64 : 1];
 
-  const int g = blockIdx.x, split = blockIdx.y;
+  const int g = blockIdx.x, split = blockIdx.y, query = blockIdx.z;
   const int G = n_head / n_kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
@@ -471,27 +474,23 @@ void attn_plan(int head_dim, int max_ctx, int& chunk, int& nsplit) {
 int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, const int32_t* pos, int n_query,
                      int n_head, int n_kv, int head_dim, int max_ctx, int chunk, int nsplit, float* part_o,
                      float* part_ml, float* o, uint8_t* qx_o, hipStream_t stream) {
-  // traced: the interval from the first split launch's start to the
-  // combine's end
+  // traced: the interval from the split launch's start to the combine's end
   hipEvent_t t0, t1;
   (void)trace_events(NT_TRACE_ATTN, &t0, &t1);
-  for (int qi = 0; qi < n_query; ++qi) {
-    const dim3 grid(n_kv, nsplit);
-    hipEvent_t ts = qi == 0 ? t0 : nullptr;
+  const dim3 grid(n_kv, nsplit, n_query);
 #define NT_ATTN_CASE(HD)                                                                                      \
   case HD:                                                                                                    \
-    hipExtLaunchKernelGGL(k_attn_split<HD>, grid, dim3(64 * attn_waves<HD>()), 0, stream, ts, nullptr, 0, q, kc, vc, \
-                          pos, qi, n_head, n_kv, max_ctx, nsplit, part_o, part_ml);                          \
+    hipExtLaunchKernelGGL(k_attn_split<HD>, grid, dim3(64 * attn_waves<HD>()), 0, stream, t0, nullptr, 0, q, kc, vc, \
+                          pos, n_head, n_kv, max_ctx, nsplit, part_o, part_ml);                              \
     break;
-    switch (head_dim) {
-      NT_ATTN_CASE(32)
-      NT_ATTN_CASE(64)
-      NT_ATTN_CASE(128)
-      NT_ATTN_CASE(256)
-      default: return NT_EUNSUPPORTED;
-    }
-#undef NT_ATTN_CASE
+  switch (head_dim) {
+    NT_ATTN_CASE(32)
+    NT_ATTN_CASE(64)
+    NT_ATTN_CASE(128)
+    NT_ATTN_CASE(256)
+    default: return NT_EUNSUPPORTED;
   }
+#undef NT_ATTN_CASE
   hipExtLaunchKernelGGL(k_attn_combine, dim3(n_head * (head_dim / 32), n_query), dim3(256), 0, stream, nullptr, t1, 0,
                         part_o, part_ml, pos, n_head, head_dim, chunk, nsplit, max_ctx, o, qx_o);
   return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;

@@ -632,7 +632,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemm_m(JobM job) {
   const uint32_t slab = job.slab + (uint32_t)wave * (uint32_t)(LPL * 1024);
   const uint32_t scl = job.scl + (uint32_t)wave * 1024u;
   if (tid == 0) sti32(job.ctl, 0);
-  // the range's staged activation (B operands, then records), loaded before
+  // the range's staged activation (B operands, X sums, scales), loaded before
   // any weight so waiting for it does not wait for the weights
   const int cb = 32 * sh.nb, cr = 8 * sh.nb, cs = 2 * ((sh.nb + 7) >> 3);  // 16-byte chunks
   uint4 xa[3];

@@ -226,7 +226,7 @@ struct JobM {
 
 int plan_job_m(JobM& job, int nmat, const uint8_t* const* W, const int* fmt, const int* rows, int cols, int paired,
                int pairs, int M);
-size_t stage_m_bytes(int cols);          // bytes of the staged activation (B layout + records)
+size_t stage_m_bytes(int cols);          // bytes of the staged activation (B layout, X sums, scales)
 // Bytes of the partial sums of a launch over `orows` output rows (paired: of
 // each matrix) and `cols` columns; independent of the device.
 size_t part_m_bytes(int64_t orows, int paired, int cols, int M);
