@@ -399,13 +399,15 @@ __device__ __forceinline__ long a_operand(const TSeg& sg, uint32_t po, int kb, i
                    ((v[1] >> sh) & 0x0F0F0F0Fu) | (((h[1] >> kb) & 0x01010101u) << 4));
     }
     default: {  // Q6_K: elements 32 kb + 8 kq .. +7: half n, quarter q'
+      // as the signed bytes q - 32 = ql + 16 (qh - 2): the high nibble is
+      // (qh + 14) mod 16 (no carry leaves a byte: qh + 14 <= 17)
       const int n = kb >> 2, qq = kb & 3;
       uint32_t h[2];
       ld_unaligned<2>(po + 64 * n + 32 * (qq & 1) + 8 * kq, v);
       ld_unaligned<2>(po + 128 + 32 * n + 8 * kq, h);
       const int sl = 4 * (qq >> 1), shh = 2 * qq;
-      const uint32_t a0 = ((v[0] >> sl) & 0x0F0F0F0Fu) | (((h[0] >> shh) & 0x03030303u) << 4);
-      const uint32_t a1 = ((v[1] >> sl) & 0x0F0F0F0Fu) | (((h[1] >> shh) & 0x03030303u) << 4);
+      const uint32_t a0 = ((v[0] >> sl) & 0x0F0F0F0Fu) | ((((h[0] >> shh) & 0x03030303u) + 0x0E0E0E0Eu) & 0x0F0F0F0Fu) << 4;
+      const uint32_t a1 = ((v[1] >> sl) & 0x0F0F0F0Fu) | ((((h[1] >> shh) & 0x03030303u) + 0x0E0E0E0Eu) & 0x0F0F0F0Fu) << 4;
       return pack2(a0, a1);
     }
   }
@@ -421,10 +423,12 @@ __device__ __forceinline__ int mad24(int a, int b, int c) { return __mul24(a, b)
 // q X in this lane's plane) and, on the lo-plane lane only, MI = sum_j m_j
 // SX_j (SX_j the sub-block's sum of X); with X = 256 hi + lo the
 // superblock's contribution is s (256 P_hi + P_lo), P = d AI - dmin MI
-// (Q6_K: d (AI - 32 MI) with the signed 16-weight scales).  Q8_0 / Q4_0
-// blocks carry their own fp16 d: P = sum_b d_b (C_b - off SX_b), off 8 for
-// Q4_0.  Every bound: |AI| < 2^26 (Q5_K), |MI| < 2^30 (Q6_K, sixteen
-// 16-sums of |X| <= 32639 times |sc| <= 128).
+// (Q6_K: P = d AI with the signed 16-weight scales, its quants entering the
+// MFMA as q - 32).  Q8_0 / Q4_0 blocks carry their own fp16 d: P = sum_b d_b
+// (C_b - off SX_b), off 8 for Q4_0.  Every bound: |AI| < 2^27 (Q6_K: 16
+// groups of |sc| <= 128 times 16 products |q - 32| |plane| <= 32 x 128),
+// |MI| < 2^30 (eight 32-sums of |X| <= 32639 times m <= 63); every factor
+// of a 24-bit multiply-add fits 24 bits.
 template <int F, int LPL, bool AL, bool FAST>
 __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, uint32_t slab, uint32_t scl, int lane,
                                                float (&acc)[4]) {
@@ -447,16 +451,14 @@ __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, 
     const int2 sx = *reinterpret_cast<const int2*>(nt_smem + job.xsl + 8u * (uint32_t)(16 * lb + (lane & 15)));
     const int sxa = sx.x, sxb = sx.y;
     if constexpr (F == NT_Q6_K) {
+      // the quants enter as q - 32, so the offset is inside the exact sums
       const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? a : 0l, bo, zero, 0, 0, 0);
       const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? 0l : a, bo, zero, 0, 0, 0);
       const int4 g0 = *reinterpret_cast<const int4*>(nt_smem + scl + 4u * (uint32_t)(16 * (2 * kb) + 4 * kq));
       const int4 g1 = *reinterpret_cast<const int4*>(nt_smem + scl + 4u * (uint32_t)(16 * (2 * kb + 1) + 4 * kq));
       const int s0[4] = {g0.x, g0.y, g0.z, g0.w}, s1[4] = {g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ai[j] = mad24(s1[j], c1[j], mad24(s0[j], c0[j], ai[j]));
-        mi[j] = mad24(s1[j], sxb, mad24(s0[j], sxa, mi[j]));
-      }
+      for (int j = 0; j < 4; ++j) ai[j] = mad24(s1[j], c1[j], mad24(s0[j], c0[j], ai[j]));
     } else if constexpr (kq_fmt) {
       const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bo, zero, 0, 0, 0);
       const uint32_t e = scl + 8u * (uint32_t)(16 * kb + 4 * kq);
@@ -498,7 +500,7 @@ __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, 
       const int src = 4 * (4 * kq + j);  // a lane holding row 4 kq + j in scale_table
       const float d = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(dd.x)));
       if constexpr (F == NT_Q6_K) {
-        P = d * ((float)ai[j] - 32.f * (float)mi[j]);
+        P = d * (float)ai[j];
       } else {
         const float dmin = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(dd.y)));
         P = d * (float)ai[j] - dmin * (float)mi[j];
