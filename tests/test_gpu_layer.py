@@ -202,3 +202,37 @@ def test_layer_argument_errors():
     with pytest.raises(nt.NtError) as e:
         nt.decode_layer(cfg, dl.struct, xd, 9, pos, torch.zeros(need, dtype=torch.uint8, device=device()))
     assert e.value.status == -1
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_layer_attention_trace_one_interval_per_call(M):
+    # the attention of a layer call is one split launch over all M queries
+    # and one combine; the trace records one interval per call, from the
+    # split's start to the combine's end, and the traced calls give the
+    # untraced result
+    import torch
+    import quantized_decode_dequant_amd as nt
+    from quantized_decode_dequant_amd.model import DeviceLayer, cfg_of
+    shape, max_ctx, n_past = GROUP8, 512, 300
+    li = wl.gen_layer(shape, wl.Q4_K_M, wl.W_TEST, 9, max_ctx, n_past)
+    dl = DeviceLayer(li, device())
+    cfg = cfg_of(shape, max_ctx)
+    x0 = to_dev(np.stack([wl.gen_x(shape.hidden, wl.W_TEST, 9, 400 + i) for i in range(M)]).astype(np.float32)
+                .reshape(-1))
+    pos = torch.tensor([n_past], dtype=torch.int32, device=device())
+    ws = torch.zeros(nt.layer_workspace_bytes(cfg, M), dtype=torch.uint8, device=device())
+    outs = []
+    for traced in (False, True, False):
+        xd = x0.clone()
+        if traced:
+            nt.trace_begin(nt.TRACE_ATTN)
+        for _ in range(2):
+            xd.copy_(x0)
+            nt.decode_layer(cfg, dl.struct, xd, M, pos, ws)
+        torch.cuda.synchronize()
+        if traced:
+            n, ms = nt.trace_end()
+            say(f"  M={M}: {n} attention intervals, {ms * 1e3 / max(n, 1):.2f} us each")
+            assert n == 2 and ms > 0.0
+        outs.append(xd.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
