@@ -236,3 +236,14 @@ def test_layer_attention_trace_one_interval_per_call(M):
             assert n == 2 and ms > 0.0
         outs.append(xd.cpu().numpy())
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("name,n_past", [("hd64_g2", 120), ("hd128_g1", 56), ("hd32_g8", 248)])
+def test_layer_verify_eight_tokens_fill_the_cache(name, n_past):
+    # eight tokens in one pass whose last position is the cache's last
+    # (pos + 7 = max_ctx - 1): one attention launch covers the eight queries,
+    # each with its own causal end, and the cache's last split holds the new
+    # tokens only
+    max_ctx = n_past + 8
+    got, ref, kc, vc, li = run_layer(ATTN_SHAPES[name], wl.ALL_Q8_0, wl.W_TEST, 13, max_ctx, n_past, 8)
+    check(got, ref, kc, vc, li, n_past, 8)
