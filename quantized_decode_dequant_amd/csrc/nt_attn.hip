@@ -6,11 +6,12 @@
 // g = h / (n_head / n_kv), scores s_t = q_h . K_g[t] / sqrt(head_dim) over
 // t = 0..n_pos-1, p = softmax(s), o_h = sum_t p_t V_g[t].
 //
-// Split over positions: workgroup (g, s) takes positions [s*chunk,
-// (s+1)*chunk) of kv head g for all query heads of the group, so every K/V
-// byte is read once.  It writes an unnormalised partial (running max m,
-// sum l, sum p*v) per head; attn_combine merges the splits.  The two
-// products of a split run on f16 matrix cores (k_attn_split below).
+// Split over positions: workgroup (g, s) of a query takes positions
+// [s*chunk, (s+1)*chunk) of kv head g for all query heads of the group, so
+// every K/V byte is read once per query.  It writes an unnormalised partial
+// (running max m, sum l, sum p*v) per head; k_attn_combine merges the
+// splits.  The two products of a split run on f16 matrix cores
+// (k_attn_split below).
 
 #include <float.h>
 

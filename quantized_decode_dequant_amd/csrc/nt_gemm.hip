@@ -303,7 +303,8 @@ __device__ __forceinline__ void tseg_store(uint32_t slab, int lane, const uint4 
 }
 
 // LDS offset of row r's piece data in the slab (rows past the tile re-read
-// the last row: their results are never stored).
+// the last row, or with fixed-offset loads hold zeros: their results are
+// never stored).
 template <bool FAST>
 __device__ __forceinline__ uint32_t piece_off(const TSeg& sg, uint32_t slab, int r) {
   if constexpr (FAST) return slab + 16u * (uint32_t)(sg.P * r) + sg.d;
