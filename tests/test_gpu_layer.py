@@ -136,6 +136,14 @@ def test_layer_8b_q4_0_full():
     check(got, ref, kc, vc, li, 512, 1)
 
 
+@pytest.mark.parametrize("M", [1, 4])
+def test_layer_8b_q8_0_full(M):
+    # a layer of the 8B-shaped Q8_0 stack the 8B decode workload times, from
+    # its first position (512 cached), one token and a four-token verify pass
+    got, ref, kc, vc, li = run_layer(wl.LLAMA8B, wl.ALL_Q8_0, wl.W_LAYER_8B, 5, 520, 512, M)
+    check(got, ref, kc, vc, li, 512, M)
+
+
 def test_layer_70b_q4_k_m_full():
     # Llama-70B-shaped layer in the Q4_K_M mix, 4096 cached positions
     got, ref, kc, vc, li = run_layer(wl.LLAMA70B, wl.Q4_K_M, wl.W_GEMV_70B, 0, 4104, 4096, 1)
