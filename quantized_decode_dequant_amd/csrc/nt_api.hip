@@ -175,14 +175,23 @@ int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const
 }
 
 // Up to this many tokens a layer runs the GEMV engine once per token rather
-// than the small-M GEMM: at two tokens two streaming passes of the 70B-shaped
-// gate matrix take about as long as one small-M pass (2 x 28.4 against
-// 54.7 us), the engine's fused gate/up launch streams both matrices for one
-// token in 46.3 us, and the two tokens come out bitwise as two decode steps.
-// For the LM head, whose single launch is long, the engine wins up to three
-// tokens.
+// than the small-M GEMM (the two tokens then come out bitwise as two decode
+// steps), unless its matrices are all Q4_K / Q6_K: the small-M GEMM's paired
+// and split forms for up to four tokens read the 70B-shaped Q4_K gate in
+// ~44 us and the Q6_K down in ~56 us for every token at once, against 2 x
+// 28.4 and 2 x 38 us for two engine passes.  For the LM head, whose single
+// launch is long, the engine wins up to three tokens.
 constexpr int kEngineLayerTokens = 2;
 constexpr int kEngineHeadTokens = 3;
+
+bool small_m_layer(const nt_layer& L, int M) {
+  if (M > kEngineLayerTokens) return true;
+  if (M < 2) return false;
+  const nt_qmat* mats[7] = {&L.wq, &L.wk, &L.wv, &L.wo, &L.wg, &L.wu, &L.wd};
+  for (const nt_qmat* q : mats)
+    if (q->fmt != NT_Q4_K && q->fmt != NT_Q6_K) return false;
+  return true;
+}
 
 // How a layer hands its input and output on as quantized activations
 // (qx_bytes(hidden) per token).
@@ -197,7 +206,7 @@ struct LayerQx {
 int run_layer(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const int32_t* pos, uint8_t* ws,
               const LayerWs& w, hipStream_t st, LayerQx* lq = nullptr) {
   if (lq) lq->x_out_written = false;
-  if (M > kEngineLayerTokens) return run_layer_m(c, L, x, M, pos, ws, w, st);
+  if (small_m_layer(L, M)) return run_layer_m(c, L, x, M, pos, ws, w, st);
   const int nq = c.n_head * c.head_dim, nkv = c.n_kv_head * c.head_dim;
   float* q = reinterpret_cast<float*>(ws + w.q);
   float* part_o = reinterpret_cast<float*>(ws + w.part_o);
@@ -462,7 +471,8 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
   // as a quantized activation (times that launch's RMSNorm gains) where the
   // layers run the GEMV engine: the embedding to the first layer, each
   // layer's down projection to the next layer that runs, the last one to the
-  // LM head.
+  // LM head (a layer that runs the small-M GEMM breaks the chain: the next
+  // launch reads the fp32 stream).
   const bool qx_step = M <= kEngineLayerTokens && qx_ok(m.cfg.hidden);
   uint8_t* qx_x = ws + w.qx_x;
   auto gain_after = [&](int l) {  // the gains of the first launch after layer l that normalizes

@@ -17,6 +17,9 @@
 //             y += alpha_r * (s S) - beta_r * (s sum X), where alpha and beta
 //             are the row's scale and offset for that block in its format
 //             (Q6_K: per 16-weight half, two MFMAs with the other half zeroed).
+//             Up to four tokens fill only columns 0..7; over Q4_K and Q6_K
+//             one v_mfma_i32_16x16x64_i8 then takes two 32-blocks, the second
+//             block's activations in columns 8..15 (the paired form).
 //   stream    A wave streams tile-slices (16 rows x 256 columns: 16 row
 //             pieces) HBM -> registers -> its LDS slab with non-temporal
 //             16-byte loads, two in flight, as the GEMV engine streams
@@ -29,7 +32,10 @@
 //
 // MFMA operand layout (measured on gfx950): A[i][k] in lane i + 16*(k/8),
 // byte k%8; B[k][n] in lane n + 16*(k/8), byte k%8; C[i][n] in lane
-// n + 16*(i/4), element i%4.
+// n + 16*(i/4), element i%4.  v_mfma_i32_16x16x64_i8: 16 bytes per lane,
+// A[i][k] in lane i + 16*(k/16), B[k][n] in lane n + 16*(k/16), byte k%16
+// (any order of the k slots that is the same in both operands gives the
+// same product); C as above.
 
 #include <algorithm>
 
@@ -430,7 +436,26 @@ __device__ __forceinline__ int mad24(int a, int b, int c) { return __mul24(a, b)
 // groups of |sc| <= 128 times 16 products |q - 32| |plane| <= 32 x 128),
 // |MI| < 2^30 (eight 32-sums of |X| <= 32639 times m <= 63); every factor
 // of a 24-bit multiply-add fits 24 bits.
-template <int F, int LPL, bool AL, bool FAST>
+//
+// BM 1 (up to four tokens, Q4_K): one v_mfma_i32_16x16x64_i8 covers
+// the adjacent 32-blocks 2p and 2p + 1.  Lane group g = lane / 16 carries 16
+// weights of block 2p + g / 2 (weights 16 (g % 2) .. + 15) in A and the same
+// 16 activations in B, and the B tile (laid out by the prologue) holds block
+// 2p's activations in columns 0..7 and block 2p + 1's in columns 8..15, zero
+// elsewhere.  Column n of the product then sums block 2p + n / 8 alone, so
+// the 16x16x32 form's empty columns (tokens 4..7) carry the second block:
+// half the MFMAs and half the per-block scale work.  The two column halves
+// of a token are added (integers, exact) before the row scales.  A Q6_K
+// matrix of such a launch keeps the 16x16x32 form (its 16-weight scales
+// would need two MFMAs per pair, and the pair form measured slower) and
+// reads its B operand out of the paired tiles.
+//
+// BM 2 (up to four tokens, Q6_K alone): split B tiles of one 32-block, its
+// activations 0..15 in columns 0..7 and 16..31 in columns 8..15, zero
+// elsewhere: one v_mfma_i32_16x16x32_i8 per block gives both 16-weight
+// groups' sums (column n: group 2 kb + n / 8), instead of two MFMAs with
+// half of A zeroed; the halves are added as above.
+template <int F, int LPL, bool AL, bool FAST, int BM = 0>
 __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, uint32_t slab, uint32_t scl, int lane,
                                                float (&acc)[4]) {
   const int kq = lane >> 4, t = (lane & 15) >> 1;
@@ -444,14 +469,29 @@ __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, 
   constexpr bool kq_fmt = F == NT_Q4_K || F == NT_Q5_K || F == NT_Q6_K;
   int ai[4] = {0, 0, 0, 0}, mi[4] = {0, 0, 0, 0};
   float af[4] = {0.f, 0.f, 0.f, 0.f};
+  const int hb = (lane >> 3) & 1;  // paired and split B tiles: this lane's column half
   auto block = [&](int kb) {
     const int lb = sg.lb0 + kb;
     const long a = a_operand<F, AL>(sg, po, kb, kq);
-    const long bo = *reinterpret_cast<const long*>(nt_smem + job.xbl + 512u * (uint32_t)lb + 8u * lane);
+    // with the paired B tiles (BM 1, a Q6_K matrix in a launch with Q4_K
+    // ones) this lane's 8 activations of column lane % 8 (columns 8..15
+    // repeat 0..7: tokens past four, never stored)
+    const uint32_t boa = BM == 1 ? job.xbl + 512u * (uint32_t)lb + 128u * (uint32_t)(lb & 1) + 16u * (uint32_t)(lane & 7) +
+                                  256u * (uint32_t)(kq >> 1) + 8u * (uint32_t)(kq & 1)
+                            : job.xbl + 512u * (uint32_t)lb + 8u * lane;
+    const long bo = *reinterpret_cast<const long*>(nt_smem + boa);
     // the X sums of this lane's column: zero on the hi plane, so they enter once
     const int2 sx = *reinterpret_cast<const int2*>(nt_smem + job.xsl + 8u * (uint32_t)(16 * lb + (lane & 15)));
     const int sxa = sx.x, sxb = sx.y;
-    if constexpr (F == NT_Q6_K) {
+    if constexpr (F == NT_Q6_K && BM == 2) {
+      // split B tile: column n sees the block's weights 16 (n / 8) .. + 15
+      // alone, the 16-weight group 2 kb + n / 8
+      const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bo, zero, 0, 0, 0);
+      const int4 g = *reinterpret_cast<const int4*>(nt_smem + scl + 4u * (uint32_t)(16 * (2 * kb + hb) + 4 * kq));
+      const int s0[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ai[j] = mad24(s0[j], c[j], ai[j]);
+    } else if constexpr (F == NT_Q6_K) {
       // the quants enter as q - 32, so the offset is inside the exact sums
       const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? a : 0l, bo, zero, 0, 0, 0);
       const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? 0l : a, bo, zero, 0, 0, 0);
@@ -481,9 +521,47 @@ __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, 
       for (int j = 0; j < 4; ++j) af[j] = fmaf(d[j], (float)(c[j] - off), af[j]);
     }
   };
-  if (sg.nblk == kTS / 32) {
+  if constexpr (BM == 1 && F == NT_Q4_K) {
+    const uint32_t xq = job.xbl + 512u * (uint32_t)sg.lb0 + 16u * (uint32_t)lane;
+    const uint32_t xsa = job.xsl + 8u * (uint32_t)(16 * (sg.lb0 + hb) + (lane & 7));
+    // pairs UP at a time (more spill)
+    constexpr int UP = 2;
+#pragma unroll 1
+    for (int pp = 0; pp < kTS / 64 / UP; ++pp) {
+#pragma unroll
+      for (int ph = 0; ph < UP; ++ph) {
+        const int p = UP * pp + ph;
+        const uint4 b4 = *reinterpret_cast<const uint4*>(nt_smem + xq + 1024u * p);
+        const v4i b = {(int)b4.x, (int)b4.y, (int)b4.z, (int)b4.w};
+        // qs bytes 16 (g % 2) .. + 15 of the pair's 32: block 2p in the low
+        // nibbles, 2p + 1 in the high
+        uint32_t v[4];
+        if constexpr (AL) {
+          const uint4 w = *reinterpret_cast<const uint4*>(nt_smem + po + 16u + 32u * p + 16u * (kq & 1));
+          v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+        } else {
+          ld_unaligned<4>(po + 16u + 32u * p + 16u * (kq & 1), v);
+        }
+        const int sh = 4 * (kq >> 1);
+        const v4i a = {(int)((v[0] >> sh) & 0x0F0F0F0Fu), (int)((v[1] >> sh) & 0x0F0F0F0Fu),
+                       (int)((v[2] >> sh) & 0x0F0F0F0Fu), (int)((v[3] >> sh) & 0x0F0F0F0Fu)};
+        const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, zero, 0, 0, 0);
+        const int2 sx = *reinterpret_cast<const int2*>(nt_smem + xsa + 256u * p);
+        const uint32_t e = scl + 8u * (uint32_t)(16 * (2 * p + hb) + 4 * kq);
+        const int4 p0 = *reinterpret_cast<const int4*>(nt_smem + e);
+        const int4 p1 = *reinterpret_cast<const int4*>(nt_smem + e + 16);
+        const int sc[4] = {p0.x, p0.z, p1.x, p1.z}, m[4] = {p0.y, p0.w, p1.y, p1.w};
+        const int sxs = sx.x + sx.y;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ai[j] = mad24(sc[j], c[j], ai[j]);
+          mi[j] = mad24(m[j], sxs, mi[j]);
+        }
+      }
+    }
+  } else if (sg.nblk == kTS / 32) {
     // blocks unrolled U at a time (more spill)
-    constexpr int U = LPL >= 5 ? 1 : (F == NT_Q6_K ? 2 : 4);
+    constexpr int U = LPL >= 5 ? 1 : (F == NT_Q6_K && BM != 2 ? 2 : 4);
 #pragma unroll 1
     for (int h = 0; h < kTS / 32; h += U) {
 #pragma unroll
@@ -491,6 +569,14 @@ __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, 
     }
   } else {
     for (int kb = 0; kb < sg.nblk; ++kb) block(kb);
+  }
+  if constexpr ((F == NT_Q4_K && BM == 1) || (F == NT_Q6_K && BM == 2)) {
+    // a token's two column halves (lanes n and n + 8 of a row of 16)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ai[j] += dpp_i<0x128>(ai[j]);  // row_ror:8
+      if constexpr (F == NT_Q4_K) mi[j] += dpp_i<0x128>(mi[j]);
+    }
   }
   // the activation's scale of this 256-block, and the rows' d (dmin)
   const float s = ldf(job.xscl + 4u * (uint32_t)((sg.lb0 >> 3) * kMaxTokens + t));
@@ -512,7 +598,7 @@ __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, 
     const float Pl = __int_as_float(dpp_i<0xB1>(__float_as_int(P)));  // quad_perm 1,0,3,2: the lo-plane lane's
     acc[j] = fmaf(s, fmaf(256.f, P, Pl), acc[j]);
   }
-  if (sg.last && (lane & 1) == 0 && t < job.M) {
+  if (sg.last && (lane & 1) == 0 && t < job.M && (BM == 0 || (lane & 8) == 0)) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int v = kTileRows * sg.vt + 4 * kq + j;
@@ -521,12 +607,25 @@ __device__ __forceinline__ void tseg_compute_f(const JobM& job, const TSeg& sg, 
   }
 }
 
-template <int LPL, bool FAST>
+template <int LPL, bool FAST, int BM>
 __device__ __forceinline__ void tseg_compute(const JobM& job, const TSeg& sg, uint32_t slab, uint32_t scl, int lane,
                                              float (&acc)[4]) {
   // row pieces laid out without alignment slack (the planner's exact P)
   // start 16-byte aligned
   const bool al = sg.P * 16 == sg.piece;
+  if constexpr (BM == 1) {  // paired B tiles: Q4_K and Q6_K matrices only
+    if (sg.fmt == NT_Q4_K) {
+      if (al) tseg_compute_f<NT_Q4_K, LPL, true, FAST, 1>(job, sg, slab, scl, lane, acc);
+      else tseg_compute_f<NT_Q4_K, LPL, false, FAST, 1>(job, sg, slab, scl, lane, acc);
+    } else {
+      tseg_compute_f<NT_Q6_K, LPL, false, FAST, 1>(job, sg, slab, scl, lane, acc);
+    }
+    return;
+  }
+  if constexpr (BM == 2) {  // split B tiles: Q6_K matrices only
+    tseg_compute_f<NT_Q6_K, LPL, false, FAST, 2>(job, sg, slab, scl, lane, acc);
+    return;
+  }
   switch (sg.fmt) {
     case NT_Q4_K:
       if (al) tseg_compute_f<NT_Q4_K, LPL, true, FAST>(job, sg, slab, scl, lane, acc);
@@ -595,7 +694,7 @@ __device__ __forceinline__ void tseg_issue(const TSeg& sg, TLoad<LPL>& tl, int l
   else tseg_load(sg, lane, pre);
 }
 
-template <int LPL, bool FAST>
+template <int LPL, bool FAST, int BM>
 __device__ __forceinline__ void stream_m(const JobM& job, const ShareM& sh, int wave, int lane, uint32_t slab,
                                          uint32_t scl, UCur& ah, float (&acc)[4], uint4 (&pre)[LPL], TSeg& sg,
                                          TLoad<LPL>& tl, bool& cur_valid, bool& nxt_valid) {
@@ -607,7 +706,7 @@ __device__ __forceinline__ void stream_m(const JobM& job, const ShareM& sh, int 
   sg = issue ? tseg_at(job, sh, ah.u, ah.j) : tseg_null(job);
   tseg_issue<LPL, FAST>(sg, tl, lane, pre);
   if (issue) ucur_next(job, sh, ah, wave, lane, true);
-  if (valid) tseg_compute<LPL, FAST>(job, cur, slab, scl, lane, acc);
+  if (valid) tseg_compute<LPL, FAST, BM>(job, cur, slab, scl, lane, acc);
   cur_valid = nxt_valid;
   nxt_valid = issue;
 }
@@ -627,7 +726,7 @@ __device__ __forceinline__ int64_t part_row(const JobM& job, const ShareM& sh, i
   return (int64_t)up * job.orows + job.row_base[m] + lr;
 }
 
-template <int LPL, bool FAST>
+template <int LPL, bool FAST, int BM>
 __global__ __launch_bounds__(kMaxThreads) void k_qgemm_m(JobM job) {
   const int tid = threadIdx.x, lane = tid & 63, NT = job.nwaves * 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -642,8 +741,32 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemm_m(JobM job) {
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
     const int c = tid + NT * i;
-    if (c < cb) xa[i] = *reinterpret_cast<const uint4*>(job.xb + 512 * (int64_t)sh.gb0 + 16 * c);
-    else if (c < cb + cr)
+    if (c < cb) {
+      if constexpr (BM == 2) {
+        // split form: chunk c % 32 of block c / 32 holds lanes l, l + 1 (l =
+        // 2 (c % 32) = n + 16 kq): activations 8 kq .. + 7 of columns n % 8
+        // and n % 8 + 1 where n / 8 == kq / 2, else zero
+        const int l = 2 * (c & 31), n = l & 15, kq = l >> 4;
+        if ((n >> 3) == (kq >> 1))
+          xa[i] = *reinterpret_cast<const uint4*>(job.xb + 512 * ((int64_t)sh.gb0 + (c >> 5)) + 8 * ((n & 7) + 16 * kq));
+        else
+          xa[i] = make_uint4(0u, 0u, 0u, 0u);
+      } else if constexpr (BM == 1) {
+        // paired form: the B tile of blocks (2q, 2q + 1), lane l = n + 16 g:
+        // block 2q + g / 2's activations 16 (g % 2) .. + 15 of column n % 8
+        // where n / 8 == g / 2, else zero
+        const int q = c >> 6, l = c & 63, n = l & 15, g = l >> 4;
+        if ((n >> 3) == (g >> 1)) {
+          const uint8_t* s = job.xb + 512 * ((int64_t)sh.gb0 + 2 * q + (g >> 1)) + 8 * ((n & 7) + 32 * (g & 1));
+          const uint2 u0 = *reinterpret_cast<const uint2*>(s), u1 = *reinterpret_cast<const uint2*>(s + 128);
+          xa[i] = make_uint4(u0.x, u0.y, u1.x, u1.y);
+        } else {
+          xa[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      } else {
+        xa[i] = *reinterpret_cast<const uint4*>(job.xb + 512 * (int64_t)sh.gb0 + 16 * c);
+      }
+    } else if (c < cb + cr)
       xa[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(job.xs) + 128 * (int64_t)sh.gb0 +
                                               16 * (c - cb));
     else if (c < cb + cr + cs)
@@ -677,8 +800,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemm_m(JobM job) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     bool cur_valid = va, nxt_valid = vb;
     do {
-      stream_m<LPL, FAST>(job, sh, wave, lane, slab, scl, ah, acc, pa, sa, tl, cur_valid, nxt_valid);
-      stream_m<LPL, FAST>(job, sh, wave, lane, slab, scl, ah, acc, pb, sb, tl, cur_valid, nxt_valid);
+      stream_m<LPL, FAST, BM>(job, sh, wave, lane, slab, scl, ah, acc, pa, sa, tl, cur_valid, nxt_valid);
+      stream_m<LPL, FAST, BM>(job, sh, wave, lane, slab, scl, ah, acc, pb, sb, tl, cur_valid, nxt_valid);
     } while (cur_valid);
   }
   __syncthreads();
@@ -762,22 +885,30 @@ int gemm_cus() {
   return v > 0 ? v : 256;
 }
 
-template <int LPL, bool FAST>
+template <int LPL, bool FAST, int BM>
 int launch_m_kernel(const JobM& job, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_qgemm_m<LPL, FAST>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    if (hipFuncSetAttribute((const void*)k_qgemm_m<LPL, FAST, BM>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             160 * 1024) != hipSuccess)
       return NT_EHIP;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_qgemm_m<LPL, FAST>), dim3(job.grid), dim3(64 * job.nwaves), job.lds_bytes, stream, job);
+  hipLaunchKernelGGL((k_qgemm_m<LPL, FAST, BM>), dim3(job.grid), dim3(64 * job.nwaves), job.lds_bytes, stream, job);
   return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
 }
 
 template <int LPL>
 int launch_m_lpl(const JobM& job, hipStream_t stream) {
-  return job.fast ? launch_m_kernel<LPL, true>(job, stream) : launch_m_kernel<LPL, false>(job, stream);
+  if constexpr (LPL <= 4) {
+    if (job.bmode == 1)
+      return job.fast ? launch_m_kernel<LPL, true, 1>(job, stream) : launch_m_kernel<LPL, false, 1>(job, stream);
+  }
+  if constexpr (LPL == 4) {
+    if (job.bmode == 2)
+      return job.fast ? launch_m_kernel<LPL, true, 2>(job, stream) : launch_m_kernel<LPL, false, 2>(job, stream);
+  }
+  return job.fast ? launch_m_kernel<LPL, true, 0>(job, stream) : launch_m_kernel<LPL, false, 0>(job, stream);
 }
 
 template <int EPI>
@@ -873,6 +1004,19 @@ int plan_job_m(JobM& job, int nmat, const uint8_t* const* W, const int* fmt, con
         (int64_t)rows[m] * job.rb[m] >= ((int64_t)1 << 32))
       job.fast = 0;
   }
+  // up to four tokens (B columns 0..7): Q4_K (with Q6_K beside it) in the
+  // paired 16x16x64 form, Q6_K alone in the split 16x16x32 form
+  job.bmode = 0;
+  if (M <= 4) {
+    bool q4k = false, q6k = false, other = false;
+    for (int m = 0; m < nmat; ++m) {
+      q4k |= fmt[m] == NT_Q4_K;
+      q6k |= fmt[m] == NT_Q6_K;
+      other |= fmt[m] != NT_Q4_K && fmt[m] != NT_Q6_K;
+    }
+    job.bmode = other ? 0 : (q4k ? 1 : (q6k ? 2 : 0));
+  }
+  if (lpl > 4 || (job.bmode == 2 && lpl != 4)) job.bmode = 0;  // (Q4_K and Q6_K pieces take 3 and 4 loads per lane)
   if (lpl > kSlabLoads) return NT_EUNSUPPORTED;
   if (orows > INT32_MAX / 16) return NT_EUNSUPPORTED;
   job.lpl = lpl;

@@ -206,6 +206,7 @@ struct JobM {
   uint32_t magicP[kMaxMats];  // ceil(65536 / P): chunk -> row by a multiply
   int nmat, paired, pairs, cols, M;
   int fast;                   // every matrix's rows are whole 16-byte chunks apart (fixed-offset tile loads)
+  int bmode;                  // B tiles for M <= 4: 0 plain, 1 paired (Q4_K, Q6_K), 2 split (Q6_K)
   int orows;                  // output rows (paired: of each matrix)
   int nts;                    // tile-slices per row
   int tsper, nsup;            // tile-slices per column range, column ranges
