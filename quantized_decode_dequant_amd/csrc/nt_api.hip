@@ -21,8 +21,10 @@ size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 // M >= 2 it also holds the small-M GEMM's staged activation and partial sums.
 // qx_o, qx_h, qx_a: the quantized activations (qx_bytes each per token) that
 // the attention, O and gate/up launches hand to the next launch.
+// stage, part, ss: the small-M GEMM's staged activation, partial sums and the
+// staged residual stream's sums of squares per 256-block.
 struct LayerWs {
-  size_t q, part_o, part_ml, o, a, err, qx_o, qx_h, qx_a, stage, part, total;
+  size_t q, part_o, part_ml, o, a, err, qx_o, qx_h, qx_a, stage, part, ss, total;
   int chunk, nsplit;
 };
 
@@ -61,6 +63,7 @@ LayerWs layer_ws(const nt_layer_cfg& c, int M) {
     pb = std::max(pb, part_m_bytes(c.ffn, 1, c.hidden, M));
     pb = std::max(pb, part_m_bytes(c.hidden, 0, c.ffn, M));
     w.part = off; off += up256(pb);
+    w.ss = off; off += up256((size_t)M * ((size_t)c.hidden / 256 + 1) * 4);
   }
   w.total = off;
   return w;
@@ -86,10 +89,22 @@ int check_layer(const nt_layer_cfg& c, const nt_layer& L) {
 
 const uint8_t* u8(const void* p) { return static_cast<const uint8_t*>(p); }
 
-// The launches of one layer for 2 <= M <= 8 tokens: each projection stages
-// its M activation rows once and reads the weights once (int8 MFMA).
+// How a small-M layer takes its input and hands its output on already staged
+// (the small-M GEMM's activation layout, written by the reduce launch before;
+// see RedArgs): the residual stream times the next launch's RMSNorm gains,
+// with its sums of squares per 256-block for the normalization factor.
+struct LayerStM {
+  bool in_staged = false;            // the layer's input is staged (times attn_norm)
+  const float* next_gain = nullptr;  // the gains of the next normalizing launch; null: no staging out
+  bool out_staged = false;           // set when the down projection staged the output
+};
+
+// The launches of one layer for 2 <= M <= 8 tokens: each projection reads the
+// weights once for all M tokens (int8 MFMA).  Its activation is staged by the
+// reduce launch of the projection before where the rows are whole 256-blocks
+// (O -> gate/up -> down -> the next layer's Q/K/V), else by a staging launch.
 int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const int32_t* pos, uint8_t* ws,
-                const LayerWs& w, hipStream_t st) {
+                const LayerWs& w, hipStream_t st, LayerStM* ls = nullptr) {
   const int nq = c.n_head * c.head_dim, nkv = c.n_kv_head * c.head_dim;
   float* q = reinterpret_cast<float*>(ws + w.q);
   float* part_o = reinterpret_cast<float*>(ws + w.part_o);
@@ -99,7 +114,16 @@ int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const
   int* err = reinterpret_cast<int*>(ws + w.err);
   void* stage = ws + w.stage;
   void* part = ws + w.part;
+  float* ss = reinterpret_cast<float*>(ws + w.ss);
   const ProArgs none{nullptr, nullptr, 0.f, 0, 0, 0.f, nullptr, 0};
+  const bool h256 = c.hidden % 256 == 0, f256 = c.ffn % 256 == 0;
+  RedArgs rn_hidden;  // the RMSNorm factor of a staged residual stream
+  rn_hidden.rn_ss = ss;
+  rn_hidden.rn_nb = c.hidden / 256;
+  rn_hidden.rn_cols = c.hidden;
+  rn_hidden.rn_eps = c.rms_eps;
+  const bool in_staged = ls && ls->in_staged && h256;
+  if (ls) ls->out_staged = false;
   int rc;
   // 1. RMSNorm -> Q,K,V projections -> RoPE -> q, K/V append (token t at pos + t)
   {
@@ -108,7 +132,8 @@ int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const
     const int fmt[3] = {L.wq.fmt, L.wk.fmt, L.wv.fmt};
     const int rows[3] = {nq, nkv, nkv};
     if ((rc = plan_job_m(job, 3, W, fmt, rows, c.hidden, 0, 1, M)) != NT_OK) return rc;
-    if ((rc = launch_stage_m(x, c.hidden, L.attn_norm, c.rms_eps, M, c.hidden, stage, st)) != NT_OK) return rc;
+    if (!in_staged && (rc = launch_stage_m(x, c.hidden, L.attn_norm, c.rms_eps, M, c.hidden, stage, st)) != NT_OK)
+      return rc;
     ProArgs pro = none;
     pro.rope_hd = c.head_dim;
     pro.rope_theta = c.rope_theta;
@@ -125,7 +150,8 @@ int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const
     ea.rope_theta = c.rope_theta;
     ea.q_rows = nq;
     ea.kv_rows = nkv;
-    if ((rc = launch_gemm_m(job, stage, part, pro, EPI_QKV, ea, st)) != NT_OK) return rc;
+    if ((rc = launch_gemm_m(job, stage, part, pro, EPI_QKV, ea, st, in_staged ? rn_hidden : RedArgs{})) != NT_OK)
+      return rc;
   }
   // 2. attention over the cache (token t sees positions 0..pos+t)
   if ((rc = launch_attention(q, L.k_cache, L.v_cache, pos, M, c.n_head, c.n_kv_head, c.head_dim, c.max_ctx, w.chunk,
@@ -142,7 +168,13 @@ int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const
     EpiArgs ea{};
     ea.y = x;
     ea.ld = c.hidden;
-    if ((rc = launch_gemm_m(job, stage, part, none, EPI_RESID, ea, st)) != NT_OK) return rc;
+    RedArgs ra;  // h staged for gate/up, times ffn_norm
+    if (h256) {
+      ra.st_stage = stage;
+      ra.st_gain = L.ffn_norm;
+      ra.st_ss = ss;
+    }
+    if ((rc = launch_gemm_m(job, stage, part, none, EPI_RESID, ea, st, ra)) != NT_OK) return rc;
   }
   // 4. a = silu(Wg hn) * (Wu hn), hn = RMSNorm(h)
   {
@@ -151,11 +183,14 @@ int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const
     const int fmt[2] = {L.wg.fmt, L.wu.fmt};
     const int rows[2] = {c.ffn, c.ffn};
     if ((rc = plan_job_m(job, 2, W, fmt, rows, c.hidden, 1, 0, M)) != NT_OK) return rc;
-    if ((rc = launch_stage_m(x, c.hidden, L.ffn_norm, c.rms_eps, M, c.hidden, stage, st)) != NT_OK) return rc;
+    if (!h256 && (rc = launch_stage_m(x, c.hidden, L.ffn_norm, c.rms_eps, M, c.hidden, stage, st)) != NT_OK)
+      return rc;
     EpiArgs ea{};
     ea.y = a;
     ea.ld = c.ffn;
-    if ((rc = launch_gemm_m(job, stage, part, none, EPI_SWIGLU, ea, st)) != NT_OK) return rc;
+    RedArgs ra = h256 ? rn_hidden : RedArgs{};
+    if (f256) ra.st_stage = stage;  // a staged for down
+    if ((rc = launch_gemm_m(job, stage, part, none, EPI_SWIGLU, ea, st, ra)) != NT_OK) return rc;
   }
   // 5. x = h + Wd a
   {
@@ -164,12 +199,20 @@ int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const
     const int fmt[1] = {L.wd.fmt};
     const int rows[1] = {c.hidden};
     if ((rc = plan_job_m(job, 1, W, fmt, rows, c.ffn, 0, 0, M)) != NT_OK) return rc;
-    if ((rc = launch_stage_m(a, c.ffn, nullptr, 0.f, M, c.ffn, stage, st)) != NT_OK) return rc;
+    if (!f256 && (rc = launch_stage_m(a, c.ffn, nullptr, 0.f, M, c.ffn, stage, st)) != NT_OK) return rc;
     EpiArgs ea{};
     ea.y = x;
     ea.ld = c.hidden;
     ea.err = err;  // NaN out when a position was out of range
-    if ((rc = launch_gemm_m(job, stage, part, none, EPI_RESID, ea, st)) != NT_OK) return rc;
+    RedArgs ra;  // the output staged for the next normalizing launch
+    const bool out = ls && ls->next_gain && h256;
+    if (out) {
+      ra.st_stage = stage;
+      ra.st_gain = ls->next_gain;
+      ra.st_ss = ss;
+    }
+    if ((rc = launch_gemm_m(job, stage, part, none, EPI_RESID, ea, st, ra)) != NT_OK) return rc;
+    if (out) ls->out_staged = true;
   }
   return NT_OK;
 }
@@ -204,9 +247,10 @@ struct LayerQx {
 
 // The launches of one layer (arguments already validated).
 int run_layer(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const int32_t* pos, uint8_t* ws,
-              const LayerWs& w, hipStream_t st, LayerQx* lq = nullptr) {
+              const LayerWs& w, hipStream_t st, LayerQx* lq = nullptr, LayerStM* ls = nullptr) {
   if (lq) lq->x_out_written = false;
-  if (small_m_layer(L, M)) return run_layer_m(c, L, x, M, pos, ws, w, st);
+  if (small_m_layer(L, M)) return run_layer_m(c, L, x, M, pos, ws, w, st, ls);
+  if (ls) ls->out_staged = false;
   const int nq = c.n_head * c.head_dim, nkv = c.n_kv_head * c.head_dim;
   float* q = reinterpret_cast<float*>(ws + w.q);
   float* part_o = reinterpret_cast<float*>(ws + w.part_o);
@@ -484,6 +528,7 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
                         qx_step ? qx_x : nullptr, qx_step ? gain_after(-1) : nullptr, st);
   if (rc != NT_OK) return rc;
   bool x_quantized = qx_step;
+  bool x_staged = false;  // x staged for a small-M launch by the last layer (times the next gains)
   StreamEvents* ev = nullptr;
   hipStream_t cs = static_cast<hipStream_t>(m.copy_stream);
   auto issue_copy = [&](int j) -> int {
@@ -532,8 +577,12 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
     lq.x_in = x_quantized ? qx_x : nullptr;
     lq.x_out = qx_step ? qx_x : nullptr;
     lq.next_gain = gain_after(l);
-    if ((rc = run_layer(m.cfg, L, x, M, pos, ws + w.layer, w.lw, st, &lq)) != NT_OK) return rc;
+    LayerStM lsm;
+    lsm.in_staged = x_staged;
+    lsm.next_gain = gain_after(l);
+    if ((rc = run_layer(m.cfg, L, x, M, pos, ws + w.layer, w.lw, st, &lq, &lsm)) != NT_OK) return rc;
     x_quantized = lq.x_out_written;
+    x_staged = lsm.out_staged;
     if (sa.cos_acc && (rc = launch_cos_acc(x_in, x, m.cfg.hidden, sa.cos_acc + l, st)) != NT_OK) return rc;
     if (l >= fs) {
       if (hipEventRecord(ev->freed[b], st) != hipSuccess) return NT_EHIP;
@@ -549,13 +598,21 @@ int run_step(const nt_model& m, const int32_t* tokens, int M, const int32_t* pos
     JobM jm;
     if ((rc = plan_job_m(jm, 1, Wl, fmtl, rowsl, m.cfg.hidden, 0, 0, M)) != NT_OK) return rc;
     void* stage = ws + w.layer + w.lw.stage;
-    if ((rc = launch_stage_m(x, m.cfg.hidden, m.out_norm, m.cfg.rms_eps, M, m.cfg.hidden, stage, st)) != NT_OK)
+    RedArgs ra;
+    if (x_staged) {  // by the last layer, times out_norm
+      ra.rn_ss = reinterpret_cast<const float*>(ws + w.layer + w.lw.ss);
+      ra.rn_nb = m.cfg.hidden / 256;
+      ra.rn_cols = m.cfg.hidden;
+      ra.rn_eps = m.cfg.rms_eps;
+    } else if ((rc = launch_stage_m(x, m.cfg.hidden, m.out_norm, m.cfg.rms_eps, M, m.cfg.hidden, stage, st)) !=
+               NT_OK) {
       return rc;
+    }
     const ProArgs none{nullptr, nullptr, 0.f, 0, 0, 0.f, nullptr, 0};
     EpiArgs ea{};
     ea.y = logits;
     ea.ld = m.vocab;
-    if ((rc = launch_gemm_m(jm, stage, ws + w.part_lm, none, EPI_STORE, ea, st)) != NT_OK) return rc;
+    if ((rc = launch_gemm_m(jm, stage, ws + w.part_lm, none, EPI_STORE, ea, st, ra)) != NT_OK) return rc;
   } else {
     Job jl;
     if ((rc = plan_job(jl, 1, Wl, fmtl, rowsl, m.cfg.hidden, 0, 0)) != NT_OK) return rc;

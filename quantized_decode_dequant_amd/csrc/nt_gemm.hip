@@ -819,16 +819,86 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemm_m(JobM job) {
 }
 
 // ------------------------------------------------------------ reduce + epilogue
+// The outputs of one 256-thread block (256 consecutive rows of token t, a
+// 256-block of the next launch's activation) staged as k_stage_m stages an
+// activation row: the values times the gains (the RMSNorm factor is left to
+// the next reduce, see RedArgs), one scale for the 256-block, X = 256 hi +
+// lo in the MFMA B layout, the X sums of each 32-block's halves; with st_ss
+// also the sum of squares of the values themselves.
+__device__ __forceinline__ void stage_out(const RedArgs& ra, float v, int t, int R, int orows) {
+  __shared__ float red[8];
+  __shared__ uint32_t hw[64], lw[64];  // the hi and lo bytes of the 256 values
+  __shared__ int xv[256];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const float gv = ra.st_gain ? v * ra.st_gain[R] : v;
+  const float ws = wave_sum(v * v), wm = wave_max(fabsf(gv));
+  if (lane == 0) {
+    red[wv] = ws;
+    red[4 + wv] = wm;
+  }
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
+  const float inv = amax > 0.f ? kXMax / amax : 0.f;
+  int X = __float2int_rn(gv * inv);
+  X = max(-32639, min(32639, X));
+  const int hi = (X + 128) >> 8;
+  const int lo = X - (hi << 8);
+  reinterpret_cast<uint8_t*>(hw)[tid] = (uint8_t)(hi & 255);
+  reinterpret_cast<uint8_t*>(lw)[tid] = (uint8_t)(lo & 255);
+  xv[tid] = X;
+  __syncthreads();
+  const int b0 = (R - tid) >> 5;  // the 256-block's first 32-block
+  const int64_t nb = orows / 32;
+  uint8_t* xb = static_cast<uint8_t*>(ra.st_stage);
+  int4* xs = reinterpret_cast<int4*>(xb + nb * 512);
+  float* xsc = reinterpret_cast<float*>(xb + nb * 512 + nb * kMaxTokens * 16);
+  if (tid < 128) {
+    // four values' bytes of one plane: column 2t + plane of lane (kq, ...)
+    const int q = tid & 63, pl = tid >> 6, b = b0 + (q >> 3), gi = q & 7;
+    *reinterpret_cast<uint32_t*>(xb + 512 * (int64_t)b + 128 * (gi >> 1) + 4 * (gi & 1) + 8 * (2 * t + pl)) =
+        pl ? lw[q] : hw[q];
+  } else if (tid < 136) {
+    const int j = tid - 128;
+    int s0 = 0, s1 = 0;
+    for (int k = 0; k < 16; ++k) {
+      s0 += xv[32 * j + k];
+      s1 += xv[32 * j + 16 + k];
+    }
+    xs[(int64_t)(b0 + j) * kMaxTokens + t] = make_int4(0, 0, s0, s1);
+  } else if (tid == 136) {
+    xsc[(int64_t)(b0 >> 3) * kMaxTokens + t] = amax / kXMax;
+    if (ra.st_ss) ra.st_ss[(int64_t)t * (orows / 256) + (b0 >> 3)] = red[0] + red[1] + red[2] + red[3];
+  }
+}
+
 // Adds the column ranges' partial sums in order and applies the epilogue for
-// (token, row) = thread (row pairs for EPI_QKV).
+// (token, row) = thread (row pairs for EPI_QKV); see RedArgs for the RMSNorm
+// factor of a prestaged input and the staging of the outputs.
 template <int EPI>
 __global__ __launch_bounds__(256) void k_reduce_m(const float* __restrict__ part, int nsup, int M, int64_t ldp,
-                                                  int orows, ProArgs pro, EpiArgs ea) {
+                                                  int orows, ProArgs pro, EpiArgs ea, RedArgs ra) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   auto total = [&](int t, int64_t R) {
     float s = 0.f;
     for (int su = 0; su < nsup; ++su) s += part[((int64_t)su * M + t) * ldp + R];
     return s;
+  };
+  // token t's RMSNorm factor (1 where the staging applied it): four
+  // interleaved partial sums, so the loads go out together
+  auto rnorm = [&](int t) {
+    if (!ra.rn_ss) return 1.0f;
+    const float* p = ra.rn_ss + (int64_t)t * ra.rn_nb;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    int b = 0;
+#pragma unroll 4
+    for (; b + 4 <= ra.rn_nb; b += 4) {
+      s0 += p[b];
+      s1 += p[b + 1];
+      s2 += p[b + 2];
+      s3 += p[b + 3];
+    }
+    for (; b < ra.rn_nb; ++b) s0 += p[b];
+    return 1.0f / sqrtf(((s0 + s1) + (s2 + s3)) / (float)ra.rn_cols + ra.rn_eps);
   };
   if constexpr (EPI == EPI_QKV) {
     const int npr = orows / 2;
@@ -839,7 +909,8 @@ __global__ __launch_bounds__(256) void k_reduce_m(const float* __restrict__ part
     // the layer's status word says which
     const bool pos_ok = *ea.pos >= 0 && *ea.pos + M - 1 < ea.max_ctx;
     if (ea.err && i == 0) *ea.err = pos_ok ? 0 : 1;
-    float a = total(t, R), b = total(t, R + 1);
+    const float rn = rnorm(t);
+    float a = rn * total(t, R), b = rn * total(t, R + 1);
     const int dd = R % ea.head_dim;
     if (R < ea.q_rows + ea.kv_rows) {
       // RoPE: the pair turns by pos * theta^(-dd/head_dim), the angle in double
@@ -864,17 +935,23 @@ __global__ __launch_bounds__(256) void k_reduce_m(const float* __restrict__ part
       cache[off + 1] = __builtin_bit_cast(uint16_t, hb);
     }
   } else {
+    // (with staging, orows * M is a whole number of blocks: no block returns
+    // in part)
     if (i >= (int64_t)orows * M) return;
     const int t = (int)(i / orows), R = (int)(i - (int64_t)t * orows);
+    const float rn = rnorm(t);
+    float v;
     if constexpr (EPI == EPI_SWIGLU) {
-      ea.y[t * ea.ld + R] = silu(total(t, R)) * total(t, (int64_t)orows + R);
+      v = silu(rn * total(t, R)) * (rn * total(t, (int64_t)orows + R));
     } else if constexpr (EPI == EPI_RESID) {
       // NaN when the layer's status word says a position was out of range
       const bool bad = ea.err && *ea.err != 0;
-      ea.y[t * ea.ld + R] = bad ? __builtin_nanf("") : ea.y[t * ea.ld + R] + total(t, R);
+      v = bad ? __builtin_nanf("") : ea.y[t * ea.ld + R] + rn * total(t, R);
     } else {
-      ea.y[t * ea.ld + R] = total(t, R);
+      v = rn * total(t, R);
     }
+    ea.y[t * ea.ld + R] = v;
+    if (ra.st_stage) stage_out(ra, v, t, R, orows);
   }
 }
 
@@ -912,12 +989,12 @@ int launch_m_lpl(const JobM& job, hipStream_t stream) {
 }
 
 template <int EPI>
-int launch_reduce(const JobM& job, const ProArgs& pro, const EpiArgs& ea, hipStream_t stream) {
+int launch_reduce(const JobM& job, const ProArgs& pro, const EpiArgs& ea, const RedArgs& ra, hipStream_t stream) {
   const int64_t n = (int64_t)(EPI == EPI_QKV ? job.orows / 2 : job.orows) * job.M;
   const int64_t blocks = (n + 255) / 256;
   if (blocks <= 0) return NT_OK;
   hipLaunchKernelGGL(k_reduce_m<EPI>, dim3((unsigned)blocks), dim3(256), 0, stream, job.part, job.nsup, job.M, job.ldp,
-                     job.orows, pro, ea);
+                     job.orows, pro, ea, ra);
   return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
 }
 
@@ -1061,7 +1138,10 @@ int plan_job_m(JobM& job, int nmat, const uint8_t* const* W, const int* fmt, con
 }
 
 int launch_gemm_m(JobM& job, const void* stage, void* part, const ProArgs& pro, int epi, const EpiArgs& ea,
-                  hipStream_t stream) {
+                  hipStream_t stream, const RedArgs& ra) {
+  // staging needs whole 256-blocks of rows per reduce block (not QKV's pairs)
+  if (ra.st_stage && (epi == EPI_QKV || job.orows % 256 != 0)) return NT_EINVAL;
+  if (ra.rn_ss && (ra.rn_nb <= 0 || ra.rn_cols <= 0)) return NT_EINVAL;
   if (job.otiles <= 0) return NT_OK;
   job.xb = static_cast<const uint8_t*>(stage);
   job.xs = reinterpret_cast<const int4*>(job.xb + (size_t)(job.cols / 32) * 512);
@@ -1075,10 +1155,10 @@ int launch_gemm_m(JobM& job, const void* stage, void* part, const ProArgs& pro, 
   }
   if (rc != NT_OK) return rc;
   switch (epi) {
-    case EPI_STORE: return launch_reduce<EPI_STORE>(job, pro, ea, stream);
-    case EPI_RESID: return launch_reduce<EPI_RESID>(job, pro, ea, stream);
-    case EPI_QKV: return launch_reduce<EPI_QKV>(job, pro, ea, stream);
-    case EPI_SWIGLU: return launch_reduce<EPI_SWIGLU>(job, pro, ea, stream);
+    case EPI_STORE: return launch_reduce<EPI_STORE>(job, pro, ea, ra, stream);
+    case EPI_RESID: return launch_reduce<EPI_RESID>(job, pro, ea, ra, stream);
+    case EPI_QKV: return launch_reduce<EPI_QKV>(job, pro, ea, ra, stream);
+    case EPI_SWIGLU: return launch_reduce<EPI_SWIGLU>(job, pro, ea, ra, stream);
   }
   return NT_EINVAL;
 }

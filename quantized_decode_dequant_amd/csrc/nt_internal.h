@@ -234,11 +234,29 @@ size_t part_m_bytes(int64_t orows, int paired, int cols, int M);
 // Stage M activation rows (optionally RMSNorm'ed) into `stage` (stage_m_bytes(cols) bytes).
 int launch_stage_m(const float* src, int64_t stride, const float* gain, float eps, int M, int cols, void* stage,
                    hipStream_t stream);
+// What the reduce launch of a small-M GEMM does besides its epilogue.
+//  - rn_ss: the staged input carries its RMSNorm gains but not the factor:
+//    the outputs are multiplied by r_t = 1 / sqrt(sum_b rn_ss[t rn_nb + b] /
+//    rn_cols + rn_eps) (rn_ss: the input rows' sums of squares per
+//    256-block, written by the launch that staged it).
+//  - st_stage: the epilogue's outputs (EPI_STORE, EPI_RESID, EPI_SWIGLU),
+//    times st_gain where given, also go out staged for the next small-M GEMM
+//    (stage_m layout over orows columns; orows a multiple of 256), and with
+//    st_ss their sums of squares per 256-block ([M][orows / 256]).
+struct RedArgs {
+  const float* rn_ss = nullptr;
+  int rn_nb = 0, rn_cols = 0;
+  float rn_eps = 0.f;
+  void* st_stage = nullptr;
+  const float* st_gain = nullptr;
+  float* st_ss = nullptr;
+};
+
 // The GEMM over a staged activation into `part` (part_m_bytes), then the
 // reduce and epilogue; `pro` supplies only the RoPE fields (rope_hd,
 // rope_theta, pos) for EPI_QKV.
 int launch_gemm_m(JobM& job, const void* stage, void* part, const ProArgs& pro, int epi, const EpiArgs& ea,
-                  hipStream_t stream);
+                  hipStream_t stream, const RedArgs& ra = RedArgs{});
 
 // Launch tracing (nt_trace.hip): true when this launch of `kind` is
 // recorded, with the events to hand to hipExtLaunchKernel (start: the first
