@@ -160,6 +160,7 @@ struct TSeg {
   int nrow;             // rows of the tile inside the matrix (<= 16)
   int nblk;             // 32-weight blocks in the tile-slice (<= 8)
   int lb0;              // first 32-block of the tile-slice, counted from the range's first
+  int ts, tsb;          // tile-slice of the row, bytes of a full tile-slice row piece
   int vt, sub;          // unit
   int first, last;      // first / last tile-slice of its unit
 };
@@ -215,11 +216,34 @@ __device__ __forceinline__ TSeg tseg_at(const JobM& job, const ShareM& sh, int u
   sg.nblk = kq ? 8 : min(8, (job.cols - kTS * ts) >> 5);
   sg.piece = kq ? tsb : sg.nblk * block_bytes(sg.fmt);
   sg.lb0 = 8 * lts;
+  sg.ts = ts;
+  sg.tsb = tsb;
   const int64_t r0 = (int64_t)(kTileRows * lt) * sg.rb, o = (int64_t)ts * tsb;
   sg.base = W + r0 + o;
   sg.d = (uint32_t)(o & 15);
   sg.ab = W + r0 + (o & ~(int64_t)15);
   sg.nrec = (uint32_t)((int64_t)rows * sg.rb - r0 - (o & ~(int64_t)15));
+  return sg;
+}
+
+// The next tile-slice of the same unit (the next 256 columns of the same 16
+// rows): only the column position moves, so this replaces tseg_at's matrix
+// and unit lookups by a few scalar adds.
+__device__ __forceinline__ TSeg tseg_next(const JobM& job, const TSeg& p, bool last) {
+  TSeg sg = p;
+  sg.first = 0;
+  sg.last = last;
+  sg.ts = p.ts + 1;
+  sg.lb0 = p.lb0 + 8;
+  const int nb = min(8, (job.cols - kTS * sg.ts) >> 5);  // 8 for the K-quants (whole superblocks)
+  if (nb < 8) {
+    sg.nblk = nb;
+    sg.piece = nb * block_bytes(sg.fmt);
+  }
+  sg.base = p.base + p.tsb;
+  sg.d = (p.d + (uint32_t)p.tsb) & 15u;
+  sg.ab = sg.base - sg.d;
+  sg.nrec = p.nrec - (uint32_t)(sg.ab - p.ab);
   return sg;
 }
 
@@ -697,13 +721,15 @@ __device__ __forceinline__ void tseg_issue(const TSeg& sg, TLoad<LPL>& tl, int l
 template <int LPL, bool FAST, int BM>
 __device__ __forceinline__ void stream_m(const JobM& job, const ShareM& sh, int wave, int lane, uint32_t slab,
                                          uint32_t scl, UCur& ah, float (&acc)[4], uint4 (&pre)[LPL], TSeg& sg,
-                                         TLoad<LPL>& tl, bool& cur_valid, bool& nxt_valid) {
+                                         const TSeg& prev, TLoad<LPL>& tl, bool& cur_valid, bool& nxt_valid) {
   const TSeg cur = sg;
   const bool valid = cur_valid;
   tseg_store(slab, lane, pre);
   if (!ah.done && ah.u < 0) ucur_set(job, sh, ah, claim_m(job, lane));  // claim left pending before the barrier
   const bool issue = !ah.done;
-  sg = issue ? tseg_at(job, sh, ah.u, ah.j) : tseg_null(job);
+  // past a unit's first tile-slice the one issued last (the other buffer's,
+  // prev) is the slice before
+  sg = issue ? (ah.j > 0 ? tseg_next(job, prev, ah.j == ah.len - 1) : tseg_at(job, sh, ah.u, ah.j)) : tseg_null(job);
   tseg_issue<LPL, FAST>(sg, tl, lane, pre);
   if (issue) ucur_next(job, sh, ah, wave, lane, true);
   if (valid) tseg_compute<LPL, FAST, BM>(job, cur, slab, scl, lane, acc);
@@ -800,8 +826,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemm_m(JobM job) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     bool cur_valid = va, nxt_valid = vb;
     do {
-      stream_m<LPL, FAST, BM>(job, sh, wave, lane, slab, scl, ah, acc, pa, sa, tl, cur_valid, nxt_valid);
-      stream_m<LPL, FAST, BM>(job, sh, wave, lane, slab, scl, ah, acc, pb, sb, tl, cur_valid, nxt_valid);
+      stream_m<LPL, FAST, BM>(job, sh, wave, lane, slab, scl, ah, acc, pa, sa, sb, tl, cur_valid, nxt_valid);
+      stream_m<LPL, FAST, BM>(job, sh, wave, lane, slab, scl, ah, acc, pb, sb, sa, tl, cur_valid, nxt_valid);
     } while (cur_valid);
   }
   __syncthreads();
