@@ -61,6 +61,23 @@ def test_layer_tiny(fmts, n_past, M):
     check(got, ref, kc, vc, li, n_past, M)
 
 
+# Output rows that are not whole 256-blocks: a small-M layer then stages the
+# gate/up and down activations with staging launches instead of in the
+# reduce launches of the projections before (hidden 288: neither; ffn 416:
+# only down's)
+ODD_SHAPES = {
+    "h288_f352": wl.LayerShape(hidden=288, n_head=4, n_kv_head=2, head_dim=32, ffn=352),
+    "h512_f416": wl.LayerShape(hidden=512, n_head=8, n_kv_head=2, head_dim=64, ffn=416),
+}
+
+
+@pytest.mark.parametrize("fmts", [wl.ALL_Q4_0, wl.ALL_Q8_0], ids=["q4_0", "q8_0"])
+@pytest.mark.parametrize("name,M", [("h288_f352", 3), ("h288_f352", 4), ("h512_f416", 3)])
+def test_layer_rows_not_whole_256_blocks(fmts, name, M):
+    got, ref, kc, vc, li = run_layer(ODD_SHAPES[name], fmts, wl.W_TEST, 13, 64, 21, M)
+    check(got, ref, kc, vc, li, 21, M)
+
+
 # 8 query heads per kv head, head_dim 128 (the 70B group size)
 GROUP8 = wl.LayerShape(hidden=2048, n_head=16, n_kv_head=2, head_dim=128, ffn=4096)
 

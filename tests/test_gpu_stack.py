@@ -173,6 +173,31 @@ def test_verify_few_tokens_equals_sequential_decode(M, mix):
     assert out.cpu().numpy().tolist() == nxt.tolist()
 
 
+@pytest.mark.parametrize("hidden,ffn", [(288, 352), (512, 416)])
+def test_verify_rows_not_whole_256_blocks(hidden, ffn):
+    # hidden 288: no layer hands its output on staged and the small-M LM head
+    # (M = 4) stages its own input; ffn 416: only down stages its activation
+    import torch
+    dev = device()
+    shape = wl.LayerShape(hidden=hidden, n_head=4, n_kv_head=2, head_dim=32, ffn=ffn)
+    hs = HostStack(shape, wl.ALL_Q8_0, n_layer=3, vocab=611, max_ctx=40, n_past=11, wid=wl.W_TEST + 10,
+                   emb_fmt=wl.Q8_0, head_fmt=wl.Q8_0)
+    M = 4
+    toks = wl.gen_tokens(wl.W_TEST + 10, M, hs.vocab)
+    hv = hs.device_model(dev)
+    out = torch.zeros(M, dtype=torch.int32, device=dev)
+    logits = torch.zeros(M * hs.vocab, dtype=torch.float32, device=dev)
+    pos = torch.tensor([11], dtype=torch.int32, device=dev)
+    hv.verify_step(torch.from_numpy(toks).to(dev), M, pos, out,
+                   torch.zeros(hv.workspace_bytes(M), dtype=torch.uint8, device=dev), logits)
+    torch.cuda.synchronize()
+    nxt, _, ref, _ = hs.oracle_model().decode(toks, 11, want_logits=True)
+    g = logits.view(M, hs.vocab)
+    for i in range(M):
+        assert rel_inf(g[i].cpu().numpy(), ref[i]) <= LOGIT_TOL, i
+    assert out.cpu().numpy().tolist() == nxt.tolist()
+
+
 @pytest.mark.parametrize("M", [1, 4])
 def test_streamed_70b_shape_bitwise_equal_resident(M):
     # Llama-70B-shaped Q6_K layers (701,890,560-byte blobs), three of five
