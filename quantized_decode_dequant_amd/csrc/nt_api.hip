@@ -101,8 +101,9 @@ struct LayerStM {
 
 // The launches of one layer for 2 <= M <= 8 tokens: each projection reads the
 // weights once for all M tokens (int8 MFMA).  Its activation is staged by the
-// reduce launch of the projection before where the rows are whole 256-blocks
-// (O -> gate/up -> down -> the next layer's Q/K/V), else by a staging launch.
+// launch before where the rows are whole 256-blocks (the attention combine ->
+// O, the reduce launches O -> gate/up -> down -> the next layer's Q/K/V),
+// else by a staging launch.
 int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const int32_t* pos, uint8_t* ws,
                 const LayerWs& w, hipStream_t st, LayerStM* ls = nullptr) {
   const int nq = c.n_head * c.head_dim, nkv = c.n_kv_head * c.head_dim;
@@ -153,9 +154,12 @@ int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const
     if ((rc = launch_gemm_m(job, stage, part, pro, EPI_QKV, ea, st, in_staged ? rn_hidden : RedArgs{})) != NT_OK)
       return rc;
   }
-  // 2. attention over the cache (token t sees positions 0..pos+t)
+  // 2. attention over the cache (token t sees positions 0..pos+t); its
+  // combine stages the output for O where it is whole 256-blocks
+  const bool o256 = nq % 256 == 0;
   if ((rc = launch_attention(q, L.k_cache, L.v_cache, pos, M, c.n_head, c.n_kv_head, c.head_dim, c.max_ctx, w.chunk,
-                             w.nsplit, part_o, part_ml, o, nullptr, st)) != NT_OK)
+                             w.nsplit, part_o, part_ml, o, nullptr, st,
+                             o256 ? static_cast<uint8_t*>(stage) : nullptr)) != NT_OK)
     return rc;
   // 3. h = x + Wo o
   {
@@ -164,7 +168,7 @@ int run_layer_m(const nt_layer_cfg& c, const nt_layer& L, float* x, int M, const
     const int fmt[1] = {L.wo.fmt};
     const int rows[1] = {c.hidden};
     if ((rc = plan_job_m(job, 1, W, fmt, rows, nq, 0, 0, M)) != NT_OK) return rc;
-    if ((rc = launch_stage_m(o, nq, nullptr, 0.f, M, nq, stage, st)) != NT_OK) return rc;
+    if (!o256 && (rc = launch_stage_m(o, nq, nullptr, 0.f, M, nq, stage, st)) != NT_OK) return rc;
     EpiArgs ea{};
     ea.y = x;
     ea.ld = c.hidden;

@@ -393,6 +393,69 @@ __device__ __forceinline__ float embed_elem(int fmt, const uint8_t* __restrict__
   return h2f(b) * (float)scale * (float)q - h2f(b + 2) * (float)mn;
 }
 
+// The combine for a small-M consumer: workgroup (b, query) merges the splits
+// of output values 256 b .. 256 b + 255 (256 / head_dim heads of the query)
+// as k_attn_combine does, writes them to o and stages them as one 256-block
+// of the O projection's activation (stage_block256), so O needs no staging
+// launch.  Thread (v, j) of the 1024 sums splits j, j + 4, ... of value v,
+// the first 16 of them loaded before the position is known (clamped
+// indices, masked below), and the four partial sums are added in order.
+__global__ __launch_bounds__(1024) void k_attn_combine_st(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_ml, const int32_t* pos_ptr,
+                                                          int n_head, int head_dim, int chunk, int nsplit, int max_ctx,
+                                                          float* __restrict__ o, uint8_t* __restrict__ stage) {
+  constexpr int kPre = 16;  // splits per thread held in registers
+  __shared__ float s_w[256 / 32][kMaxSplits];  // e^(m_s - M) per head of the block and split
+  __shared__ float s_inv[256 / 32];
+  __shared__ float s_acc[4][256];
+  const int b = blockIdx.x, query = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int vi = tid & 255, j = tid >> 8;
+  const int nq = n_head * head_dim, hpb = 256 / head_dim, h0 = 256 * b / head_dim;
+  const int d = 256 * b + vi, h = d / head_dim, dd = d - h * head_dim;
+  const float* po = part_o + ((int64_t)query * nsplit * n_head + h) * head_dim + dd;
+  const float* ml = part_ml + (int64_t)query * nsplit * n_head * 2;
+  const int64_t sst = (int64_t)n_head * head_dim;
+  float ov[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) ov[k] = po[min(j + 4 * k, nsplit - 1) * sst];
+  __builtin_amdgcn_sched_barrier(0);
+  const int pos = *pos_ptr;
+  const bool ok = pos >= 0 && pos + query < max_ctx;
+  const int ns = ok ? min(nsplit, (pos + query + 1 + chunk - 1) / chunk) : 0;
+  // per head (one wave each): M = max over splits, the weights and 1 / L
+  if (wave < hpb) {
+    const float* mh = ml + (int64_t)(h0 + wave) * 2;
+    float m = -FLT_MAX;
+    for (int s = lane; s < ns; s += 64) m = fmaxf(m, mh[(int64_t)s * n_head * 2]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int s = lane; s < ns; s += 64) {
+      const float w = expf(mh[(int64_t)s * n_head * 2] - m);
+      s_w[wave][s] = w;
+      l += w * mh[(int64_t)s * n_head * 2 + 1];
+    }
+    l = wave_sum(l);
+    if (lane == 0) s_inv[wave] = ns > 0 ? 1.0f / l : 0.f;
+  }
+  __syncthreads();
+  const float* wv = s_w[h - h0];
+  float v = 0.f;
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int s = j + 4 * k;
+    if (s < ns) v += wv[s] * ov[k];
+  }
+  for (int s = j + 4 * kPre; s < ns; s += 4) v += wv[s] * po[s * sst];
+  s_acc[j][vi] = v;
+  __syncthreads();
+  float y = 0.f;
+  if (tid < 256) {
+    y = ((s_acc[0][tid] + s_acc[1][tid]) + s_acc[2][tid] + s_acc[3][tid]) * s_inv[h - h0];
+    o[(int64_t)query * nq + d] = y;
+  }
+  stage_block256(y, y, query, d, nq, stage, nullptr);
+}
+
 // x[m][:] = decoded row tokens[m] of an embedding matrix (fp32), one thread
 // per element.  It also clears the step's status word (err), which the layers
 // set when a position is out of range.
@@ -474,7 +537,7 @@ void attn_plan(int head_dim, int max_ctx, int& chunk, int& nsplit) {
 
 int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, const int32_t* pos, int n_query,
                      int n_head, int n_kv, int head_dim, int max_ctx, int chunk, int nsplit, float* part_o,
-                     float* part_ml, float* o, uint8_t* qx_o, hipStream_t stream) {
+                     float* part_ml, float* o, uint8_t* qx_o, hipStream_t stream, uint8_t* stage_o) {
   // traced: the interval from the split launch's start to the combine's end
   hipEvent_t t0, t1;
   (void)trace_events(NT_TRACE_ATTN, &t0, &t1);
@@ -492,8 +555,14 @@ int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, con
     default: return NT_EUNSUPPORTED;
   }
 #undef NT_ATTN_CASE
-  hipExtLaunchKernelGGL(k_attn_combine, dim3(n_head * (head_dim / 32), n_query), dim3(256), 0, stream, nullptr, t1, 0,
-                        part_o, part_ml, pos, n_head, head_dim, chunk, nsplit, max_ctx, o, qx_o);
+  if (stage_o) {
+    if ((n_head * head_dim) % 256 != 0 || qx_o) return NT_EINVAL;
+    hipExtLaunchKernelGGL(k_attn_combine_st, dim3(n_head * head_dim / 256, n_query), dim3(1024), 0, stream, nullptr, t1,
+                          0, part_o, part_ml, pos, n_head, head_dim, chunk, nsplit, max_ctx, o, stage_o);
+  } else {
+    hipExtLaunchKernelGGL(k_attn_combine, dim3(n_head * (head_dim / 32), n_query), dim3(256), 0, stream, nullptr, t1, 0,
+                          part_o, part_ml, pos, n_head, head_dim, chunk, nsplit, max_ctx, o, qx_o);
+  }
   return hipGetLastError() == hipSuccess ? NT_OK : NT_EHIP;
 }
 

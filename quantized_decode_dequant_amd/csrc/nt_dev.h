@@ -178,5 +178,57 @@ __device__ __forceinline__ void qx_store_block32(uint8_t* q, int64_t n, int b, i
   }
 }
 
+// The first 256 threads of a block stage one 256-block of an activation row
+// for the small-M GEMM (the layout k_stage_m writes over `ncols` columns at
+// `stage`): thread i holds element R = 256 b + i of token t with value gv
+// (already times any gains); one fixed-point scale for the 256-block, X =
+// 256 hi + lo in the MFMA B layout (column 2t + plane), the X sums of each
+// 32-block's two 16-element halves; with ss (may be null) also the sum of
+// squares of the values y, at ss[t * ncols / 256 + b].  Every thread of the
+// block calls it (threads past 256 only for the barriers).
+__device__ __forceinline__ void stage_block256(float gv, float y, int t, int R, int ncols, uint8_t* stage, float* ss) {
+  __shared__ float red[8];
+  __shared__ uint32_t hw[64], lw[64];  // the hi and lo bytes of the 256 values
+  __shared__ int xv[256];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (wv < 4) {
+    const float ws = wave_sum(y * y), wm = wave_max(fabsf(gv));
+    if (lane == 0) {
+      red[wv] = ws;
+      red[4 + wv] = wm;
+    }
+  }
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
+  if (tid < 256) {
+    const int X = fx_quant(gv, amax);
+    reinterpret_cast<uint8_t*>(hw)[tid] = (uint8_t)(fx_hi(X) & 255);
+    reinterpret_cast<uint8_t*>(lw)[tid] = (uint8_t)(fx_lo(X) & 255);
+    xv[tid] = X;
+  }
+  __syncthreads();
+  const int b0 = (R - tid) >> 5;  // the 256-block's first 32-block
+  const int64_t nb = ncols / 32;
+  int4* xs = reinterpret_cast<int4*>(stage + nb * 512);
+  float* xsc = reinterpret_cast<float*>(stage + nb * 512 + nb * kMaxTokens * 16);
+  if (tid < 128) {
+    // four values' bytes of one plane: column 2t + plane of lane (kq, ...)
+    const int q = tid & 63, pl = tid >> 6, b = b0 + (q >> 3), gi = q & 7;
+    *reinterpret_cast<uint32_t*>(stage + 512 * (int64_t)b + 128 * (gi >> 1) + 4 * (gi & 1) + 8 * (2 * t + pl)) =
+        pl ? lw[q] : hw[q];
+  } else if (tid < 136) {
+    const int j = tid - 128;
+    int s0 = 0, s1 = 0;
+    for (int k = 0; k < 16; ++k) {
+      s0 += xv[32 * j + k];
+      s1 += xv[32 * j + 16 + k];
+    }
+    xs[(int64_t)(b0 + j) * kMaxTokens + t] = make_int4(0, 0, s0, s1);
+  } else if (tid == 136) {
+    xsc[(int64_t)(b0 >> 3) * kMaxTokens + t] = amax / kXMax;
+    if (ss) ss[(int64_t)t * (ncols / 256) + (b0 >> 3)] = red[0] + red[1] + red[2] + red[3];
+  }
+}
+
 }  // namespace
 }  // namespace nt

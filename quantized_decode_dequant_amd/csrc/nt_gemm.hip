@@ -845,58 +845,6 @@ __global__ __launch_bounds__(kMaxThreads) void k_qgemm_m(JobM job) {
 }
 
 // ------------------------------------------------------------ reduce + epilogue
-// The outputs of one 256-thread block (256 consecutive rows of token t, a
-// 256-block of the next launch's activation) staged as k_stage_m stages an
-// activation row: the values times the gains (the RMSNorm factor is left to
-// the next reduce, see RedArgs), one scale for the 256-block, X = 256 hi +
-// lo in the MFMA B layout, the X sums of each 32-block's halves; with st_ss
-// also the sum of squares of the values themselves.
-__device__ __forceinline__ void stage_out(const RedArgs& ra, float v, int t, int R, int orows) {
-  __shared__ float red[8];
-  __shared__ uint32_t hw[64], lw[64];  // the hi and lo bytes of the 256 values
-  __shared__ int xv[256];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const float gv = ra.st_gain ? v * ra.st_gain[R] : v;
-  const float ws = wave_sum(v * v), wm = wave_max(fabsf(gv));
-  if (lane == 0) {
-    red[wv] = ws;
-    red[4 + wv] = wm;
-  }
-  __syncthreads();
-  const float amax = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
-  const float inv = amax > 0.f ? kXMax / amax : 0.f;
-  int X = __float2int_rn(gv * inv);
-  X = max(-32639, min(32639, X));
-  const int hi = (X + 128) >> 8;
-  const int lo = X - (hi << 8);
-  reinterpret_cast<uint8_t*>(hw)[tid] = (uint8_t)(hi & 255);
-  reinterpret_cast<uint8_t*>(lw)[tid] = (uint8_t)(lo & 255);
-  xv[tid] = X;
-  __syncthreads();
-  const int b0 = (R - tid) >> 5;  // the 256-block's first 32-block
-  const int64_t nb = orows / 32;
-  uint8_t* xb = static_cast<uint8_t*>(ra.st_stage);
-  int4* xs = reinterpret_cast<int4*>(xb + nb * 512);
-  float* xsc = reinterpret_cast<float*>(xb + nb * 512 + nb * kMaxTokens * 16);
-  if (tid < 128) {
-    // four values' bytes of one plane: column 2t + plane of lane (kq, ...)
-    const int q = tid & 63, pl = tid >> 6, b = b0 + (q >> 3), gi = q & 7;
-    *reinterpret_cast<uint32_t*>(xb + 512 * (int64_t)b + 128 * (gi >> 1) + 4 * (gi & 1) + 8 * (2 * t + pl)) =
-        pl ? lw[q] : hw[q];
-  } else if (tid < 136) {
-    const int j = tid - 128;
-    int s0 = 0, s1 = 0;
-    for (int k = 0; k < 16; ++k) {
-      s0 += xv[32 * j + k];
-      s1 += xv[32 * j + 16 + k];
-    }
-    xs[(int64_t)(b0 + j) * kMaxTokens + t] = make_int4(0, 0, s0, s1);
-  } else if (tid == 136) {
-    xsc[(int64_t)(b0 >> 3) * kMaxTokens + t] = amax / kXMax;
-    if (ra.st_ss) ra.st_ss[(int64_t)t * (orows / 256) + (b0 >> 3)] = red[0] + red[1] + red[2] + red[3];
-  }
-}
-
 // Adds the column ranges' partial sums in order and applies the epilogue for
 // (token, row) = thread (row pairs for EPI_QKV); see RedArgs for the RMSNorm
 // factor of a prestaged input and the staging of the outputs.
@@ -977,7 +925,9 @@ __global__ __launch_bounds__(256) void k_reduce_m(const float* __restrict__ part
       v = rn * total(t, R);
     }
     ea.y[t * ea.ld + R] = v;
-    if (ra.st_stage) stage_out(ra, v, t, R, orows);
+    // the outputs staged for the next small-M GEMM (times the next gains)
+    if (ra.st_stage)
+      stage_block256(ra.st_gain ? v * ra.st_gain[R] : v, v, t, R, orows, static_cast<uint8_t*>(ra.st_stage), ra.st_ss);
   }
 }
 

@@ -267,10 +267,12 @@ bool trace_events(int kind, hipEvent_t* start, hipEvent_t* stop);
 void attn_plan(int head_dim, int max_ctx, int& chunk, int& nsplit);
 // o [n_query][n_head * head_dim] fp32; with qx_o (may be null) each query's
 // output also goes out as a quantized activation of n_head * head_dim values
-// (qx_bytes apart per query).
+// (qx_bytes apart per query); with stage_o (may be null; n_head * head_dim a
+// multiple of 256, no qx_o) the outputs also go out staged for a small-M GEMM
+// (stage_m_bytes(n_head * head_dim) bytes).
 int launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, const int32_t* pos, int n_query,
                      int n_head, int n_kv, int head_dim, int max_ctx, int chunk, int nsplit, float* part_o,
-                     float* part_ml, float* o, uint8_t* qx_o, hipStream_t stream);
+                     float* part_ml, float* o, uint8_t* qx_o, hipStream_t stream, uint8_t* stage_o = nullptr);
 // Embedding rows of tokens[0..M) into x; also clears the status word *err
 // (may be null).  With qx (may be null) each row, times qx_gain, also goes
 // out as a quantized activation (qx_bytes(cols) apart per token).
