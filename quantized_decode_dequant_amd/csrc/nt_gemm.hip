@@ -852,9 +852,19 @@ template <int EPI>
 __global__ __launch_bounds__(256) void k_reduce_m(const float* __restrict__ part, int nsup, int M, int64_t ldp,
                                                   int orows, ProArgs pro, EpiArgs ea, RedArgs ra) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  // the column ranges' partial sums, added in order; the first 16 are
+  // loaded at once (predicated), so their latencies overlap
   auto total = [&](int t, int64_t R) {
+    const float* p = part + (int64_t)t * ldp + R;
+    const int64_t st = (int64_t)M * ldp;
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = k < nsup ? p[k * st] : 0.f;
     float s = 0.f;
-    for (int su = 0; su < nsup; ++su) s += part[((int64_t)su * M + t) * ldp + R];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k < nsup) s += v[k];
+    for (int su = 16; su < nsup; ++su) s += p[su * st];
     return s;
   };
   // token t's RMSNorm factor (1 where the staging applied it): four
