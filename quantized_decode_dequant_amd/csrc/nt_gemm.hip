@@ -10,20 +10,25 @@
 //             B operand of v_mfma_i32_16x16x32_i8 (column n = 2t + plane: hi,
 //             lo), 512 contiguous bytes per 32-block, followed by the X sums
 //             of each block's two 16-element halves per B column (zero in the
-//             hi-plane column) and the scales.
+//             hi-plane column) and the scales.  Within a layer the reduce
+//             launch before (and the attention combine) writes this layout
+//             directly where its rows are whole 256-blocks (stage_block256).
 //   product   One MFMA multiplies a 16-row x 32-weight tile of raw quants by
 //             every token and plane with exact int32 sums.  Adjacent columns
 //             are combined, S = 256 C_hi + C_lo (exact), and scaled:
 //             y += alpha_r * (s S) - beta_r * (s sum X), where alpha and beta
 //             are the row's scale and offset for that block in its format
 //             (Q6_K: per 16-weight half, two MFMAs with the other half zeroed).
-//             Up to four tokens fill only columns 0..7; over Q4_K and Q6_K
-//             one v_mfma_i32_16x16x64_i8 then takes two 32-blocks, the second
-//             block's activations in columns 8..15 (the paired form).
+//             Up to four tokens fill only columns 0..7: over Q4_K one
+//             v_mfma_i32_16x16x64_i8 then takes two 32-blocks, the second
+//             block's activations in columns 8..15 (the paired form); over
+//             Q6_K alone one 16x16x32 MFMA takes both 16-weight groups of a
+//             block, one per column half (the split form).
 //   stream    A wave streams tile-slices (16 rows x 256 columns: 16 row
-//             pieces) HBM -> registers -> its LDS slab with non-temporal
-//             16-byte loads, two in flight, as the GEMV engine streams
-//             segments.  A unit (one tile over one column range) accumulates
+//             pieces) HBM -> registers -> its LDS slab with 16-byte loads
+//             (cached, range-checked buffer loads where the rows are whole
+//             16-byte chunks apart), two in flight, as the GEMV engine
+//             streams segments.  A unit (one tile over one column range) accumulates
 //             in registers; units are claimed from an LDS counter inside the
 //             workgroup's share of tiles and land in a (row, column range,
 //             token) table that the epilogue adds in order (deterministic).
