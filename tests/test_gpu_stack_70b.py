@@ -192,6 +192,64 @@ def test_stack_70b_q4_k_m_teacher_forced():
         f"magnitude")
 
 
+# verify windows (M, first step): every step of each is posed at the bar
+VERIFY_WINDOWS = [(4, 0), (4, 28), (4, 36), (4, 44), (4, 52), (4, 60), (2, 0), (2, 30), (2, 50), (3, 1), (3, 33),
+                  (3, 55), (8, 28), (8, 40), (8, 56)]
+
+
+@pytest.mark.timeout(600)
+def test_stack_70b_q4_k_m_verify_passes_teacher_forced():
+    """Verify passes (M = 2, 3, 4 and 8: the engine per token, the paired /
+    split small-M forms and the plain one) over windows of the stored
+    trajectory.  The caches hold the oracle's rows of every step before the
+    window; a pass over the window's M input tokens appends the rows of its
+    own earlier tokens on the GPU, so row i starts from the oracle's state up
+    to the window and from the GPU's own rows inside it.  Each row is held to
+    the bar (logits within 5e-3 of the largest |logit|, the oracle's token);
+    the windows are chosen among steps whose conditioning estimate poses them
+    at the bar."""
+    import torch
+    dev = device()
+    g, kv, ref_logits, n = load_teacher()
+    hs = HostStack(wl.LLAMA70B, wl.Q4_K_M, n_layer=80, vocab=128256, max_ctx=N_PAST + n, n_past=N_PAST,
+                   wid=wl.W_STACK_70B)
+    h = hs.device_model(dev)
+    dls = h.keep["dls"]
+
+    def put_rows(s):
+        for l, d in enumerate(dls):
+            for c, cache in enumerate((d.k_cache, d.v_cache)):
+                cache[:, N_PAST + s, :] = torch.from_numpy(kv[s, l, c].view(np.int16)).to(dev)
+
+    for s in range(n):
+        put_rows(s)
+    worst = 0.0
+    for M, s0 in VERIFY_WINDOWS:
+        if s0 + M > n:
+            continue
+        steps = g["steps"][s0:s0 + M]
+        assert all(st.get("cond_err") is not None and st["cond_err"] <= TOL / 10 for st in steps), (M, s0)
+        ws = torch.zeros(h.workspace_bytes(M), dtype=torch.uint8, device=dev)
+        toks = torch.tensor([st["token_in"] for st in steps], dtype=torch.int32, device=dev)
+        pos = torch.tensor([N_PAST + s0], dtype=torch.int32, device=dev)
+        out = torch.zeros(M, dtype=torch.int32, device=dev)
+        lg = torch.zeros(M * hs.vocab, dtype=torch.float32, device=dev)
+        h.verify_step(toks, M, pos, out, ws, lg)
+        torch.cuda.synchronize()
+        got = lg.view(M, hs.vocab).cpu().numpy().astype(np.float64)
+        errs = [rel_inf(got[i], ref_logits[s0 + i]) for i in range(M)]
+        say(f"verify M={M} from step {s0}: logits within {['%.2e' % e for e in errs]}, tokens "
+            f"{out.cpu().numpy().tolist()} (oracle {[st['next'] for st in steps]})")
+        for i, st in enumerate(steps):
+            assert errs[i] <= TOL, (M, s0, i)
+            assert int(out[i].item()) == st["next"], (M, s0, i)
+        worst = max(worst, max(errs))
+        for i in range(M):
+            put_rows(s0 + i)  # the next window starts from the oracle's rows again
+        del ws
+    say(f"verify windows: logits within {worst:.2e} of the largest |logit| (bar {TOL}), every token the oracle's")
+
+
 @pytest.mark.timeout(600)
 def test_stack_70b_q4_k_m_free_running_record():
     import torch
